@@ -1,0 +1,145 @@
+"""Throughput of the SwiftKV prefill on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+One step = one skv_prefill call over the whole batch (every row of the hot
+path: layers 1..l for all prompt tokens, the fused skipped-layer KV GEMM,
+the last-token path through layers l+1..L and the LM head), inputs and
+weights already resident in HBM.  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "prefill tok/s + normalized TFLOPs (full-depth FLOPs/s), 8B & 70B SwiftKV-50%"
+MI355X_BF16_DENSE_TFLOPS = 2500.0   # 256 CU x 2.4 GHz x 4096 FLOP/clk/CU (dense, no sparsity)
+MI355X_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(workload, batch, cached, budget_prompt=None):
+    """Time the oracle on one prompt of the batch (the shortest) on the host cores."""
+    from threadpoolctl import threadpool_info
+    from oracle import swiftkv_oracle as O
+    from tests.helpers import dims_of, oracle_weights
+    b = int(np.argmin(batch.lengths)) if budget_prompt is None else budget_prompt
+    W = oracle_weights(workload, cached)
+    t0 = time.perf_counter()
+    O.swiftkv_prefill(dims_of(workload.shape), W, [batch.tokens[b]], workload.swiftkv_l, workload.acrosskv_g)
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    n = int(batch.lengths[b])
+    return {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"prompt {b} of the batch ({n} tokens), fp32 NumPy oracle, {dt:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama8b_l16_b16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import skv_inputs as si
+    from swiftkv_prefill_skipping_amd import _lib as L, runner
+    from tests.helpers import CachedLayers
+
+    w = si.WORKLOADS[args.workload]
+    batch = si.make_batch(w)
+    T, B = batch.total_tokens, len(batch.lengths)
+    log(f"[bench] workload {w.name}: {B} prompts, {T} tokens, lengths {list(batch.lengths)}")
+    cached = CachedLayers() if not args.no_cpu_baseline else None
+    t0 = time.time()
+    model = runner.load_seeded_model(w, T, B, batch.max_seqlen, layer_hook=cached.hook if cached else None)
+    log(f"[bench] weights generated and loaded in {time.time() - t0:.1f} s")
+    cache = runner.Cache(model, batch.num_blocks)
+    db = runner.device_batch(batch)
+    logits = torch.empty((B, w.shape.vocab), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    for i in range(args.warmup):
+        runner.prefill(model, cache, db, logits, stream)
+    torch.cuda.synchronize()
+    log("[bench] warmup done")
+
+    dominant = L.SKV_K_GEMM_GATEUP
+    L.skv_profile_enable(model.handle, dominant, True)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        runner.prefill(model, cache, db, logits, stream)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    prof = L.skv_profile_read(model.handle)
+    L.skv_profile_enable(model.handle, dominant, False)
+    ms = ev0.elapsed_time(ev1) / args.steps
+    log(f"[bench] {args.steps} steps: {ms:.3f} ms/step (events), {wall / args.steps * 1e3:.3f} ms/step (wall)")
+
+    full, swift = L.skv_flops(model.cfg, batch.lengths)
+    t = ms / 1e3
+    tok_s = T / t
+    norm_tf = full / t / 1e12
+    act_tf = swift / t / 1e12
+    avg_launch_ms = prof["total_ms"] / max(prof["launches"], 1)
+    flops_per_launch = prof["flops"] / max(prof["launches"], 1)
+    achieved = flops_per_launch / (avg_launch_ms / 1e3) / 1e12
+    res = {
+        "metric": METRIC,
+        "value": round(tok_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "description": "Llama-3.1-8B-shaped decoder (random init), SwiftKV l=16 of "
+                   "32 layers, 16 prompts with lengths uniform in [500,1000], uniform random token ids"
+                   if w.name == "llama8b_l16_b16" else w.name,
+                   "prompts": B, "prompt_tokens": T, "swiftkv_l": w.swiftkv_l, "acrosskv_g": w.acrosskv_g},
+        "normalized_tflops": round(norm_tf, 2),
+        "actual_tflops": round(act_tf, 2),
+        "normalized_frac_of_bf16_peak": round(norm_tf / MI355X_BF16_DENSE_TFLOPS, 4),
+        "actual_frac_of_bf16_peak": round(act_tf / MI355X_BF16_DENSE_TFLOPS, 4),
+        "flops_full_depth": full,
+        "flops_swiftkv": swift,
+        "roofline": {"kernel": "gemm_gateup (bf16 MFMA GEMM + SwiGLU epilogue)", "bound": "mfma",
+                     "achieved": round(achieved, 2), "peak": MI355X_BF16_DENSE_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / MI355X_BF16_DENSE_TFLOPS, 4), "traffic": None,
+                     "avg_launch_ms": round(avg_launch_ms, 4), "launches": prof["launches"],
+                     "flops_per_launch": flops_per_launch},
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the oracle on the host")
+        res["cpu_baseline"] = cpu_baseline(w, batch, cached)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,206 @@
+/*
+ * swiftkv.h -- C ABI of the MI355X (gfx950) SwiftKV prefill library.
+ *
+ * SwiftKV ("SwiftKV: Fast Prefill-Optimized Inference with Knowledge-
+ * Preserving Model Transformation", arXiv 2410.03960) rewires a Llama-style
+ * GQA decoder so that prompt tokens run only layers 1..l.  After layer l the
+ * KV cache of every later layer j is computed from the one hidden state
+ * x_{l+1} (summary page, section 3.4, Eq. 2: KV_j = W_KV^j . x_{l+1}), and
+ * only the last prompt token continues through layers l+1..L to produce the
+ * first-token logits (section 3.4, "What the first generated token does
+ * differently").  AcrossKV (section 3.4, Eq. KV_group) lets each group of g
+ * consecutive skipped layers share one KV tensor.  The paper's section 3.5
+ * ("Optimized Implementation for Inference", quoted on the
+ * AI_PARSE_DOCUMENT page) states the serving form: after layer l the KV of
+ * the remaining layers is computed at once and the prompt tokens exit.
+ *
+ * Everything is asynchronous on the caller's HIP stream except where a
+ * function says it is synchronous.  No C++ exception crosses this ABI; every
+ * failure returns a negative skv_status and leaves a message readable through
+ * skv_last_error() on the calling thread.
+ *
+ * Conventions
+ *   - "device" pointers are HIP device memory of the current device; "host"
+ *     pointers are ordinary CPU memory.  Weight pointers may be either (the
+ *     copy direction is inferred from unified addressing).
+ *   - Linear weights are row-major [out_features, in_features] (output row n
+ *     holds the n-th weight vector), RMSNorm gains are [d_model].
+ *   - bf16 tensors are raw IEEE bfloat16 bit patterns (uint16_t).
+ *   - Layers are numbered 1..n_layers.
+ */
+#ifndef SWIFTKV_H_
+#define SWIFTKV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SKV_OK = 0,
+  SKV_ERR_INVALID_ARG = -1, /* argument or shape check failed on the host; nothing was enqueued */
+  SKV_ERR_OOM = -2,         /* device allocation failed */
+  SKV_ERR_HIP = -3,         /* a HIP runtime call or kernel launch failed */
+  SKV_ERR_UNSUPPORTED = -4  /* valid but not implemented for this shape/dtype */
+} skv_status;
+
+typedef enum { SKV_BF16 = 0, SKV_FP32 = 1 } skv_dtype;
+
+/* Model description.  The transformation is the one of section 3.4:
+ * swiftkv_l = number of layers every prompt token runs (0..n_layers;
+ * n_layers means no skipping, 0 means every layer's KV comes from the
+ * embeddings), acrosskv_g = AcrossKV group size (1 = no merging).
+ * Groups are consecutive skipped layers l+1..l+g, l+g+1..l+2g, ...; the
+ * first layer of a group is its representative; a short last group is
+ * allowed.
+ * dtype SKV_BF16: bf16 weights, activations and KV cache, fp32 accumulation,
+ * fp32 residual stream, fp32 logits.  SKV_FP32: fp32 throughout.
+ * max_tokens / max_batch / max_seqlen size the workspace reserved at create
+ * time: a skv_prefill call may carry at most max_tokens prompt tokens in at
+ * most max_batch prompts of at most max_seqlen tokens each. */
+typedef struct {
+  int32_t n_layers, d_model, n_q_heads, n_kv_heads, head_dim, ffn_dim, vocab;
+  float rope_theta; /* RoPE base: pair i of a head rotates by pos * theta^(-2i/head_dim) */
+  float rms_eps;    /* RMSNorm epsilon */
+  int32_t swiftkv_l;
+  int32_t acrosskv_g;
+  int32_t dtype; /* skv_dtype */
+  int32_t max_tokens, max_batch, max_seqlen;
+} skv_model_config;
+
+typedef struct skv_model skv_model;
+typedef struct skv_kv_cache skv_kv_cache;
+
+/* One layer's weights, dtype = the model's dtype.  For a skipped layer
+ * (layer > swiftkv_l) wk/wv are read only if the layer is its AcrossKV
+ * group's representative and may be NULL otherwise. */
+typedef struct {
+  const void *attn_norm, *wq, *wk, *wv, *wo, *ffn_norm, *w_gate, *w_up, *w_down;
+} skv_layer_weights;
+
+/* Validate cfg and reserve device memory for weights and workspace on the
+ * current device.  Synchronous.  Errors: INVALID_ARG (bad dims, l outside
+ * 0..n_layers, g < 1, head counts not dividing), UNSUPPORTED (bf16 needs
+ * head_dim 128, q heads per kv head a multiple of 4, d_model and ffn_dim
+ * multiples of 128, max_batch <= 32), OOM. */
+skv_status skv_model_create(const skv_model_config* cfg, skv_model** out);
+
+/* Copy the embedding [vocab, d_model], the final RMSNorm gain [d_model] and
+ * the (untied) LM head [vocab, d_model] into the model.  Synchronous; the
+ * caller's buffers may be reused when it returns. */
+skv_status skv_model_load_globals(skv_model* m, const void* embed, const void* final_norm, const void* lm_head);
+
+/* Copy layer `layer`'s weights into the model and repack them on the
+ * device: Q/K/V rows concatenated for unskipped layers; gate and up rows
+ * interleaved; for an AcrossKV representative j > l, its input-RMSNorm gain
+ * folded into its K and V rows (W~ = W_KV diag(gamma_j), exact in real
+ * arithmetic: RMSNorm(x; gamma) W^T = r (x (W diag gamma)^T) with
+ * r = 1/sqrt(mean x^2 + eps)).  Synchronous. */
+skv_status skv_model_load_layer(skv_model* m, int32_t layer, const skv_layer_weights* w);
+
+/* Free everything the model owns.  Accepts NULL. */
+void skv_model_destroy(skv_model* m);
+
+/* Paged KV cache for the model: num_kv_slots(m) slots (swiftkv_l unskipped
+ * layers + one per AcrossKV group), each holding num_blocks blocks of
+ * block_size token positions for every kv head.  block_size must be 16.
+ * Zero-filled at creation.  Synchronous. */
+skv_status skv_kv_cache_create(const skv_model* m, int32_t num_blocks, int32_t block_size, skv_kv_cache** out);
+void skv_kv_cache_destroy(skv_kv_cache* c);
+int32_t skv_num_kv_slots(const skv_model* m);
+
+/* Non-owning strided view of one cache tensor, valid until the cache is
+ * destroyed.  Element (i0, i1, i2, i3) lives at data + sum_k i_k*stride[k]
+ * elements. */
+typedef struct {
+  void* data;
+  int32_t dtype; /* skv_dtype */
+  int32_t ndim;
+  int64_t shape[4];
+  int64_t stride[4];
+} skv_tensor_view;
+
+/* K and V of layer `layer` (1-based).  Layers of one AcrossKV group return
+ * the same memory.  Layout:
+ *   K: [num_blocks, n_kv_heads, block_size, head_dim]
+ *   V: [num_blocks, n_kv_heads, head_dim, block_size]  (keys innermost)
+ * Token position p of a prompt with block table row bt lives in block
+ * bt[p / block_size] at offset p % block_size.  K holds RoPE-rotated keys. */
+skv_status skv_kv_cache_view(const skv_kv_cache* c, int32_t layer, skv_tensor_view* k, skv_tensor_view* v);
+
+/* A batch of independent prompts packed back to back (varlen).
+ * cu_seqlens[b]..cu_seqlens[b+1] are prompt b's tokens; every prompt has at
+ * least one token.  block_tables is [batch, max_blocks_per_seq] physical
+ * block ids; prompt b needs ceil(len_b / block_size) valid entries.  The
+ * host copies are used for validation and launch geometry and must hold the
+ * same values as the device copies. */
+typedef struct {
+  int32_t batch;
+  int32_t total_tokens;
+  int32_t max_seqlen;
+  int32_t max_blocks_per_seq;
+  const int32_t* cu_seqlens_host;   /* host   [batch + 1] */
+  const int32_t* block_tables_host; /* host   [batch * max_blocks_per_seq] */
+  const int32_t* token_ids;         /* device [total_tokens], ids in [0, vocab) */
+  const int32_t* cu_seqlens;        /* device [batch + 1] */
+  const int32_t* block_tables;      /* device [batch * max_blocks_per_seq] */
+} skv_batch;
+
+/* SwiftKV prefill (section 3.4 "Inference Implementation"; section 3.5):
+ *  1. every prompt token runs layers 1..l (RMSNorm, QKV + RoPE, causal GQA
+ *     attention, O + residual, RMSNorm, SwiGLU MLP + residual), its K/V
+ *     written to slots 0..l-1;
+ *  2. one GEMM of x_{l+1} (RMS-normalised) against the concatenated folded
+ *     K/V rows of every AcrossKV group (Eq. 2 / Eq. KV_group) writes, after
+ *     RoPE on K, the KV of slots l..l+G-1 for every token, the last included;
+ *  3. the last token of each prompt runs layers l+1..L, attending at layer j
+ *     to the N positions of its slot;
+ *  4. logits[b, :] = RMSNorm(y_b; final gain) W_lm^T in fp32.
+ * Writes the cache positions the batch covers and logits (device, fp32,
+ * [batch, vocab]).  Asynchronous on `stream` (a hipStream_t, NULL = the
+ * default stream); the caller synchronises.  Every layer must have been
+ * loaded.  Errors (host-side, nothing enqueued): INVALID_ARG for
+ * inconsistent cu_seqlens, an empty prompt, total_tokens > max_tokens,
+ * batch > max_batch, a prompt longer than max_seqlen, a block table entry
+ * outside [0, num_blocks) or too few blocks; HIP on launch failure. */
+skv_status skv_prefill(skv_model* m, skv_kv_cache* c, const skv_batch* batch, float* logits, void* stream);
+
+/* Closed-form FLOPs of a prefill over prompts of the given lengths (host
+ * array).  full = the unmodified model (all layers for every token, LM head
+ * for the last token); swiftkv = layers 1..l for every token, one K/V
+ * projection per group for every token, layers l+1..L for the last token.
+ * Matmuls count 2mnk, attention 4*ctx*head_dim per query per head. */
+skv_status skv_flops(const skv_model_config* cfg, const int32_t* seqlens, int32_t batch, double* full,
+                     double* swiftkv);
+
+/* Kernel classes that skv_profile_* can time. */
+typedef enum {
+  SKV_K_GEMM_QKV = 0,
+  SKV_K_ATTN_PREFILL = 1,
+  SKV_K_GEMM_O = 2,
+  SKV_K_GEMM_GATEUP = 3,
+  SKV_K_GEMM_DOWN = 4,
+  SKV_K_GEMM_KVSKIP = 5,
+  SKV_K_RMSNORM = 6,
+  SKV_K_LAST_TOKEN = 7,
+  SKV_K_NUM = 8
+} skv_kernel_class;
+
+/* Bracket every launch of one kernel class with HIP events on the prefill
+ * stream (enable != 0) or stop doing so.  Clears earlier records. */
+skv_status skv_profile_enable(skv_model* m, int32_t kernel_class, int32_t enable);
+
+/* Synchronise the recorded events and report, over the launches of the
+ * enabled class since skv_profile_enable: total device time (ms), launch
+ * count, algorithmic FLOPs and algorithmic HBM bytes of those launches. */
+skv_status skv_profile_read(skv_model* m, double* total_ms, int64_t* launches, double* flops, double* bytes);
+
+/* Message of the last failure on this thread ("" if none). */
+const char* skv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SWIFTKV_H_ */

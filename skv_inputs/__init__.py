@@ -312,7 +312,7 @@ def make_batch(w: Workload, lengths: Optional[List[int]] = None, shuffle: Option
     return Batch(lengths, toks, w.block_size, bt, nblk)
 
 
-def small_workload(name: str, *, n_layers=4, d_model=512, n_q_heads=8, n_kv_heads=2, head_dim=128, ffn_dim=1408,
+def small_workload(name: str, *, n_layers=4, d_model=512, n_q_heads=8, n_kv_heads=2, head_dim=128, ffn_dim=1536,
                    vocab=2048, rope_theta=500000.0, dtype="bf16", l=2, g=1, lengths=(100,), seed=11,
                    shuffle=False, gain="normal", weight_seed=101) -> Workload:
     """A small model for parity tests that still spans several kernel tiles."""

@@ -1,0 +1,677 @@
+// C ABI of libswiftkv: model and cache objects, load-time repacking,
+// host-side validation and the prefill launch sequence.
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <string>
+#include <vector>
+
+#include "../../include/swiftkv.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+skv_status fail(skv_status s, const std::string& msg) {
+  g_err = msg;
+  return s;
+}
+
+#define SKV_HIP(call)                                                                         \
+  do {                                                                                        \
+    hipError_t e_ = (call);                                                                   \
+    if (e_ != hipSuccess)                                                                     \
+      return fail(SKV_ERR_HIP, std::string(#call) + ": " + hipGetErrorString(e_));            \
+  } while (0)
+
+int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+}  // namespace
+
+struct LayerDev {
+  float* attn_norm = nullptr;  // fp32 [d]
+  float* ffn_norm = nullptr;
+  void* wqkv = nullptr;  // unskipped: [dq + 2 dkv, d]; skipped: [dq, d]
+  void* wo = nullptr;    // [d, dq]
+  void* wgu = nullptr;   // [2f, d], gate/up interleaved in blocks of P_mlp rows
+  void* wdown = nullptr; // [d, f]
+  bool loaded = false;
+};
+
+struct ProfRec {
+  hipEvent_t a, b;
+};
+
+struct skv_model {
+  skv_model_config cfg;
+  bool bf16;
+  size_t esz;
+  int G;       // AcrossKV groups of skipped layers
+  int p_mlp;   // gate/up interleave distance
+  int dq, dkv;
+  std::vector<void*> allocs;
+
+  void* embed = nullptr;
+  void* lm_head = nullptr;
+  float* final_norm = nullptr;
+  float* rope_cos = nullptr;
+  float* rope_sin = nullptr;
+  bool globals_loaded = false;
+  std::vector<LayerDev> layers;
+  void* wkv_skip = nullptr;  // [G * 2 dkv, d]
+  void* staging = nullptr;
+  size_t staging_bytes = 0;
+  void* gamma_stage = nullptr;
+
+  // workspace
+  float* x = nullptr;
+  void* act = nullptr;
+  void* qbuf = nullptr;
+  void* obuf = nullptr;
+  void* hbuf = nullptr;
+  int32_t* pos = nullptr;
+  int32_t* slot = nullptr;
+  int32_t* seq = nullptr;
+  int32_t* last_pos = nullptr;
+  int32_t* last_row = nullptr;
+  int32_t* iota = nullptr;
+  float* y = nullptr;
+  void* ya = nullptr;
+  void* yq = nullptr;
+  void* yo = nullptr;
+  void* yh = nullptr;
+  float* partial = nullptr;
+  int64_t partial_elems = 0;
+  float* attn_ws = nullptr;
+  int64_t attn_ws_elems = 0;
+
+  // profiling
+  int prof_class = -1;
+  std::vector<ProfRec> prof;
+  double prof_flops = 0, prof_bytes = 0;
+};
+
+struct skv_kv_cache {
+  const skv_model* m;
+  int num_blocks, block_size, n_slots;
+  void* k;
+  void* v;
+  int64_t slot_elems;
+};
+
+namespace {
+
+template <typename T>
+skv_status dev_alloc(skv_model* m, T** p, size_t bytes) {
+  void* q = nullptr;
+  if (bytes == 0) bytes = 16;
+  if (hipMalloc(&q, bytes) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(SKV_ERR_OOM, "hipMalloc of " + std::to_string(bytes) + " bytes failed");
+  }
+  m->allocs.push_back(q);
+  *p = reinterpret_cast<T*>(q);
+  return SKV_OK;
+}
+
+#define SKV_TRY(x)                  \
+  do {                              \
+    skv_status s_ = (x);            \
+    if (s_ != SKV_OK) return s_;    \
+  } while (0)
+
+skv_status validate_config(const skv_model_config* c) {
+  if (!c) return fail(SKV_ERR_INVALID_ARG, "config is NULL");
+  if (c->n_layers < 1 || c->d_model < 1 || c->n_q_heads < 1 || c->n_kv_heads < 1 || c->head_dim < 2 ||
+      c->ffn_dim < 1 || c->vocab < 1)
+    return fail(SKV_ERR_INVALID_ARG, "model dimensions must be positive");
+  if (c->head_dim % 2) return fail(SKV_ERR_INVALID_ARG, "head_dim must be even (rotate-half RoPE)");
+  if (c->n_q_heads % c->n_kv_heads) return fail(SKV_ERR_INVALID_ARG, "n_q_heads must be a multiple of n_kv_heads");
+  if (c->swiftkv_l < 0 || c->swiftkv_l > c->n_layers)
+    return fail(SKV_ERR_INVALID_ARG, "swiftkv_l must lie in 0..n_layers");
+  if (c->acrosskv_g < 1) return fail(SKV_ERR_INVALID_ARG, "acrosskv_g must be >= 1");
+  if (c->dtype != SKV_BF16 && c->dtype != SKV_FP32) return fail(SKV_ERR_INVALID_ARG, "unknown dtype");
+  if (c->max_tokens < 1 || c->max_batch < 1 || c->max_seqlen < 1)
+    return fail(SKV_ERR_INVALID_ARG, "max_tokens, max_batch and max_seqlen must be positive");
+  if (!(c->rope_theta > 0.f) || !(c->rms_eps >= 0.f)) return fail(SKV_ERR_INVALID_ARG, "bad rope_theta or rms_eps");
+  if (c->d_model % 4) return fail(SKV_ERR_UNSUPPORTED, "d_model must be a multiple of 4");
+  if (c->n_q_heads / c->n_kv_heads > 16) return fail(SKV_ERR_UNSUPPORTED, "at most 16 q heads per kv head");
+  if (c->dtype == SKV_BF16) {
+    if (c->head_dim != 128) return fail(SKV_ERR_UNSUPPORTED, "bf16 path needs head_dim 128");
+    if ((c->n_q_heads / c->n_kv_heads) % 4) return fail(SKV_ERR_UNSUPPORTED, "bf16 path needs hq/hkv % 4 == 0");
+    if (c->d_model % 256 || c->ffn_dim % 256)
+      return fail(SKV_ERR_UNSUPPORTED, "bf16 path needs d_model and ffn_dim multiples of 256");
+    if (c->vocab % 128) return fail(SKV_ERR_UNSUPPORTED, "bf16 path needs vocab % 128 == 0");
+    if (c->max_batch > 32) return fail(SKV_ERR_UNSUPPORTED, "bf16 path supports at most 32 prompts per call");
+  } else {
+    if (c->head_dim != 32 && c->head_dim != 64 && c->head_dim != 128)
+      return fail(SKV_ERR_UNSUPPORTED, "fp32 path needs head_dim 32, 64 or 128");
+    if (c->d_model % 32 || c->ffn_dim % 16 || c->vocab % 32)
+      return fail(SKV_ERR_UNSUPPORTED, "fp32 path needs d_model % 32, ffn_dim % 16, vocab % 32 == 0");
+    if (c->n_q_heads / c->n_kv_heads > 16) return fail(SKV_ERR_UNSUPPORTED, "at most 16 q heads per kv head");
+  }
+  return SKV_OK;
+}
+
+int slot_of_layer(const skv_model_config& c, int j) {
+  return j <= c.swiftkv_l ? j - 1 : c.swiftkv_l + (j - c.swiftkv_l - 1) / c.acrosskv_g;
+}
+bool is_representative(const skv_model_config& c, int j) {
+  return j > c.swiftkv_l && (j - c.swiftkv_l - 1) % c.acrosskv_g == 0;
+}
+
+struct Prof {
+  skv_model* m;
+  bool on;
+  hipEvent_t a{}, b{};
+  hipStream_t s;
+  Prof(skv_model* m_, int cls, hipStream_t s_, double flops, double bytes) : m(m_), on(m_->prof_class == cls), s(s_) {
+    if (on) {
+      hipEventCreate(&a);
+      hipEventCreate(&b);
+      hipEventRecord(a, s);
+      m->prof_flops += flops;
+      m->prof_bytes += bytes;
+    }
+  }
+  ~Prof() {
+    if (on) {
+      hipEventRecord(b, s);
+      m->prof.push_back({a, b});
+    }
+  }
+};
+
+double gemm_bytes(double M, double N, double K, double esz, double out_bytes_per) {
+  return (M * K + N * K) * esz + M * N * out_bytes_per;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* skv_last_error(void) { return g_err.c_str(); }
+
+skv_status skv_flops(const skv_model_config* c, const int32_t* seqlens, int32_t batch, double* full, double* swift) {
+  SKV_TRY(validate_config(c));
+  if (batch < 0 || (batch > 0 && !seqlens) || !full || !swift) return fail(SKV_ERR_INVALID_ARG, "bad arguments");
+  const double d = c->d_model, dq = (double)c->n_q_heads * c->head_dim, dkv = (double)c->n_kv_heads * c->head_dim;
+  const double f = c->ffn_dim, V = c->vocab, L = c->n_layers, l = c->swiftkv_l, hq = c->n_q_heads,
+               dh = c->head_dim;
+  const double G = ceil_div(c->n_layers - c->swiftkv_l, c->acrosskv_g);
+  const double lin = 2 * d * dq + 2 * dq * d + 6 * d * f + 4 * d * dkv;
+  double F = 0, S = 0;
+  for (int b = 0; b < batch; ++b) {
+    const double n = seqlens[b];
+    const double layer_full = n * lin + 2 * n * (n + 1) * dh * hq;
+    F += L * layer_full + 2 * d * V;
+    S += l * layer_full + G * n * 4 * d * dkv + (L - l) * (2 * d * dq + 2 * dq * d + 6 * d * f + 4 * n * dh * hq) +
+         2 * d * V;
+  }
+  *full = F;
+  *swift = S;
+  return SKV_OK;
+}
+
+skv_status skv_model_create(const skv_model_config* cfg, skv_model** out) {
+  if (!out) return fail(SKV_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  SKV_TRY(validate_config(cfg));
+  skv_model* m = new skv_model();
+  m->cfg = *cfg;
+  const auto& c = m->cfg;
+  m->bf16 = c.dtype == SKV_BF16;
+  m->esz = m->bf16 ? 2 : 4;
+  m->G = ceil_div(c.n_layers - c.swiftkv_l, c.acrosskv_g);
+  m->p_mlp = m->bf16 ? 64 : 16;
+  m->dq = c.n_q_heads * c.head_dim;
+  m->dkv = c.n_kv_heads * c.head_dim;
+  m->layers.resize(c.n_layers);
+  const size_t d = c.d_model, dq = m->dq, dkv = m->dkv, f = c.ffn_dim, V = c.vocab, E = m->esz;
+  const size_t T = c.max_tokens, B = c.max_batch;
+  auto bail = [&](skv_status s) {
+    std::string msg = g_err;
+    skv_model_destroy(m);
+    g_err = msg;
+    return s;
+  };
+#define ALLOC(p, bytes)                                \
+  do {                                                 \
+    skv_status s_ = dev_alloc(m, &(p), (bytes));       \
+    if (s_ != SKV_OK) return bail(s_);                 \
+  } while (0)
+  ALLOC(m->embed, V * d * E);
+  ALLOC(m->lm_head, V * d * E);
+  ALLOC(m->final_norm, d * 4);
+  const size_t half = c.head_dim / 2;
+  ALLOC(m->rope_cos, (size_t)c.max_seqlen * half * 4);
+  ALLOC(m->rope_sin, (size_t)c.max_seqlen * half * 4);
+  for (int i = 1; i <= c.n_layers; ++i) {
+    LayerDev& L = m->layers[i - 1];
+    ALLOC(L.attn_norm, d * 4);
+    ALLOC(L.ffn_norm, d * 4);
+    ALLOC(L.wqkv, (i <= c.swiftkv_l ? dq + 2 * dkv : dq) * d * E);
+    ALLOC(L.wo, d * dq * E);
+    ALLOC(L.wgu, 2 * f * d * E);
+    ALLOC(L.wdown, d * f * E);
+  }
+  if (m->G > 0) ALLOC(m->wkv_skip, (size_t)m->G * 2 * dkv * d * E);
+  m->staging_bytes = std::max(2 * f * d, 2 * dkv * d) * E;
+  ALLOC(m->staging, m->staging_bytes);
+  ALLOC(m->gamma_stage, d * E);
+
+  ALLOC(m->x, T * d * 4);
+  ALLOC(m->act, T * d * E);
+  ALLOC(m->qbuf, T * dq * E);
+  ALLOC(m->obuf, T * dq * E);
+  ALLOC(m->hbuf, T * f * E);
+  ALLOC(m->pos, T * 4);
+  ALLOC(m->slot, T * 4);
+  ALLOC(m->seq, T * 4);
+  ALLOC(m->last_pos, B * 4);
+  ALLOC(m->last_row, B * 4);
+  ALLOC(m->iota, B * 4);
+  ALLOC(m->y, B * d * 4);
+  ALLOC(m->ya, B * d * E);
+  ALLOC(m->yq, B * dq * E);
+  ALLOC(m->yo, B * dq * E);
+  ALLOC(m->yh, B * f * E);
+  if (m->bf16) {
+    int64_t pe = 0;
+    pe = std::max(pe, skinny_partial_elems((int)dq, (int)d));
+    pe = std::max(pe, skinny_partial_elems((int)d, (int)dq));
+    pe = std::max(pe, skinny_partial_elems((int)(2 * f), (int)d));
+    pe = std::max(pe, skinny_partial_elems((int)d, (int)f));
+    pe = std::max(pe, skinny_partial_elems((int)V, (int)d));
+    m->partial_elems = pe;
+    ALLOC(m->partial, (size_t)pe * 4);
+    m->attn_ws_elems = attn_rows_ws_elems((int)B, c.max_seqlen, c.n_q_heads, c.head_dim);
+  } else {
+    m->attn_ws_elems = attn_rows_ws_elems((int)std::max(T, B), c.max_seqlen, c.n_q_heads, c.head_dim);
+  }
+  ALLOC(m->attn_ws, (size_t)m->attn_ws_elems * 4);
+#undef ALLOC
+
+  // RoPE tables: angle p * theta^(-2i/dh) in double, cos/sin rounded to fp32
+  {
+    std::vector<float> cs((size_t)c.max_seqlen * half), sn((size_t)c.max_seqlen * half);
+    for (size_t i = 0; i < half; ++i) {
+      const double inv = pow((double)c.rope_theta, -2.0 * (double)i / (double)c.head_dim);
+      for (size_t p = 0; p < (size_t)c.max_seqlen; ++p) {
+        const double a = (double)p * inv;
+        cs[p * half + i] = (float)cos(a);
+        sn[p * half + i] = (float)sin(a);
+      }
+    }
+    if (hipMemcpy(m->rope_cos, cs.data(), cs.size() * 4, hipMemcpyHostToDevice) != hipSuccess ||
+        hipMemcpy(m->rope_sin, sn.data(), sn.size() * 4, hipMemcpyHostToDevice) != hipSuccess)
+      return bail(fail(SKV_ERR_HIP, "uploading RoPE tables failed"));
+    std::vector<int32_t> io(B);
+    for (size_t b = 0; b < B; ++b) io[b] = (int32_t)b;
+    if (hipMemcpy(m->iota, io.data(), B * 4, hipMemcpyHostToDevice) != hipSuccess)
+      return bail(fail(SKV_ERR_HIP, "upload failed"));
+  }
+  *out = m;
+  return SKV_OK;
+}
+
+void skv_model_destroy(skv_model* m) {
+  if (!m) return;
+  for (auto& r : m->prof) {
+    hipEventDestroy(r.a);
+    hipEventDestroy(r.b);
+  }
+  for (void* p : m->allocs) (void)hipFree(p);
+  delete m;
+}
+
+static skv_status copy_in(void* dst, const void* src, size_t bytes, const char* what) {
+  if (!src) return fail(SKV_ERR_INVALID_ARG, std::string(what) + " is NULL");
+  SKV_HIP(hipMemcpy(dst, src, bytes, hipMemcpyDefault));
+  return SKV_OK;
+}
+
+static skv_status gain_to_f32(skv_model* m, const void* src, float* dst, const char* what) {
+  const size_t d = m->cfg.d_model;
+  SKV_TRY(copy_in(m->gamma_stage, src, d * m->esz, what));
+  if (m->bf16)
+    SKV_HIP(launch_to_f32<bf16_t>((const bf16_t*)m->gamma_stage, (int64_t)d, dst, 0));
+  else
+    SKV_HIP(launch_to_f32<float>((const float*)m->gamma_stage, (int64_t)d, dst, 0));
+  SKV_HIP(hipDeviceSynchronize());
+  return SKV_OK;
+}
+
+skv_status skv_model_load_globals(skv_model* m, const void* embed, const void* final_norm, const void* lm_head) {
+  if (!m) return fail(SKV_ERR_INVALID_ARG, "model is NULL");
+  const size_t d = m->cfg.d_model, V = m->cfg.vocab;
+  SKV_TRY(copy_in(m->embed, embed, V * d * m->esz, "embed"));
+  SKV_TRY(copy_in(m->lm_head, lm_head, V * d * m->esz, "lm_head"));
+  SKV_TRY(gain_to_f32(m, final_norm, m->final_norm, "final_norm"));
+  m->globals_loaded = true;
+  return SKV_OK;
+}
+
+skv_status skv_model_load_layer(skv_model* m, int32_t layer, const skv_layer_weights* w) {
+  if (!m || !w) return fail(SKV_ERR_INVALID_ARG, "NULL argument");
+  const auto& c = m->cfg;
+  if (layer < 1 || layer > c.n_layers) return fail(SKV_ERR_INVALID_ARG, "layer outside 1..n_layers");
+  LayerDev& L = m->layers[layer - 1];
+  const size_t d = c.d_model, dq = m->dq, dkv = m->dkv, f = c.ffn_dim, E = m->esz;
+  char* qkv = (char*)L.wqkv;
+  SKV_TRY(gain_to_f32(m, w->ffn_norm, L.ffn_norm, "ffn_norm"));
+  SKV_TRY(gain_to_f32(m, w->attn_norm, L.attn_norm, "attn_norm"));  // leaves gamma_stage = attn gain
+  SKV_TRY(copy_in(qkv, w->wq, dq * d * E, "wq"));
+  if (layer <= c.swiftkv_l) {
+    SKV_TRY(copy_in(qkv + dq * d * E, w->wk, dkv * d * E, "wk"));
+    SKV_TRY(copy_in(qkv + (dq + dkv) * d * E, w->wv, dkv * d * E, "wv"));
+  } else if (is_representative(c, layer)) {
+    // fold this layer's input-RMSNorm gain into its K and V rows
+    const int grp = (layer - c.swiftkv_l - 1) / c.acrosskv_g;
+    char* dst = (char*)m->wkv_skip + (size_t)grp * 2 * dkv * d * E;
+    SKV_TRY(copy_in(m->staging, w->wk, dkv * d * E, "wk"));
+    SKV_TRY(copy_in((char*)m->staging + dkv * d * E, w->wv, dkv * d * E, "wv"));
+    if (m->bf16)
+      SKV_HIP(launch_fold_rows<bf16_t>((const bf16_t*)m->staging, (const bf16_t*)m->gamma_stage, (int)(2 * dkv),
+                                       (int)d, (bf16_t*)dst, 0));
+    else
+      SKV_HIP(launch_fold_rows<float>((const float*)m->staging, (const float*)m->gamma_stage, (int)(2 * dkv), (int)d,
+                                      (float*)dst, 0));
+    SKV_HIP(hipDeviceSynchronize());
+  }
+  SKV_TRY(copy_in(L.wo, w->wo, d * dq * E, "wo"));
+  SKV_TRY(copy_in(L.wdown, w->w_down, d * f * E, "w_down"));
+  SKV_TRY(copy_in(m->staging, w->w_gate, f * d * E, "w_gate"));
+  SKV_TRY(copy_in((char*)m->staging + f * d * E, w->w_up, f * d * E, "w_up"));
+  if (m->bf16)
+    SKV_HIP(launch_interleave<bf16_t>((const bf16_t*)m->staging, (const bf16_t*)m->staging + f * d, (int)f, (int)d,
+                                      m->p_mlp, (bf16_t*)L.wgu, 0));
+  else
+    SKV_HIP(launch_interleave<float>((const float*)m->staging, (const float*)m->staging + f * d, (int)f, (int)d,
+                                     m->p_mlp, (float*)L.wgu, 0));
+  SKV_HIP(hipDeviceSynchronize());
+  L.loaded = true;
+  return SKV_OK;
+}
+
+int32_t skv_num_kv_slots(const skv_model* m) { return m ? m->cfg.swiftkv_l + m->G : 0; }
+
+skv_status skv_kv_cache_create(const skv_model* m, int32_t num_blocks, int32_t block_size, skv_kv_cache** out) {
+  if (!m || !out) return fail(SKV_ERR_INVALID_ARG, "NULL argument");
+  *out = nullptr;
+  if (block_size != kBlockSize) return fail(SKV_ERR_UNSUPPORTED, "block_size must be 16");
+  if (num_blocks < 1) return fail(SKV_ERR_INVALID_ARG, "num_blocks must be positive");
+  const int n_slots = skv_num_kv_slots(m);
+  const int64_t slot_elems = (int64_t)num_blocks * m->cfg.n_kv_heads * block_size * m->cfg.head_dim;
+  const size_t bytes = (size_t)slot_elems * n_slots * m->esz;
+  void *k = nullptr, *v = nullptr;
+  if (hipMalloc(&k, bytes) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(SKV_ERR_OOM, "KV cache allocation failed");
+  }
+  if (hipMalloc(&v, bytes) != hipSuccess) {
+    (void)hipGetLastError();
+    (void)hipFree(k);
+    return fail(SKV_ERR_OOM, "KV cache allocation failed");
+  }
+  if (hipMemset(k, 0, bytes) != hipSuccess || hipMemset(v, 0, bytes) != hipSuccess ||
+      hipDeviceSynchronize() != hipSuccess) {
+    (void)hipFree(k);
+    (void)hipFree(v);
+    return fail(SKV_ERR_HIP, "KV cache clear failed");
+  }
+  *out = new skv_kv_cache{m, num_blocks, block_size, n_slots, k, v, slot_elems};
+  return SKV_OK;
+}
+
+void skv_kv_cache_destroy(skv_kv_cache* c) {
+  if (!c) return;
+  (void)hipFree(c->k);
+  (void)hipFree(c->v);
+  delete c;
+}
+
+skv_status skv_kv_cache_view(const skv_kv_cache* c, int32_t layer, skv_tensor_view* k, skv_tensor_view* v) {
+  if (!c || !k || !v) return fail(SKV_ERR_INVALID_ARG, "NULL argument");
+  const auto& cfg = c->m->cfg;
+  if (layer < 1 || layer > cfg.n_layers) return fail(SKV_ERR_INVALID_ARG, "layer outside 1..n_layers");
+  const int s = slot_of_layer(cfg, layer);
+  const int64_t nb = c->num_blocks, hkv = cfg.n_kv_heads, bs = c->block_size, dh = cfg.head_dim;
+  const size_t off = (size_t)s * c->slot_elems * c->m->esz;
+  *k = skv_tensor_view{(char*)c->k + off, cfg.dtype, 4, {nb, hkv, bs, dh}, {hkv * bs * dh, bs * dh, dh, 1}};
+  *v = skv_tensor_view{(char*)c->v + off, cfg.dtype, 4, {nb, hkv, dh, bs}, {hkv * dh * bs, dh * bs, bs, 1}};
+  return SKV_OK;
+}
+
+skv_status skv_profile_enable(skv_model* m, int32_t kernel_class, int32_t enable) {
+  if (!m) return fail(SKV_ERR_INVALID_ARG, "model is NULL");
+  if (kernel_class < 0 || kernel_class >= SKV_K_NUM) return fail(SKV_ERR_INVALID_ARG, "unknown kernel class");
+  for (auto& r : m->prof) {
+    hipEventDestroy(r.a);
+    hipEventDestroy(r.b);
+  }
+  m->prof.clear();
+  m->prof_flops = m->prof_bytes = 0;
+  m->prof_class = enable ? kernel_class : -1;
+  return SKV_OK;
+}
+
+skv_status skv_profile_read(skv_model* m, double* total_ms, int64_t* launches, double* flops, double* bytes) {
+  if (!m || !total_ms || !launches || !flops || !bytes) return fail(SKV_ERR_INVALID_ARG, "NULL argument");
+  double t = 0;
+  for (auto& r : m->prof) {
+    SKV_HIP(hipEventSynchronize(r.b));
+    float ms = 0;
+    SKV_HIP(hipEventElapsedTime(&ms, r.a, r.b));
+    t += ms;
+  }
+  *total_ms = t;
+  *launches = (int64_t)m->prof.size();
+  *flops = m->prof_flops;
+  *bytes = m->prof_bytes;
+  return SKV_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+template <typename T>
+skv_status run_prefill(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, float* logits, int max_len,
+                       hipStream_t s) {
+  const auto& c = m->cfg;
+  const int T_ = bt->total_tokens, B = bt->batch, d = c.d_model, dq = m->dq, dkv = m->dkv, f = c.ffn_dim,
+            V = c.vocab, dh = c.head_dim, hq = c.n_q_heads, l = c.swiftkv_l, L = c.n_layers;
+  const int P = dh / 2;
+  const double E = (double)m->esz;
+  T* act = (T*)m->act;
+  T* qbuf = (T*)m->qbuf;
+  T* obuf = (T*)m->obuf;
+  T* hbuf = (T*)m->hbuf;
+  T* ya = (T*)m->ya;
+  T* yq = (T*)m->yq;
+  T* yo = (T*)m->yo;
+  T* yh = (T*)m->yh;
+  auto slot_of = [&](int s_) {
+    return CacheSlot<T>{(T*)kc->k + (int64_t)s_ * kc->slot_elems, (T*)kc->v + (int64_t)s_ * kc->slot_elems,
+                        c.n_kv_heads, dh};
+  };
+  constexpr bool kBf16 = sizeof(T) == 2;
+
+  SKV_HIP(launch_meta(bt->cu_seqlens, bt->block_tables, B, bt->max_blocks_per_seq, kc->num_blocks, T_, m->pos,
+                      m->slot, m->last_pos, m->last_row, s));
+  if (!kBf16) SKV_HIP(launch_token_seq(bt->cu_seqlens, B, T_, m->seq, s));
+  SKV_HIP(launch_embed<T>(bt->token_ids, (const T*)m->embed, V, d, T_, m->x, s));
+
+  // ---- layers 1..l for every prompt token
+  for (int i = 1; i <= l; ++i) {
+    const LayerDev& Ly = m->layers[i - 1];
+    CacheSlot<T> cs = slot_of(i - 1);
+    {
+      Prof p(m, SKV_K_RMSNORM, s, 0, (double)T_ * d * (4 + E));
+      SKV_HIP(launch_rmsnorm<T>(m->x, nullptr, Ly.attn_norm, T_, d, c.rms_eps, act, s));
+    }
+    {
+      const int N = dq + 2 * dkv;
+      EpiQKV<T> epi{qbuf, cs, m->pos, m->slot, m->rope_cos, m->rope_sin, dq, dkv, dh, P};
+      Prof p(m, SKV_K_GEMM_QKV, s, 2.0 * T_ * N * d, gemm_bytes(T_, N, d, E, E));
+      if constexpr (kBf16)
+        SKV_HIP(launch_gemm_bf16((const bf16_t*)act, d, (const bf16_t*)Ly.wqkv, d, T_, N, d, epi, s));
+      else if (P == 16)
+        SKV_HIP((launch_gemm_f32<16>((const float*)act, d, (const float*)Ly.wqkv, d, T_, N, d, epi, s)));
+      else if (P == 32)
+        SKV_HIP((launch_gemm_f32<32>((const float*)act, d, (const float*)Ly.wqkv, d, T_, N, d, epi, s)));
+      else
+        SKV_HIP((launch_gemm_f32<64>((const float*)act, d, (const float*)Ly.wqkv, d, T_, N, d, epi, s)));
+    }
+    {
+      Prof p(m, SKV_K_ATTN_PREFILL, s, 0, 0);
+      if constexpr (kBf16)
+        SKV_HIP(launch_attn_prefill_bf16((const bf16_t*)qbuf, cs, bt->cu_seqlens, bt->block_tables,
+                                         bt->max_blocks_per_seq, B, max_len, hq, (bf16_t*)obuf, s));
+      else
+        SKV_HIP(launch_attn_rows<T>(qbuf, cs, m->seq, m->pos, bt->block_tables, bt->max_blocks_per_seq, T_, max_len,
+                                    hq, m->attn_ws, obuf, s));
+    }
+    {
+      EpiResidual epi{m->x, d, kBf16 ? 64 : 16};
+      Prof p(m, SKV_K_GEMM_O, s, 2.0 * T_ * d * dq, gemm_bytes(T_, d, dq, E, 8));
+      if constexpr (kBf16)
+        SKV_HIP(launch_gemm_bf16((const bf16_t*)obuf, dq, (const bf16_t*)Ly.wo, dq, T_, d, dq, epi, s));
+      else
+        SKV_HIP((launch_gemm_f32<16>((const float*)obuf, dq, (const float*)Ly.wo, dq, T_, d, dq, epi, s)));
+    }
+    {
+      Prof p(m, SKV_K_RMSNORM, s, 0, (double)T_ * d * (4 + E));
+      SKV_HIP(launch_rmsnorm<T>(m->x, nullptr, Ly.ffn_norm, T_, d, c.rms_eps, act, s));
+    }
+    {
+      EpiSwiGLU<T> epi{hbuf, f, m->p_mlp};
+      Prof p(m, SKV_K_GEMM_GATEUP, s, 2.0 * T_ * 2 * f * d, gemm_bytes(T_, 2.0 * f, d, E, 0) + (double)T_ * f * E);
+      if constexpr (kBf16)
+        SKV_HIP(launch_gemm_bf16((const bf16_t*)act, d, (const bf16_t*)Ly.wgu, d, T_, 2 * f, d, epi, s));
+      else
+        SKV_HIP((launch_gemm_f32<16>((const float*)act, d, (const float*)Ly.wgu, d, T_, 2 * f, d, epi, s)));
+    }
+    {
+      EpiResidual epi{m->x, d, kBf16 ? 64 : 16};
+      Prof p(m, SKV_K_GEMM_DOWN, s, 2.0 * T_ * d * f, gemm_bytes(T_, d, f, E, 8));
+      if constexpr (kBf16)
+        SKV_HIP(launch_gemm_bf16((const bf16_t*)hbuf, f, (const bf16_t*)Ly.wdown, f, T_, d, f, epi, s));
+      else
+        SKV_HIP((launch_gemm_f32<16>((const float*)hbuf, f, (const float*)Ly.wdown, f, T_, d, f, epi, s)));
+    }
+  }
+
+  // ---- boundary: KV of every skipped layer / AcrossKV group from x_{l+1}
+  if (m->G > 0) {
+    {
+      Prof p(m, SKV_K_RMSNORM, s, 0, (double)T_ * d * (4 + E));
+      SKV_HIP(launch_rmsnorm<T>(m->x, nullptr, nullptr, T_, d, c.rms_eps, act, s));  // x * r, gains folded into W~
+    }
+    CacheSlot<T> first = slot_of(l);
+    const int N = m->G * 2 * dkv;
+    EpiKVSkip<T> epi{first.k, first.v, kc->slot_elems, m->pos, m->slot, m->rope_cos, m->rope_sin, dkv, dh, P,
+                     c.n_kv_heads};
+    Prof p(m, SKV_K_GEMM_KVSKIP, s, 2.0 * T_ * N * d, gemm_bytes(T_, N, d, E, E));
+    if constexpr (kBf16)
+      SKV_HIP(launch_gemm_bf16((const bf16_t*)act, d, (const bf16_t*)m->wkv_skip, d, T_, N, d, epi, s));
+    else if (P == 16)
+      SKV_HIP((launch_gemm_f32<16>((const float*)act, d, (const float*)m->wkv_skip, d, T_, N, d, epi, s)));
+    else if (P == 32)
+      SKV_HIP((launch_gemm_f32<32>((const float*)act, d, (const float*)m->wkv_skip, d, T_, N, d, epi, s)));
+    else
+      SKV_HIP((launch_gemm_f32<64>((const float*)act, d, (const float*)m->wkv_skip, d, T_, N, d, epi, s)));
+  }
+
+  // ---- last prompt token of each prompt through layers l+1..L, then the LM head
+  Prof plast(m, SKV_K_LAST_TOKEN, s, 0, 0);
+  SKV_HIP(launch_gather_rows(m->x, m->last_row, B, d, m->y, s));
+  for (int j = l + 1; j <= L; ++j) {
+    const LayerDev& Ly = m->layers[j - 1];
+    CacheSlot<T> cs = slot_of(slot_of_layer(c, j));
+    SKV_HIP(launch_rmsnorm<T>(m->y, nullptr, Ly.attn_norm, B, d, c.rms_eps, ya, s));
+    EpiQKV<T> eq{yq, cs, m->last_pos, nullptr, m->rope_cos, m->rope_sin, dq, dkv, dh, P};
+    EpiResidual er{m->y, d, kBf16 ? 64 : 16};
+    EpiSwiGLU<T> esw{yh, f, m->p_mlp};
+    if constexpr (kBf16) {
+      SKV_HIP(launch_skinny_bf16((const bf16_t*)ya, d, (const bf16_t*)Ly.wqkv, d, B, dq, d, m->partial,
+                                 m->partial_elems, eq, s));
+    } else if (P == 16) {
+      SKV_HIP((launch_gemm_f32<16>((const float*)ya, d, (const float*)Ly.wqkv, d, B, dq, d, eq, s)));
+    } else if (P == 32) {
+      SKV_HIP((launch_gemm_f32<32>((const float*)ya, d, (const float*)Ly.wqkv, d, B, dq, d, eq, s)));
+    } else {
+      SKV_HIP((launch_gemm_f32<64>((const float*)ya, d, (const float*)Ly.wqkv, d, B, dq, d, eq, s)));
+    }
+    SKV_HIP(launch_attn_rows<T>(yq, cs, m->iota, m->last_pos, bt->block_tables, bt->max_blocks_per_seq, B, max_len,
+                                hq, m->attn_ws, yo, s));
+    if constexpr (kBf16) {
+      SKV_HIP(launch_skinny_bf16((const bf16_t*)yo, dq, (const bf16_t*)Ly.wo, dq, B, d, dq, m->partial,
+                                 m->partial_elems, er, s));
+    } else {
+      SKV_HIP((launch_gemm_f32<16>((const float*)yo, dq, (const float*)Ly.wo, dq, B, d, dq, er, s)));
+    }
+    SKV_HIP(launch_rmsnorm<T>(m->y, nullptr, Ly.ffn_norm, B, d, c.rms_eps, ya, s));
+    if constexpr (kBf16) {
+      SKV_HIP(launch_skinny_bf16((const bf16_t*)ya, d, (const bf16_t*)Ly.wgu, d, B, 2 * f, d, m->partial,
+                                 m->partial_elems, esw, s));
+      SKV_HIP(launch_skinny_bf16((const bf16_t*)yh, f, (const bf16_t*)Ly.wdown, f, B, d, f, m->partial,
+                                 m->partial_elems, er, s));
+    } else {
+      SKV_HIP((launch_gemm_f32<16>((const float*)ya, d, (const float*)Ly.wgu, d, B, 2 * f, d, esw, s)));
+      SKV_HIP((launch_gemm_f32<16>((const float*)yh, f, (const float*)Ly.wdown, f, B, d, f, er, s)));
+    }
+  }
+  SKV_HIP(launch_rmsnorm<T>(m->y, nullptr, m->final_norm, B, d, c.rms_eps, ya, s));
+  EpiStoreF32 el{logits, V, kBf16 ? 64 : 16};
+  if constexpr (kBf16)
+    SKV_HIP(launch_skinny_bf16((const bf16_t*)ya, d, (const bf16_t*)m->lm_head, d, B, V, d, m->partial,
+                               m->partial_elems, el, s));
+  else
+    SKV_HIP((launch_gemm_f32<16>((const float*)ya, d, (const float*)m->lm_head, d, B, V, d, el, s)));
+  return SKV_OK;
+}
+
+}  // namespace
+
+extern "C" skv_status skv_prefill(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, float* logits,
+                                  void* stream) {
+  if (!m || !kc || !bt || !logits) return fail(SKV_ERR_INVALID_ARG, "NULL argument");
+  if (kc->m != m) return fail(SKV_ERR_INVALID_ARG, "cache was created for another model");
+  const auto& c = m->cfg;
+  if (!m->globals_loaded) return fail(SKV_ERR_INVALID_ARG, "embedding / LM head not loaded");
+  for (int i = 0; i < c.n_layers; ++i)
+    if (!m->layers[i].loaded) return fail(SKV_ERR_INVALID_ARG, "layer " + std::to_string(i + 1) + " not loaded");
+  const int B = bt->batch;
+  if (B < 1 || B > c.max_batch) return fail(SKV_ERR_INVALID_ARG, "batch must lie in 1..max_batch");
+  if (bt->total_tokens < 1 || bt->total_tokens > c.max_tokens)
+    return fail(SKV_ERR_INVALID_ARG, "total_tokens must lie in 1..max_tokens");
+  if (!bt->cu_seqlens_host || !bt->block_tables_host || !bt->token_ids || !bt->cu_seqlens || !bt->block_tables)
+    return fail(SKV_ERR_INVALID_ARG, "batch arrays must be non-NULL");
+  if (bt->max_blocks_per_seq < 1) return fail(SKV_ERR_INVALID_ARG, "max_blocks_per_seq must be positive");
+  const int32_t* cu = bt->cu_seqlens_host;
+  if (cu[0] != 0 || cu[B] != bt->total_tokens)
+    return fail(SKV_ERR_INVALID_ARG, "cu_seqlens must start at 0 and end at total_tokens");
+  int max_len = 0;
+  for (int b = 0; b < B; ++b) {
+    const int n = cu[b + 1] - cu[b];
+    if (n < 1) return fail(SKV_ERR_INVALID_ARG, "prompt " + std::to_string(b) + " is empty");
+    if (n > c.max_seqlen) return fail(SKV_ERR_INVALID_ARG, "prompt longer than max_seqlen");
+    const int nb = ceil_div(n, kc->block_size);
+    if (nb > bt->max_blocks_per_seq) return fail(SKV_ERR_INVALID_ARG, "block table too small");
+    for (int i = 0; i < nb; ++i) {
+      const int blk = bt->block_tables_host[(int64_t)b * bt->max_blocks_per_seq + i];
+      if (blk < 0 || blk >= kc->num_blocks)
+        return fail(SKV_ERR_INVALID_ARG, "block table entry outside [0, num_blocks)");
+    }
+    max_len = std::max(max_len, n);
+  }
+  if (bt->max_seqlen < max_len) return fail(SKV_ERR_INVALID_ARG, "max_seqlen smaller than the longest prompt");
+  hipStream_t s = (hipStream_t)stream;
+  if (m->bf16) return run_prefill<bf16_t>(m, kc, bt, logits, max_len, s);
+  return run_prefill<float>(m, kc, bt, logits, max_len, s);
+}

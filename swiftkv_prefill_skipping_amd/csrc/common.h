@@ -1,0 +1,86 @@
+// Shared device helpers for the gfx950 SwiftKV kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef uint16_t bf16_t;  // raw IEEE bfloat16 bits
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+#define SKV_DEV __device__ __forceinline__
+
+SKV_DEV float bf16_to_f32(bf16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
+
+// round to nearest even; NaN stays NaN
+SKV_DEV bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+SKV_DEV uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+template <typename T>
+SKV_DEV float to_f32(T v);
+template <>
+SKV_DEV float to_f32<float>(float v) { return v; }
+template <>
+SKV_DEV float to_f32<bf16_t>(bf16_t v) { return bf16_to_f32(v); }
+
+template <typename T>
+SKV_DEV T from_f32(float v);
+template <>
+SKV_DEV float from_f32<float>(float v) { return v; }
+template <>
+SKV_DEV bf16_t from_f32<bf16_t>(float v) { return f32_to_bf16(v); }
+
+SKV_DEV bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+SKV_DEV float warp_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+SKV_DEV float warp_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+SKV_DEV float silu_f(float x) { return x / (1.0f + __expf(-x)); }
+
+// Per-token metadata of one prefill call, filled by the meta kernel.
+struct TokenMeta {
+  const int32_t* pos;   // [T] position of the token within its prompt
+  const int32_t* slot;  // [T] physical cache slot = block * block_size + offset, -1 if unmapped
+};
+
+// Paged cache geometry of one KV slot (one layer or AcrossKV group).
+//   K: [num_blocks, hkv, BS, dh]     V: [num_blocks, hkv, dh, BS]
+template <typename T>
+struct CacheSlot {
+  T* k;
+  T* v;
+  int hkv;
+  int dh;
+};
+
+constexpr int kBlockSize = 16;
+
+template <typename T>
+SKV_DEV int64_t k_index(int slot_phys, int h, int d, int hkv, int dh) {
+  int blk = slot_phys >> 4, off = slot_phys & 15;
+  return (((int64_t)blk * hkv + h) * kBlockSize + off) * dh + d;
+}
+template <typename T>
+SKV_DEV int64_t v_index(int slot_phys, int h, int d, int hkv, int dh) {
+  int blk = slot_phys >> 4, off = slot_phys & 15;
+  return (((int64_t)blk * hkv + h) * dh + d) * kBlockSize + off;
+}

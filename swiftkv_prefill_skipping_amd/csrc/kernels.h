@@ -1,0 +1,76 @@
+// Host-side launchers of the gfx950 kernels (internal to libswiftkv).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.h"
+#include "epilogues.h"
+
+// C[M,N] = A[M,K] B[N,K]^T on MFMA (bf16 in, fp32 accumulate), pair distance 64.
+// Requires K % 64 == 0, N % 128 == 0.
+template <class Epi>
+hipError_t launch_gemm_bf16(const bf16_t* A, int lda, const bf16_t* B, int ldb, int M, int N, int K, const Epi& epi,
+                            hipStream_t stream);
+
+// Same product in fp32 on the vector ALUs (fp32 models), pair distance P
+// (P in {16, 32, 64}); requires N % (2P) == 0.
+template <int P, class Epi>
+hipError_t launch_gemm_f32(const float* A, int lda, const float* B, int ldb, int M, int N, int K, const Epi& epi,
+                           hipStream_t stream);
+
+// Skinny bf16 product for the last-token path (M <= 32 rows): split-K MFMA
+// partial sums into `partial` [splits, 32, N] fp32, then a finalize pass
+// that reduces them in fixed order and applies the epilogue (pair distance
+// 64).  Requires K % 256 == 0, N % 128 == 0.
+template <class Epi>
+hipError_t launch_skinny_bf16(const bf16_t* A, int lda, const bf16_t* B, int ldb, int M, int N, int K,
+                              float* partial, int64_t partial_elems, const Epi& epi, hipStream_t stream);
+int64_t skinny_partial_elems(int N, int K);
+
+// Per-token metadata: pos[t], slot[t], and last_pos[b] = len_b - 1, last_row[b] = cu[b+1] - 1.
+hipError_t launch_meta(const int32_t* cu_seqlens, const int32_t* block_tables, int batch, int max_blocks,
+                       int num_blocks, int total_tokens, int32_t* pos, int32_t* slot, int32_t* last_pos,
+                       int32_t* last_row, hipStream_t stream);
+
+// x[t, :] = E[tok[t], :] as fp32.
+template <typename T>
+hipError_t launch_embed(const int32_t* tok, const T* E, int vocab, int d, int T_, float* x, hipStream_t stream);
+
+// y[r, :] = x[r, :] / sqrt(mean(x^2) + eps) * gamma  (gamma NULL -> 1), fp32 math.
+// rows_idx (optional) gathers input rows: input row = rows_idx[r].
+template <typename T>
+hipError_t launch_rmsnorm(const float* x, const int32_t* rows_idx, const float* gamma, int rows, int d, float eps,
+                          T* y, hipStream_t stream);
+
+// y[r, :] = x[rows_idx[r], :]  (fp32 rows)
+hipError_t launch_gather_rows(const float* x, const int32_t* rows_idx, int rows, int d, float* y,
+                              hipStream_t stream);
+
+// Causal GQA flash attention for prompt tokens (bf16, MFMA): q [T, hq, dh],
+// K/V from one cache slot, o [T, hq * dh].  head_dim 128, hq/hkv % 4 == 0.
+hipError_t launch_attn_prefill_bf16(const bf16_t* q, CacheSlot<bf16_t> cache, const int32_t* cu_seqlens,
+                                    const int32_t* block_tables, int max_blocks, int batch, int max_seqlen, int hq,
+                                    bf16_t* o, hipStream_t stream);
+
+// Attention for a list of query rows, each attending to positions
+// [0, ctx) of its prompt (ctx = pos + 1), split over key chunks with a
+// combine pass.  Used for the last-token path and for fp32 prompt tokens.
+// rows: number of query rows; q [rows, hq, dh]; row_seq[r] = prompt index;
+// row_pos[r] = position (ctx = pos + 1).  Workspace: attn_ws_elems floats.
+template <typename T>
+hipError_t launch_attn_rows(const T* q, CacheSlot<T> cache, const int32_t* row_seq, const int32_t* row_pos,
+                            const int32_t* block_tables, int max_blocks, int rows, int max_ctx, int hq, float* ws,
+                            T* o, hipStream_t stream);
+int64_t attn_rows_ws_elems(int rows, int max_ctx, int hq, int dh);
+
+// For fp32 prompt-token attention: row_seq[t] for every token.
+hipError_t launch_token_seq(const int32_t* cu_seqlens, int batch, int total_tokens, int32_t* seq,
+                            hipStream_t stream);
+
+// Weight repacking at load time.
+template <typename T>
+hipError_t launch_fold_rows(const T* W, const T* gamma, int rows, int cols, T* out, hipStream_t stream);
+template <typename T>
+hipError_t launch_interleave(const T* gate, const T* up, int f, int d, int P, T* out, hipStream_t stream);
+template <typename T>
+hipError_t launch_to_f32(const T* in, int64_t n, float* out, hipStream_t stream);

@@ -1,0 +1,132 @@
+// Skinny bf16 products for the last-token path (at most 32 rows, one per
+// prompt): the layer weights are streamed from HBM exactly once, so the
+// kernel is laid out for bandwidth.  Each wave64 owns 64 output columns and
+// one K split; A (activations, tiny and L2 resident) and B (weights) are
+// read 16 bytes per lane straight into v_mfma_f32_16x16x32_bf16 operands.
+// Split-K partial sums land in an fp32 buffer [splits, 32, N] and a second
+// pass adds them in fixed split order (deterministic) and applies the
+// epilogue on column pairs (col, col + 64).
+#include "common.h"
+#include "epilogues.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr int SK_ROWS = 32;
+
+__global__ __launch_bounds__(256) void skinny_partial_kernel(const bf16_t* __restrict__ A, int lda,
+                                                             const bf16_t* __restrict__ B, int ldb, int M, int N,
+                                                             int kc, float* __restrict__ partial) {
+  const int lane = threadIdx.x & 63;
+  const int cb = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (cb * 64 >= N) return;
+  const int s = blockIdx.y;
+  const int kbeg = s * kc;
+  const int r16 = lane & 15, kq = (lane >> 4) * 8;
+  const bool two = M > 16;
+
+  f32x4_t acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0, 0, 0, 0};
+
+  const bf16_t* bp[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) bp[j] = B + (int64_t)(cb * 64 + j * 16 + r16) * ldb + kbeg + kq;
+  const bool a0ok = r16 < M, a1ok = (16 + r16) < M;
+  const bf16_t* ap0 = A + (int64_t)r16 * lda + kbeg + kq;
+  const bf16_t* ap1 = A + (int64_t)(16 + r16) * lda + kbeg + kq;
+
+  for (int k = 0; k < kc; k += 32) {
+    u32x4_t b[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b[j] = *reinterpret_cast<const u32x4_t*>(bp[j] + k);
+    u32x4_t a0 = a0ok ? *reinterpret_cast<const u32x4_t*>(ap0 + k) : u32x4_t{0, 0, 0, 0};
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a0), as_bf16x8(b[j]), acc[0][j], 0, 0, 0);
+    if (two) {
+      u32x4_t a1 = a1ok ? *reinterpret_cast<const u32x4_t*>(ap1 + k) : u32x4_t{0, 0, 0, 0};
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[1][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a1), as_bf16x8(b[j]), acc[1][j], 0, 0, 0);
+    }
+  }
+  // C layout of 16x16: row 4*(lane/16) + v, column lane % 16
+  float* out = partial + (int64_t)s * SK_ROWS * N;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    if (i == 1 && !two) break;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        int row = i * 16 + 4 * (lane >> 4) + v;
+        if (row < M) out[(int64_t)row * N + cb * 64 + j * 16 + r16] = acc[i][j][v];
+      }
+  }
+}
+
+template <class Epi>
+__global__ void skinny_finalize_kernel(const float* __restrict__ partial, int M, int N, int nsplit, Epi epi) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t half = N / 2;
+  if (idx >= (int64_t)M * half) return;
+  const int row = (int)(idx / half);
+  const int j = (int)(idx % half);
+  const int col = (j / 64) * 128 + (j % 64);
+  float v0 = 0.f, v1 = 0.f;
+  for (int s = 0; s < nsplit; ++s) {
+    const float* p = partial + ((int64_t)s * SK_ROWS + row) * N + col;
+    v0 += p[0];
+    v1 += p[64];
+  }
+  epi(row, col, v0, v1);
+}
+
+int choose_splits(int N, int K) {
+  const int units = K / 256;  // splits are multiples of 256 in K
+  const int colblocks = N / 64;
+  int target = (4096 + colblocks - 1) / colblocks;
+  int best = units;
+  for (int s = 1; s <= units; ++s)
+    if (units % s == 0 && s >= target) {
+      best = s;
+      break;
+    }
+  return best;
+}
+
+}  // namespace
+
+int64_t skinny_partial_elems(int N, int K) { return (int64_t)choose_splits(N, K) * SK_ROWS * N; }
+
+template <class Epi>
+hipError_t launch_skinny_bf16(const bf16_t* A, int lda, const bf16_t* B, int ldb, int M, int N, int K,
+                              float* partial, int64_t partial_elems, const Epi& epi, hipStream_t stream) {
+  if (M <= 0) return hipSuccess;
+  if (M > SK_ROWS || K % 256 != 0 || N % 128 != 0) return hipErrorInvalidValue;
+  const int ns = choose_splits(N, K);
+  if ((int64_t)ns * SK_ROWS * N > partial_elems) return hipErrorInvalidValue;
+  const int kc = K / ns;
+  dim3 grid((N / 64 + 3) / 4, ns);
+  hipLaunchKernelGGL(skinny_partial_kernel, grid, dim3(256), 0, stream, A, lda, B, ldb, M, N, kc, partial);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t work = (int64_t)M * (N / 2);
+  hipLaunchKernelGGL(skinny_finalize_kernel<Epi>, dim3((unsigned)((work + 255) / 256)), dim3(256), 0, stream, partial,
+                     M, N, ns, epi);
+  return hipGetLastError();
+}
+
+template hipError_t launch_skinny_bf16<EpiQKV<bf16_t>>(const bf16_t*, int, const bf16_t*, int, int, int, int, float*,
+                                                       int64_t, const EpiQKV<bf16_t>&, hipStream_t);
+template hipError_t launch_skinny_bf16<EpiResidual>(const bf16_t*, int, const bf16_t*, int, int, int, int, float*,
+                                                    int64_t, const EpiResidual&, hipStream_t);
+template hipError_t launch_skinny_bf16<EpiSwiGLU<bf16_t>>(const bf16_t*, int, const bf16_t*, int, int, int, int,
+                                                          float*, int64_t, const EpiSwiGLU<bf16_t>&, hipStream_t);
+template hipError_t launch_skinny_bf16<EpiStoreF32>(const bf16_t*, int, const bf16_t*, int, int, int, int, float*,
+                                                    int64_t, const EpiStoreF32&, hipStream_t);
+template hipError_t launch_skinny_bf16<EpiStore<bf16_t>>(const bf16_t*, int, const bf16_t*, int, int, int, int,
+                                                         float*, int64_t, const EpiStore<bf16_t>&, hipStream_t);

@@ -1,0 +1,174 @@
+"""Python-side plumbing around libswiftkv: build a model from seeded weights,
+put a batch in device memory, call skv_prefill, read the paged KV cache back
+in logical order.  PyTorch provides device memory and streams only; all
+arithmetic of the path runs in the library's kernels.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+from typing import Dict, Optional
+
+import numpy as np
+
+from . import _lib as L
+
+_hip = None
+
+
+def _hiprt():
+    global _hip
+    if _hip is None:
+        _hip = ctypes.CDLL("libamdhip64.so")
+        _hip.hipMemcpy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
+        _hip.hipMemcpy.restype = ctypes.c_int
+    return _hip
+
+
+def _torch():
+    import torch
+    if not torch.cuda.is_available():
+        raise RuntimeError("no HIP device visible to torch")
+    return torch
+
+
+def config_from(shape, dtype: str, l: int, g: int, max_tokens: int, max_batch: int, max_seqlen: int):
+    return L.make_config(shape.n_layers, shape.d_model, shape.n_q_heads, shape.n_kv_heads, shape.head_dim,
+                         shape.ffn_dim, shape.vocab, shape.rope_theta, shape.rms_eps, l, g,
+                         L.SKV_BF16 if dtype == "bf16" else L.SKV_FP32, max_tokens, max_batch, max_seqlen)
+
+
+class Model:
+    """Owns an skv_model handle."""
+
+    def __init__(self, cfg: L.skv_model_config):
+        self.cfg = cfg
+        self.handle = L.skv_model_create(cfg)
+
+    def load_globals(self, embed, final_norm, lm_head):
+        L.skv_model_load_globals(self.handle, embed, final_norm, lm_head)
+
+    def load_layer(self, layer: int, w: Dict[str, np.ndarray]):
+        L.skv_model_load_layer(self.handle, layer, w)
+
+    @property
+    def num_kv_slots(self) -> int:
+        return L.skv_num_kv_slots(self.handle)
+
+    def close(self):
+        if self.handle:
+            L.skv_model_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def load_seeded_model(workload, max_tokens: int, max_batch: int, max_seqlen: int, layer_hook=None) -> Model:
+    """Create a model for `workload` and load its seeded weights layer by layer.
+
+    layer_hook(i, weights) (optional) sees each layer's host arrays after
+    they were loaded (used to stream the same arrays to the oracle).
+    """
+    import skv_inputs as si
+    s = workload.shape
+    cfg = config_from(s, workload.dtype, workload.swiftkv_l, workload.acrosskv_g, max_tokens, max_batch, max_seqlen)
+    m = Model(cfg)
+    gw = si.global_weights(s, workload.dtype)
+    m.load_globals(gw["embed"], gw["final_norm"], gw["lm_head"])
+    del gw
+    for i in range(1, s.n_layers + 1):
+        w = si.layer_weights(s, i, workload.dtype)
+        m.load_layer(i, w)
+        if layer_hook is not None:
+            layer_hook(i, w)
+    return m
+
+
+class Cache:
+    """Owns an skv_kv_cache handle."""
+
+    def __init__(self, model: Model, num_blocks: int, block_size: int = 16):
+        self.model = model
+        self.num_blocks = num_blocks
+        self.block_size = block_size
+        self.handle = L.skv_kv_cache_create(model.handle, num_blocks, block_size)
+
+    def view(self, layer: int):
+        return L.skv_kv_cache_view(self.handle, layer)
+
+    def _copy_view(self, v: L.skv_tensor_view):
+        torch = _torch()
+        shape = tuple(v.shape[i] for i in range(v.ndim))
+        dt = torch.uint16 if v.dtype == L.SKV_BF16 else torch.float32
+        t = torch.empty(shape, dtype=dt, device="cuda")
+        nbytes = t.numel() * t.element_size()
+        torch.cuda.synchronize()
+        rc = _hiprt().hipMemcpy(t.data_ptr(), v.data, nbytes, 3)  # device to device
+        if rc != 0:
+            raise RuntimeError(f"hipMemcpy failed ({rc})")
+        return t.view(torch.bfloat16) if v.dtype == L.SKV_BF16 else t
+
+    def read_layer(self, layer: int):
+        """Device copies of (K [nb, hkv, bs, dh], V [nb, hkv, dh, bs]) of a layer."""
+        k, v = self.view(layer)
+        return self._copy_view(k), self._copy_view(v)
+
+    def close(self):
+        if self.handle:
+            L.skv_kv_cache_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def logical_kv(kt, vt, block_row: np.ndarray, n: int):
+    """Gather one prompt's K/V in position order: ([n, hkv, dh], [n, hkv, dh]) fp32 on the host."""
+    torch = _torch()
+    bs = kt.shape[2]
+    nb = -(-n // bs)
+    idx = torch.as_tensor(np.asarray(block_row[:nb], dtype=np.int64), device=kt.device)
+    k = kt.index_select(0, idx).permute(0, 2, 1, 3).reshape(nb * bs, kt.shape[1], kt.shape[3])[:n]
+    v = vt.index_select(0, idx).permute(0, 3, 1, 2).reshape(nb * bs, vt.shape[1], vt.shape[2])[:n]
+    return k.float().cpu().numpy(), v.float().cpu().numpy()
+
+
+@dataclass
+class DeviceBatch:
+    batch: object                 # skv_inputs.Batch
+    token_ids: object             # torch int32 cuda
+    cu_dev: object
+    bt_dev: object
+    cu_host: np.ndarray
+    bt_host: np.ndarray
+    struct: L.skv_batch
+
+
+def device_batch(batch) -> DeviceBatch:
+    torch = _torch()
+    cu = np.ascontiguousarray(batch.cu_seqlens, dtype=np.int32)
+    bt = np.ascontiguousarray(batch.block_tables, dtype=np.int32)
+    tok = torch.as_tensor(batch.token_ids, dtype=torch.int32).cuda()
+    cu_d = torch.as_tensor(cu).cuda()
+    bt_d = torch.as_tensor(bt.reshape(-1)).cuda()
+    st = L.skv_batch(len(batch.lengths), batch.total_tokens, batch.max_seqlen, bt.shape[1], cu.ctypes.data,
+                     bt.ctypes.data, tok.data_ptr(), cu_d.data_ptr(), bt_d.data_ptr())
+    return DeviceBatch(batch, tok, cu_d, bt_d, cu, bt, st)
+
+
+def prefill(model: Model, cache: Cache, db: DeviceBatch, logits=None, stream=None):
+    """Enqueue skv_prefill on `stream` (torch stream; default = current) and return the logits tensor."""
+    torch = _torch()
+    B = db.struct.batch
+    if logits is None:
+        logits = torch.empty((B, model.cfg.vocab), dtype=torch.float32, device="cuda")
+    s = stream if stream is not None else torch.cuda.current_stream()
+    L.skv_prefill(model.handle, cache.handle, db.struct, logits.data_ptr(), s.cuda_stream)
+    return logits

@@ -1,0 +1,45 @@
+"""Shared helpers of the tests: seeded inputs -> oracle inputs, error metrics."""
+from __future__ import annotations
+
+import numpy as np
+
+import skv_inputs as si
+from oracle import swiftkv_oracle as O
+
+
+def dims_of(shape: si.ModelShape) -> O.Dims:
+    return O.Dims(shape.n_layers, shape.d_model, shape.n_q_heads, shape.n_kv_heads, shape.head_dim, shape.ffn_dim,
+                  shape.vocab, shape.rope_theta, shape.rms_eps)
+
+
+class CachedLayers:
+    """Layer weights kept as generated (bf16 bits or fp32) and widened to fp32 on request."""
+
+    def __init__(self):
+        self.layers = {}
+
+    def hook(self, i, w):
+        self.layers[i] = w
+
+    def make(self, i):
+        return {k: si.as_f32(v) for k, v in self.layers[i].items()}
+
+
+def oracle_weights(w: si.Workload, cached: CachedLayers = None) -> O.WeightSource:
+    """The oracle's view of the seeded weights: the exact stored values in fp32."""
+    gw = si.global_weights(w.shape, w.dtype)
+    if cached is None:
+        make = lambda i: {k: si.as_f32(v) for k, v in si.layer_weights(w.shape, i, w.dtype).items()}
+    else:
+        make = cached.make
+    return O.LazyWeights(si.as_f32(gw["embed"]), si.as_f32(gw["final_norm"]), si.as_f32(gw["lm_head"]), make)
+
+
+def max_rel(got, ref) -> float:
+    """max |got - ref| / max |ref| over one tensor (the parity metric)."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    den = float(np.max(np.abs(ref))) if ref.size else 0.0
+    if den == 0.0:
+        return float(np.max(np.abs(got))) if got.size else 0.0
+    return float(np.max(np.abs(got - ref)) / den)

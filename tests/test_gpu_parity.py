@@ -1,0 +1,198 @@
+"""HIP path vs the CPU oracle on identical seeded inputs (needs a gfx950 GPU).
+
+Metric (per tensor): max |gpu - oracle| / max |oracle| for K and V of every
+KV slot of every checked prompt (positions 0..N-1) and for each checked
+prompt's logits row.  Bars: 1e-4 for fp32 models, 2e-2 for bf16 models.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import skv_inputs as si
+from oracle import swiftkv_oracle as O
+from tests.helpers import CachedLayers, dims_of, max_rel, oracle_weights
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"fp32": 1e-4, "bf16": 2e-2}
+
+
+def _say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def run_gpu(w, batch, max_tokens=None, max_seqlen=None, cached=None, num_blocks=None):
+    import torch
+    from swiftkv_prefill_skipping_amd import runner
+    T, B = batch.total_tokens, len(batch.lengths)
+    model = runner.load_seeded_model(w, max_tokens or T, max(B, 1), max_seqlen or batch.max_seqlen,
+                                     layer_hook=cached.hook if cached is not None else None)
+    cache = runner.Cache(model, num_blocks or batch.num_blocks)
+    db = runner.device_batch(batch)
+    logits = runner.prefill(model, cache, db)
+    torch.cuda.synchronize()
+    return model, cache, db, logits
+
+
+def gpu_kv(cache, w, batch, b):
+    """{slot: (K, V)} of prompt b read back from the paged cache in position order."""
+    from swiftkv_prefill_skipping_amd import runner
+    L_, l, g = w.shape.n_layers, w.swiftkv_l, w.acrosskv_g
+    out = {}
+    n = int(batch.lengths[b])
+    for j in range(1, L_ + 1):
+        s = O.slot_of_layer(j, L_, l, g)
+        if s in out:
+            continue
+        kt, vt = cache.read_layer(j)
+        out[s] = runner.logical_kv(kt, vt, batch.block_tables[b], n)
+    return out
+
+
+def compare(w, batch, logits, cache, ores, prompts, tol=None, label=""):
+    tol = tol if tol is not None else TOL[w.dtype]
+    worst = 0.0
+    lg = logits.float().cpu().numpy()
+    for ob, b in enumerate(prompts):
+        gkv = gpu_kv(cache, w, batch, b)
+        assert set(gkv) == set(ores.kv[ob]), "slot sets differ"
+        for s in sorted(gkv):
+            for t, name in ((0, "K"), (1, "V")):
+                e = max_rel(gkv[s][t], ores.kv[ob][s][t])
+                worst = max(worst, e)
+                assert e < tol, f"{label} prompt {b} slot {s} {name}: max rel err {e:.3e} >= {tol}"
+        e = max_rel(lg[b], ores.logits[ob])
+        worst = max(worst, e)
+        assert e < tol, f"{label} prompt {b} logits: max rel err {e:.3e} >= {tol}"
+    _say(f"[parity] {label}: worst max-rel error {worst:.3e} (bar {tol})")
+    return worst
+
+
+def oracle_for(w, batch, prompts, cached=None):
+    W = oracle_weights(w, cached)
+    return O.swiftkv_prefill(dims_of(w.shape), W, [batch.tokens[b] for b in prompts], w.swiftkv_l, w.acrosskv_g)
+
+
+# ----------------------------------------------------------------------------
+# small models, every prompt compared
+# ----------------------------------------------------------------------------
+
+def test_tiny_fp32_workload():
+    """The tiny fp32 model (4 layers, d=256, 4/2 heads, dh=64, l=2): all KV slots and the logits."""
+    w = si.WORKLOADS["tiny_fp32_l2"]
+    batch = si.make_batch(w)
+    _say(f"[case] tiny fp32 lengths={list(batch.lengths)}")
+    model, cache, db, logits = run_gpu(w, batch)
+    ores = oracle_for(w, batch, [0])
+    compare(w, batch, logits, cache, ores, [0], label="tiny_fp32_l2")
+
+
+SMALL_CASES = [
+    # name, kwargs
+    ("l2_ragged", dict(l=2, g=1, lengths=(100, 37, 300, 1, 64))),
+    ("l0_from_embeddings", dict(l=0, g=1, lengths=(77, 130))),
+    ("lL_no_skip", dict(l=4, g=1, lengths=(90, 257))),
+    ("l1_acrosskv_g2_short_last_group", dict(l=1, g=2, lengths=(150, 33))),
+    ("l2_acrosskv_g2", dict(l=2, g=2, lengths=(200,))),
+    ("l2_long_prompt", dict(l=2, g=1, lengths=(700, 129))),
+    ("l2_hq8_per_kv", dict(l=2, g=1, lengths=(180, 45), n_q_heads=16, n_kv_heads=2)),
+    ("l3_shuffled_blocks", dict(l=3, g=1, lengths=(333, 65, 16), shuffle=True)),
+]
+
+
+@pytest.mark.parametrize("name,kw", SMALL_CASES, ids=[c[0] for c in SMALL_CASES])
+def test_small_bf16(name, kw):
+    w = si.small_workload(name, **kw)
+    batch = si.make_batch(w)
+    _say(f"[case] small bf16 {name} lengths={list(batch.lengths)} l={w.swiftkv_l} g={w.acrosskv_g}")
+    model, cache, db, logits = run_gpu(w, batch)
+    prompts = list(range(len(batch.lengths)))
+    ores = oracle_for(w, batch, prompts)
+    compare(w, batch, logits, cache, ores, prompts, label=name)
+
+
+def test_small_fp32_acrosskv():
+    w = si.small_workload("fp32_g2", n_layers=5, d_model=128, n_q_heads=4, n_kv_heads=2, head_dim=32, ffn_dim=176,
+                          vocab=512, dtype="fp32", l=2, g=2, lengths=(50, 9, 120))
+    batch = si.make_batch(w)
+    _say(f"[case] small fp32 acrosskv lengths={list(batch.lengths)}")
+    model, cache, db, logits = run_gpu(w, batch)
+    prompts = list(range(len(batch.lengths)))
+    ores = oracle_for(w, batch, prompts)
+    compare(w, batch, logits, cache, ores, prompts, label="fp32_g2")
+
+
+def test_uniform_gains_fold():
+    """Gains far from 1 (U(0.5, 1.5)) make the folded skipped-layer projection visibly different from the unfolded one."""
+    w = si.small_workload("gain_uniform", l=1, g=1, lengths=(120, 60), gain="uniform")
+    batch = si.make_batch(w)
+    _say("[case] uniform gains")
+    model, cache, db, logits = run_gpu(w, batch)
+    ores = oracle_for(w, batch, [0, 1])
+    compare(w, batch, logits, cache, ores, [0, 1], label="gain_uniform")
+
+
+def test_paged_layout_is_invisible_and_runs_are_deterministic():
+    """Shuffled vs in-order physical blocks give bitwise identical logical KV and logits; reruns are bitwise equal."""
+    import torch
+    from swiftkv_prefill_skipping_amd import runner
+    w = si.small_workload("paged", l=2, g=2, lengths=(211, 47, 90))
+    b_id = si.make_batch(w, shuffle=False)
+    b_sh = si.make_batch(w, shuffle=True)
+    assert not np.array_equal(b_id.block_tables, b_sh.block_tables)
+    _say("[case] paged layout / determinism")
+    model, c1, _, lg1 = run_gpu(w, b_id)
+    c2 = runner.Cache(model, b_sh.num_blocks)
+    lg2 = runner.prefill(model, c2, runner.device_batch(b_sh))
+    lg3 = runner.prefill(model, c1, runner.device_batch(b_id))
+    torch.cuda.synchronize()
+    assert torch.equal(lg1, lg2)
+    assert torch.equal(lg1, lg3)
+    for b in range(3):
+        k1 = gpu_kv(c1, w, b_id, b)
+        k2 = gpu_kv(c2, w, b_sh, b)
+        for s in k1:
+            assert np.array_equal(k1[s][0], k2[s][0]) and np.array_equal(k1[s][1], k2[s][1])
+
+
+def test_prompts_independent_on_gpu():
+    import torch
+    from swiftkv_prefill_skipping_amd import runner
+    w = si.small_workload("indep", l=2, g=1, lengths=(140, 70, 260))
+    batch = si.make_batch(w)
+    _say("[case] prompt independence")
+    model, cache, db, logits = run_gpu(w, batch)
+    one = si.Batch(batch.lengths[1:2], batch.tokens[1:2], 16, *si.make_block_tables(batch.lengths[1:2], 16, 0, False))
+    c2 = runner.Cache(model, one.num_blocks)
+    lg = runner.prefill(model, c2, runner.device_batch(one))
+    torch.cuda.synchronize()
+    e = max_rel(lg[0].cpu().numpy(), logits[1].cpu().numpy())
+    assert e < 5e-3, e
+
+
+def test_host_side_errors():
+    """Bad batches are rejected on the host with a message and nothing enqueued."""
+    from swiftkv_prefill_skipping_amd import _lib as L, runner
+    w = si.small_workload("errs", l=1, g=1, lengths=(40, 20))
+    batch = si.make_batch(w)
+    model, cache, db, logits = run_gpu(w, batch)
+    s = db.struct
+    bad_cu = np.array([0, 40, 50], dtype=np.int32)          # does not end at total_tokens
+    st = L.skv_batch(2, 60, 40, s.max_blocks_per_seq, bad_cu.ctypes.data, s.block_tables_host, s.token_ids,
+                     s.cu_seqlens, s.block_tables)
+    with pytest.raises(L.SkvError):
+        L.skv_prefill(model.handle, cache.handle, st, logits.data_ptr(), 0)
+    bt = db.bt_host.copy()
+    bt[0, 0] = cache.num_blocks + 5                           # block id out of range
+    st = L.skv_batch(2, 60, 40, s.max_blocks_per_seq, db.cu_host.ctypes.data, bt.ctypes.data, s.token_ids,
+                     s.cu_seqlens, s.block_tables)
+    with pytest.raises(L.SkvError):
+        L.skv_prefill(model.handle, cache.handle, st, logits.data_ptr(), 0)
+    st = L.skv_batch(2, 60, 40, s.max_blocks_per_seq, db.cu_host.ctypes.data, db.bt_host.ctypes.data, s.token_ids,
+                     s.cu_seqlens, s.block_tables)
+    big = L.skv_batch(3, 60, 40, s.max_blocks_per_seq, db.cu_host.ctypes.data, db.bt_host.ctypes.data, s.token_ids,
+                      s.cu_seqlens, s.block_tables)
+    with pytest.raises(L.SkvError):                           # batch above max_batch
+        L.skv_prefill(model.handle, cache.handle, big, logits.data_ptr(), 0)
+    L.skv_prefill(model.handle, cache.handle, st, logits.data_ptr(), 0)   # the good one still works
