@@ -2,7 +2,7 @@
 // accumulation, results handed to an epilogue functor as column pairs
 // (col, col + 64).
 //
-// Tile 256 x 256, k-slices of 32.  512 threads = 8 wave64s, two per SIMD;
+// Tile 256 x 256, k-stages of 64.  512 threads = 8 wave64s, two per SIMD;
 // wave w owns output rows 64*(w%4) .. +64 and columns 128*(w/4) .. +128 as
 // 2 x 4 tiles of v_mfma_f32_32x32x16_bf16.  A wave's 128 columns are 4
 // MFMA column tiles; tiles t and t+2 are 64 columns apart, which is the RoPE
@@ -10,12 +10,11 @@
 // every epilogue pair sits in one lane.
 //
 // Operand staging: global -> LDS directly (global_load_lds_dwordx4, no
-// register round trip) into a ring of 4 k-slices (4 x 32 KB), loads issued 3
-// slices ahead so HBM / infinity-cache latency is covered.  LDS rows are
-// 64 B (32 bf16); the 16 B chunk c of row r is stored at chunk
-// c ^ ((r >> 2) & 3).  gfx950's LDS serves a ds_read_b128 16 lanes (256 B,
-// all 64 banks) per pass; with this swizzle the 16 rows read by one pass
-// cover all 16 bank groups, so the reads are conflict free.
+// register round trip) into two 64 KB stages.  LDS rows are 128 B (64
+// bf16); the 16 B chunk c of row r is stored at chunk c ^ ((r >> 1) & 7).
+// gfx950's LDS serves a ds_read_b128 16 lanes (256 B, all 64 banks) per
+// pass; with this swizzle the 16 rows read by one pass cover all 16 bank
+// groups, so the reads are conflict free.
 //
 // The two waves of a SIMD alternate between a memory phase and an MFMA
 // phase (ping-pong, separated by workgroup barriers), so the matrix core of
@@ -31,8 +30,7 @@
 
 namespace {
 
-constexpr int BM = 256, BN = 256, BK = 32;
-constexpr int kStages = 4;  // LDS ring of k-slices; loads run kStages-1 slices ahead
+constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int kThreads = 512;
 constexpr int kGroupM = 4;
 constexpr int kXcds = 8;
@@ -43,20 +41,19 @@ SKV_DEV int xcd_remap(int wg, int n) {
   return (xcd < r) ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
 }
 
-// "s_waitcnt vmcnt(8) lgkmcnt(0); s_barrier" and a bare "s_barrier", written
-// out because a workgroup fence (__syncthreads) would also wait for every
-// outstanding direct load and empty the ring.  The memory clobber keeps the
-// compiler from moving LDS accesses across them.
-// sched_barrier(0) on both sides stops the scheduler from moving any
-// instruction (MFMAs included) across, which is what keeps the phases apart.
-SKV_DEV void wait_ring_and_barrier() {
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-}
+// Workgroup barriers written out: a workgroup fence (__syncthreads) would
+// also wait for every outstanding direct load.  sched_barrier(0) on both
+// sides keeps the scheduler from moving any instruction (MFMAs included)
+// across, which is what keeps the ping-pong phases apart; the memory
+// clobber keeps LDS accesses in place at the IR level.
 SKV_DEV void barrier_only() {
   __builtin_amdgcn_sched_barrier(0);
   asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+SKV_DEV void wait_loads_and_reads() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -64,7 +61,7 @@ template <class Epi>
 __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(const bf16_t* __restrict__ A,
                                                                  const bf16_t* __restrict__ B, int M, int N,
                                                                  int K, int lda, int ldb, Epi epi) {
-  __shared__ __attribute__((aligned(16))) bf16_t smem[kStages][(BM + BN) * BK];
+  __shared__ __attribute__((aligned(16))) bf16_t smem[2][(BM + BN) * BK];
 
   const int tiles_m = (M + BM - 1) / BM;
   const int tiles_n = (N + BN - 1) / BN;
@@ -86,33 +83,35 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(const bf16_t* __
   const int wm = wave & 3, wn = pp;                           // 64 x 128 output block of this wave
 
   // Direct global -> LDS loads (global_load_lds_dwordx4): one instruction
-  // moves 1 KB = 16 rows x 64 B and lane l's 16 bytes land at byte 16*l of
-  // the destination, so the XOR swizzle is applied on the global side: lane
-  // l fetches the logical chunk of row (l >> 2) that belongs at physical
-  // chunk l & 3.  A k-slice is 16 row groups of A and 16 of B; wave w loads
-  // groups 4w .. 4w+3 (A for w < 4, B otherwise).
+  // moves 1 KB = 8 rows x 128 B (whole cache lines: the vector memory path
+  // pays per line, so half-line row segments would halve its throughput)
+  // and lane l's 16 bytes land at byte 16*l of the destination, so the XOR
+  // swizzle is applied on the global side: lane l fetches the logical chunk
+  // of row (l >> 3) that belongs at physical chunk l & 7.  A stage is 32 row
+  // groups of A and 32 of B; group 0 loads A, group 1 loads B, 8
+  // instructions per wave.
   const bf16_t* gsrc_base;
-  int gsrc_off[4];
-  int lds_dst[4];
+  int gsrc_off[8];
+  int lds_dst[8];
   {
-    const int is_b = wave >> 2;
+    const int is_b = pp;
     gsrc_base = is_b ? B : A;
     const int ld = is_b ? ldb : lda;
     const int lim = is_b ? N - 1 : M - 1;
     const int r0 = is_b ? n0 : m0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int grp = (wave & 3) * 4 + i;
-      const int row = grp * 16 + (lane >> 2);
-      const int c = (lane & 3) ^ ((row >> 2) & 3);
+    for (int i = 0; i < 8; ++i) {
+      const int grp = (wave & 3) * 8 + i;
+      const int row = grp * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ ((row >> 1) & 7);
       gsrc_off[i] = min(r0 + row, lim) * ld + c * 8;
-      lds_dst[i] = (is_b ? BM * BK : 0) + grp * 16 * BK;
+      lds_dst[i] = (is_b ? BM * BK : 0) + grp * 8 * BK;
     }
   }
   auto gload = [&](int buf, int k0) {
     bf16_t* base = smem[buf];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 8; ++i)
       __builtin_amdgcn_global_load_lds(gsrc_base + gsrc_off[i] + k0,
                                        (__attribute__((address_space(3))) void*)(base + lds_dst[i]), 16, 0, 0);
   };
@@ -125,52 +124,68 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(const bf16_t* __
 
   const int frag_row = lane & 31;
   const int khalf = lane >> 5;
-  const int swz = (lane >> 2) & 3;  // (row >> 2) & 3 of the fragment row
+  const int swz = (lane >> 1) & 7;  // (row >> 1) & 7 of the fragment row
   const int a_off = (wm * 64 + frag_row) * BK;
   const int b_off = BM * BK + (wn * 128 + frag_row) * BK;
 
-  // operands of one k-slice: 2 substeps x (2 A + 4 B) fragments
+  // operands of half a stage: 2 k-substeps x (2 A + 4 B) fragments
   bf16x8_t af[2][2], bfr[2][4];
-  auto fload = [&](int buf) {
+  auto fload = [&](int buf, int half) {
     const bf16_t* sa = smem[buf] + a_off;
     const bf16_t* sb = smem[buf] + b_off;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int ch = ((ks * 2 + khalf) ^ swz) << 3;
+    for (int kk = 0; kk < 2; ++kk) {
+      const int ch = (((half * 2 + kk) * 2 + khalf) ^ swz) << 3;
 #pragma unroll
-      for (int i = 0; i < 2; ++i) af[ks][i] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(sa + i * 32 * BK + ch));
+      for (int i = 0; i < 2; ++i) af[kk][i] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(sa + i * 32 * BK + ch));
 #pragma unroll
-      for (int j = 0; j < 4; ++j) bfr[ks][j] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(sb + j * 32 * BK + ch));
+      for (int j = 0; j < 4; ++j) bfr[kk][j] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(sb + j * 32 * BK + ch));
     }
   };
-
-  // Ping-pong over the two waves of each SIMD.  Per k-slice every wave runs
-  // a memory phase (read its operands of slice kt from LDS, issue its 4
-  // direct loads of slice kt+3 into the ring, wait until slice kt+1 has
-  // landed) and a compute phase (16 MFMAs), each closed by a workgroup
-  // barrier.  Group 1 starts one barrier late, so at any time one wave of a
-  // SIMD computes while the other does memory work.  Every wave passes the
-  // same number of barriers (1 + 1 + 2 nk).  Slices past the end are dummy
-  // loads of slice 0 into a buffer nothing reads again, keeping the
-  // outstanding-load count uniform (vmcnt(8) = slices kt+2, kt+3).
-  const int nk = K / BK;
+  auto compute = [&]() {
 #pragma unroll
-  for (int st = 0; st < kStages - 1; ++st) gload(st, (st < nk ? st : 0) * BK);
-  wait_ring_and_barrier();
-  if (pp == 1) barrier_only();
-
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & (kStages - 1);
-    fload(cur);
-    gload((kt + kStages - 1) & (kStages - 1), (kt + kStages - 1 < nk ? kt + kStages - 1 : 0) * BK);
-    wait_ring_and_barrier();
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+    for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks][i], bfr[ks][j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk][i], bfr[kk][j], acc[i][j], 0, 0, 0);
+  };
+
+  // Ping-pong over the two waves of each SIMD: every wave runs the same
+  // sequence of phases separated by workgroup barriers -- read the first
+  // half of stage s from LDS, multiply it (16 MFMAs), read the second half,
+  // multiply it -- and group 1 starts one barrier late, so in every slot one
+  // wave of each SIMD is on the matrix core while the other reads LDS.
+  // Group 0 reads stage s in slots 4s and 4s+2, group 1 in 4s+1 and 4s+3.
+  // The loads of stage s+1 go into the other buffer in slot 4s, after its
+  // last reads (stage s-1, slot 4s-1): group 0 issues them in its first read
+  // phase of stage s, group 1 right after its last MFMAs of stage s-1.  Each
+  // wave waits for them at the end of slot 4s+3 (group 0 after its last
+  // MFMAs of stage s, group 1 after its last reads), before stage s+1 is
+  // first read in slot 4s+4: three slots of latency cover.  Every wave
+  // passes 2 + 4 nk barriers.
+  const int nk = K / BK;
+  gload(0, 0);
+  wait_loads_and_reads();
+  barrier_only();
+  if (pp == 1) {
+    if (nk > 1) gload(1, BK);
+    barrier_only();
+  }
+  for (int s = 0; s < nk; ++s) {
+    const int cur = s & 1;
+    fload(cur, 0);
+    if (pp == 0 && s + 1 < nk) gload(cur ^ 1, (s + 1) * BK);
+    barrier_only();
+    compute();
+    barrier_only();
+    fload(cur, 1);
+    if (pp == 1) wait_loads_and_reads();
+    barrier_only();
+    compute();
+    if (pp == 1 && s + 2 < nk) gload(cur, (s + 2) * BK);
+    if (pp == 0) wait_loads_and_reads();
     barrier_only();
   }
   if (pp == 0) barrier_only();
@@ -201,7 +216,7 @@ hipError_t launch_gemm_bf16(const bf16_t* A, int lda, const bf16_t* B, int ldb, 
                             hipStream_t stream) {
   if (M <= 0) return hipSuccess;
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  hipLaunchKernelGGL(gemm_bf16_kernel<Epi>, dim3(tiles), dim3(kThreads), 0, stream, A, B, M, N, K, lda, ldb, epi);
+  hipLaunchKernelGGL((gemm_bf16_kernel<Epi>), dim3(tiles), dim3(kThreads), 0, stream, A, B, M, N, K, lda, ldb, epi);
   return hipGetLastError();
 }
 

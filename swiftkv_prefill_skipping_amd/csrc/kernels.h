@@ -7,7 +7,7 @@
 #include "epilogues.h"
 
 // C[M,N] = A[M,K] B[N,K]^T on MFMA (bf16 in, fp32 accumulate), pair distance 64.
-// Requires K % 32 == 0, N % 128 == 0.
+// Requires K % 64 == 0, N % 128 == 0.
 template <class Epi>
 hipError_t launch_gemm_bf16(const bf16_t* A, int lda, const bf16_t* B, int ldb, int M, int N, int K, const Epi& epi,
                             hipStream_t stream);
