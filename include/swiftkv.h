@@ -123,11 +123,11 @@ typedef struct {
 } skv_tensor_view;
 
 /* K and V of layer `layer` (1-based).  Layers of one AcrossKV group return
- * the same memory.  Layout:
- *   K: [num_blocks, n_kv_heads, block_size, head_dim]
- *   V: [num_blocks, n_kv_heads, head_dim, block_size]  (keys innermost)
- * Token position p of a prompt with block table row bt lives in block
- * bt[p / block_size] at offset p % block_size.  K holds RoPE-rotated keys. */
+ * the same memory.  Layout of both: [num_blocks, n_kv_heads, block_size,
+ * head_dim].  Token position p of a prompt with block table row bt lives in
+ * block bt[p / block_size] at offset p % block_size.  K holds RoPE-rotated
+ * keys.  Positions of a prompt's last block beyond its length keep whatever
+ * they held (zero after creation); they must stay finite. */
 skv_status skv_kv_cache_view(const skv_kv_cache* c, int32_t layer, skv_tensor_view* k, skv_tensor_view* v);
 
 /* A batch of independent prompts packed back to back (varlen).

@@ -442,7 +442,7 @@ skv_status skv_kv_cache_view(const skv_kv_cache* c, int32_t layer, skv_tensor_vi
   const int64_t nb = c->num_blocks, hkv = cfg.n_kv_heads, bs = c->block_size, dh = cfg.head_dim;
   const size_t off = (size_t)s * c->slot_elems * c->m->esz;
   *k = skv_tensor_view{(char*)c->k + off, cfg.dtype, 4, {nb, hkv, bs, dh}, {hkv * bs * dh, bs * dh, dh, 1}};
-  *v = skv_tensor_view{(char*)c->v + off, cfg.dtype, 4, {nb, hkv, dh, bs}, {hkv * dh * bs, dh * bs, bs, 1}};
+  *v = skv_tensor_view{(char*)c->v + off, cfg.dtype, 4, {nb, hkv, bs, dh}, {hkv * bs * dh, bs * dh, dh, 1}};
   return SKV_OK;
 }
 

@@ -8,12 +8,15 @@
 //                                     registers (v_mfma_f32_32x32x16_bf16);
 //      each lane then owns one query column, so the online-softmax max and
 //      sum need only the lane's own 32 scores plus one exchange with lane^32;
-//      O^T (dims x queries) += V^T P^T with A = V^T from LDS and B = P^T
-//      taken straight from the score registers (rounded to bf16).
+//      O^T (dims x queries) += V^T P^T with B = P^T taken straight from the
+//      score registers (rounded to bf16) and A = V^T read from the
+//      token-major V tile with ds_read_b64_tr_b16 (gfx950's transposing LDS
+//      read: within 16 lanes, lane j receives element j%4 of the rows
+//      addressed by lanes 4e+j/4, e = 0..3).
 //    The score accumulator holds, in lane half h and element e of 16-key
-//    step kk, key kk*16 + 8*(e/4) + 4*h + e%4; V^T is read from LDS with the
-//    same key order, so both operands agree.  The cache keeps V with keys
-//    innermost per block, so V^T tiles load without a transpose.
+//    step kk, key kk*16 + 8*(e/4) + 4*h + e%4; the V^T reads gather the same
+//    keys, so both operands agree.  K and V tiles share one LDS layout
+//    ([64 keys][128 dims], 16-byte chunk c of key row r at c ^ (r & 15)).
 //    O^T is transposed through LDS at the end and written 8 bytes per lane.
 //
 // 2. attn_rows_kernel + attn_combine_kernel (fp32 or bf16, vector ALU):
@@ -27,6 +30,9 @@
 
 namespace {
 
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef s16x4_t short4_lds_t;
+
 constexpr int FA_DH = 128;
 constexpr int FA_KT = 64;  // keys per tile
 
@@ -35,9 +41,9 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_kernel(const bf16_t* __re
                                                               const int32_t* __restrict__ cu,
                                                               const int32_t* __restrict__ bt, int max_blocks, int hq,
                                                               int rep, float scale_log2, bf16_t* __restrict__ o) {
-  // double-buffered K [64 keys][128] and V^T [128 dims][64 keys]
+  // double-buffered K and V tiles, [64 keys][128 dims] each
   __shared__ __attribute__((aligned(16))) bf16_t sK[2][FA_KT * FA_DH];
-  __shared__ __attribute__((aligned(16))) bf16_t sV[2][FA_DH * FA_KT];
+  __shared__ __attribute__((aligned(16))) bf16_t sV[2][FA_KT * FA_DH];
 
   const int b = blockIdx.y;
   const int tok0 = cu[b];
@@ -81,8 +87,8 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_kernel(const bf16_t* __re
   const int ntiles = (kend + FA_KT - 1) / FA_KT;
   const int32_t* btb = bt + (int64_t)b * max_blocks;
 
-  // tile loader: 4 blocks of 16 keys; thread -> (key = tid/16, chunk = tid%16) for K,
-  // (dim = tid/2, key half = tid%2) for V
+  // tile loader: 4 blocks of 16 keys, each block a contiguous [16][128]
+  // (key, dim) slab of K and of V; thread -> (key = tid/16, chunk = tid%16)
   u32x4_t rk[4], rv[4];
   auto gload = [&](int kt) {
 #pragma unroll
@@ -90,20 +96,10 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_kernel(const bf16_t* __re
       int key0 = kt * FA_KT + r * 16;
       int blk = (key0 < N) ? btb[key0 / 16] : -1;
       if (blk >= 0) {
-        const bf16_t* kb = cache.k + ((int64_t)blk * hkv + g) * (16 * FA_DH);
-        const bf16_t* vb = cache.v + ((int64_t)blk * hkv + g) * (FA_DH * 16);
-        rk[r] = *reinterpret_cast<const u32x4_t*>(kb + tid * 8);
-        u32x4_t vv = *reinterpret_cast<const u32x4_t*>(vb + tid * 8);
-        // zero values of keys beyond the prompt (stale cache contents)
-        int kfirst = key0 + (tid & 1) * 8;
-        if (kfirst + 8 > N) {
-          uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (kfirst + e >= N) w[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
-          vv = u32x4_t{w[0], w[1], w[2], w[3]};
-        }
-        rv[r] = vv;
+        const int64_t off = ((int64_t)blk * hkv + g) * (16 * FA_DH) + tid * 8;
+        rk[r] = *reinterpret_cast<const u32x4_t*>(cache.k + off);
+        // values of keys beyond the prompt (stale cache contents) are zeroed
+        rv[r] = (key0 + (tid >> 4) < N) ? *reinterpret_cast<const u32x4_t*>(cache.v + off) : u32x4_t{0, 0, 0, 0};
       } else {
         rk[r] = u32x4_t{0, 0, 0, 0};
         rv[r] = u32x4_t{0, 0, 0, 0};
@@ -115,12 +111,9 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_kernel(const bf16_t* __re
     for (int r = 0; r < 4; ++r) {
       int key = r * 16 + (tid >> 4);
       int ch = tid & 15;
-      *reinterpret_cast<u32x4_t*>(&sK[buf][key * FA_DH + ((ch ^ (key & 15)) << 3)]) = rk[r];
-      int d = tid >> 1;
-      int u0 = r * 4 + (tid & 1) * 2;  // 8-byte quad index (4 keys) within the 64-key row
-      bf16_t* vrow = &sV[buf][d * FA_KT];
-      *reinterpret_cast<u32x2_t*>(vrow + ((u0 ^ (d & 15)) << 2)) = u32x2_t{rv[r].x, rv[r].y};
-      *reinterpret_cast<u32x2_t*>(vrow + (((u0 + 1) ^ (d & 15)) << 2)) = u32x2_t{rv[r].z, rv[r].w};
+      const int o = key * FA_DH + ((ch ^ (key & 15)) << 3);
+      *reinterpret_cast<u32x4_t*>(&sK[buf][o]) = rk[r];
+      *reinterpret_cast<u32x4_t*>(&sV[buf][o]) = rv[r];
     }
   };
 
@@ -202,17 +195,23 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_kernel(const bf16_t* __re
       }
     }
 
-    // O^T += V^T P^T
+    // O^T += V^T P^T.  Transposing reads: lane l = 16 grp + 4 a + b points
+    // at key kk*16 + 4*(l/32) + a (and +8), dims dbase + 4b .. +3, and
+    // receives keys kk*16 + 4*(l/32) + 0..3 (and +8) of dim dbase + l%16.
+    const int tj = lane & 15, ta = tj >> 2, tb = tj & 3;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
-      const int d = dt * 32 + (lane & 31);
-      const bf16_t* vrow = sv + d * FA_KT;
+      const int d = dt * 32 + 16 * ((lane >> 4) & 1) + 4 * tb;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        const int ua = kk * 4 + hh, ub = kk * 4 + 2 + hh;
-        u32x2_t lo = *reinterpret_cast<const u32x2_t*>(vrow + ((ua ^ (d & 15)) << 2));
-        u32x2_t hi = *reinterpret_cast<const u32x2_t*>(vrow + ((ub ^ (d & 15)) << 2));
-        bf16x8_t vf = as_bf16x8(u32x4_t{lo.x, lo.y, hi.x, hi.y});
+        const int k1 = kk * 16 + 4 * hh + ta, k2 = k1 + 8;
+        typedef __attribute__((address_space(3))) short4_lds_t* lds_s4p;
+        s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s4p)(sv + k1 * FA_DH + (((d >> 3) ^ (k1 & 15)) << 3) + (d & 7)));
+        s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s4p)(sv + k2 * FA_DH + (((d >> 3) ^ (k2 & 15)) << 3) + (d & 7)));
+        u32x2_t lo2 = __builtin_bit_cast(u32x2_t, lo), hi2 = __builtin_bit_cast(u32x2_t, hi);
+        bf16x8_t vf = as_bf16x8(u32x4_t{lo2.x, lo2.y, hi2.x, hi2.y});
 #pragma unroll
         for (int s = 0; s < QT; ++s)
           oacc[s][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[s][kk], oacc[s][dt], 0, 0, 0);
@@ -307,7 +306,7 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const T* __restrict__ q,
 #pragma unroll
   for (int hl = 0; hl < RW_MAXREP; ++hl) sc[hl] = 0.f;
   if (valid) {
-    const T* kr = cache.k + k_index<T>(sl, g, 0, hkv, dh);
+    const T* kr = cache.k + kv_index(sl, g, 0, hkv, dh);
     for (int d = 0; d < dh; ++d) {
       float kv = to_f32<T>(kr[d]);
 #pragma unroll
@@ -342,7 +341,7 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const T* __restrict__ q,
   for (int hl = 0; hl < rep; ++hl) {
     float acc = 0.f;
     for (int j = part * span; j < min(nk, (part + 1) * span); ++j) {
-      acc = fmaf(ps[hl][j], to_f32<T>(cache.v[v_index<T>(sl_s[j], g, d, hkv, dh)]), acc);
+      acc = fmaf(ps[hl][j], to_f32<T>(cache.v[kv_index(sl_s[j], g, d, hkv, dh)]), acc);
     }
     opart[part][d] = acc;
     __syncthreads();

@@ -63,7 +63,8 @@ struct TokenMeta {
 };
 
 // Paged cache geometry of one KV slot (one layer or AcrossKV group).
-//   K: [num_blocks, hkv, BS, dh]     V: [num_blocks, hkv, dh, BS]
+// K and V share the layout [num_blocks, hkv, BS, dh]: a (token, head) row of
+// dh values is contiguous, so GEMM epilogues write whole row segments.
 template <typename T>
 struct CacheSlot {
   T* k;
@@ -74,13 +75,8 @@ struct CacheSlot {
 
 constexpr int kBlockSize = 16;
 
-template <typename T>
-SKV_DEV int64_t k_index(int slot_phys, int h, int d, int hkv, int dh) {
+// element index of (physical slot, head, dim) in one cache tensor
+SKV_DEV int64_t kv_index(int slot_phys, int h, int d, int hkv, int dh) {
   int blk = slot_phys >> 4, off = slot_phys & 15;
   return (((int64_t)blk * hkv + h) * kBlockSize + off) * dh + d;
-}
-template <typename T>
-SKV_DEV int64_t v_index(int slot_phys, int h, int d, int hkv, int dh) {
-  int blk = slot_phys >> 4, off = slot_phys & 15;
-  return (((int64_t)blk * hkv + h) * dh + d) * kBlockSize + off;
 }

@@ -95,12 +95,12 @@ struct EpiQKV {
       float c = rope_cos[(int64_t)p * P + i], s = rope_sin[(int64_t)p * P + i];
       float y0, y1;
       rope_pair(v0, v1, c, s, y0, y1);
-      cache.k[k_index<T>(sl, h, i, cache.hkv, dh)] = from_f32<T>(y0);
-      cache.k[k_index<T>(sl, h, i + P, cache.hkv, dh)] = from_f32<T>(y1);
+      cache.k[kv_index(sl, h, i, cache.hkv, dh)] = from_f32<T>(y0);
+      cache.k[kv_index(sl, h, i + P, cache.hkv, dh)] = from_f32<T>(y1);
     } else {
       int vc = col - dq - dkv, h = vc / dh, i = vc % dh;
-      cache.v[v_index<T>(sl, h, i, cache.hkv, dh)] = from_f32<T>(v0);
-      cache.v[v_index<T>(sl, h, i + P, cache.hkv, dh)] = from_f32<T>(v1);
+      cache.v[kv_index(sl, h, i, cache.hkv, dh)] = from_f32<T>(v0);
+      cache.v[kv_index(sl, h, i + P, cache.hkv, dh)] = from_f32<T>(v1);
     }
   }
 };
@@ -130,13 +130,13 @@ struct EpiKVSkip {
       float y0, y1;
       rope_pair(a, b, cs, sn, y0, y1);
       T* kp = k0 + g * slot_stride;
-      kp[k_index<T>(sl, h, i, hkv, dh)] = from_f32<T>(y0);
-      kp[k_index<T>(sl, h, i + P, hkv, dh)] = from_f32<T>(y1);
+      kp[kv_index(sl, h, i, hkv, dh)] = from_f32<T>(y0);
+      kp[kv_index(sl, h, i + P, hkv, dh)] = from_f32<T>(y1);
     } else {
       int vc = c - dkv, h = vc / dh, i = vc % dh;
       T* vp = v0 + g * slot_stride;
-      vp[v_index<T>(sl, h, i, hkv, dh)] = from_f32<T>(a);
-      vp[v_index<T>(sl, h, i + P, hkv, dh)] = from_f32<T>(b);
+      vp[kv_index(sl, h, i, hkv, dh)] = from_f32<T>(a);
+      vp[kv_index(sl, h, i + P, hkv, dh)] = from_f32<T>(b);
     }
   }
 };

@@ -113,7 +113,7 @@ class Cache:
         return t.view(torch.bfloat16) if v.dtype == L.SKV_BF16 else t
 
     def read_layer(self, layer: int):
-        """Device copies of (K [nb, hkv, bs, dh], V [nb, hkv, dh, bs]) of a layer."""
+        """Device copies of (K, V) of a layer, each [num_blocks, hkv, block_size, dh]."""
         k, v = self.view(layer)
         return self._copy_view(k), self._copy_view(v)
 
@@ -136,7 +136,7 @@ def logical_kv(kt, vt, block_row: np.ndarray, n: int):
     nb = -(-n // bs)
     idx = torch.as_tensor(np.asarray(block_row[:nb], dtype=np.int64), device=kt.device)
     k = kt.index_select(0, idx).permute(0, 2, 1, 3).reshape(nb * bs, kt.shape[1], kt.shape[3])[:n]
-    v = vt.index_select(0, idx).permute(0, 3, 1, 2).reshape(nb * bs, vt.shape[1], vt.shape[2])[:n]
+    v = vt.index_select(0, idx).permute(0, 2, 1, 3).reshape(nb * bs, vt.shape[1], vt.shape[3])[:n]
     return k.float().cpu().numpy(), v.float().cpu().numpy()
 
 
