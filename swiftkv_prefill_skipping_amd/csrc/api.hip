@@ -87,6 +87,8 @@ struct skv_model {
   int64_t partial_elems = 0;
   float* attn_ws = nullptr;
   int64_t attn_ws_elems = 0;
+  float* gemm_ws = nullptr;  // split partial tiles of the GEMMs
+  int64_t gemm_ws_elems = 0;
 
   // profiling
   int prof_class = -1;
@@ -293,6 +295,10 @@ skv_status skv_model_create(const skv_model_config* cfg, skv_model** out) {
     m->attn_ws_elems = attn_rows_ws_elems((int)std::max(T, B), c.max_seqlen, c.n_q_heads, c.head_dim);
   }
   ALLOC(m->attn_ws, (size_t)m->attn_ws_elems * 4);
+  if (m->bf16) {
+    m->gemm_ws_elems = gemm_bf16_ws_elems();
+    ALLOC(m->gemm_ws, (size_t)m->gemm_ws_elems * 4);
+  }
 #undef ALLOC
 
   // RoPE tables: angle p * theta^(-2i/dh) in double, cos/sin rounded to fp32
@@ -519,7 +525,7 @@ skv_status run_prefill(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, floa
       EpiQKV<T> epi{qbuf, cs, m->pos, m->slot, m->rope_cos, m->rope_sin, dq, dkv, dh, P};
       Prof p(m, SKV_K_GEMM_QKV, s, 2.0 * T_ * N * d, gemm_bytes(T_, N, d, E, E));
       if constexpr (kBf16)
-        SKV_HIP(launch_gemm_bf16((const bf16_t*)act, d, (const bf16_t*)Ly.wqkv, d, T_, N, d, epi, s));
+        SKV_HIP(launch_gemm_bf16((const bf16_t*)act, d, (const bf16_t*)Ly.wqkv, d, T_, N, d, epi, m->gemm_ws, m->gemm_ws_elems, s));
       else if (P == 16)
         SKV_HIP((launch_gemm_f32<16>((const float*)act, d, (const float*)Ly.wqkv, d, T_, N, d, epi, s)));
       else if (P == 32)
@@ -540,7 +546,7 @@ skv_status run_prefill(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, floa
       EpiResidual epi{m->x, d, kBf16 ? 64 : 16};
       Prof p(m, SKV_K_GEMM_O, s, 2.0 * T_ * d * dq, gemm_bytes(T_, d, dq, E, 8));
       if constexpr (kBf16)
-        SKV_HIP(launch_gemm_bf16((const bf16_t*)obuf, dq, (const bf16_t*)Ly.wo, dq, T_, d, dq, epi, s));
+        SKV_HIP(launch_gemm_bf16((const bf16_t*)obuf, dq, (const bf16_t*)Ly.wo, dq, T_, d, dq, epi, m->gemm_ws, m->gemm_ws_elems, s));
       else
         SKV_HIP((launch_gemm_f32<16>((const float*)obuf, dq, (const float*)Ly.wo, dq, T_, d, dq, epi, s)));
     }
@@ -552,7 +558,7 @@ skv_status run_prefill(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, floa
       EpiSwiGLU<T> epi{hbuf, f, m->p_mlp};
       Prof p(m, SKV_K_GEMM_GATEUP, s, 2.0 * T_ * 2 * f * d, gemm_bytes(T_, 2.0 * f, d, E, 0) + (double)T_ * f * E);
       if constexpr (kBf16)
-        SKV_HIP(launch_gemm_bf16((const bf16_t*)act, d, (const bf16_t*)Ly.wgu, d, T_, 2 * f, d, epi, s));
+        SKV_HIP(launch_gemm_bf16((const bf16_t*)act, d, (const bf16_t*)Ly.wgu, d, T_, 2 * f, d, epi, m->gemm_ws, m->gemm_ws_elems, s));
       else
         SKV_HIP((launch_gemm_f32<16>((const float*)act, d, (const float*)Ly.wgu, d, T_, 2 * f, d, epi, s)));
     }
@@ -560,7 +566,7 @@ skv_status run_prefill(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, floa
       EpiResidual epi{m->x, d, kBf16 ? 64 : 16};
       Prof p(m, SKV_K_GEMM_DOWN, s, 2.0 * T_ * d * f, gemm_bytes(T_, d, f, E, 8));
       if constexpr (kBf16)
-        SKV_HIP(launch_gemm_bf16((const bf16_t*)hbuf, f, (const bf16_t*)Ly.wdown, f, T_, d, f, epi, s));
+        SKV_HIP(launch_gemm_bf16((const bf16_t*)hbuf, f, (const bf16_t*)Ly.wdown, f, T_, d, f, epi, m->gemm_ws, m->gemm_ws_elems, s));
       else
         SKV_HIP((launch_gemm_f32<16>((const float*)hbuf, f, (const float*)Ly.wdown, f, T_, d, f, epi, s)));
     }
@@ -578,7 +584,7 @@ skv_status run_prefill(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, floa
                      c.n_kv_heads};
     Prof p(m, SKV_K_GEMM_KVSKIP, s, 2.0 * T_ * N * d, gemm_bytes(T_, N, d, E, E));
     if constexpr (kBf16)
-      SKV_HIP(launch_gemm_bf16((const bf16_t*)act, d, (const bf16_t*)m->wkv_skip, d, T_, N, d, epi, s));
+      SKV_HIP(launch_gemm_bf16((const bf16_t*)act, d, (const bf16_t*)m->wkv_skip, d, T_, N, d, epi, m->gemm_ws, m->gemm_ws_elems, s));
     else if (P == 16)
       SKV_HIP((launch_gemm_f32<16>((const float*)act, d, (const float*)m->wkv_skip, d, T_, N, d, epi, s)));
     else if (P == 32)

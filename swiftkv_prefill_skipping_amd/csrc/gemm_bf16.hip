@@ -57,23 +57,52 @@ SKV_DEV void wait_loads_and_reads() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// Tile index -> (row tile, column tile) in grouped order: kGroupM row tiles
+// walked down, then the next column tile.
+SKV_DEV void tile_coords(int tile, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int per_group = kGroupM * tiles_n;
+  const int first_m = (tile / per_group) * kGroupM;
+  const int gsize = min(tiles_m - first_m, kGroupM);
+  tm = first_m + (tile % per_group) % gsize;
+  tn = (tile % per_group) / gsize;
+}
+
+// Work split of one launch.  The first dp_tiles tiles are computed whole
+// (data parallel, grid blocks 0 .. dp_tiles-1, XCD remapped); each of the
+// remaining tiles is split along K into `splits` ranges (stream-K tail),
+// one grid block per range, whose fp32 partial tiles go to `ws` and are
+// summed in fixed order by gemm_reduce_kernel.
+struct SplitPlan {
+  int dp_tiles;
+  int splits;
+  float* ws;
+};
+
 template <class Epi>
 __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(const bf16_t* __restrict__ A,
                                                                  const bf16_t* __restrict__ B, int M, int N,
-                                                                 int K, int lda, int ldb, Epi epi) {
+                                                                 int K, int lda, int ldb, SplitPlan plan, Epi epi) {
   __shared__ __attribute__((aligned(16))) bf16_t smem[2][(BM + BN) * BK];
 
   const int tiles_m = (M + BM - 1) / BM;
   const int tiles_n = (N + BN - 1) / BN;
-  const int ntiles = tiles_m * tiles_n;
-  const int tile = xcd_remap(blockIdx.x, ntiles);
-  // grouped order: kGroupM row tiles walked down, then the next column tile
-  const int per_group = kGroupM * tiles_n;
-  const int grp_t = tile / per_group;
-  const int first_m = grp_t * kGroupM;
-  const int gsize = min(tiles_m - first_m, kGroupM);
-  const int tm = first_m + (tile % per_group) % gsize;
-  const int tn = (tile % per_group) / gsize;
+  const int nk_all = K / BK;
+  const int bid = blockIdx.x;
+  const bool split = bid >= plan.dp_tiles;
+  int tile, kb, ke, unit = 0;
+  if (!split) {
+    tile = xcd_remap(bid, plan.dp_tiles);
+    kb = 0;
+    ke = nk_all;
+  } else {
+    unit = bid - plan.dp_tiles;
+    tile = plan.dp_tiles + unit / plan.splits;
+    const int sp = unit % plan.splits;
+    kb = sp * nk_all / plan.splits;
+    ke = (sp + 1) * nk_all / plan.splits;
+  }
+  int tm, tn;
+  tile_coords(tile, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
 
   const int tid = threadIdx.x;
@@ -154,44 +183,52 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(const bf16_t* __
 
   // Ping-pong over the two waves of each SIMD: every wave runs the same
   // sequence of phases separated by workgroup barriers -- read the first
-  // half of stage s from LDS, multiply it (16 MFMAs), read the second half,
-  // multiply it -- and group 1 starts one barrier late, so in every slot one
-  // wave of each SIMD is on the matrix core while the other reads LDS.
-  // Group 0 reads stage s in slots 4s and 4s+2, group 1 in 4s+1 and 4s+3.
-  // The loads of stage s+1 go into the other buffer in slot 4s, after its
-  // last reads (stage s-1, slot 4s-1): group 0 issues them in its first read
-  // phase of stage s, group 1 right after its last MFMAs of stage s-1.  Each
-  // wave waits for them at the end of slot 4s+3 (group 0 after its last
-  // MFMAs of stage s, group 1 after its last reads), before stage s+1 is
-  // first read in slot 4s+4: three slots of latency cover.  Every wave
-  // passes 2 + 4 nk barriers.
-  const int nk = K / BK;
-  gload(0, 0);
+  // half of stage s from LDS (and issue its share of the loads of stage s+1
+  // into the other buffer), multiply it (16 MFMAs), read the second half and
+  // wait for its loads, multiply it -- and group 1 starts one barrier late,
+  // so in every slot one wave of each SIMD is on the matrix core while the
+  // other reads LDS.  Group 0 reads stage s in slots 4s and 4s+2, group 1 in
+  // 4s+1 and 4s+3; the loads of stage s+1 go out in slots 4s / 4s+1, after
+  // the last reads of that buffer (stage s-1, slot 4s-1), and each wave
+  // waits for them at the end of its second read phase (slot 4s+2 / 4s+3),
+  // before stage s+1 is first read in slot 4s+4.  Every wave passes
+  // 2 + 4 nk barriers.
+  const int nk = ke - kb;
+  const int k_base = kb * BK;
+  gload(0, k_base);
   wait_loads_and_reads();
   barrier_only();
-  if (pp == 1) {
-    if (nk > 1) gload(1, BK);
-    barrier_only();
-  }
+  if (pp == 1) barrier_only();
   for (int s = 0; s < nk; ++s) {
     const int cur = s & 1;
     fload(cur, 0);
-    if (pp == 0 && s + 1 < nk) gload(cur ^ 1, (s + 1) * BK);
+    if (s + 1 < nk) gload(cur ^ 1, k_base + (s + 1) * BK);
     barrier_only();
     compute();
     barrier_only();
     fload(cur, 1);
-    if (pp == 1) wait_loads_and_reads();
+    wait_loads_and_reads();
     barrier_only();
     compute();
-    if (pp == 1 && s + 2 < nk) gload(cur, (s + 2) * BK);
-    if (pp == 0) wait_loads_and_reads();
     barrier_only();
   }
   if (pp == 0) barrier_only();
 
   // epilogue: lane holds column (lane & 31) of each 32x32 tile and rows
   // 8*(v/4) + 4*(lane/32) + (v%4)
+  if (split) {
+    float* part = plan.ws + (int64_t)unit * (BM * BN);
+    const int cl = wn * 128 + (lane & 31);
+    const int rl = wm * 64 + 4 * (lane >> 5);
+#pragma clang loop unroll(full)
+    for (int i = 0; i < 2; ++i)
+#pragma clang loop unroll(full)
+      for (int j = 0; j < 4; ++j)
+#pragma clang loop unroll(full)
+        for (int v = 0; v < 16; ++v)
+          part[(rl + i * 32 + 8 * (v >> 2) + (v & 3)) * BN + cl + j * 32] = acc[i][j][v];
+    return;
+  }
   const int col_base = n0 + wn * 128 + (lane & 31);
   const int row_base = m0 + wm * 64 + 4 * (lane >> 5);
 #pragma clang loop unroll(full)
@@ -209,26 +246,78 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(const bf16_t* __
   }
 }
 
+// Sum the split partial tiles in fixed order and apply the epilogue:
+// thread -> (tail tile, row, column pair (c, c + 64)).
+template <class Epi>
+__global__ __launch_bounds__(256) void gemm_reduce_kernel(int M, int N, SplitPlan plan, Epi epi) {
+  const int tiles_n = (N + BN - 1) / BN;
+  const int tiles_m = (M + BM - 1) / BM;
+  const int r = blockIdx.y;  // tail tile
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;  // row * 128 + pair
+  const int row = idx >> 7, pair = idx & 127;
+  const int cl = (pair >> 6) * 128 + (pair & 63);
+  int tm, tn;
+  tile_coords(plan.dp_tiles + r, tiles_m, tiles_n, tm, tn);
+  const int grow = tm * BM + row, gcol = tn * BN + cl;
+  if (grow >= M || gcol >= N) return;
+  const float* part = plan.ws + (int64_t)r * plan.splits * (BM * BN) + row * BN + cl;
+  float v0 = 0.f, v1 = 0.f;
+  for (int sp = 0; sp < plan.splits; ++sp) {
+    v0 += part[(int64_t)sp * (BM * BN)];
+    v1 += part[(int64_t)sp * (BM * BN) + 64];
+  }
+  epi(grow, gcol, v0, v1);
+}
+
+int num_cus() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+  }
+  return n;
+}
+
 }  // namespace
+
+int64_t gemm_bf16_ws_elems() { return (int64_t)num_cus() * BM * BN; }
 
 template <class Epi>
 hipError_t launch_gemm_bf16(const bf16_t* A, int lda, const bf16_t* B, int ldb, int M, int N, int K, const Epi& epi,
-                            hipStream_t stream) {
+                            float* ws, int64_t ws_elems, hipStream_t stream) {
   if (M <= 0) return hipSuccess;
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_bf16_kernel<Epi>), dim3(tiles), dim3(kThreads), 0, stream, A, B, M, N, K, lda, ldb, epi);
+  const int P = num_cus();
+  const int nk = K / BK;
+  // a partly filled last wave of whole tiles is replaced by K-split units
+  // that fill every CU (at least 2 k-stages per unit)
+  SplitPlan plan{tiles, 1, ws};
+  const int rem = tiles % P;
+  if (ws != nullptr && tiles >= P && rem != 0) {
+    const int splits = min(P / rem, nk / 2);
+    if (splits >= 2 && (int64_t)rem * splits * BM * BN <= ws_elems) {
+      plan.dp_tiles = tiles - rem;
+      plan.splits = splits;
+    }
+  }
+  const int grid = plan.dp_tiles + (tiles - plan.dp_tiles) * plan.splits;
+  hipLaunchKernelGGL((gemm_bf16_kernel<Epi>), dim3(grid), dim3(kThreads), 0, stream, A, B, M, N, K, lda, ldb, plan,
+                     epi);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || plan.dp_tiles == tiles) return e;
+  hipLaunchKernelGGL((gemm_reduce_kernel<Epi>), dim3(BM * 128 / 256, tiles - plan.dp_tiles), dim3(256), 0, stream, M,
+                     N, plan, epi);
   return hipGetLastError();
 }
 
-template hipError_t launch_gemm_bf16<EpiQKV<bf16_t>>(const bf16_t*, int, const bf16_t*, int, int, int, int,
-                                                     const EpiQKV<bf16_t>&, hipStream_t);
-template hipError_t launch_gemm_bf16<EpiKVSkip<bf16_t>>(const bf16_t*, int, const bf16_t*, int, int, int, int,
-                                                        const EpiKVSkip<bf16_t>&, hipStream_t);
-template hipError_t launch_gemm_bf16<EpiResidual>(const bf16_t*, int, const bf16_t*, int, int, int, int,
-                                                  const EpiResidual&, hipStream_t);
-template hipError_t launch_gemm_bf16<EpiSwiGLU<bf16_t>>(const bf16_t*, int, const bf16_t*, int, int, int, int,
-                                                        const EpiSwiGLU<bf16_t>&, hipStream_t);
-template hipError_t launch_gemm_bf16<EpiStore<bf16_t>>(const bf16_t*, int, const bf16_t*, int, int, int, int,
-                                                       const EpiStore<bf16_t>&, hipStream_t);
-template hipError_t launch_gemm_bf16<EpiStoreF32>(const bf16_t*, int, const bf16_t*, int, int, int, int,
-                                                  const EpiStoreF32&, hipStream_t);
+#define SKV_INST_GEMM(E)                                                                                      \
+  template hipError_t launch_gemm_bf16<E>(const bf16_t*, int, const bf16_t*, int, int, int, int, const E&, float*, \
+                                          int64_t, hipStream_t);
+SKV_INST_GEMM(EpiQKV<bf16_t>)
+SKV_INST_GEMM(EpiKVSkip<bf16_t>)
+SKV_INST_GEMM(EpiResidual)
+SKV_INST_GEMM(EpiSwiGLU<bf16_t>)
+SKV_INST_GEMM(EpiStore<bf16_t>)
+SKV_INST_GEMM(EpiStoreF32)

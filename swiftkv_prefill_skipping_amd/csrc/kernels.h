@@ -7,10 +7,12 @@
 #include "epilogues.h"
 
 // C[M,N] = A[M,K] B[N,K]^T on MFMA (bf16 in, fp32 accumulate), pair distance 64.
-// Requires K % 64 == 0, N % 128 == 0.
+// Requires K % 64 == 0, N % 128 == 0.  ws (gemm_bf16_ws_elems() floats, or
+// NULL) holds the split partial tiles of a partly filled last wave.
 template <class Epi>
 hipError_t launch_gemm_bf16(const bf16_t* A, int lda, const bf16_t* B, int ldb, int M, int N, int K, const Epi& epi,
-                            hipStream_t stream);
+                            float* ws, int64_t ws_elems, hipStream_t stream);
+int64_t gemm_bf16_ws_elems();
 
 // Same product in fp32 on the vector ALUs (fp32 models), pair distance P
 // (P in {16, 32, 64}); requires N % (2P) == 0.
