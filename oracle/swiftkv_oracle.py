@@ -189,25 +189,36 @@ def swiglu_mlp(m: np.ndarray, W: Dict[str, np.ndarray], fc: Optional[FlopCounter
     return matmul_wt(h, W["w_down"], fc)
 
 
+def _keep(t: np.ndarray) -> np.ndarray:
+    return t
+
+
 def qkv_projection(x: np.ndarray, W: Dict[str, np.ndarray], pos: np.ndarray, dims: Dims,
-                   fc: Optional[FlopCounter]):
+                   fc: Optional[FlopCounter], store: Callable = _keep):
     """RMSNorm then q/k/v projections, RoPE on q and k.  Returns q [n,hq,dh], k, v [n,hkv,dh]."""
     n = x.shape[0]
-    a = rmsnorm(x, W["attn_norm"], dims.rms_eps)
+    a = store(rmsnorm(x, W["attn_norm"], dims.rms_eps))
     q = matmul_wt(a, W["wq"], fc).reshape(n, dims.n_q_heads, dims.head_dim)
     k = matmul_wt(a, W["wk"], fc).reshape(n, dims.n_kv_heads, dims.head_dim)
     v = matmul_wt(a, W["wv"], fc).reshape(n, dims.n_kv_heads, dims.head_dim)
-    return rope(q, pos, dims.rope_theta), rope(k, pos, dims.rope_theta), v
+    return store(rope(q, pos, dims.rope_theta)), store(rope(k, pos, dims.rope_theta)), store(v)
+
+
+def mlp_residual(x: np.ndarray, W: Dict[str, np.ndarray], dims: Dims, fc: Optional[FlopCounter],
+                 store: Callable = _keep) -> np.ndarray:
+    """x + W_d(silu(W_g m) * W_u m) with m = RMSNorm(x; ffn gain)."""
+    m = store(rmsnorm(x, W["ffn_norm"], dims.rms_eps))
+    h = store(silu(matmul_wt(m, W["w_gate"], fc)) * matmul_wt(m, W["w_up"], fc))
+    return x + matmul_wt(h, W["w_down"], fc)
 
 
 def decoder_layer(x: np.ndarray, W: Dict[str, np.ndarray], pos: np.ndarray, dims: Dims,
-                  fc: Optional[FlopCounter]):
+                  fc: Optional[FlopCounter], store: Callable = _keep):
     """Standard pre-norm layer over all n positions of one prompt.  Returns (x_next, K, V)."""
-    q, k, v = qkv_projection(x, W, pos, dims, fc)
-    o = causal_gqa_attention(q, k, v, fc)
+    q, k, v = qkv_projection(x, W, pos, dims, fc, store)
+    o = store(causal_gqa_attention(q, k, v, fc))
     x = x + matmul_wt(o, W["wo"], fc)
-    x = x + swiglu_mlp(rmsnorm(x, W["ffn_norm"], dims.rms_eps), W, fc)
-    return x, k, v
+    return mlp_residual(x, W, dims, fc, store), k, v
 
 
 # ----------------------------------------------------------------------------
@@ -286,12 +297,20 @@ class OracleResult:
 
 
 def swiftkv_prefill(dims: Dims, weights: WeightSource, prompts: Sequence[np.ndarray], l: int, g: int = 1,
-                    dtype=np.float32) -> OracleResult:
+                    dtype=np.float32, store: Optional[Callable] = None) -> OracleResult:
     """SwiftKV prefill of a batch of independent prompts (steps 1-5 of the module docstring).
 
     Layers are visited in increasing order exactly once (layer-major), so a
     streaming WeightSource can generate each layer when it is asked for.
+
+    ``store`` (default: keep values as computed) is applied where a reduced-
+    precision inference path stores a tensor: the RMSNorm outputs fed to the
+    projections, q / k / v after RoPE, the attention output, the SwiGLU
+    output.  With a bf16 rounding function this evaluates the same definition
+    with bf16 storage (the precision the pages serve in), which measures how
+    far bf16 storage alone moves each output from the plain evaluation.
     """
+    st = store if store is not None else _keep
     L = dims.n_layers
     if not 0 <= l <= L:
         raise ValueError(f"swiftkv l={l} outside 0..{L}")
@@ -308,7 +327,7 @@ def swiftkv_prefill(dims: Dims, weights: WeightSource, prompts: Sequence[np.ndar
     for i in range(1, l + 1):                                                     # step 2
         W = weights.layer(i)
         for b in range(len(prompts)):
-            xs[b], k, v = decoder_layer(xs[b], W, pos[b], dims, fc)
+            xs[b], k, v = decoder_layer(xs[b], W, pos[b], dims, fc, st)
             kv[b][i - 1] = (k, v)
 
     ys = [x[-1:].copy() for x in xs]                                              # last token rows
@@ -318,22 +337,22 @@ def swiftkv_prefill(dims: Dims, weights: WeightSource, prompts: Sequence[np.ndar
         if representative(j, l, g) == j:                                          # step 3 (Eq. 2)
             for b in range(len(prompts)):
                 n = xs[b].shape[0]
-                a = rmsnorm(xs[b], W["attn_norm"], eps)
+                a = st(rmsnorm(xs[b], W["attn_norm"], eps))
                 k = matmul_wt(a, W["wk"], fc).reshape(n, dims.n_kv_heads, dims.head_dim)
                 v = matmul_wt(a, W["wv"], fc).reshape(n, dims.n_kv_heads, dims.head_dim)
-                kv[b][s] = (rope(k, pos[b], dims.rope_theta), v)
+                kv[b][s] = (st(rope(k, pos[b], dims.rope_theta)), st(v))
         for b in range(len(prompts)):                                             # step 4
             n = xs[b].shape[0]
             K, V = kv[b][s]
-            a = rmsnorm(ys[b], W["attn_norm"], eps)
+            a = st(rmsnorm(ys[b], W["attn_norm"], eps))
             q = matmul_wt(a, W["wq"], fc).reshape(1, dims.n_q_heads, dims.head_dim)
-            q = rope(q, np.array([n - 1]), dims.rope_theta)
-            o = single_query_attention(q[0], K, V, fc)[None, :]
+            q = st(rope(q, np.array([n - 1]), dims.rope_theta))
+            o = st(single_query_attention(q[0], K, V, fc)[None, :])
             y = ys[b] + matmul_wt(o, W["wo"], fc)
-            ys[b] = y + swiglu_mlp(rmsnorm(y, W["ffn_norm"], eps), W, fc)
+            ys[b] = mlp_residual(y, W, dims, fc, st)
 
     logits = np.concatenate(                                                      # step 5
-        [matmul_wt(rmsnorm(y, weights.final_norm, eps), weights.lm_head, fc) for y in ys], axis=0)
+        [matmul_wt(st(rmsnorm(y, weights.final_norm, eps)), weights.lm_head, fc) for y in ys], axis=0)
     return OracleResult(kv, logits, fc.total, xs)
 
 

@@ -50,22 +50,64 @@ def gpu_kv(cache, w, batch, b):
     return out
 
 
-def compare(w, batch, logits, cache, ores, prompts, tol=None, label=""):
+def frob_rel(got, ref) -> float:
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    return float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300))
+
+
+# bf16-limited regime: a tensor whose bf16-storage evaluation itself differs
+# from the fp32 evaluation by more than the bar passes if the GPU is no worse
+# than that (1.5x on the max-normalised error, 1.1x + 1e-3 on the norm ratio)
+BF16_MAX_FACTOR, BF16_FROB_FACTOR, BF16_FROB_SLACK = 1.5, 1.1, 1e-3
+
+
+def compare(w, batch, logits, cache, ores, prompts, tol=None, label="", bf16_ref=None):
+    """Compare every KV slot and the logits of the given prompts; print the whole error profile, then assert.
+
+    Per tensor: e = max|gpu - oracle| / max|oracle| must stay below tol.
+    With ``bf16_ref`` (the oracle evaluated with bf16 storage), a tensor
+    with e >= tol still passes if e <= 1.5 e_bf16 and
+    frob(gpu) <= 1.1 frob(bf16) + 1e-3, e_bf16 / frob(bf16) being the same
+    measures of the bf16-storage evaluation against the plain one.
+    """
     tol = tol if tol is not None else TOL[w.dtype]
-    worst = 0.0
+    worst, fails, lines, limited = 0.0, [], [], 0
     lg = logits.float().cpu().numpy()
+
+    def judge(g, o, r, name):
+        nonlocal worst, limited
+        e = max_rel(g, o)
+        worst = max(worst, e)
+        if e < tol:
+            return f"{e:.1e}"
+        if r is not None:
+            er, fg, fr = max_rel(r, o), frob_rel(g, o), frob_rel(r, o)
+            if e <= BF16_MAX_FACTOR * er and fg <= BF16_FROB_FACTOR * fr + BF16_FROB_SLACK:
+                limited += 1
+                return f"{e:.1e}(bf16 {er:.1e}, frob {fg:.1e}/{fr:.1e})"
+            fails.append(f"{name}: {e:.3e} (bf16-storage {er:.3e}; frob {fg:.3e} vs {fr:.3e})")
+        else:
+            fails.append(f"{name}: {e:.3e}")
+        return f"{e:.1e}!"
+
     for ob, b in enumerate(prompts):
         gkv = gpu_kv(cache, w, batch, b)
         assert set(gkv) == set(ores.kv[ob]), "slot sets differ"
+        row = []
         for s in sorted(gkv):
-            for t, name in ((0, "K"), (1, "V")):
-                e = max_rel(gkv[s][t], ores.kv[ob][s][t])
-                worst = max(worst, e)
-                assert e < tol, f"{label} prompt {b} slot {s} {name}: max rel err {e:.3e} >= {tol}"
-        e = max_rel(lg[b], ores.logits[ob])
-        worst = max(worst, e)
-        assert e < tol, f"{label} prompt {b} logits: max rel err {e:.3e} >= {tol}"
-    _say(f"[parity] {label}: worst max-rel error {worst:.3e} (bar {tol})")
+            rk = bf16_ref.kv[ob][s] if bf16_ref is not None else (None, None)
+            ek = judge(gkv[s][0], ores.kv[ob][s][0], rk[0], f"prompt {b} slot {s} K")
+            ev = judge(gkv[s][1], ores.kv[ob][s][1], rk[1], f"prompt {b} slot {s} V")
+            row.append(f"{s}:{ek}/{ev}")
+        el = judge(lg[b], ores.logits[ob], bf16_ref.logits[ob] if bf16_ref is not None else None,
+                   f"prompt {b} logits")
+        lines.append(f"  prompt {b}: logits {el}; slot K/V " + " ".join(row))
+    _say(f"[parity] {label}: worst max-rel error {worst:.3e} (bar {tol}; {limited} tensors in the bf16-limited "
+         f"regime)")
+    for ln in lines:
+        _say(ln)
+    assert not fails, f"{label}: " + "; ".join(fails[:8]) + (" ..." if len(fails) > 8 else "")
     return worst
 
 

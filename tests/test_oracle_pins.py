@@ -439,3 +439,34 @@ def test_invalid_arguments_rejected():
         O.swiftkv_prefill(dims, W, [np.array([1, 2])], l=1, g=0)
     with pytest.raises(ValueError):
         O.swiftkv_prefill(dims, W, [np.array([], dtype=np.int64)], l=1)
+
+
+def _round_bf16(x):
+    return si.bf16_to_f32(si.f32_to_bf16(np.ascontiguousarray(x, dtype=np.float32))).reshape(x.shape)
+
+
+def test_storage_mode_identity_is_plain_evaluation():
+    dims = tiny_dims()
+    W = tiny_weights(dims, dtype=np.float32)
+    ps = prompts_for(dims, [13, 6])
+    a = O.swiftkv_prefill(dims, W, ps, l=2, g=1)
+    b = O.swiftkv_prefill(dims, W, ps, l=2, g=1, store=lambda t: t)
+    assert np.array_equal(a.logits, b.logits)
+    for i in range(2):
+        for s in a.kv[i]:
+            assert np.array_equal(a.kv[i][s][0], b.kv[i][s][0]) and np.array_equal(a.kv[i][s][1], b.kv[i][s][1])
+
+
+def test_bf16_storage_mode_rounds_what_it_stores():
+    """With bf16 storage every K/V tensor is bf16-representable and the outputs move by bf16-sized amounts."""
+    dims = tiny_dims()
+    W = tiny_weights(dims, dtype=np.float32)
+    ps = prompts_for(dims, [17])
+    ref = O.swiftkv_prefill(dims, W, ps, l=2, g=2)
+    emu = O.swiftkv_prefill(dims, W, ps, l=2, g=2, store=_round_bf16)
+    for s, (k, v) in emu.kv[0].items():
+        assert np.array_equal(k, _round_bf16(k)) and np.array_equal(v, _round_bf16(v))
+        e = rel(k, ref.kv[0][s][0])
+        assert 0 < e < 0.05, (s, e)
+    e = rel(emu.logits, ref.logits)
+    assert 0 < e < 0.05
