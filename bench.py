@@ -1,6 +1,7 @@
 """Throughput of the SwiftKV prefill on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py --copy-calibration MIB   # plain device copy of known size, for HBM counter scaling
 
 One step = one skv_prefill call over the whole batch (every row of the hot
 path: layers 1..l for all prompt tokens, the fused skipped-layer KV GEMM,
@@ -25,6 +26,31 @@ MI355X_BF16_DENSE_TFLOPS = 2500.0   # 256 CU x 2.4 GHz x 4096 FLOP/clk/CU (dense
 MI355X_HBM_GBS = 8000.0
 
 
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "gemm_bf16_hbm_traffic_llama8b_l16_b16.md")
+
+
+def measured_traffic(kernel_key: str):
+    """HBM-side bytes per launch of one GEMM kernel from the committed counter record, or None.
+
+    The record holds FETCH_SIZE / WRITE_SIZE per dispatch scaled by a copy
+    kernel of known size; it is used only while the GEMM sources still hash to
+    the value it was taken with.
+    """
+    import hashlib
+    try:
+        text = open(TRAFFIC_RECORD).read()
+        rec = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
+        csrc = os.path.join(ROOT, "swiftkv_prefill_skipping_amd", "csrc")
+        sha = hashlib.sha256(b"".join(open(os.path.join(csrc, f), "rb").read() for f in rec["files"])).hexdigest()
+        if sha != rec["source_sha256"]:
+            return None
+        k = rec["kernels"][kernel_key]
+        return {"read_bytes": k["read_bytes_per_launch"], "write_bytes": k["write_bytes_per_launch"],
+                "bytes": k["read_bytes_per_launch"] + k["write_bytes_per_launch"], "unit": "bytes/launch"}
+    except (OSError, IndexError, KeyError, ValueError):
+        return None
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -45,6 +71,20 @@ def cpu_baseline(workload, batch, cached, budget_prompt=None):
             "sample": f"prompt {b} of the batch ({n} tokens), fp32 NumPy oracle, {dt:.1f} s wall"}
 
 
+def copy_calibration(mib: int):
+    """Three launches of one elementwise kernel that reads and writes `mib` MiB each."""
+    import torch
+    n = mib * 2**20 // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"launches": 3, "bytes_read_per_launch": n * 4,
+                                           "bytes_written_per_launch": n * 4}}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -52,6 +92,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama8b_l16_b16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run 3 fp32 device copies of MIB MiB each (reference for FETCH_SIZE/WRITE_SIZE)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
@@ -59,6 +101,9 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     import skv_inputs as si
     from swiftkv_prefill_skipping_amd import _lib as L, runner
     from tests.helpers import CachedLayers
@@ -131,7 +176,11 @@ def main():
         "flops_swiftkv": swift,
         "roofline": {"kernel": "gemm_gateup (bf16 MFMA GEMM + SwiGLU epilogue)", "bound": "mfma",
                      "achieved": round(achieved, 2), "peak": MI355X_BF16_DENSE_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / MI355X_BF16_DENSE_TFLOPS, 4), "traffic": None,
+                     "frac": round(achieved / MI355X_BF16_DENSE_TFLOPS, 4),
+                     "traffic": (measured_traffic("EpiSwiGLU") or {}).get("bytes") if w.name == "llama8b_l16_b16"
+                     else None,
+                     "traffic_detail": measured_traffic("EpiSwiGLU") if w.name == "llama8b_l16_b16" else None,
+                     "algorithmic_bytes_per_launch": prof["bytes"] / max(prof["launches"], 1),
                      "avg_launch_ms": round(avg_launch_ms, 4), "launches": prof["launches"],
                      "flops_per_launch": flops_per_launch},
     }
