@@ -507,6 +507,18 @@ skv_status run_prefill(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, floa
   };
   constexpr bool kBf16 = sizeof(T) == 2;
 
+  // algorithmic work of the attention and last-token rows, for the profiling hook
+  double attn_flops = 0, ctx_tokens = 0;
+  for (int b = 0; b < B; ++b) {
+    const double n = bt->cu_seqlens_host[b + 1] - bt->cu_seqlens_host[b];
+    attn_flops += 2.0 * n * (n + 1) * dh * hq;
+    ctx_tokens += n;
+  }
+  const double attn_bytes = (double)T_ * (2.0 * dq + 2.0 * dkv) * E;
+  const double n_deep = L - l;
+  const double last_flops = n_deep * (B * (4.0 * d * dq + 6.0 * d * f) + 4.0 * ctx_tokens * dh * hq) + 2.0 * d * V * B;
+  const double last_bytes = n_deep * ((2.0 * dq * d + 3.0 * f * d) * E + ctx_tokens * 2.0 * dkv * E) + (double)V * d * E;
+
   SKV_HIP(launch_meta(bt->cu_seqlens, bt->block_tables, B, bt->max_blocks_per_seq, kc->num_blocks, T_, m->pos,
                       m->slot, m->last_pos, m->last_row, s));
   if (!kBf16) SKV_HIP(launch_token_seq(bt->cu_seqlens, B, T_, m->seq, s));
@@ -534,7 +546,7 @@ skv_status run_prefill(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, floa
         SKV_HIP((launch_gemm_f32<64>((const float*)act, d, (const float*)Ly.wqkv, d, T_, N, d, epi, s)));
     }
     {
-      Prof p(m, SKV_K_ATTN_PREFILL, s, 0, 0);
+      Prof p(m, SKV_K_ATTN_PREFILL, s, attn_flops, attn_bytes);
       if constexpr (kBf16)
         SKV_HIP(launch_attn_prefill_bf16((const bf16_t*)qbuf, cs, bt->cu_seqlens, bt->block_tables,
                                          bt->max_blocks_per_seq, B, max_len, hq, (bf16_t*)obuf, s));
@@ -594,7 +606,7 @@ skv_status run_prefill(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, floa
   }
 
   // ---- last prompt token of each prompt through layers l+1..L, then the LM head
-  Prof plast(m, SKV_K_LAST_TOKEN, s, 0, 0);
+  Prof plast(m, SKV_K_LAST_TOKEN, s, last_flops, last_bytes);
   SKV_HIP(launch_gather_rows(m->x, m->last_row, B, d, m->y, s));
   for (int j = l + 1; j <= L; ++j) {
     const LayerDev& Ly = m->layers[j - 1];
