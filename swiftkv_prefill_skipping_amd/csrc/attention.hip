@@ -18,6 +18,14 @@
 //    keys, so both operands agree.  K and V tiles share one LDS layout
 //    ([64 keys][128 dims], 16-byte chunk c of key row r at c ^ (r & 15)).
 //    O^T is transposed through LDS at the end and written 8 bytes per lane.
+//    K/V tiles move global -> LDS directly (global_load_lds_dwordx4) into a
+//    two-stage ring, the next tile's loads in flight while the current one
+//    is computed; the prompt's block ids are staged in LDS so no load waits
+//    on a block-table read.  Keys past the prompt (or causally masked) get
+//    probability exactly 0, so the cache contents loaded for them only need
+//    to be finite, which the cache guarantees (zero-filled at creation,
+//    written only with results).  Two workgroups fit per CU (<= 256 VGPRs,
+//    66 KB LDS).
 //
 // 2. attn_rows_kernel + attn_combine_kernel (fp32 or bf16, vector ALU):
 //    attention of an explicit list of query rows (the last prompt token of
@@ -36,14 +44,23 @@ typedef s16x4_t short4_lds_t;
 constexpr int FA_DH = 128;
 constexpr int FA_KT = 64;  // keys per tile
 
+constexpr int FA_BTW = 32;  // block-table entries staged in LDS at a time (8 key tiles)
+
+SKV_DEV void wait_loads_then_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 template <int QT>
-__global__ __launch_bounds__(256, 1) void attn_prefill_kernel(const bf16_t* __restrict__ q, CacheSlot<bf16_t> cache,
-                                                              const int32_t* __restrict__ cu,
-                                                              const int32_t* __restrict__ bt, int max_blocks, int hq,
-                                                              int rep, float scale_log2, bf16_t* __restrict__ o) {
-  // double-buffered K and V tiles, [64 keys][128 dims] each
-  __shared__ __attribute__((aligned(16))) bf16_t sK[2][FA_KT * FA_DH];
-  __shared__ __attribute__((aligned(16))) bf16_t sV[2][FA_KT * FA_DH];
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_prefill_kernel(
+    const bf16_t* __restrict__ q, CacheSlot<bf16_t> cache, const int32_t* __restrict__ cu,
+    const int32_t* __restrict__ bt, int max_blocks, int hq, int rep, float scale_log2, bf16_t* __restrict__ o) {
+  // double-buffered K and V tiles, [64 keys][128 dims] each, filled by
+  // direct global -> LDS loads
+  __shared__ __attribute__((aligned(1024))) bf16_t sK[2][FA_KT * FA_DH];
+  __shared__ __attribute__((aligned(1024))) bf16_t sV[2][FA_KT * FA_DH];
+  __shared__ int32_t sBT[FA_BTW];
 
   const int b = blockIdx.y;
   const int tok0 = cu[b];
@@ -56,12 +73,29 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_kernel(const bf16_t* __re
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hh = lane >> 5;
   const int h = blockIdx.z * 4 + wave;
   const int g = (blockIdx.z * 4) / rep;
   const int hkv = cache.hkv;
   const int dq = hq * FA_DH;
+
+  const int kend = min(N, q0 + QB);
+  const int ntiles = (kend + FA_KT - 1) / FA_KT;
+  const int nblk_need = (kend + kBlockSize - 1) / kBlockSize;
+  const int32_t* btb = bt + (int64_t)b * max_blocks;
+
+  // Block ids of tiles t0 .. t0+7.  Entries past the keys this workgroup
+  // needs (causally masked or beyond the prompt) repeat block 0, a valid
+  // block of the prompt, so every load stays inside the cache.
+  auto stage_block_ids = [&](int t0) {
+    if (tid < FA_BTW) {
+      const int i = tid;
+      const int bi = t0 * (FA_KT / kBlockSize) + i;
+      sBT[i] = btb[bi < nblk_need ? bi : 0];
+    }
+  };
+  stage_block_ids(0);
 
   // Q^T fragments: lane holds query (lane & 31), dims ks*16 + hh*8 .. +8
   bf16x8_t qf[QT][8];
@@ -82,48 +116,37 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_kernel(const bf16_t* __re
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) oacc[s][dt] = f32x16_t{0};
   }
-
-  const int kend = min(N, q0 + QB);
-  const int ntiles = (kend + FA_KT - 1) / FA_KT;
-  const int32_t* btb = bt + (int64_t)b * max_blocks;
-
-  // tile loader: 4 blocks of 16 keys, each block a contiguous [16][128]
-  // (key, dim) slab of K and of V; thread -> (key = tid/16, chunk = tid%16)
-  u32x4_t rk[4], rv[4];
-  auto gload = [&](int kt) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      int key0 = kt * FA_KT + r * 16;
-      int blk = (key0 < N) ? btb[key0 / 16] : -1;
-      if (blk >= 0) {
-        const int64_t off = ((int64_t)blk * hkv + g) * (16 * FA_DH) + tid * 8;
-        rk[r] = *reinterpret_cast<const u32x4_t*>(cache.k + off);
-        // values of keys beyond the prompt (stale cache contents) are zeroed
-        rv[r] = (key0 + (tid >> 4) < N) ? *reinterpret_cast<const u32x4_t*>(cache.v + off) : u32x4_t{0, 0, 0, 0};
-      } else {
-        rk[r] = u32x4_t{0, 0, 0, 0};
-        rv[r] = u32x4_t{0, 0, 0, 0};
-      }
-    }
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      int key = r * 16 + (tid >> 4);
-      int ch = tid & 15;
-      const int o = key * FA_DH + ((ch ^ (key & 15)) << 3);
-      *reinterpret_cast<u32x4_t*>(&sK[buf][o]) = rk[r];
-      *reinterpret_cast<u32x4_t*>(&sV[buf][o]) = rv[r];
-    }
-  };
-
-  gload(0);
-  sstore(0);
   __syncthreads();
+
+  // Tile loads: per 16-key block r of the tile, wave w moves key rows
+  // w*4 .. w*4+3 of K and of V (1 KB each, one instruction).  Lane l's 16
+  // bytes land at LDS row w*4 + l/16, physical chunk l%16, so it fetches the
+  // logical chunk (l%16) ^ (row & 15): the XOR swizzle of the tile layout.
+  const int lrow = wave * 4 + (lane >> 4);
+  const int lane_off = lrow * FA_DH + (((lane & 15) ^ lrow) << 3);
+  auto issue_tile = [&](int t, int buf) {
+    const int wb = (t * (FA_KT / kBlockSize)) % FA_BTW;
+#pragma unroll
+    for (int r = 0; r < FA_KT / kBlockSize; ++r) {
+      const int64_t base = ((int64_t)sBT[wb + r] * hkv + g) * (kBlockSize * FA_DH) + lane_off;
+      typedef __attribute__((address_space(3))) void* lds_ptr;
+      __builtin_amdgcn_global_load_lds(cache.k + base, (lds_ptr)(&sK[buf][(r * 16 + wave * 4) * FA_DH]), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(cache.v + base, (lds_ptr)(&sV[buf][(r * 16 + wave * 4) * FA_DH]), 16, 0, 0);
+    }
+  };
+
+  issue_tile(0, 0);
+  wait_loads_then_barrier();
 
   for (int kt = 0; kt < ntiles; ++kt) {
     const int cur = kt & 1;
-    if (kt + 1 < ntiles) gload(kt + 1);
+    if (kt + 1 < ntiles) {
+      if ((kt + 1) % (FA_BTW / (FA_KT / kBlockSize)) == 0) {  // next window of block ids
+        stage_block_ids(kt + 1);
+        __syncthreads();
+      }
+      issue_tile(kt + 1, cur ^ 1);
+    }
     const int k0 = kt * FA_KT;
     const bf16_t* sk = sK[cur];
     const bf16_t* sv = sV[cur];
@@ -218,8 +241,7 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_kernel(const bf16_t* __re
       }
     }
 
-    if (kt + 1 < ntiles) sstore(cur ^ 1);
-    __syncthreads();
+    wait_loads_then_barrier();
   }
 
   // normalise and write: O^T -> LDS [32 q][128 d] per wave (8-byte quads
@@ -254,105 +276,167 @@ __global__ __launch_bounds__(256, 1) void attn_prefill_kernel(const bf16_t* __re
   }
 }
 
-constexpr int RW_CH = 256;     // keys per chunk
+constexpr int RW_CH = 256;     // keys per chunk (one workgroup, 4 waves x 64 keys)
 constexpr int RW_MAXREP = 16;  // q heads per kv head
 constexpr int RW_MAXDH = 128;
+constexpr int RW_HG = 4;       // q heads handled per pass over the chunk
 
-template <typename T>
+// One query row (a token with its position and prompt) against one kv head's
+// keys [c*256, c*256+256) of that prompt, for the rep q heads that share the
+// kv head.  Writes (max, sum, unnormalised o) per head for the combine pass.
+// Lanes read key and value rows as 16-byte slices: LPK lanes cover one row
+// (DH elements), so one wave load instruction covers 64/LPK whole rows.
+template <typename T, int DH>
 __global__ __launch_bounds__(256) void attn_rows_kernel(const T* __restrict__ q, CacheSlot<T> cache,
                                                         const int32_t* __restrict__ row_seq,
                                                         const int32_t* __restrict__ row_pos,
                                                         const int32_t* __restrict__ bt, int max_blocks, int hq,
                                                         int nchunks, float scale, float* __restrict__ ws) {
-  __shared__ float qs[RW_MAXREP][RW_MAXDH];
-  __shared__ float ps[RW_MAXREP][RW_CH];
+  constexpr int VEC = 16 / (int)sizeof(T);  // elements per lane load
+  constexpr int LPK = DH / VEC;             // lanes per key row
+  constexpr int KPI = 64 / LPK;             // key rows per wave load
+  constexpr int ITERS = 64 / KPI;           // loads per wave per chunk
+  static_assert(LPK >= 1 && LPK <= 64 && 64 % LPK == 0, "head_dim / vector width");
+  __shared__ float qs[RW_MAXREP][DH];
+  __shared__ float ps[RW_HG][RW_CH];
   __shared__ int sl_s[RW_CH];
-  __shared__ float red[RW_MAXREP][4];
-  __shared__ float opart[256 / 32][RW_MAXDH];  // 256 / head_dim key partitions (head_dim >= 32)
+  __shared__ float red[RW_HG][4];
+  __shared__ float opart[4][RW_HG][DH];
 
   const int r = blockIdx.x, g = blockIdx.y, c = blockIdx.z;
-  const int tid = threadIdx.x;
-  const int hkv = cache.hkv, dh = cache.dh;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int hkv = cache.hkv;
   const int rep = hq / hkv;
   const int ctx = row_pos[r] + 1;
   const int seq = row_seq[r];
   const int kbeg = c * RW_CH;
-  const int stride = dh + 2;
+  const int stride = DH + 2;
   float* wsr = ws + ((int64_t)r * hq + g * rep) * nchunks * stride;
 
   if (kbeg >= ctx) {  // empty chunk
     for (int hl = tid; hl < rep; hl += 256) {
-      float* w = wsr + ((int64_t)hl * nchunks + c) * stride;
-      w[0] = -INFINITY;
-      w[1] = 0.f;
+      float* o = wsr + ((int64_t)hl * nchunks + c) * stride;
+      o[0] = -INFINITY;
+      o[1] = 0.f;
     }
     return;
   }
-  for (int i = tid; i < rep * dh; i += 256) {
-    int hl = i / dh, d = i % dh;
-    qs[hl][d] = to_f32<T>(q[((int64_t)r * hq + g * rep + hl) * dh + d]);
+  for (int i = tid; i < rep * DH; i += 256) {
+    int hl = i / DH, d = i % DH;
+    qs[hl][d] = to_f32<T>(q[((int64_t)r * hq + g * rep + hl) * DH + d]);
   }
-  const int key = kbeg + tid;
-  const bool valid = key < ctx;
-  int sl = -1;
-  if (valid) {
-    int blk = bt[(int64_t)seq * max_blocks + key / kBlockSize];
-    sl = blk * kBlockSize + key % kBlockSize;
-  }
-  sl_s[tid] = sl;
-  __syncthreads();
-
-  float sc[RW_MAXREP];
-#pragma unroll
-  for (int hl = 0; hl < RW_MAXREP; ++hl) sc[hl] = 0.f;
-  if (valid) {
-    const T* kr = cache.k + kv_index(sl, g, 0, hkv, dh);
-    for (int d = 0; d < dh; ++d) {
-      float kv = to_f32<T>(kr[d]);
-#pragma unroll
-      for (int hl = 0; hl < RW_MAXREP; ++hl)
-        if (hl < rep) sc[hl] = fmaf(qs[hl][d], kv, sc[hl]);
-    }
-  }
-  const int w = tid >> 6;
-  for (int hl = 0; hl < rep; ++hl) {
-    float x = valid ? sc[hl] * scale : -INFINITY;
-    float m = warp_max(x);
-    if ((tid & 63) == 0) red[hl][w] = m;
-    sc[hl] = x;
-  }
-  __syncthreads();
-  float mh[RW_MAXREP];
-  for (int hl = 0; hl < rep; ++hl) mh[hl] = fmaxf(fmaxf(red[hl][0], red[hl][1]), fmaxf(red[hl][2], red[hl][3]));
-  __syncthreads();
-  for (int hl = 0; hl < rep; ++hl) {
-    float p = valid ? __expf(sc[hl] - mh[hl]) : 0.f;
-    ps[hl][tid] = p;
-    float s = warp_sum(p);
-    if ((tid & 63) == 0) red[hl][w] = s;
+  {
+    const int key = kbeg + tid;
+    int sl = -1;
+    if (key < ctx) sl = bt[(int64_t)seq * max_blocks + key / kBlockSize] * kBlockSize + key % kBlockSize;
+    sl_s[tid] = sl;
   }
   __syncthreads();
 
-  // P V: thread -> (dim d, part) with parts = 256 / dh key ranges
-  const int parts = 256 / dh;
-  const int d = tid % dh, part = tid / dh;
-  const int span = RW_CH / parts;
   const int nk = min(RW_CH, ctx - kbeg);
-  for (int hl = 0; hl < rep; ++hl) {
-    float acc = 0.f;
-    for (int j = part * span; j < min(nk, (part + 1) * span); ++j) {
-      acc = fmaf(ps[hl][j], to_f32<T>(cache.v[kv_index(sl_s[j], g, d, hkv, dh)]), acc);
+  const int sub = lane / LPK;          // key row within one wave load
+  const int d0 = (lane % LPK) * VEC;   // first element of this lane's slice
+  const int kw = w * 64;               // this wave's first key within the chunk
+
+  for (int h0 = 0; h0 < rep; h0 += RW_HG) {
+    // ---- scores s[h][key] for heads h0..h0+3
+#pragma unroll 4
+    for (int it = 0; it < ITERS; ++it) {
+      const int kk = kw + it * KPI + sub;
+      float part[RW_HG];
+#pragma unroll
+      for (int hh = 0; hh < RW_HG; ++hh) part[hh] = 0.f;
+      if (kk < nk) {
+        const T* kr = cache.k + kv_index(sl_s[kk], g, d0, hkv, DH);
+        const u32x4_t raw = *reinterpret_cast<const u32x4_t*>(kr);
+        float kv[VEC];
+        unpack16<T>(raw, kv);
+#pragma unroll
+        for (int hh = 0; hh < RW_HG; ++hh) {
+          if (h0 + hh < rep) {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) part[hh] = fmaf(qs[h0 + hh][d0 + e], kv[e], part[hh]);
+          }
+        }
+      }
+#pragma unroll
+      for (int hh = 0; hh < RW_HG; ++hh) {
+#pragma unroll
+        for (int off = 1; off < LPK; off <<= 1) part[hh] += __shfl_xor(part[hh], off);
+      }
+      if (lane % LPK == 0) {
+#pragma unroll
+        for (int hh = 0; hh < RW_HG; ++hh) ps[hh][kk] = kk < nk ? part[hh] * scale : -INFINITY;
+      }
     }
-    opart[part][d] = acc;
     __syncthreads();
-    if (tid < dh) {
-      float o = 0.f;
-      for (int p = 0; p < parts; ++p) o += opart[p][tid];
-      float* wp = wsr + ((int64_t)hl * nchunks + c) * stride;
-      wp[2 + tid] = o;
-      if (tid == 0) {
-        wp[0] = mh[hl];
-        wp[1] = red[hl][0] + red[hl][1] + red[hl][2] + red[hl][3];
+
+    // ---- softmax statistics over the chunk; thread t owns key t
+    float mh[RW_HG];
+#pragma unroll
+    for (int hh = 0; hh < RW_HG; ++hh) {
+      float m = warp_max(ps[hh][tid]);
+      if (lane == 0) red[hh][w] = m;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int hh = 0; hh < RW_HG; ++hh) mh[hh] = fmaxf(fmaxf(red[hh][0], red[hh][1]), fmaxf(red[hh][2], red[hh][3]));
+    __syncthreads();
+#pragma unroll
+    for (int hh = 0; hh < RW_HG; ++hh) {
+      const float x = ps[hh][tid];
+      const float p = x == -INFINITY ? 0.f : __expf(x - mh[hh]);
+      ps[hh][tid] = p;
+      const float sm = warp_sum(p);
+      if (lane == 0) red[hh][w] = sm;
+    }
+    __syncthreads();
+
+    // ---- o[h][d] = sum_k p[h][k] v[k][d], lanes on 16-byte slices of value rows
+    float acc[RW_HG][VEC];
+#pragma unroll
+    for (int hh = 0; hh < RW_HG; ++hh)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) acc[hh][e] = 0.f;
+#pragma unroll 4
+    for (int it = 0; it < ITERS; ++it) {
+      const int kk = kw + it * KPI + sub;
+      if (kk < nk) {
+        const T* vr = cache.v + kv_index(sl_s[kk], g, d0, hkv, DH);
+        const u32x4_t raw = *reinterpret_cast<const u32x4_t*>(vr);
+        float vv[VEC];
+        unpack16<T>(raw, vv);
+#pragma unroll
+        for (int hh = 0; hh < RW_HG; ++hh) {
+          const float p = ps[hh][kk];
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) acc[hh][e] = fmaf(p, vv[e], acc[hh][e]);
+        }
+      }
+    }
+    // reduce over the KPI key rows of one wave load, then over the 4 waves
+#pragma unroll
+    for (int hh = 0; hh < RW_HG; ++hh)
+#pragma unroll
+      for (int e = 0; e < VEC; ++e)
+#pragma unroll
+        for (int off = LPK; off < 64; off <<= 1) acc[hh][e] += __shfl_xor(acc[hh][e], off);
+    if (sub == 0) {
+#pragma unroll
+      for (int hh = 0; hh < RW_HG; ++hh)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) opart[w][hh][d0 + e] = acc[hh][e];
+    }
+    __syncthreads();
+    for (int i = tid; i < RW_HG * DH; i += 256) {
+      const int hh = i / DH, d = i % DH;
+      if (h0 + hh < rep) {
+        float* o = wsr + ((int64_t)(h0 + hh) * nchunks + c) * stride;
+        o[2 + d] = opart[0][hh][d] + opart[1][hh][d] + opart[2][hh][d] + opart[3][hh][d];
+        if (d == 0) {
+          o[0] = mh[hh];
+          o[1] = red[hh][0] + red[hh][1] + red[hh][2] + red[hh][3];
+        }
       }
     }
     __syncthreads();
@@ -405,8 +489,23 @@ hipError_t launch_attn_rows(const T* q, CacheSlot<T> cache, const int32_t* row_s
   if (rows <= 0) return hipSuccess;
   const int nchunks = (max_ctx + RW_CH - 1) / RW_CH;
   const float scale = 1.0f / sqrtf((float)cache.dh);
-  hipLaunchKernelGGL(attn_rows_kernel<T>, dim3(rows, cache.hkv, nchunks), dim3(256), 0, stream, q, cache, row_seq,
-                     row_pos, block_tables, max_blocks, hq, nchunks, scale, ws);
+  const dim3 grid(rows, cache.hkv, nchunks);
+  switch (cache.dh) {
+    case 128:
+      hipLaunchKernelGGL((attn_rows_kernel<T, 128>), grid, dim3(256), 0, stream, q, cache, row_seq, row_pos,
+                         block_tables, max_blocks, hq, nchunks, scale, ws);
+      break;
+    case 64:
+      hipLaunchKernelGGL((attn_rows_kernel<T, 64>), grid, dim3(256), 0, stream, q, cache, row_seq, row_pos,
+                         block_tables, max_blocks, hq, nchunks, scale, ws);
+      break;
+    case 32:
+      hipLaunchKernelGGL((attn_rows_kernel<T, 32>), grid, dim3(256), 0, stream, q, cache, row_seq, row_pos,
+                         block_tables, max_blocks, hq, nchunks, scale, ws);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(attn_combine_kernel<T>, dim3(rows, hq), dim3(RW_MAXDH), 0, stream, ws, hq, cache.dh, nchunks, o);

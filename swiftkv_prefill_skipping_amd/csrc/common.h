@@ -43,6 +43,23 @@ SKV_DEV bf16_t from_f32<bf16_t>(float v) { return f32_to_bf16(v); }
 
 SKV_DEV bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
 
+// 16 loaded bytes -> 16 / sizeof(T) floats, element order preserved.
+template <typename T>
+SKV_DEV void unpack16(u32x4_t w, float* out);
+template <>
+SKV_DEV void unpack16<float>(u32x4_t w, float* out) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) out[i] = __uint_as_float(w[i]);
+}
+template <>
+SKV_DEV void unpack16<bf16_t>(u32x4_t w, float* out) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    out[2 * i] = __uint_as_float(w[i] << 16);
+    out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+
 SKV_DEV float warp_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
