@@ -28,9 +28,14 @@ skv_status fail(skv_status s, const std::string& msg) {
   } while (0)
 
 int ceil_div(int a, int b) { return (a + b - 1) / b; }
+size_t round_up(size_t a, size_t b) { return (a + b - 1) / b * b; }
 
 }  // namespace
 
+// Weights of layers 1..l feed the prompt-token GEMMs and are kept in the
+// panel layout (bf16 models); those of skipped layers feed only the
+// last-token path and stay row-major.  fp32 models keep everything
+// row-major.
 struct LayerDev {
   float* attn_norm = nullptr;  // fp32 [d]
   float* ffn_norm = nullptr;
@@ -38,6 +43,7 @@ struct LayerDev {
   void* wo = nullptr;    // [d, dq]
   void* wgu = nullptr;   // [2f, d], gate/up interleaved in blocks of P_mlp rows
   void* wdown = nullptr; // [d, f]
+  bool panels = false;   // stored in the panel layout
   bool loaded = false;
 };
 
@@ -61,7 +67,7 @@ struct skv_model {
   float* rope_sin = nullptr;
   bool globals_loaded = false;
   std::vector<LayerDev> layers;
-  void* wkv_skip = nullptr;  // [G * 2 dkv, d]
+  void* wkv_skip = nullptr;  // [G * 2 dkv, d] (panel layout for bf16)
   void* staging = nullptr;
   size_t staging_bytes = 0;
   void* gamma_stage = nullptr;
@@ -251,25 +257,30 @@ skv_status skv_model_create(const skv_model_config* cfg, skv_model** out) {
   const size_t half = c.head_dim / 2;
   ALLOC(m->rope_cos, (size_t)c.max_seqlen * half * 4);
   ALLOC(m->rope_sin, (size_t)c.max_seqlen * half * 4);
+  // panel-layout matrices round their row count up to whole panels
+  const size_t R = m->bf16 ? 256 : 1;
   for (int i = 1; i <= c.n_layers; ++i) {
     LayerDev& L = m->layers[i - 1];
+    L.panels = m->bf16 && i <= c.swiftkv_l;
+    const size_t r = L.panels ? R : 1;
     ALLOC(L.attn_norm, d * 4);
     ALLOC(L.ffn_norm, d * 4);
-    ALLOC(L.wqkv, (i <= c.swiftkv_l ? dq + 2 * dkv : dq) * d * E);
-    ALLOC(L.wo, d * dq * E);
-    ALLOC(L.wgu, 2 * f * d * E);
-    ALLOC(L.wdown, d * f * E);
+    ALLOC(L.wqkv, round_up(i <= c.swiftkv_l ? dq + 2 * dkv : dq, r) * d * E);
+    ALLOC(L.wo, round_up(d, r) * dq * E);
+    ALLOC(L.wgu, round_up(2 * f, r) * d * E);
+    ALLOC(L.wdown, round_up(d, r) * f * E);
   }
-  if (m->G > 0) ALLOC(m->wkv_skip, (size_t)m->G * 2 * dkv * d * E);
-  m->staging_bytes = std::max(2 * f * d, 2 * dkv * d) * E;
+  if (m->G > 0) ALLOC(m->wkv_skip, round_up((size_t)m->G * 2 * dkv, R) * d * E);
+  m->staging_bytes = std::max({2 * f * d, (dq + 2 * dkv) * d, d * dq, d * f}) * E;
   ALLOC(m->staging, m->staging_bytes);
   ALLOC(m->gamma_stage, d * E);
 
+  const size_t Tp = round_up(T, R);  // token rows of the panel-layout activations
   ALLOC(m->x, T * d * 4);
-  ALLOC(m->act, T * d * E);
+  ALLOC(m->act, Tp * d * E);
   ALLOC(m->qbuf, T * dq * E);
-  ALLOC(m->obuf, T * dq * E);
-  ALLOC(m->hbuf, T * f * E);
+  ALLOC(m->obuf, Tp * dq * E);
+  ALLOC(m->hbuf, Tp * f * E);
   ALLOC(m->pos, T * 4);
   ALLOC(m->slot, T * 4);
   ALLOC(m->seq, T * 4);
@@ -300,6 +311,12 @@ skv_status skv_model_create(const skv_model_config* cfg, skv_model** out) {
     ALLOC(m->gemm_ws, (size_t)m->gemm_ws_elems * 4);
   }
 #undef ALLOC
+
+  // the panel padding rows of the activations are read (never stored) by
+  // the GEMMs: start them at zero so they hold finite values
+  if (hipMemset(m->act, 0, Tp * d * E) != hipSuccess || hipMemset(m->obuf, 0, Tp * dq * E) != hipSuccess ||
+      hipMemset(m->hbuf, 0, Tp * f * E) != hipSuccess || hipDeviceSynchronize() != hipSuccess)
+    return bail(fail(SKV_ERR_HIP, "clearing the activation buffers failed"));
 
   // RoPE tables: angle p * theta^(-2i/dh) in double, cos/sin rounded to fp32
   {
@@ -361,35 +378,63 @@ skv_status skv_model_load_globals(skv_model* m, const void* embed, const void* f
   return SKV_OK;
 }
 
+// Copy a row-major host/device matrix into `dst`, either as is or through the
+// staging buffer into the panel layout.
+static skv_status load_matrix(skv_model* m, void* dst, const void* src, size_t rows, size_t cols, bool panels,
+                              const char* what) {
+  const size_t bytes = rows * cols * m->esz;
+  if (!panels) return copy_in(dst, src, bytes, what);
+  SKV_TRY(copy_in(m->staging, src, bytes, what));
+  SKV_HIP(launch_to_panels((const bf16_t*)m->staging, (int)rows, (int)cols, (bf16_t*)dst, 0));
+  SKV_HIP(hipDeviceSynchronize());
+  return SKV_OK;
+}
+
 skv_status skv_model_load_layer(skv_model* m, int32_t layer, const skv_layer_weights* w) {
   if (!m || !w) return fail(SKV_ERR_INVALID_ARG, "NULL argument");
   const auto& c = m->cfg;
   if (layer < 1 || layer > c.n_layers) return fail(SKV_ERR_INVALID_ARG, "layer outside 1..n_layers");
   LayerDev& L = m->layers[layer - 1];
   const size_t d = c.d_model, dq = m->dq, dkv = m->dkv, f = c.ffn_dim, E = m->esz;
-  char* qkv = (char*)L.wqkv;
   SKV_TRY(gain_to_f32(m, w->ffn_norm, L.ffn_norm, "ffn_norm"));
   SKV_TRY(gain_to_f32(m, w->attn_norm, L.attn_norm, "attn_norm"));  // leaves gamma_stage = attn gain
-  SKV_TRY(copy_in(qkv, w->wq, dq * d * E, "wq"));
   if (layer <= c.swiftkv_l) {
-    SKV_TRY(copy_in(qkv + dq * d * E, w->wk, dkv * d * E, "wk"));
-    SKV_TRY(copy_in(qkv + (dq + dkv) * d * E, w->wv, dkv * d * E, "wv"));
-  } else if (is_representative(c, layer)) {
-    // fold this layer's input-RMSNorm gain into its K and V rows
-    const int grp = (layer - c.swiftkv_l - 1) / c.acrosskv_g;
-    char* dst = (char*)m->wkv_skip + (size_t)grp * 2 * dkv * d * E;
-    SKV_TRY(copy_in(m->staging, w->wk, dkv * d * E, "wk"));
-    SKV_TRY(copy_in((char*)m->staging + dkv * d * E, w->wv, dkv * d * E, "wv"));
-    if (m->bf16)
-      SKV_HIP(launch_fold_rows<bf16_t>((const bf16_t*)m->staging, (const bf16_t*)m->gamma_stage, (int)(2 * dkv),
-                                       (int)d, (bf16_t*)dst, 0));
-    else
-      SKV_HIP(launch_fold_rows<float>((const float*)m->staging, (const float*)m->gamma_stage, (int)(2 * dkv), (int)d,
-                                      (float*)dst, 0));
-    SKV_HIP(hipDeviceSynchronize());
+    // [wq; wk; wv] concatenated row-major, then (bf16) into panels
+    char* dst = L.panels ? (char*)m->staging : (char*)L.wqkv;
+    SKV_TRY(copy_in(dst, w->wq, dq * d * E, "wq"));
+    SKV_TRY(copy_in(dst + dq * d * E, w->wk, dkv * d * E, "wk"));
+    SKV_TRY(copy_in(dst + (dq + dkv) * d * E, w->wv, dkv * d * E, "wv"));
+    if (L.panels) {
+      SKV_HIP(launch_to_panels((const bf16_t*)m->staging, (int)(dq + 2 * dkv), (int)d, (bf16_t*)L.wqkv, 0));
+      SKV_HIP(hipDeviceSynchronize());
+    }
+  } else {
+    SKV_TRY(copy_in(L.wqkv, w->wq, dq * d * E, "wq"));
+    if (is_representative(c, layer)) {
+      // fold this layer's input-RMSNorm gain into its K and V rows (in place
+      // in the staging buffer), then store them as this group's block of the
+      // skipped-layer projection
+      const int grp = (layer - c.swiftkv_l - 1) / c.acrosskv_g;
+      SKV_TRY(copy_in(m->staging, w->wk, dkv * d * E, "wk"));
+      SKV_TRY(copy_in((char*)m->staging + dkv * d * E, w->wv, dkv * d * E, "wv"));
+      if (m->bf16) {
+        // 2 dkv = 256 * hkv rows: every group starts on a panel boundary
+        bf16_t* dst = (bf16_t*)m->wkv_skip + (size_t)grp * 2 * dkv * d;
+        SKV_HIP(launch_fold_rows<bf16_t>((const bf16_t*)m->staging, (const bf16_t*)m->gamma_stage, (int)(2 * dkv),
+                                         (int)d, (bf16_t*)m->staging, 0));
+        SKV_HIP(launch_to_panels((const bf16_t*)m->staging, (int)(2 * dkv), (int)d, dst, 0));
+      } else {
+        float* dst = (float*)m->wkv_skip + (size_t)grp * 2 * dkv * d;
+        SKV_HIP(launch_fold_rows<float>((const float*)m->staging, (const float*)m->gamma_stage, (int)(2 * dkv),
+                                        (int)d, dst, 0));
+      }
+      SKV_HIP(hipDeviceSynchronize());
+    }
   }
-  SKV_TRY(copy_in(L.wo, w->wo, d * dq * E, "wo"));
-  SKV_TRY(copy_in(L.wdown, w->w_down, d * f * E, "w_down"));
+  SKV_TRY(load_matrix(m, L.wo, w->wo, d, dq, L.panels, "wo"));
+  SKV_TRY(load_matrix(m, L.wdown, w->w_down, d, f, L.panels, "w_down"));
+  // gate/up: interleave rows in blocks of P_mlp into L.wgu (row-major), then
+  // (bf16, unskipped) into panels through the staging buffer
   SKV_TRY(copy_in(m->staging, w->w_gate, f * d * E, "w_gate"));
   SKV_TRY(copy_in((char*)m->staging + f * d * E, w->w_up, f * d * E, "w_up"));
   if (m->bf16)
@@ -398,6 +443,10 @@ skv_status skv_model_load_layer(skv_model* m, int32_t layer, const skv_layer_wei
   else
     SKV_HIP(launch_interleave<float>((const float*)m->staging, (const float*)m->staging + f * d, (int)f, (int)d,
                                      m->p_mlp, (float*)L.wgu, 0));
+  if (L.panels) {
+    SKV_HIP(launch_to_panels((const bf16_t*)L.wgu, (int)(2 * f), (int)d, (bf16_t*)m->staging, 0));
+    SKV_HIP(hipMemcpyAsync(L.wgu, m->staging, round_up(2 * f, 256) * d * E, hipMemcpyDeviceToDevice, 0));
+  }
   SKV_HIP(hipDeviceSynchronize());
   L.loaded = true;
   return SKV_OK;
@@ -530,14 +579,17 @@ skv_status run_prefill(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, floa
     CacheSlot<T> cs = slot_of(i - 1);
     {
       Prof p(m, SKV_K_RMSNORM, s, 0, (double)T_ * d * (4 + E));
-      SKV_HIP(launch_rmsnorm<T>(m->x, nullptr, Ly.attn_norm, T_, d, c.rms_eps, act, s));
+      if constexpr (kBf16)
+        SKV_HIP(launch_rmsnorm_panel(m->x, Ly.attn_norm, T_, d, c.rms_eps, (bf16_t*)act, s));
+      else
+        SKV_HIP(launch_rmsnorm<T>(m->x, nullptr, Ly.attn_norm, T_, d, c.rms_eps, act, s));
     }
     {
       const int N = dq + 2 * dkv;
       EpiQKV<T> epi{qbuf, cs, m->pos, m->slot, m->rope_cos, m->rope_sin, dq, dkv, dh, P};
       Prof p(m, SKV_K_GEMM_QKV, s, 2.0 * T_ * N * d, gemm_bytes(T_, N, d, E, E));
       if constexpr (kBf16)
-        SKV_HIP(launch_gemm_bf16((const bf16_t*)act, d, (const bf16_t*)Ly.wqkv, d, T_, N, d, epi, m->gemm_ws, m->gemm_ws_elems, s));
+        SKV_HIP(launch_gemm_bf16((const bf16_t*)act, (const bf16_t*)Ly.wqkv, T_, N, d, epi, m->gemm_ws, m->gemm_ws_elems, s));
       else if (P == 16)
         SKV_HIP((launch_gemm_f32<16>((const float*)act, d, (const float*)Ly.wqkv, d, T_, N, d, epi, s)));
       else if (P == 32)
@@ -558,27 +610,32 @@ skv_status run_prefill(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, floa
       EpiResidual epi{m->x, d, kBf16 ? 64 : 16};
       Prof p(m, SKV_K_GEMM_O, s, 2.0 * T_ * d * dq, gemm_bytes(T_, d, dq, E, 8));
       if constexpr (kBf16)
-        SKV_HIP(launch_gemm_bf16((const bf16_t*)obuf, dq, (const bf16_t*)Ly.wo, dq, T_, d, dq, epi, m->gemm_ws, m->gemm_ws_elems, s));
+        SKV_HIP(launch_gemm_bf16((const bf16_t*)obuf, (const bf16_t*)Ly.wo, T_, d, dq, epi, m->gemm_ws, m->gemm_ws_elems, s));
       else
         SKV_HIP((launch_gemm_f32<16>((const float*)obuf, dq, (const float*)Ly.wo, dq, T_, d, dq, epi, s)));
     }
     {
       Prof p(m, SKV_K_RMSNORM, s, 0, (double)T_ * d * (4 + E));
-      SKV_HIP(launch_rmsnorm<T>(m->x, nullptr, Ly.ffn_norm, T_, d, c.rms_eps, act, s));
+      if constexpr (kBf16)
+        SKV_HIP(launch_rmsnorm_panel(m->x, Ly.ffn_norm, T_, d, c.rms_eps, (bf16_t*)act, s));
+      else
+        SKV_HIP(launch_rmsnorm<T>(m->x, nullptr, Ly.ffn_norm, T_, d, c.rms_eps, act, s));
     }
     {
-      EpiSwiGLU<T> epi{hbuf, f, m->p_mlp};
       Prof p(m, SKV_K_GEMM_GATEUP, s, 2.0 * T_ * 2 * f * d, gemm_bytes(T_, 2.0 * f, d, E, 0) + (double)T_ * f * E);
-      if constexpr (kBf16)
-        SKV_HIP(launch_gemm_bf16((const bf16_t*)act, d, (const bf16_t*)Ly.wgu, d, T_, 2 * f, d, epi, m->gemm_ws, m->gemm_ws_elems, s));
-      else
+      if constexpr (kBf16) {
+        EpiSwiGLUPanel epi{(bf16_t*)hbuf, f, m->p_mlp};
+        SKV_HIP(launch_gemm_bf16((const bf16_t*)act, (const bf16_t*)Ly.wgu, T_, 2 * f, d, epi, m->gemm_ws, m->gemm_ws_elems, s));
+      } else {
+        EpiSwiGLU<T> epi{hbuf, f, m->p_mlp};
         SKV_HIP((launch_gemm_f32<16>((const float*)act, d, (const float*)Ly.wgu, d, T_, 2 * f, d, epi, s)));
+      }
     }
     {
       EpiResidual epi{m->x, d, kBf16 ? 64 : 16};
       Prof p(m, SKV_K_GEMM_DOWN, s, 2.0 * T_ * d * f, gemm_bytes(T_, d, f, E, 8));
       if constexpr (kBf16)
-        SKV_HIP(launch_gemm_bf16((const bf16_t*)hbuf, f, (const bf16_t*)Ly.wdown, f, T_, d, f, epi, m->gemm_ws, m->gemm_ws_elems, s));
+        SKV_HIP(launch_gemm_bf16((const bf16_t*)hbuf, (const bf16_t*)Ly.wdown, T_, d, f, epi, m->gemm_ws, m->gemm_ws_elems, s));
       else
         SKV_HIP((launch_gemm_f32<16>((const float*)hbuf, f, (const float*)Ly.wdown, f, T_, d, f, epi, s)));
     }
@@ -588,7 +645,11 @@ skv_status run_prefill(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, floa
   if (m->G > 0) {
     {
       Prof p(m, SKV_K_RMSNORM, s, 0, (double)T_ * d * (4 + E));
-      SKV_HIP(launch_rmsnorm<T>(m->x, nullptr, nullptr, T_, d, c.rms_eps, act, s));  // x * r, gains folded into W~
+      // x * r, gains folded into W~
+      if constexpr (kBf16)
+        SKV_HIP(launch_rmsnorm_panel(m->x, nullptr, T_, d, c.rms_eps, (bf16_t*)act, s));
+      else
+        SKV_HIP(launch_rmsnorm<T>(m->x, nullptr, nullptr, T_, d, c.rms_eps, act, s));
     }
     CacheSlot<T> first = slot_of(l);
     const int N = m->G * 2 * dkv;
@@ -596,7 +657,7 @@ skv_status run_prefill(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, floa
                      c.n_kv_heads};
     Prof p(m, SKV_K_GEMM_KVSKIP, s, 2.0 * T_ * N * d, gemm_bytes(T_, N, d, E, E));
     if constexpr (kBf16)
-      SKV_HIP(launch_gemm_bf16((const bf16_t*)act, d, (const bf16_t*)m->wkv_skip, d, T_, N, d, epi, m->gemm_ws, m->gemm_ws_elems, s));
+      SKV_HIP(launch_gemm_bf16((const bf16_t*)act, (const bf16_t*)m->wkv_skip, T_, N, d, epi, m->gemm_ws, m->gemm_ws_elems, s));
     else if (P == 16)
       SKV_HIP((launch_gemm_f32<16>((const float*)act, d, (const float*)m->wkv_skip, d, T_, N, d, epi, s)));
     else if (P == 32)

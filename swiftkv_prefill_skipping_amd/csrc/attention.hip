@@ -17,7 +17,8 @@
 //    step kk, key kk*16 + 8*(e/4) + 4*h + e%4; the V^T reads gather the same
 //    keys, so both operands agree.  K and V tiles share one LDS layout
 //    ([64 keys][128 dims], 16-byte chunk c of key row r at c ^ (r & 15)).
-//    O^T is transposed through LDS at the end and written 8 bytes per lane.
+//    O^T is transposed through LDS at the end and written 8 bytes per lane
+//    into the panel layout of the O projection's A operand.
 //    K/V tiles move global -> LDS directly (global_load_lds_dwordx4) into a
 //    two-stage ring, the next tile's loads in flight while the current one
 //    is computed; the prompt's block ids are staged in LDS so no load waits
@@ -245,7 +246,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 
   // normalise and write: O^T -> LDS [32 q][128 d] per wave (8-byte quads
-  // swizzled by q) -> global rows
+  // swizzled by q) -> panel rows (a row's 128 dims are four 64-byte runs)
   bf16_t* so = &sK[0][0] + wave * (32 * FA_DH);
 #pragma unroll
   for (int s = 0; s < QT; ++s) {
@@ -269,7 +270,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const int qi = q0 + s * 32 + ql2;
       if (qi < N) {
         u32x2_t w = *reinterpret_cast<const u32x2_t*>(so + ql2 * FA_DH + ((u ^ ql2) << 2));
-        *reinterpret_cast<u32x2_t*>(o + (int64_t)(tok0 + qi) * dq + h * FA_DH + u * 4) = w;
+        *reinterpret_cast<u32x2_t*>(o + panel_off(tok0 + qi, h * FA_DH + u * 4, dq)) = w;
       }
     }
     __syncthreads();

@@ -15,17 +15,15 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 SKV_DEV float bf16_to_f32(bf16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
 
-// round to nearest even; NaN stays NaN
-SKV_DEV bf16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (bf16_t)(u >> 16);
-}
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
+// fp32 -> bf16 with round to nearest even (NaN stays NaN): gfx950's
+// v_cvt_pk_bf16_f32, two values per instruction.
 SKV_DEV uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
+SKV_DEV bf16_t f32_to_bf16(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
 
 template <typename T>
 SKV_DEV float to_f32(T v);
@@ -71,7 +69,8 @@ SKV_DEV float warp_max(float v) {
   return v;
 }
 
-SKV_DEV float silu_f(float x) { return x / (1.0f + __expf(-x)); }
+// silu(x) = x / (1 + e^-x), with the hardware reciprocal (1 ulp)
+SKV_DEV float silu_f(float x) { return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 
 // Per-token metadata of one prefill call, filled by the meta kernel.
 struct TokenMeta {
@@ -91,6 +90,17 @@ struct CacheSlot {
 };
 
 constexpr int kBlockSize = 16;
+
+// Panel layout of the bf16 GEMM operands (activations of the prompt-token
+// path and the weights of unskipped layers): rows are grouped in panels of
+// 256, and each panel is stored as consecutive blocks of 32 columns, each
+// block [256 rows][32] contiguous (16 KB).  One k-stage of the GEMM is then
+// one contiguous 16 KB block per operand.  K must be a multiple of 32; the
+// row count is padded to a multiple of 256.
+constexpr int kPanelRows = 256, kPanelCols = 32;
+SKV_DEV int64_t panel_off(int r, int k, int K) {
+  return ((int64_t)(r >> 8) * (K >> 5) + (k >> 5)) * (kPanelRows * kPanelCols) + (r & 255) * kPanelCols + (k & 31);
+}
 
 // element index of (physical slot, head, dim) in one cache tensor
 SKV_DEV int64_t kv_index(int slot_phys, int h, int d, int hkv, int dh) {

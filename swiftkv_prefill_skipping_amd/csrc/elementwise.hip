@@ -95,6 +95,63 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
   }
 }
 
+// RMSNorm into the panel layout: each wave normalises a pair of rows (lanes
+// 0-31 the even row, 32-63 the odd one), 8 columns per lane per step, so
+// one store instruction writes the two rows' 64-byte runs of eight column
+// blocks, which are adjacent in the panel (128 bytes each).
+__global__ __launch_bounds__(256) void rmsnorm_panel_kernel(const float* __restrict__ x,
+                                                            const float* __restrict__ gamma, int rows, int d,
+                                                            float eps, bf16_t* __restrict__ y) {
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 8 + (threadIdx.x >> 6) * 2 + (lane >> 5);
+  const int c0 = (lane & 31) * 8;
+  const float* xr = x + (int64_t)min(r, rows - 1) * d;
+  float ss = 0.f;
+  for (int c = c0; c < d; c += 256) {
+    const float4 a = *reinterpret_cast<const float4*>(xr + c);
+    const float4 b = *reinterpret_cast<const float4*>(xr + c + 4);
+    ss += a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w + b.x * b.x + b.y * b.y + b.z * b.z + b.w * b.w;
+  }
+#pragma unroll
+  for (int o = 16; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);  // within each half-wave
+  const float inv = 1.0f / sqrtf(ss / (float)d + eps);
+  if (r >= rows) return;
+  for (int c = c0; c < d; c += 256) {
+    const float4 a = *reinterpret_cast<const float4*>(xr + c);
+    const float4 b = *reinterpret_cast<const float4*>(xr + c + 4);
+    float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    if (gamma) {
+      const float4 ga = *reinterpret_cast<const float4*>(gamma + c);
+      const float4 gb = *reinterpret_cast<const float4*>(gamma + c + 4);
+      const float g[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = v[e] * inv * g[e];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = v[e] * inv;
+    }
+    *reinterpret_cast<u32x4_t*>(y + panel_off(r, c, d)) =
+        u32x4_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
+  }
+}
+
+// Row-major [rows, K] -> panel layout, eight elements (16 bytes) per thread
+// in destination order; rows beyond `rows` (panel padding) become zero.
+__global__ void to_panels_kernel(const bf16_t* __restrict__ W, int rows, int K, int64_t n8,
+                                 bf16_t* __restrict__ out) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t e = i * 8;
+    const int64_t blk = e / (kPanelRows * kPanelCols);
+    const int within = (int)(e % (kPanelRows * kPanelCols));
+    const int kbs = K / kPanelCols;
+    const int r = (int)(blk / kbs) * kPanelRows + within / kPanelCols;
+    const int k = (int)(blk % kbs) * kPanelCols + within % kPanelCols;
+    u32x4_t v = {0u, 0u, 0u, 0u};
+    if (r < rows) v = *reinterpret_cast<const u32x4_t*>(W + (int64_t)r * K + k);
+    *reinterpret_cast<u32x4_t*>(out + e) = v;
+  }
+}
+
 __global__ void gather_rows_kernel(const float* __restrict__ x, const int32_t* __restrict__ idx, int d,
                                    float* __restrict__ y) {
   int r = blockIdx.x;
@@ -169,6 +226,23 @@ hipError_t launch_rmsnorm(const float* x, const int32_t* rows_idx, const float* 
                           T* y, hipStream_t stream) {
   if (rows <= 0) return hipSuccess;
   hipLaunchKernelGGL(rmsnorm_kernel<T>, dim3(rows), dim3(256), 0, stream, x, rows_idx, gamma, d, eps, y);
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm_panel(const float* x, const float* gamma, int rows, int d, float eps, bf16_t* y,
+                                hipStream_t stream) {
+  if (rows <= 0) return hipSuccess;
+  if (d % 256) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(rmsnorm_panel_kernel, dim3((rows + 7) / 8), dim3(256), 0, stream, x, gamma, rows, d, eps, y);
+  return hipGetLastError();
+}
+
+hipError_t launch_to_panels(const bf16_t* W, int rows, int K, bf16_t* out, hipStream_t stream) {
+  if (rows <= 0) return hipSuccess;
+  if (K % kPanelCols) return hipErrorInvalidValue;
+  const int64_t rows_pad = (int64_t)(rows + kPanelRows - 1) / kPanelRows * kPanelRows;
+  const int64_t n8 = rows_pad * K / 8;
+  hipLaunchKernelGGL(to_panels_kernel, dim3(grid_for(n8)), dim3(256), 0, stream, W, rows, K, n8, out);
   return hipGetLastError();
 }
 

@@ -3,8 +3,33 @@
 // rotate-half RoPE pair (i, i + head_dim/2) and the interleaved SwiGLU pair
 // (gate, up) meet in one thread.  P is the pair distance the producing GEMM
 // was built for.
+//
+// Two entry points: operator()(row, col, v0, v1) takes one pair, and
+// vec8(row, col, a, b) takes eight: a[e] is column col + e and b[e] column
+// col + P + e (col % 8 == 0).  The bf16 MFMA GEMM uses vec8 so that every
+// lane stores whole 16-byte runs.  An epilogue that reads the output it
+// updates (the residual add) also offers pre8(row, col), which loads those
+// values early, and vec8(row, col, a, b, pre), which consumes them.
 #pragma once
 #include "common.h"
+
+SKV_DEV void load8(const float* p, float* v) {
+  const f32x4_t x0 = *reinterpret_cast<const f32x4_t*>(p);
+  const f32x4_t x1 = *reinterpret_cast<const f32x4_t*>(p + 4);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    v[e] = x0[e];
+    v[e + 4] = x1[e];
+  }
+}
+SKV_DEV void store8(float* p, const float* v) {
+  *reinterpret_cast<f32x4_t*>(p) = f32x4_t{v[0], v[1], v[2], v[3]};
+  *reinterpret_cast<f32x4_t*>(p + 4) = f32x4_t{v[4], v[5], v[6], v[7]};
+}
+SKV_DEV void store8(bf16_t* p, const float* v) {
+  *reinterpret_cast<u32x4_t*>(p) =
+      u32x4_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
+}
 
 // Plain fp32 store (logits).
 struct EpiStoreF32 {
@@ -14,6 +39,10 @@ struct EpiStoreF32 {
   SKV_DEV void operator()(int row, int col, float v0, float v1) const {
     out[(int64_t)row * ld + col] = v0;
     out[(int64_t)row * ld + col + P] = v1;
+  }
+  SKV_DEV void vec8(int row, int col, const float* a, const float* b) const {
+    store8(out + (int64_t)row * ld + col, a);
+    store8(out + (int64_t)row * ld + col + P, b);
   }
 };
 
@@ -27,6 +56,10 @@ struct EpiStore {
     out[(int64_t)row * ld + col] = from_f32<T>(v0);
     out[(int64_t)row * ld + col + P] = from_f32<T>(v1);
   }
+  SKV_DEV void vec8(int row, int col, const float* a, const float* b) const {
+    store8(out + (int64_t)row * ld + col, a);
+    store8(out + (int64_t)row * ld + col + P, b);
+  }
 };
 
 // Residual add into the fp32 residual stream: x += o W^T  (O and down projections).
@@ -39,6 +72,29 @@ struct EpiResidual {
     p[0] += v0;
     p[P] += v1;
   }
+  // the residual values of an eight-pair unit, loaded ahead of the sums
+  struct Pre {
+    float r0[8], r1[8];
+  };
+  SKV_DEV Pre pre8(int row, int col) const {
+    Pre r;
+    const float* p = x + (int64_t)row * ld + col;
+    load8(p, r.r0);
+    load8(p + P, r.r1);
+    return r;
+  }
+  SKV_DEV void vec8(int row, int col, const float* a, const float* b, const Pre& r) const {
+    float* p = x + (int64_t)row * ld + col;
+    float y0[8], y1[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      y0[e] = r.r0[e] + a[e];
+      y1[e] = r.r1[e] + b[e];
+    }
+    store8(p, y0);
+    store8(p + P, y1);
+  }
+  SKV_DEV void vec8(int row, int col, const float* a, const float* b) const { vec8(row, col, a, b, pre8(row, col)); }
 };
 
 // SwiGLU on gate/up rows interleaved in blocks of P: GEMM column
@@ -54,11 +110,46 @@ struct EpiSwiGLU {
     int c = col - blk * 2 * P;
     h[(int64_t)row * ld + blk * P + c] = from_f32<T>(silu_f(g) * u);
   }
+  SKV_DEV void vec8(int row, int col, const float* g, const float* u) const {
+    int blk = col / (2 * P);
+    int c = col - blk * 2 * P;
+    float y[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = silu_f(g[e]) * u[e];
+    store8(h + (int64_t)row * ld + blk * P + c, y);
+  }
+};
+
+// SwiGLU for the prompt-token GEMM: h is written in the panel layout
+// (panel_off with F columns), where it is the A operand of the down
+// projection.  Gate/up columns interleaved in blocks of P as in EpiSwiGLU.
+struct EpiSwiGLUPanel {
+  bf16_t* h;
+  int F;
+  int P;
+  SKV_DEV void vec8(int row, int col, const float* g, const float* u) const {
+    int blk = col / (2 * P);
+    int c = col - blk * 2 * P;
+    float y[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = silu_f(g[e]) * u[e];
+    store8(h + panel_off(row, blk * P + c, F), y);
+  }
 };
 
 SKV_DEV void rope_pair(float x0, float x1, float c, float s, float& y0, float& y1) {
   y0 = x0 * c - x1 * s;
   y1 = x1 * c + x0 * s;
+}
+
+// Eight rotate-half pairs (x0[e], x1[e]) at angle index i0 + e of position p.
+SKV_DEV void rope8(const float* x0, const float* x1, const float* rope_cos, const float* rope_sin, int p, int P,
+                   int i0, float* y0, float* y1) {
+  float c[8], s[8];
+  load8(rope_cos + (int64_t)p * P + i0, c);
+  load8(rope_sin + (int64_t)p * P + i0, s);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) rope_pair(x0[e], x1[e], c[e], s[e], y0[e], y1[e]);
 }
 
 // Q/K/V projection of an unskipped layer (or Q alone for the last-token
@@ -103,6 +194,28 @@ struct EpiQKV {
       cache.v[kv_index(sl, h, i + P, cache.hkv, dh)] = from_f32<T>(v1);
     }
   }
+  SKV_DEV void vec8(int row, int col, const float* a, const float* b) const {
+    float y0[8], y1[8];
+    if (col < dq) {
+      rope8(a, b, rope_cos, rope_sin, pos[row], P, col % dh, y0, y1);
+      T* qp = q + (int64_t)row * dq + col;
+      store8(qp, y0);
+      store8(qp + P, y1);
+      return;
+    }
+    int sl = slot[row];
+    if (sl < 0) return;
+    if (col < dq + dkv) {
+      int kc = col - dq, h = kc / dh, i = kc % dh;
+      rope8(a, b, rope_cos, rope_sin, pos[row], P, i, y0, y1);
+      store8(cache.k + kv_index(sl, h, i, cache.hkv, dh), y0);
+      store8(cache.k + kv_index(sl, h, i + P, cache.hkv, dh), y1);
+    } else {
+      int vc = col - dq - dkv, h = vc / dh, i = vc % dh;
+      store8(cache.v + kv_index(sl, h, i, cache.hkv, dh), a);
+      store8(cache.v + kv_index(sl, h, i + P, cache.hkv, dh), b);
+    }
+  }
 };
 
 // Skipped-layer KV (Eq. 2 / AcrossKV): column block g of width 2*dkv holds
@@ -137,6 +250,25 @@ struct EpiKVSkip {
       T* vp = v0 + g * slot_stride;
       vp[kv_index(sl, h, i, hkv, dh)] = from_f32<T>(a);
       vp[kv_index(sl, h, i + P, hkv, dh)] = from_f32<T>(b);
+    }
+  }
+  SKV_DEV void vec8(int row, int col, const float* a, const float* b) const {
+    int sl = slot[row];
+    if (sl < 0) return;
+    int g = col / (2 * dkv);
+    int c = col - g * 2 * dkv;
+    if (c < dkv) {
+      int h = c / dh, i = c % dh;
+      float y0[8], y1[8];
+      rope8(a, b, rope_cos, rope_sin, pos[row], P, i, y0, y1);
+      T* kp = k0 + g * slot_stride;
+      store8(kp + kv_index(sl, h, i, hkv, dh), y0);
+      store8(kp + kv_index(sl, h, i + P, hkv, dh), y1);
+    } else {
+      int vc = c - dkv, h = vc / dh, i = vc % dh;
+      T* vp = v0 + g * slot_stride;
+      store8(vp + kv_index(sl, h, i, hkv, dh), a);
+      store8(vp + kv_index(sl, h, i + P, hkv, dh), b);
     }
   }
 };

@@ -1,13 +1,12 @@
 // bf16 MFMA GEMM for gfx950: C[M,N] = A[M,K] . B[N,K]^T with fp32
-// accumulation, results handed to an epilogue functor as column pairs
-// (col, col + 64).
+// accumulation, results handed to an epilogue functor eight column pairs
+// (col + e, col + 64 + e) at a time.
 //
-// Tile 256 x 256, k-stages of 64.  512 threads = 8 wave64s, two per SIMD;
-// wave w owns output rows 64*(w%4) .. +64 and columns 128*(w/4) .. +128 as
-// 2 x 4 tiles of v_mfma_f32_32x32x16_bf16.  A wave's 128 columns are 4
-// MFMA column tiles; tiles t and t+2 are 64 columns apart, which is the RoPE
-// pair distance for head_dim 128 and the gate/up interleave distance, so
-// every epilogue pair sits in one lane.
+// Tile 256 x 256, k-stages of 64.  256 threads = 4 wave64s, one per SIMD;
+// wave w owns output rows 128*(w&1) .. +128 and columns 128*(w>>1) .. +128
+// as 4 x 4 tiles of v_mfma_f32_32x32x16_bf16 (256 accumulator registers).
+// The MFMA takes the B fragment as its first operand, so each lane ends up
+// holding one output row (lane & 31) and runs of four consecutive columns.
 //
 // Operand staging: global -> LDS directly (global_load_lds_dwordx4, no
 // register round trip) into two 64 KB stages.  LDS rows are 128 B (64
@@ -16,9 +15,15 @@
 // pass; with this swizzle the 16 rows read by one pass cover all 16 bank
 // groups, so the reads are conflict free.
 //
-// The two waves of a SIMD alternate between a memory phase and an MFMA
-// phase (ping-pong, separated by workgroup barriers), so the matrix core of
-// every SIMD is fed by one wave while the other waits on LDS / VMEM.
+// Schedule: each k-stage is four k-substeps of 16 MFMAs; the fragment reads
+// of the next substep are interleaved with the MFMAs of the current one.
+// One workgroup barrier per stage publishes the next stage and frees the
+// current buffer, whose next load goes out right after it.
+//
+// Epilogue: the accumulators go through LDS (each wave stages 32 rows x 128
+// columns of fp32 at a time in a padded, conflict-free layout), so the
+// epilogue functor sees eight consecutive columns per call and every global
+// store is a whole 16-byte run.
 //
 // Workgroups are dispatched round robin over the 8 XCDs; the tile index is
 // remapped so each XCD processes a contiguous run of tiles, and runs are
@@ -30,31 +35,21 @@
 
 namespace {
 
-constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int kThreads = 512;
+constexpr int BM = 256, BN = 256;
+constexpr int kNBuf = 4;  // LDS stages (32-column k-blocks) in flight
+constexpr int kThreads = 256;
 constexpr int kGroupM = 4;
 constexpr int kXcds = 8;
+// epilogue staging: 32 rows x 128 fp32 columns per wave, rows padded by 4
+// floats so that both the column-run writes and the row reads are
+// conflict free
+constexpr int kStageLd = 132;
+constexpr int kStageWave = 32 * kStageLd;  // floats
 
 SKV_DEV int xcd_remap(int wg, int n) {
   int q = n / kXcds, r = n % kXcds;
   int xcd = wg % kXcds, local = wg / kXcds;
   return (xcd < r) ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
-}
-
-// Workgroup barriers written out: a workgroup fence (__syncthreads) would
-// also wait for every outstanding direct load.  sched_barrier(0) on both
-// sides keeps the scheduler from moving any instruction (MFMAs included)
-// across, which is what keeps the ping-pong phases apart; the memory
-// clobber keeps LDS accesses in place at the IR level.
-SKV_DEV void barrier_only() {
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_barrier" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-}
-SKV_DEV void wait_loads_and_reads() {
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
 }
 
 // Tile index -> (row tile, column tile) in grouped order: kGroupM row tiles
@@ -67,22 +62,89 @@ SKV_DEV void tile_coords(int tile, int tiles_m, int tiles_n, int& tm, int& tn) {
   tn = (tile % per_group) / gsize;
 }
 
+// Wait for this wave's direct loads and LDS reads, then a workgroup barrier.
+// (__syncthreads would add a fence; the memory clobber and the scheduling
+// barriers keep every LDS access and MFMA on its side.)
+SKV_DEV void wait_all_then_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+template <int N>
+SKV_DEV void wait_vm_then_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+SKV_DEV void wait_lds() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Physical 16-byte chunk of logical chunk 0 in LDS row `row` (XOR
+// swizzle).  A ds_read_b128 pass serves 16 lanes = 256 B = all 64 banks; the
+// fragment reads of one pass touch 16 consecutive rows at one logical chunk,
+// and the swizzle sends them to 16 different bank groups: with 8 chunks per
+// row (128 B) rows pair up per 256 B, with 4 chunks (64 B) rows come in
+// fours.
+template <int CH>
+SKV_DEV int swizzle(int row) {
+  return CH == 8 ? (row >> 1) & 7 : (row >> 2) & 3;
+}
+
+// Shape of one k-stage of BK columns: LDS rows are BK bf16 = CH chunks of
+// 16 B; one direct load instruction moves RPI rows; each wave issues LPW of
+// them per stage; a stage is NSUB k-substeps of 16.
+template <int BK>
+struct StageShape {
+  static constexpr int CH = BK / 8;
+  static constexpr int RPI = 64 / CH;
+  static constexpr int LPW = (BM + BN) / RPI / 4;
+  static constexpr int NSUB = BK / 16;
+};
+
+// Epilogue read-ahead: the residual add loads the values it updates one
+// epilogue pass ahead (so those loads overlap the previous pass); every
+// other epilogue only stores and has nothing to load.
+template <class Epi>
+struct EpiAhead {
+  struct Pre {};
+  static SKV_DEV Pre load(const Epi&, int, int) { return {}; }
+  static SKV_DEV void apply(const Epi& e, int row, int col, const float* a, const float* b, const Pre&) {
+    e.vec8(row, col, a, b);
+  }
+};
+template <>
+struct EpiAhead<EpiResidual> {
+  using Pre = EpiResidual::Pre;
+  static SKV_DEV Pre load(const EpiResidual& e, int row, int col) { return e.pre8(row, col); }
+  static SKV_DEV void apply(const EpiResidual& e, int row, int col, const float* a, const float* b, const Pre& p) {
+    e.vec8(row, col, a, b, p);
+  }
+};
+
 // Work split of one launch.  The first dp_tiles tiles are computed whole
 // (data parallel, grid blocks 0 .. dp_tiles-1, XCD remapped); each of the
-// remaining tiles is split along K into `splits` ranges (stream-K tail),
-// one grid block per range, whose fp32 partial tiles go to `ws` and are
-// summed in fixed order by gemm_reduce_kernel.
+// remaining tiles is split along K into `splits` ranges (a partly filled
+// last wave of tiles becomes K-split units that fill every CU), one grid
+// block per range, whose fp32 partial tiles go to `ws` and are summed in
+// fixed order by gemm_reduce_kernel.
 struct SplitPlan {
   int dp_tiles;
   int splits;
   float* ws;
 };
 
-template <class Epi>
+template <int NBUF, class Epi>
 __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(const bf16_t* __restrict__ A,
                                                                  const bf16_t* __restrict__ B, int M, int N,
-                                                                 int K, int lda, int ldb, SplitPlan plan, Epi epi) {
-  __shared__ __attribute__((aligned(16))) bf16_t smem[2][(BM + BN) * BK];
+                                                                 int K, SplitPlan plan, Epi epi) {
+  constexpr int BK = kPanelCols;  // one k-stage = one 32-column block of a panel
+  constexpr int CH = StageShape<BK>::CH, RPI = StageShape<BK>::RPI, LPW = StageShape<BK>::LPW;
+  constexpr int NSUB = StageShape<BK>::NSUB;
+  static_assert(NSUB % 2 == 0 && NBUF >= 2, "stage shape");
+  __shared__ __attribute__((aligned(1024))) bf16_t smem[NBUF][(BM + BN) * BK];
 
   const int tiles_m = (M + BM - 1) / BM;
   const int tiles_n = (N + BN - 1) / BN;
@@ -107,166 +169,219 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(const bf16_t* __
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // 0..7; SIMD = wave & 3
-  const int pp = wave >> 2;                                   // ping-pong group
-  const int wm = wave & 3, wn = pp;                           // 64 x 128 output block of this wave
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // 0..3, one per SIMD
+  const int wm = wave & 1, wn = wave >> 1;                    // 128 x 128 output block
 
-  // Direct global -> LDS loads (global_load_lds_dwordx4): one instruction
-  // moves 1 KB = 8 rows x 128 B (whole cache lines: the vector memory path
-  // pays per line, so half-line row segments would halve its throughput)
-  // and lane l's 16 bytes land at byte 16*l of the destination, so the XOR
-  // swizzle is applied on the global side: lane l fetches the logical chunk
-  // of row (l >> 3) that belongs at physical chunk l & 7.  A stage is 32 row
-  // groups of A and 32 of B; group 0 loads A, group 1 loads B, 8
-  // instructions per wave.
-  const bf16_t* gsrc_base;
-  int gsrc_off[8];
-  int lds_dst[8];
-  {
-    const int is_b = pp;
-    gsrc_base = is_b ? B : A;
-    const int ld = is_b ? ldb : lda;
-    const int lim = is_b ? N - 1 : M - 1;
-    const int r0 = is_b ? n0 : m0;
+  // Direct global -> LDS loads.  Stage s of row panel tm of A is the
+  // contiguous 16 KB block a_panel + s * 8192 (likewise B), so every load
+  // instruction moves one contiguous 1 KB run (RPI = 16 rows of 64 B).  Lane
+  // l's 16 bytes land at byte 16*l of the instruction's LDS destination, so
+  // the XOR swizzle of the LDS layout is applied on the global side: lane l
+  // fetches the logical chunk of row l / CH that belongs at physical chunk
+  // l % CH.  Wave w moves row groups w*LPW/2 .. +LPW/2 of both A and B.
+  constexpr int LH = LPW / 2;
+  const int nkb = K / BK;
+  const bf16_t* a_panel = A + (int64_t)tm * nkb * (BM * BK);
+  const bf16_t* b_panel = B + (int64_t)tn * nkb * (BN * BK);
+  int g_off[LH];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int grp = (wave & 3) * 8 + i;
-      const int row = grp * 8 + (lane >> 3);
-      const int c = (lane & 7) ^ ((row >> 1) & 7);
-      gsrc_off[i] = min(r0 + row, lim) * ld + c * 8;
-      lds_dst[i] = (is_b ? BM * BK : 0) + grp * 8 * BK;
-    }
+  for (int i = 0; i < LH; ++i) {
+    const int row = (wave * LH + i) * RPI + lane / CH;
+    g_off[i] = row * BK + (((lane % CH) ^ swizzle<CH>(row)) << 3);
   }
-  auto gload = [&](int buf, int k0) {
-    bf16_t* base = smem[buf];
+  auto gload = [&](int buf, int stage_idx) {
+    typedef __attribute__((address_space(3))) void* lds_ptr;
+    const int64_t so = (int64_t)stage_idx * (BM * BK);
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      __builtin_amdgcn_global_load_lds(gsrc_base + gsrc_off[i] + k0,
-                                       (__attribute__((address_space(3))) void*)(base + lds_dst[i]), 16, 0, 0);
+    for (int i = 0; i < LH; ++i) {
+      const int grp = wave * LH + i;
+      const bf16_t* sa = a_panel + so + g_off[i];
+      const bf16_t* sb = b_panel + so + g_off[i];
+      __builtin_amdgcn_global_load_lds(sa, (lds_ptr)(&smem[buf][grp * RPI * BK]), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(sb, (lds_ptr)(&smem[buf][BM * BK + grp * RPI * BK]), 16, 0, 0);
+    }
   };
 
-  f32x16_t acc[2][4];
+  f32x16_t acc[4][4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16_t{0};
 
   const int frag_row = lane & 31;
   const int khalf = lane >> 5;
-  const int swz = (lane >> 1) & 7;  // (row >> 1) & 7 of the fragment row
-  const int a_off = (wm * 64 + frag_row) * BK;
+  const int swz = swizzle<CH>(frag_row);  // rows 32 apart share it
+  const int a_off = (wm * 128 + frag_row) * BK;
   const int b_off = BM * BK + (wn * 128 + frag_row) * BK;
 
-  // operands of half a stage: 2 k-substeps x (2 A + 4 B) fragments
-  bf16x8_t af[2][2], bfr[2][4];
-  auto fload = [&](int buf, int half) {
+  // fragments of one k-substep (16 deep): 4 A row tiles, 4 B column tiles
+  bf16x8_t af[2][4], bfr[2][4];
+  auto fload = [&](int buf, int kk, int slot) {
     const bf16_t* sa = smem[buf] + a_off;
     const bf16_t* sb = smem[buf] + b_off;
+    const int ch = ((kk * 2 + khalf) ^ swz) << 3;
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int ch = (((half * 2 + kk) * 2 + khalf) ^ swz) << 3;
+    for (int i = 0; i < 4; ++i) af[slot][i] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(sa + i * 32 * BK + ch));
 #pragma unroll
-      for (int i = 0; i < 2; ++i) af[kk][i] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(sa + i * 32 * BK + ch));
-#pragma unroll
-      for (int j = 0; j < 4; ++j) bfr[kk][j] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(sb + j * 32 * BK + ch));
-    }
+    for (int j = 0; j < 4; ++j) bfr[slot][j] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(sb + j * 32 * BK + ch));
   };
-  auto compute = [&]() {
+  // acc[i][j] (transposed tile): lane holds output row i*32 + (lane & 31),
+  // columns j*32 + 8*(v/4) + 4*(lane/32) + (v%4)
+  auto compute = [&](int slot) {
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk][i], bfr[kk][j], acc[i][j], 0, 0, 0);
-  };
-
-  // Ping-pong over the two waves of each SIMD: every wave runs the same
-  // sequence of phases separated by workgroup barriers -- read the first
-  // half of stage s from LDS (and issue its share of the loads of stage s+1
-  // into the other buffer), multiply it (16 MFMAs), read the second half and
-  // wait for its loads, multiply it -- and group 1 starts one barrier late,
-  // so in every slot one wave of each SIMD is on the matrix core while the
-  // other reads LDS.  Group 0 reads stage s in slots 4s and 4s+2, group 1 in
-  // 4s+1 and 4s+3; the loads of stage s+1 go out in slots 4s / 4s+1, after
-  // the last reads of that buffer (stage s-1, slot 4s-1), and each wave
-  // waits for them at the end of its second read phase (slot 4s+2 / 4s+3),
-  // before stage s+1 is first read in slot 4s+4.  Every wave passes
-  // 2 + 4 nk barriers.
-  const int nk = ke - kb;
-  const int k_base = kb * BK;
-  gload(0, k_base);
-  wait_loads_and_reads();
-  barrier_only();
-  if (pp == 1) barrier_only();
-  for (int s = 0; s < nk; ++s) {
-    const int cur = s & 1;
-    fload(cur, 0);
-    if (s + 1 < nk) gload(cur ^ 1, k_base + (s + 1) * BK);
-    barrier_only();
-    compute();
-    barrier_only();
-    fload(cur, 1);
-    wait_loads_and_reads();
-    barrier_only();
-    compute();
-    barrier_only();
-  }
-  if (pp == 0) barrier_only();
-
-  // epilogue: lane holds column (lane & 31) of each 32x32 tile and rows
-  // 8*(v/4) + 4*(lane/32) + (v%4)
-  if (split) {
-    float* part = plan.ws + (int64_t)unit * (BM * BN);
-    const int cl = wn * 128 + (lane & 31);
-    const int rl = wm * 64 + 4 * (lane >> 5);
-#pragma clang loop unroll(full)
-    for (int i = 0; i < 2; ++i)
-#pragma clang loop unroll(full)
       for (int j = 0; j < 4; ++j)
-#pragma clang loop unroll(full)
-        for (int v = 0; v < 16; ++v)
-          part[(rl + i * 32 + 8 * (v >> 2) + (v & 3)) * BN + cl + j * 32] = acc[i][j][v];
-    return;
-  }
-  const int col_base = n0 + wn * 128 + (lane & 31);
-  const int row_base = m0 + wm * 64 + 4 * (lane >> 5);
-#pragma clang loop unroll(full)
-  for (int i = 0; i < 2; ++i) {
-#pragma clang loop unroll(full)
-    for (int j = 0; j < 2; ++j) {
-      const int col = col_base + j * 32;
-      if (col >= N) continue;
-#pragma clang loop unroll(full)
-      for (int v = 0; v < 16; ++v) {
-        const int row = row_base + i * 32 + 8 * (v >> 2) + (v & 3);
-        if (row < M) epi(row, col, acc[i][j][v], acc[i][j + 2][v]);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[slot][j], af[slot][i], acc[i][j], 0, 0, 0);
+  };
+
+  const int nk = ke - kb;
+  // one k-substep: 16 MFMAs on fragment slot `slot`, with the 8 fragment
+  // reads of the next substep interleaved between the first 8 of them
+  auto step = [&](int slot, int buf, int kk_next) {
+    fload(buf, kk_next, slot ^ 1);
+    compute(slot);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // Wait until this wave's loads of stage s+1 have landed while those of
+  // the `after` later stages may still be in flight, then a workgroup
+  // barrier: every wave's share of stage s+1 is then in LDS, and every wave
+  // has finished reading the buffer of stage s.
+  auto wait_then_barrier = [&](int after) {
+    constexpr int L = StageShape<BK>::LPW;
+    if (after <= 0) wait_vm_then_barrier<0>();
+    else if (after == 1) wait_vm_then_barrier<L>();
+    else if (after == 2) wait_vm_then_barrier<2 * L>();
+    else if (after == 3) wait_vm_then_barrier<3 * L>();
+    else wait_vm_then_barrier<4 * L>();
+  };
+
+  // Pipeline: all NBUF buffers are filled up front.  At the end of stage s
+  // (after the barrier that publishes stage s+1) the buffer of stage s is
+  // free and receives stage s+NBUF, while the last k-substep of stage s runs
+  // and the first fragments of stage s+1 are read.  The flags are constants
+  // at each call site, so every stage body is one straight-line block and
+  // the group barriers interleave its loads and LDS reads with the MFMAs.
+  auto stage = [&](int s, bool load, bool next) {
+    const int cur = s % NBUF;
+#pragma unroll
+    for (int kk = 0; kk < StageShape<BK>::NSUB - 1; ++kk) step(kk & 1, cur, kk + 1);
+    if (next) {
+      if (load) wait_vm_then_barrier<(NBUF - 2) * StageShape<BK>::LPW>();
+      else wait_vm_then_barrier<0>();
+    }
+    if (load) gload(cur, kb + s + NBUF);
+    if (next) fload((s + 1) % NBUF, 0, 0);
+    compute(1);
+    if (load) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, StageShape<BK>::LPW / 8, 0);
       }
     }
+    if (next) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  const int pre = min(NBUF, nk);
+  for (int p = 0; p < pre; ++p) gload(p, kb + p);
+  wait_then_barrier(pre - 1);
+  fload(0, 0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  int s = 0;
+  for (; s < nk - NBUF; ++s) stage(s, true, true);
+  for (; s < nk - 1; ++s) stage(s, false, true);
+  stage(s, false, false);
+
+  // Epilogue through LDS.  The last stage's reads are complete in every wave
+  // after this barrier, so the stage buffers can be reused.
+  wait_all_then_barrier();
+  float* stg = reinterpret_cast<float*>(&smem[0][0]) + wave * kStageWave;
+  const int er = lane >> 3;        // row within a group of 8
+  const int ec = (lane & 7) * 8;   // first of eight columns, 0..56
+  const int wr = lane & 31;        // row written by this lane
+  const int wc = 4 * (lane >> 5);  // column offset within a group of 8
+  const int lcol = wn * 128 + ec;
+  const bool cols_ok = n0 + wn * 128 < N;
+  // unit (pass i, it): row wm*128 + i*32 + it*8 + er, columns lcol.. and lcol+64..
+  using Ahead = EpiAhead<Epi>;
+  typename Ahead::Pre ahead[4];
+  auto unit_row = [&](int i, int it) { return wm * 128 + i * 32 + it * 8 + er; };
+  if (!split && cols_ok) {
+#pragma clang loop unroll(full)
+    for (int it = 0; it < 4; ++it)
+      if (m0 + unit_row(0, it) < M) ahead[it] = Ahead::load(epi, m0 + unit_row(0, it), n0 + lcol);
+  }
+#pragma clang loop unroll(full)
+  for (int i = 0; i < 4; ++i) {
+    // stage rows i*32 .. +32 of this wave's block: tile (i, j) value v is
+    // column j*32 + 8*(v/4) + wc + (v%4) of row wr
+#pragma clang loop unroll(full)
+    for (int j = 0; j < 4; ++j)
+#pragma clang loop unroll(full)
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<f32x4_t*>(stg + wr * kStageLd + j * 32 + 8 * g + wc) =
+            f32x4_t{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+    wait_lds();
+#pragma clang loop unroll(full)
+    for (int it = 0; it < 4; ++it) {
+      const int r = it * 8 + er;
+      float a[8], b[8];
+      load8(stg + r * kStageLd + ec, a);
+      load8(stg + r * kStageLd + ec + 64, b);
+      const int lrow = unit_row(i, it);
+      if (split) {
+        float* part = plan.ws + (int64_t)unit * (BM * BN) + lrow * BN + lcol;
+        store8(part, a);
+        store8(part + 64, b);
+      } else if (cols_ok) {
+        if (m0 + lrow < M) Ahead::apply(epi, m0 + lrow, n0 + lcol, a, b, ahead[it]);
+        if (i < 3 && m0 + unit_row(i + 1, it) < M) ahead[it] = Ahead::load(epi, m0 + unit_row(i + 1, it), n0 + lcol);
+      }
+    }
+    wait_lds();
   }
 }
 
 // Sum the split partial tiles in fixed order and apply the epilogue:
-// thread -> (tail tile, row, column pair (c, c + 64)).
+// thread -> (tail tile, row, eight column pairs).
 template <class Epi>
 __global__ __launch_bounds__(256) void gemm_reduce_kernel(int M, int N, SplitPlan plan, Epi epi) {
   const int tiles_n = (N + BN - 1) / BN;
   const int tiles_m = (M + BM - 1) / BM;
-  const int r = blockIdx.y;  // tail tile
-  const int idx = blockIdx.x * blockDim.x + threadIdx.x;  // row * 128 + pair
-  const int row = idx >> 7, pair = idx & 127;
-  const int cl = (pair >> 6) * 128 + (pair & 63);
+  const int r = blockIdx.y;                               // tail tile
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;  // row * 16 + unit
+  const int row = idx >> 4, u = idx & 15;
+  const int cl = (u >> 3) * 128 + (u & 7) * 8;  // first column of the unit (pair at +64)
   int tm, tn;
   tile_coords(plan.dp_tiles + r, tiles_m, tiles_n, tm, tn);
   const int grow = tm * BM + row, gcol = tn * BN + cl;
   if (grow >= M || gcol >= N) return;
   const float* part = plan.ws + (int64_t)r * plan.splits * (BM * BN) + row * BN + cl;
-  float v0 = 0.f, v1 = 0.f;
+  float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, b[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int sp = 0; sp < plan.splits; ++sp) {
-    v0 += part[(int64_t)sp * (BM * BN)];
-    v1 += part[(int64_t)sp * (BM * BN) + 64];
+    float pa[8], pb[8];
+    load8(part + (int64_t)sp * (BM * BN), pa);
+    load8(part + (int64_t)sp * (BM * BN) + 64, pb);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      a[e] += pa[e];
+      b[e] += pb[e];
+    }
   }
-  epi(grow, gcol, v0, v1);
+  epi.vec8(grow, gcol, a, b);
 }
 
 int num_cus() {
@@ -284,10 +399,12 @@ int num_cus() {
 
 int64_t gemm_bf16_ws_elems() { return (int64_t)num_cus() * BM * BN; }
 
-template <class Epi>
-hipError_t launch_gemm_bf16(const bf16_t* A, int lda, const bf16_t* B, int ldb, int M, int N, int K, const Epi& epi,
-                            float* ws, int64_t ws_elems, hipStream_t stream) {
+template <int NBUF, class Epi>
+hipError_t launch_gemm_cfg(const bf16_t* A, const bf16_t* B, int M, int N, int K, const Epi& epi, float* ws,
+                           int64_t ws_elems, hipStream_t stream) {
+  constexpr int BK = kPanelCols;
   if (M <= 0) return hipSuccess;
+  if (K % BK != 0 || N % 128 != 0) return hipErrorInvalidValue;
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   const int P = num_cus();
   const int nk = K / BK;
@@ -303,21 +420,27 @@ hipError_t launch_gemm_bf16(const bf16_t* A, int lda, const bf16_t* B, int ldb, 
     }
   }
   const int grid = plan.dp_tiles + (tiles - plan.dp_tiles) * plan.splits;
-  hipLaunchKernelGGL((gemm_bf16_kernel<Epi>), dim3(grid), dim3(kThreads), 0, stream, A, B, M, N, K, lda, ldb, plan,
-                     epi);
+  hipLaunchKernelGGL((gemm_bf16_kernel<NBUF, Epi>), dim3(grid), dim3(kThreads), 0, stream, A, B, M, N, K, plan, epi);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || plan.dp_tiles == tiles) return e;
-  hipLaunchKernelGGL((gemm_reduce_kernel<Epi>), dim3(BM * 128 / 256, tiles - plan.dp_tiles), dim3(256), 0, stream, M,
+  hipLaunchKernelGGL((gemm_reduce_kernel<Epi>), dim3(BM * 16 / 256, tiles - plan.dp_tiles), dim3(256), 0, stream, M,
                      N, plan, epi);
   return hipGetLastError();
 }
 
+template <class Epi>
+hipError_t launch_gemm_bf16(const bf16_t* A, const bf16_t* B, int M, int N, int K, const Epi& epi, float* ws,
+                            int64_t ws_elems, hipStream_t stream) {
+  return launch_gemm_cfg<kNBuf>(A, B, M, N, K, epi, ws, ws_elems, stream);
+}
+
 #define SKV_INST_GEMM(E)                                                                                      \
-  template hipError_t launch_gemm_bf16<E>(const bf16_t*, int, const bf16_t*, int, int, int, int, const E&, float*, \
-                                          int64_t, hipStream_t);
+  template hipError_t launch_gemm_bf16<E>(const bf16_t*, const bf16_t*, int, int, int, const E&, float*, int64_t, \
+                                          hipStream_t);
 SKV_INST_GEMM(EpiQKV<bf16_t>)
 SKV_INST_GEMM(EpiKVSkip<bf16_t>)
 SKV_INST_GEMM(EpiResidual)
 SKV_INST_GEMM(EpiSwiGLU<bf16_t>)
+SKV_INST_GEMM(EpiSwiGLUPanel)
 SKV_INST_GEMM(EpiStore<bf16_t>)
 SKV_INST_GEMM(EpiStoreF32)

@@ -7,11 +7,13 @@
 #include "epilogues.h"
 
 // C[M,N] = A[M,K] B[N,K]^T on MFMA (bf16 in, fp32 accumulate), pair distance 64.
-// Requires K % 64 == 0, N % 128 == 0.  ws (gemm_bf16_ws_elems() floats, or
-// NULL) holds the split partial tiles of a partly filled last wave.
+// A and B are in the panel layout (panel_off; row counts rounded up to 256,
+// padding rows are read but their results are never stored).  Requires
+// K % 32 == 0, N % 128 == 0.  ws (gemm_bf16_ws_elems() floats, or NULL)
+// holds the split partial tiles of a partly filled last wave.
 template <class Epi>
-hipError_t launch_gemm_bf16(const bf16_t* A, int lda, const bf16_t* B, int ldb, int M, int N, int K, const Epi& epi,
-                            float* ws, int64_t ws_elems, hipStream_t stream);
+hipError_t launch_gemm_bf16(const bf16_t* A, const bf16_t* B, int M, int N, int K, const Epi& epi, float* ws,
+                            int64_t ws_elems, hipStream_t stream);
 int64_t gemm_bf16_ws_elems();
 
 // Same product in fp32 on the vector ALUs (fp32 models), pair distance P
@@ -44,12 +46,18 @@ template <typename T>
 hipError_t launch_rmsnorm(const float* x, const int32_t* rows_idx, const float* gamma, int rows, int d, float eps,
                           T* y, hipStream_t stream);
 
+// Same RMSNorm for rows 0..rows-1 of x into bf16 y in the panel layout
+// (panel_off with d columns); d % 256 == 0.
+hipError_t launch_rmsnorm_panel(const float* x, const float* gamma, int rows, int d, float eps, bf16_t* y,
+                                hipStream_t stream);
+
 // y[r, :] = x[rows_idx[r], :]  (fp32 rows)
 hipError_t launch_gather_rows(const float* x, const int32_t* rows_idx, int rows, int d, float* y,
                               hipStream_t stream);
 
 // Causal GQA flash attention for prompt tokens (bf16, MFMA): q [T, hq, dh],
-// K/V from one cache slot, o [T, hq * dh].  head_dim 128, hq/hkv % 4 == 0.
+// K/V from one cache slot, o [T, hq * dh] in the panel layout (panel_off with
+// hq * dh columns).  head_dim 128, hq/hkv % 4 == 0.
 hipError_t launch_attn_prefill_bf16(const bf16_t* q, CacheSlot<bf16_t> cache, const int32_t* cu_seqlens,
                                     const int32_t* block_tables, int max_blocks, int batch, int max_seqlen, int hq,
                                     bf16_t* o, hipStream_t stream);
@@ -74,5 +82,8 @@ template <typename T>
 hipError_t launch_fold_rows(const T* W, const T* gamma, int rows, int cols, T* out, hipStream_t stream);
 template <typename T>
 hipError_t launch_interleave(const T* gate, const T* up, int f, int d, int P, T* out, hipStream_t stream);
+// Row-major W [rows, K] -> panel layout with rows rounded up to 256 (padding
+// rows zero); K % 32 == 0.
+hipError_t launch_to_panels(const bf16_t* W, int rows, int K, bf16_t* out, hipStream_t stream);
 template <typename T>
 hipError_t launch_to_f32(const T* in, int64_t n, float* out, hipStream_t stream);
