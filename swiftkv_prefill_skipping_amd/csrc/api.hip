@@ -152,6 +152,7 @@ skv_status validate_config(const skv_model_config* c) {
     if ((c->n_q_heads / c->n_kv_heads) % 4) return fail(SKV_ERR_UNSUPPORTED, "bf16 path needs hq/hkv % 4 == 0");
     if (c->d_model % 256 || c->ffn_dim % 256)
       return fail(SKV_ERR_UNSUPPORTED, "bf16 path needs d_model and ffn_dim multiples of 256");
+    if (c->d_model > 8192) return fail(SKV_ERR_UNSUPPORTED, "bf16 path supports d_model up to 8192");
     if (c->vocab % 128) return fail(SKV_ERR_UNSUPPORTED, "bf16 path needs vocab % 128 == 0");
     if (c->max_batch > 32) return fail(SKV_ERR_UNSUPPORTED, "bf16 path supports at most 32 prompts per call");
   } else {

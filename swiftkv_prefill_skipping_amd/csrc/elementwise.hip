@@ -3,6 +3,7 @@
 // 256-thread workgroup with 16-byte (or 8-byte) contiguous accesses per
 // thread so a wavefront reads whole 1 KB spans.
 #include "common.h"
+#include "epilogues.h"
 #include "kernels.h"
 
 namespace {
@@ -95,43 +96,42 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
   }
 }
 
-// RMSNorm into the panel layout: each wave normalises a pair of rows (lanes
-// 0-31 the even row, 32-63 the odd one), 8 columns per lane per step, so
-// one store instruction writes the two rows' 64-byte runs of eight column
-// blocks, which are adjacent in the panel (128 bytes each).
+// RMSNorm into the panel layout: one wave per row, lane l holding columns
+// [8l + 512i, 8l + 512i + 8) (those below d) in registers, so x is read
+// once.  A store instruction writes 16 bytes per lane: 64-byte runs, one
+// per 32-column block, which the next row's wave completes to full lines.
+constexpr int kNormMaxChunks = 16;  // d <= 8192
 __global__ __launch_bounds__(256) void rmsnorm_panel_kernel(const float* __restrict__ x,
                                                             const float* __restrict__ gamma, int rows, int d,
                                                             float eps, bf16_t* __restrict__ y) {
   const int lane = threadIdx.x & 63;
-  const int r = blockIdx.x * 8 + (threadIdx.x >> 6) * 2 + (lane >> 5);
-  const int c0 = (lane & 31) * 8;
-  const float* xr = x + (int64_t)min(r, rows - 1) * d;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;  // whole waves
+  const int nch = (d + 511) / 512;
+  const float* xr = x + (int64_t)r * d + lane * 8;
+  float v[kNormMaxChunks][8];
   float ss = 0.f;
-  for (int c = c0; c < d; c += 256) {
-    const float4 a = *reinterpret_cast<const float4*>(xr + c);
-    const float4 b = *reinterpret_cast<const float4*>(xr + c + 4);
-    ss += a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w + b.x * b.x + b.y * b.y + b.z * b.z + b.w * b.w;
-  }
 #pragma unroll
-  for (int o = 16; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);  // within each half-wave
-  const float inv = 1.0f / sqrtf(ss / (float)d + eps);
-  if (r >= rows) return;
-  for (int c = c0; c < d; c += 256) {
-    const float4 a = *reinterpret_cast<const float4*>(xr + c);
-    const float4 b = *reinterpret_cast<const float4*>(xr + c + 4);
-    float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-    if (gamma) {
-      const float4 ga = *reinterpret_cast<const float4*>(gamma + c);
-      const float4 gb = *reinterpret_cast<const float4*>(gamma + c + 4);
-      const float g[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
+  for (int i = 0; i < kNormMaxChunks; ++i) {
+    if (i < nch && lane * 8 + i * 512 < d) {
+      load8(xr + i * 512, v[i]);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = v[e] * inv * g[e];
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = v[e] * inv;
+      for (int e = 0; e < 8; ++e) ss += v[i][e] * v[i][e];
     }
-    *reinterpret_cast<u32x4_t*>(y + panel_off(r, c, d)) =
-        u32x4_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
+  }
+  ss = warp_sum(ss);
+  const float inv = 1.0f / sqrtf(ss / (float)d + eps);
+#pragma unroll
+  for (int i = 0; i < kNormMaxChunks; ++i) {
+    if (i < nch && lane * 8 + i * 512 < d) {
+      const int c = lane * 8 + i * 512;
+      float g[8] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
+      if (gamma) load8(gamma + c, g);
+      float o[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = v[i][e] * inv * g[e];
+      store8(y + panel_off(r, c, d), o);
+    }
   }
 }
 
@@ -232,8 +232,8 @@ hipError_t launch_rmsnorm(const float* x, const int32_t* rows_idx, const float* 
 hipError_t launch_rmsnorm_panel(const float* x, const float* gamma, int rows, int d, float eps, bf16_t* y,
                                 hipStream_t stream) {
   if (rows <= 0) return hipSuccess;
-  if (d % 256) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(rmsnorm_panel_kernel, dim3((rows + 7) / 8), dim3(256), 0, stream, x, gamma, rows, d, eps, y);
+  if (d % kPanelCols || d > 512 * kNormMaxChunks) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(rmsnorm_panel_kernel, dim3((rows + 3) / 4), dim3(256), 0, stream, x, gamma, rows, d, eps, y);
   return hipGetLastError();
 }
 

@@ -2,20 +2,24 @@
 // accumulation, results handed to an epilogue functor eight column pairs
 // (col + e, col + 64 + e) at a time.
 //
-// Tile 256 x 256, k-stages of 64.  256 threads = 4 wave64s, one per SIMD;
+// Operands are in the panel layout (common.h): 256-row panels stored as
+// contiguous [256][32] blocks, so the k-stage s of an output tile is one
+// contiguous 16 KB block of A's panel and one of B's.
+//
+// Tile 256 x 256, k-stages of 32.  256 threads = 4 wave64s, one per SIMD;
 // wave w owns output rows 128*(w&1) .. +128 and columns 128*(w>>1) .. +128
 // as 4 x 4 tiles of v_mfma_f32_32x32x16_bf16 (256 accumulator registers).
 // The MFMA takes the B fragment as its first operand, so each lane ends up
 // holding one output row (lane & 31) and runs of four consecutive columns.
 //
 // Operand staging: global -> LDS directly (global_load_lds_dwordx4, no
-// register round trip) into two 64 KB stages.  LDS rows are 128 B (64
-// bf16); the 16 B chunk c of row r is stored at chunk c ^ ((r >> 1) & 7).
-// gfx950's LDS serves a ds_read_b128 16 lanes (256 B, all 64 banks) per
-// pass; with this swizzle the 16 rows read by one pass cover all 16 bank
-// groups, so the reads are conflict free.
+// register round trip) into a ring of kNBuf 32 KB stages, kNBuf - 1 of them
+// in flight while one is multiplied.  LDS rows are 64 B (32 bf16); the 16 B
+// chunk c of row r is stored at chunk c ^ ((r >> 2) & 3), so the 16 rows
+// read by one ds_read_b128 pass (16 lanes, 256 B, all 64 banks) cover all
+// 16 bank groups: the fragment reads are conflict free.
 //
-// Schedule: each k-stage is four k-substeps of 16 MFMAs; the fragment reads
+// Schedule: each k-stage is two k-substeps of 16 MFMAs; the fragment reads
 // of the next substep are interleaved with the MFMAs of the current one.
 // One workgroup barrier per stage publishes the next stage and frees the
 // current buffer, whose next load goes out right after it.
@@ -28,7 +32,7 @@
 // Workgroups are dispatched round robin over the 8 XCDs; the tile index is
 // remapped so each XCD processes a contiguous run of tiles, and runs are
 // ordered in groups of kGroupM row tiles so concurrently resident tiles share
-// A rows and B columns in that XCD's L2.
+// A and B panels in that XCD's L2.
 #include "common.h"
 #include "epilogues.h"
 #include "kernels.h"

@@ -47,7 +47,7 @@ hipError_t launch_rmsnorm(const float* x, const int32_t* rows_idx, const float* 
                           T* y, hipStream_t stream);
 
 // Same RMSNorm for rows 0..rows-1 of x into bf16 y in the panel layout
-// (panel_off with d columns); d % 256 == 0.
+// (panel_off with d columns); d % 32 == 0 and d <= 8192.
 hipError_t launch_rmsnorm_panel(const float* x, const float* gamma, int rows, int d, float eps, bf16_t* y,
                                 hipStream_t stream);
 
