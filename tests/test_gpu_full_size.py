@@ -78,6 +78,47 @@ def test_midsize_split_tail_gemms():
     _check_sampled(w, batch, [0, 7])
 
 
+class _ProgressLayers:
+    """Seeded layers generated on demand for the oracle (no host copy of the whole model), with a progress line
+    every few layers so a long evaluation is visibly alive."""
+
+    def __init__(self, w, every=8, tag=""):
+        self.w, self.every, self.tag, self.count, self.t0 = w, every, tag, 0, time.time()
+
+    def make(self, i):
+        self.count += 1
+        if self.count % self.every == 0:
+            _say(f"[full] {self.tag}: {self.count} layer evaluations ({time.time() - self.t0:.0f} s)")
+        return {k: si.as_f32(v) for k, v in si.layer_weights(self.w.shape, i, self.w.dtype).items()}
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(1500)
+def test_llama70b_l40_b32_sampled():
+    """70B shape (80 layers, d=8192, 64/8 heads, f=28672) on one GPU, l=40, 32 prompts x 1000 tokens; the GPU runs
+    the whole batch, the oracle one prompt (layers generated on demand: the fp32 model would not fit in host memory)."""
+    import torch
+    w = si.WORKLOADS["llama70b_l40_b32"]
+    batch = si.make_batch(w)
+    b = 5
+    t0 = time.time()
+    model, cache, db, logits = run_gpu(w, batch)
+    _say(f"[full] {w.name}: weights loaded and GPU prefill of {batch.total_tokens} tokens done "
+         f"({time.time() - t0:.1f} s); oracle on prompt {b}")
+    assert torch.isfinite(logits).all()
+    gw = si.global_weights(w.shape, w.dtype)
+    toks = [batch.tokens[b]]
+    res = {}
+    for mode, store in (("fp32", None), ("bf16-storage", round_bf16)):
+        t1 = time.time()
+        src = _ProgressLayers(w, tag=f"oracle {mode}")
+        W = O.LazyWeights(si.as_f32(gw["embed"]), si.as_f32(gw["final_norm"]), si.as_f32(gw["lm_head"]), src.make)
+        kw = {} if store is None else {"store": store}
+        res[mode] = O.swiftkv_prefill(dims_of(w.shape), W, toks, w.swiftkv_l, w.acrosskv_g, **kw)
+        _say(f"[full] oracle ({mode}) done ({time.time() - t1:.1f} s)")
+    compare(w, batch, logits, cache, res["fp32"], [b], label=w.name, bf16_ref=res["bf16-storage"])
+
+
 def _logical_device(kt, vt, block_row, n):
     """One prompt's K and V in position order, on the device (no host copy)."""
     import torch
