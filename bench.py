@@ -177,9 +177,9 @@ def main():
         "roofline": {"kernel": "gemm_gateup (bf16 MFMA GEMM + SwiGLU epilogue)", "bound": "mfma",
                      "achieved": round(achieved, 2), "peak": MI355X_BF16_DENSE_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / MI355X_BF16_DENSE_TFLOPS, 4),
-                     "traffic": (measured_traffic("EpiSwiGLU") or {}).get("bytes") if w.name == "llama8b_l16_b16"
+                     "traffic": (measured_traffic("EpiSwiGLUPanel") or {}).get("bytes") if w.name == "llama8b_l16_b16"
                      else None,
-                     "traffic_detail": measured_traffic("EpiSwiGLU") if w.name == "llama8b_l16_b16" else None,
+                     "traffic_detail": measured_traffic("EpiSwiGLUPanel") if w.name == "llama8b_l16_b16" else None,
                      "algorithmic_bytes_per_launch": prof["bytes"] / max(prof["launches"], 1),
                      "avg_launch_ms": round(avg_launch_ms, 4), "launches": prof["launches"],
                      "flops_per_launch": flops_per_launch},
