@@ -1,12 +1,14 @@
 """Throughput of the SwiftKV prefill on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--no-full-depth]
     python bench.py --copy-calibration MIB   # plain device copy of known size, for HBM counter scaling
 
 One step = one skv_prefill call over the whole batch (every row of the hot
 path: layers 1..l for all prompt tokens, the fused skipped-layer KV GEMM,
 the last-token path through layers l+1..L and the LM head), inputs and
-weights already resident in HBM.  Prints one JSON line.
+weights already resident in HBM.  Prints one JSON line.  The same batch is
+then also timed through the unmodified model (l = L, same kernels), so the
+line carries the SwiftKV / full-depth wall-clock ratio next to the FLOP ratio.
 """
 from __future__ import annotations
 
@@ -92,6 +94,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama8b_l16_b16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-full-depth", action="store_true",
+                    help="skip timing the same batch through all layers (l = L) with the same kernels")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 3 fp32 device copies of MIB MiB each (reference for FETCH_SIZE/WRITE_SIZE)")
     args = ap.parse_args()
@@ -184,6 +188,34 @@ def main():
                      "avg_launch_ms": round(avg_launch_ms, 4), "launches": prof["launches"],
                      "flops_per_launch": flops_per_launch},
     }
+    if not args.no_full_depth and w.swiftkv_l < w.shape.n_layers:
+        # the unmodified model (every layer for every prompt token), same weights, batch and kernels: the
+        # wall-clock ratio to compare with the FLOP ratio
+        import dataclasses
+        model.close()
+        cache.close()
+        wf = dataclasses.replace(w, name=w.name + "_full_depth", swiftkv_l=w.shape.n_layers, acrosskv_g=1)
+        t0 = time.time()
+        mf = runner.load_seeded_model(wf, T, B, batch.max_seqlen)
+        cf = runner.Cache(mf, batch.num_blocks)
+        log(f"[bench] full-depth model loaded in {time.time() - t0:.1f} s")
+        for i in range(args.warmup):
+            runner.prefill(mf, cf, db, logits, stream)
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for i in range(args.steps):
+            runner.prefill(mf, cf, db, logits, stream)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        ms_full = ev0.elapsed_time(ev1) / args.steps
+        full_f, _ = L.skv_flops(mf.cfg, batch.lengths)
+        log(f"[bench] full depth: {ms_full:.3f} ms/step")
+        res["full_depth_baseline"] = {
+            "ms_per_step": round(ms_full, 4), "tokens_per_s": round(T / (ms_full / 1e3), 1),
+            "tflops": round(full_f / (ms_full / 1e3) / 1e12, 2),
+            "swiftkv_time_ratio": round(ms / ms_full, 4), "swiftkv_flops_ratio": round(swift / full, 4)}
+        cf.close()
+        mf.close()
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on the host")
         res["cpu_baseline"] = cpu_baseline(w, batch, cached)

@@ -33,9 +33,9 @@ size_t round_up(size_t a, size_t b) { return (a + b - 1) / b * b; }
 }  // namespace
 
 // Weights of layers 1..l feed the prompt-token GEMMs and are kept in the
-// panel layout (bf16 models); those of skipped layers feed only the
-// last-token path and stay row-major.  fp32 models keep everything
-// row-major.
+// panel layout with 256-row panels; those of skipped layers (and the LM
+// head) feed only the last-token path and use 64-row panels (bf16 models).
+// fp32 models keep everything row-major.
 struct LayerDev {
   float* attn_norm = nullptr;  // fp32 [d]
   float* ffn_norm = nullptr;
@@ -43,7 +43,7 @@ struct LayerDev {
   void* wo = nullptr;    // [d, dq]
   void* wgu = nullptr;   // [2f, d], gate/up interleaved in blocks of P_mlp rows
   void* wdown = nullptr; // [d, f]
-  bool panels = false;   // stored in the panel layout
+  int panel_rows = 0;    // 0: row-major; else the panel height of the layout
   bool loaded = false;
 };
 
@@ -259,11 +259,11 @@ skv_status skv_model_create(const skv_model_config* cfg, skv_model** out) {
   ALLOC(m->rope_cos, (size_t)c.max_seqlen * half * 4);
   ALLOC(m->rope_sin, (size_t)c.max_seqlen * half * 4);
   // panel-layout matrices round their row count up to whole panels
-  const size_t R = m->bf16 ? 256 : 1;
+  const size_t R = m->bf16 ? kPanelRows : 1;
   for (int i = 1; i <= c.n_layers; ++i) {
     LayerDev& L = m->layers[i - 1];
-    L.panels = m->bf16 && i <= c.swiftkv_l;
-    const size_t r = L.panels ? R : 1;
+    L.panel_rows = !m->bf16 ? 0 : i <= c.swiftkv_l ? kPanelRows : kSkinnyPanelRows;
+    const size_t r = L.panel_rows ? L.panel_rows : 1;
     ALLOC(L.attn_norm, d * 4);
     ALLOC(L.ffn_norm, d * 4);
     ALLOC(L.wqkv, round_up(i <= c.swiftkv_l ? dq + 2 * dkv : dq, r) * d * E);
@@ -369,25 +369,33 @@ static skv_status gain_to_f32(skv_model* m, const void* src, float* dst, const c
   return SKV_OK;
 }
 
+// Copy a row-major host/device matrix into `dst`, either as is
+// (panel_rows == 0) or through the staging buffer into the panel layout,
+// in chunks of whole panels that fit the staging buffer.
+static skv_status load_matrix(skv_model* m, void* dst, const void* src, size_t rows, size_t cols, int panel_rows,
+                              const char* what) {
+  const size_t row_bytes = cols * m->esz;
+  if (!panel_rows) return copy_in(dst, src, rows * row_bytes, what);
+  if (!src) return fail(SKV_ERR_INVALID_ARG, std::string(what) + " is NULL");
+  const size_t chunk = m->staging_bytes / row_bytes / panel_rows * panel_rows;
+  if (chunk == 0) return fail(SKV_ERR_UNSUPPORTED, "staging buffer smaller than one panel");
+  for (size_t r0 = 0; r0 < rows; r0 += chunk) {
+    const size_t n = std::min(chunk, rows - r0);
+    SKV_TRY(copy_in(m->staging, (const char*)src + r0 * row_bytes, n * row_bytes, what));
+    SKV_HIP(launch_to_panels((const bf16_t*)m->staging, (int)n, (int)cols, panel_rows,
+                             (bf16_t*)dst + r0 * cols, 0));
+    SKV_HIP(hipDeviceSynchronize());
+  }
+  return SKV_OK;
+}
+
 skv_status skv_model_load_globals(skv_model* m, const void* embed, const void* final_norm, const void* lm_head) {
   if (!m) return fail(SKV_ERR_INVALID_ARG, "model is NULL");
   const size_t d = m->cfg.d_model, V = m->cfg.vocab;
   SKV_TRY(copy_in(m->embed, embed, V * d * m->esz, "embed"));
-  SKV_TRY(copy_in(m->lm_head, lm_head, V * d * m->esz, "lm_head"));
+  SKV_TRY(load_matrix(m, m->lm_head, lm_head, V, d, m->bf16 ? kSkinnyPanelRows : 0, "lm_head"));
   SKV_TRY(gain_to_f32(m, final_norm, m->final_norm, "final_norm"));
   m->globals_loaded = true;
-  return SKV_OK;
-}
-
-// Copy a row-major host/device matrix into `dst`, either as is or through the
-// staging buffer into the panel layout.
-static skv_status load_matrix(skv_model* m, void* dst, const void* src, size_t rows, size_t cols, bool panels,
-                              const char* what) {
-  const size_t bytes = rows * cols * m->esz;
-  if (!panels) return copy_in(dst, src, bytes, what);
-  SKV_TRY(copy_in(m->staging, src, bytes, what));
-  SKV_HIP(launch_to_panels((const bf16_t*)m->staging, (int)rows, (int)cols, (bf16_t*)dst, 0));
-  SKV_HIP(hipDeviceSynchronize());
   return SKV_OK;
 }
 
@@ -401,16 +409,17 @@ skv_status skv_model_load_layer(skv_model* m, int32_t layer, const skv_layer_wei
   SKV_TRY(gain_to_f32(m, w->attn_norm, L.attn_norm, "attn_norm"));  // leaves gamma_stage = attn gain
   if (layer <= c.swiftkv_l) {
     // [wq; wk; wv] concatenated row-major, then (bf16) into panels
-    char* dst = L.panels ? (char*)m->staging : (char*)L.wqkv;
+    char* dst = L.panel_rows ? (char*)m->staging : (char*)L.wqkv;
     SKV_TRY(copy_in(dst, w->wq, dq * d * E, "wq"));
     SKV_TRY(copy_in(dst + dq * d * E, w->wk, dkv * d * E, "wk"));
     SKV_TRY(copy_in(dst + (dq + dkv) * d * E, w->wv, dkv * d * E, "wv"));
-    if (L.panels) {
-      SKV_HIP(launch_to_panels((const bf16_t*)m->staging, (int)(dq + 2 * dkv), (int)d, (bf16_t*)L.wqkv, 0));
+    if (L.panel_rows) {
+      SKV_HIP(launch_to_panels((const bf16_t*)m->staging, (int)(dq + 2 * dkv), (int)d, L.panel_rows,
+                               (bf16_t*)L.wqkv, 0));
       SKV_HIP(hipDeviceSynchronize());
     }
   } else {
-    SKV_TRY(copy_in(L.wqkv, w->wq, dq * d * E, "wq"));
+    SKV_TRY(load_matrix(m, L.wqkv, w->wq, dq, d, L.panel_rows, "wq"));
     if (is_representative(c, layer)) {
       // fold this layer's input-RMSNorm gain into its K and V rows (in place
       // in the staging buffer), then store them as this group's block of the
@@ -423,7 +432,7 @@ skv_status skv_model_load_layer(skv_model* m, int32_t layer, const skv_layer_wei
         bf16_t* dst = (bf16_t*)m->wkv_skip + (size_t)grp * 2 * dkv * d;
         SKV_HIP(launch_fold_rows<bf16_t>((const bf16_t*)m->staging, (const bf16_t*)m->gamma_stage, (int)(2 * dkv),
                                          (int)d, (bf16_t*)m->staging, 0));
-        SKV_HIP(launch_to_panels((const bf16_t*)m->staging, (int)(2 * dkv), (int)d, dst, 0));
+        SKV_HIP(launch_to_panels((const bf16_t*)m->staging, (int)(2 * dkv), (int)d, kPanelRows, dst, 0));
       } else {
         float* dst = (float*)m->wkv_skip + (size_t)grp * 2 * dkv * d;
         SKV_HIP(launch_fold_rows<float>((const float*)m->staging, (const float*)m->gamma_stage, (int)(2 * dkv),
@@ -432,10 +441,10 @@ skv_status skv_model_load_layer(skv_model* m, int32_t layer, const skv_layer_wei
       SKV_HIP(hipDeviceSynchronize());
     }
   }
-  SKV_TRY(load_matrix(m, L.wo, w->wo, d, dq, L.panels, "wo"));
-  SKV_TRY(load_matrix(m, L.wdown, w->w_down, d, f, L.panels, "w_down"));
+  SKV_TRY(load_matrix(m, L.wo, w->wo, d, dq, L.panel_rows, "wo"));
+  SKV_TRY(load_matrix(m, L.wdown, w->w_down, d, f, L.panel_rows, "w_down"));
   // gate/up: interleave rows in blocks of P_mlp into L.wgu (row-major), then
-  // (bf16, unskipped) into panels through the staging buffer
+  // (bf16) into the layer's panel layout through the staging buffer
   SKV_TRY(copy_in(m->staging, w->w_gate, f * d * E, "w_gate"));
   SKV_TRY(copy_in((char*)m->staging + f * d * E, w->w_up, f * d * E, "w_up"));
   if (m->bf16)
@@ -444,8 +453,8 @@ skv_status skv_model_load_layer(skv_model* m, int32_t layer, const skv_layer_wei
   else
     SKV_HIP(launch_interleave<float>((const float*)m->staging, (const float*)m->staging + f * d, (int)f, (int)d,
                                      m->p_mlp, (float*)L.wgu, 0));
-  if (L.panels) {
-    SKV_HIP(launch_to_panels((const bf16_t*)L.wgu, (int)(2 * f), (int)d, (bf16_t*)m->staging, 0));
+  if (L.panel_rows) {
+    SKV_HIP(launch_to_panels((const bf16_t*)L.wgu, (int)(2 * f), (int)d, L.panel_rows, (bf16_t*)m->staging, 0));
     SKV_HIP(hipMemcpyAsync(L.wgu, m->staging, round_up(2 * f, 256) * d * E, hipMemcpyDeviceToDevice, 0));
   }
   SKV_HIP(hipDeviceSynchronize());
@@ -678,7 +687,7 @@ skv_status run_prefill(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, floa
     EpiResidual er{m->y, d, kBf16 ? 64 : 16};
     EpiSwiGLU<T> esw{yh, f, m->p_mlp};
     if constexpr (kBf16) {
-      SKV_HIP(launch_skinny_bf16((const bf16_t*)ya, d, (const bf16_t*)Ly.wqkv, d, B, dq, d, m->partial,
+      SKV_HIP(launch_skinny_bf16((const bf16_t*)ya, d, (const bf16_t*)Ly.wqkv, B, dq, d, m->partial,
                                  m->partial_elems, eq, s));
     } else if (P == 16) {
       SKV_HIP((launch_gemm_f32<16>((const float*)ya, d, (const float*)Ly.wqkv, d, B, dq, d, eq, s)));
@@ -690,16 +699,16 @@ skv_status run_prefill(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, floa
     SKV_HIP(launch_attn_rows<T>(yq, cs, m->iota, m->last_pos, bt->block_tables, bt->max_blocks_per_seq, B, max_len,
                                 hq, m->attn_ws, yo, s));
     if constexpr (kBf16) {
-      SKV_HIP(launch_skinny_bf16((const bf16_t*)yo, dq, (const bf16_t*)Ly.wo, dq, B, d, dq, m->partial,
+      SKV_HIP(launch_skinny_bf16((const bf16_t*)yo, dq, (const bf16_t*)Ly.wo, B, d, dq, m->partial,
                                  m->partial_elems, er, s));
     } else {
       SKV_HIP((launch_gemm_f32<16>((const float*)yo, dq, (const float*)Ly.wo, dq, B, d, dq, er, s)));
     }
     SKV_HIP(launch_rmsnorm<T>(m->y, nullptr, Ly.ffn_norm, B, d, c.rms_eps, ya, s));
     if constexpr (kBf16) {
-      SKV_HIP(launch_skinny_bf16((const bf16_t*)ya, d, (const bf16_t*)Ly.wgu, d, B, 2 * f, d, m->partial,
+      SKV_HIP(launch_skinny_bf16((const bf16_t*)ya, d, (const bf16_t*)Ly.wgu, B, 2 * f, d, m->partial,
                                  m->partial_elems, esw, s));
-      SKV_HIP(launch_skinny_bf16((const bf16_t*)yh, f, (const bf16_t*)Ly.wdown, f, B, d, f, m->partial,
+      SKV_HIP(launch_skinny_bf16((const bf16_t*)yh, f, (const bf16_t*)Ly.wdown, B, d, f, m->partial,
                                  m->partial_elems, er, s));
     } else {
       SKV_HIP((launch_gemm_f32<16>((const float*)ya, d, (const float*)Ly.wgu, d, B, 2 * f, d, esw, s)));
@@ -709,7 +718,7 @@ skv_status run_prefill(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, floa
   SKV_HIP(launch_rmsnorm<T>(m->y, nullptr, m->final_norm, B, d, c.rms_eps, ya, s));
   EpiStoreF32 el{logits, V, kBf16 ? 64 : 16};
   if constexpr (kBf16)
-    SKV_HIP(launch_skinny_bf16((const bf16_t*)ya, d, (const bf16_t*)m->lm_head, d, B, V, d, m->partial,
+    SKV_HIP(launch_skinny_bf16((const bf16_t*)ya, d, (const bf16_t*)m->lm_head, B, V, d, m->partial,
                                m->partial_elems, el, s));
   else
     SKV_HIP((launch_gemm_f32<16>((const float*)ya, d, (const float*)m->lm_head, d, B, V, d, el, s)));

@@ -97,7 +97,11 @@ constexpr int kBlockSize = 16;
 // block [256 rows][32] contiguous (16 KB).  One k-stage of the GEMM is then
 // one contiguous 16 KB block per operand.  K must be a multiple of 32; the
 // row count is padded to a multiple of 256.
-constexpr int kPanelRows = 256, kPanelCols = 32;
+//
+// The weights of the last-token path use the same layout with 64-row
+// panels (kSkinnyPanelRows): a wave that owns 64 output columns then streams
+// one contiguous run of its panel.
+constexpr int kPanelRows = 256, kPanelCols = 32, kSkinnyPanelRows = 64;
 SKV_DEV int64_t panel_off(int r, int k, int K) {
   return ((int64_t)(r >> 8) * (K >> 5) + (k >> 5)) * (kPanelRows * kPanelCols) + (r & 255) * kPanelCols + (k & 31);
 }

@@ -135,16 +135,17 @@ __global__ __launch_bounds__(256) void rmsnorm_panel_kernel(const float* __restr
   }
 }
 
-// Row-major [rows, K] -> panel layout, eight elements (16 bytes) per thread
-// in destination order; rows beyond `rows` (panel padding) become zero.
-__global__ void to_panels_kernel(const bf16_t* __restrict__ W, int rows, int K, int64_t n8,
+// Row-major [rows, K] -> panel layout with panels of pr rows, eight
+// elements (16 bytes) per thread in destination order; rows beyond `rows`
+// (panel padding) become zero.
+__global__ void to_panels_kernel(const bf16_t* __restrict__ W, int rows, int K, int pr, int64_t n8,
                                  bf16_t* __restrict__ out) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8; i += (int64_t)gridDim.x * blockDim.x) {
     const int64_t e = i * 8;
-    const int64_t blk = e / (kPanelRows * kPanelCols);
-    const int within = (int)(e % (kPanelRows * kPanelCols));
+    const int64_t blk = e / ((int64_t)pr * kPanelCols);
+    const int within = (int)(e % ((int64_t)pr * kPanelCols));
     const int kbs = K / kPanelCols;
-    const int r = (int)(blk / kbs) * kPanelRows + within / kPanelCols;
+    const int r = (int)(blk / kbs) * pr + within / kPanelCols;
     const int k = (int)(blk % kbs) * kPanelCols + within % kPanelCols;
     u32x4_t v = {0u, 0u, 0u, 0u};
     if (r < rows) v = *reinterpret_cast<const u32x4_t*>(W + (int64_t)r * K + k);
@@ -237,12 +238,12 @@ hipError_t launch_rmsnorm_panel(const float* x, const float* gamma, int rows, in
   return hipGetLastError();
 }
 
-hipError_t launch_to_panels(const bf16_t* W, int rows, int K, bf16_t* out, hipStream_t stream) {
+hipError_t launch_to_panels(const bf16_t* W, int rows, int K, int panel_rows, bf16_t* out, hipStream_t stream) {
   if (rows <= 0) return hipSuccess;
-  if (K % kPanelCols) return hipErrorInvalidValue;
-  const int64_t rows_pad = (int64_t)(rows + kPanelRows - 1) / kPanelRows * kPanelRows;
+  if (K % kPanelCols || (panel_rows != kPanelRows && panel_rows != kSkinnyPanelRows)) return hipErrorInvalidValue;
+  const int64_t rows_pad = (int64_t)(rows + panel_rows - 1) / panel_rows * panel_rows;
   const int64_t n8 = rows_pad * K / 8;
-  hipLaunchKernelGGL(to_panels_kernel, dim3(grid_for(n8)), dim3(256), 0, stream, W, rows, K, n8, out);
+  hipLaunchKernelGGL(to_panels_kernel, dim3(grid_for(n8)), dim3(256), 0, stream, W, rows, K, panel_rows, n8, out);
   return hipGetLastError();
 }
 

@@ -25,9 +25,10 @@ hipError_t launch_gemm_f32(const float* A, int lda, const float* B, int ldb, int
 // Skinny bf16 product for the last-token path (M <= 32 rows): split-K MFMA
 // partial sums into `partial` [splits, 32, N] fp32, then a finalize pass
 // that reduces them in fixed order and applies the epilogue (pair distance
-// 64).  Requires K % 256 == 0, N % 128 == 0.
+// 64).  A is row-major [M, lda]; B [N, K] is in the panel layout with
+// 64-row panels.  Requires K % 256 == 0, N % 128 == 0.
 template <class Epi>
-hipError_t launch_skinny_bf16(const bf16_t* A, int lda, const bf16_t* B, int ldb, int M, int N, int K,
+hipError_t launch_skinny_bf16(const bf16_t* A, int lda, const bf16_t* B, int M, int N, int K,
                               float* partial, int64_t partial_elems, const Epi& epi, hipStream_t stream);
 int64_t skinny_partial_elems(int N, int K);
 
@@ -82,8 +83,9 @@ template <typename T>
 hipError_t launch_fold_rows(const T* W, const T* gamma, int rows, int cols, T* out, hipStream_t stream);
 template <typename T>
 hipError_t launch_interleave(const T* gate, const T* up, int f, int d, int P, T* out, hipStream_t stream);
-// Row-major W [rows, K] -> panel layout with rows rounded up to 256 (padding
-// rows zero); K % 32 == 0.
-hipError_t launch_to_panels(const bf16_t* W, int rows, int K, bf16_t* out, hipStream_t stream);
+// Row-major W [rows, K] -> panel layout with panels of panel_rows rows
+// (kPanelRows or kSkinnyPanelRows), rows rounded up to a whole panel
+// (padding rows zero); K % 32 == 0.
+hipError_t launch_to_panels(const bf16_t* W, int rows, int K, int panel_rows, bf16_t* out, hipStream_t stream);
 template <typename T>
 hipError_t launch_to_f32(const T* in, int64_t n, float* out, hipStream_t stream);

@@ -3,6 +3,9 @@
 // kernel is laid out for bandwidth.  Each wave64 owns 64 output columns and
 // one K split; A (activations, tiny and L2 resident) and B (weights) are
 // read 16 bytes per lane straight into v_mfma_f32_16x16x32_bf16 operands.
+// B is stored in 64-row panels of [64][32] blocks, so the wave's 64 columns
+// are one panel and each load instruction (16 rows x 32 k) reads 1 KB of
+// contiguous memory; a wave streams one contiguous run of its panel.
 // Split-K partial sums land in an fp32 buffer [splits, 32, N] and a second
 // pass adds them in fixed split order (deterministic) and applies the
 // epilogue on column pairs (col, col + 64).
@@ -14,8 +17,13 @@ namespace {
 
 constexpr int SK_ROWS = 32;
 
+// U k-steps of 32 per loop trip: all U x 4 weight loads (and the few
+// activation loads) are issued before the MFMAs that consume them, so each
+// wave keeps U x 4 KB of weights in flight.
+constexpr int SK_U = 4;
+
 __global__ __launch_bounds__(256) void skinny_partial_kernel(const bf16_t* __restrict__ A, int lda,
-                                                             const bf16_t* __restrict__ B, int ldb, int M, int N,
+                                                             const bf16_t* __restrict__ B, int K, int M, int N,
                                                              int kc, float* __restrict__ partial) {
   const int lane = threadIdx.x & 63;
   const int cb = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -31,26 +39,38 @@ __global__ __launch_bounds__(256) void skinny_partial_kernel(const bf16_t* __res
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0, 0, 0, 0};
 
+  // panel cb, k-block kbeg/32 onwards: block b at + b * 2048, row r at + r * 32
+  constexpr int kBlk = kSkinnyPanelRows * kPanelCols;
+  const bf16_t* bpanel = B + ((int64_t)cb * (K / kPanelCols) + kbeg / kPanelCols) * kBlk;
   const bf16_t* bp[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) bp[j] = B + (int64_t)(cb * 64 + j * 16 + r16) * ldb + kbeg + kq;
+  for (int j = 0; j < 4; ++j) bp[j] = bpanel + (j * 16 + r16) * kPanelCols + kq;
   const bool a0ok = r16 < M, a1ok = (16 + r16) < M;
   const bf16_t* ap0 = A + (int64_t)r16 * lda + kbeg + kq;
   const bf16_t* ap1 = A + (int64_t)(16 + r16) * lda + kbeg + kq;
 
-  for (int k = 0; k < kc; k += 32) {
-    u32x4_t b[4];
+  for (int k = 0; k < kc; k += 32 * SK_U) {
+    u32x4_t b[SK_U][4], a0[SK_U], a1[SK_U];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) b[j] = *reinterpret_cast<const u32x4_t*>(bp[j] + k);
-    u32x4_t a0 = a0ok ? *reinterpret_cast<const u32x4_t*>(ap0 + k) : u32x4_t{0, 0, 0, 0};
+    for (int u = 0; u < SK_U; ++u)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      acc[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a0), as_bf16x8(b[j]), acc[0][j], 0, 0, 0);
-    if (two) {
-      u32x4_t a1 = a1ok ? *reinterpret_cast<const u32x4_t*>(ap1 + k) : u32x4_t{0, 0, 0, 0};
+      for (int j = 0; j < 4; ++j) b[u][j] = *reinterpret_cast<const u32x4_t*>(bp[j] + (int64_t)(k / 32 + u) * kBlk);
+#pragma unroll
+    for (int u = 0; u < SK_U; ++u) {
+      a0[u] = a0ok ? *reinterpret_cast<const u32x4_t*>(ap0 + k + u * 32) : u32x4_t{0, 0, 0, 0};
+      a1[u] = (two && a1ok) ? *reinterpret_cast<const u32x4_t*>(ap1 + k + u * 32) : u32x4_t{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < SK_U; ++u) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        acc[1][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a1), as_bf16x8(b[j]), acc[1][j], 0, 0, 0);
+        acc[0][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a0[u]), as_bf16x8(b[u][j]), acc[0][j], 0, 0, 0);
+      if (two) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[1][j] =
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a1[u]), as_bf16x8(b[u][j]), acc[1][j], 0, 0, 0);
+      }
     }
   }
   // C layout of 16x16: row 4*(lane/16) + v, column lane % 16
@@ -85,13 +105,15 @@ __global__ void skinny_finalize_kernel(const float* __restrict__ partial, int M,
   epi(row, col, v0, v1);
 }
 
+// K splits (each a multiple of 256 columns): the fewest that still give
+// about 2048 waves (8 per CU), so the fp32 partials stay small next to the
+// weights streamed.
 int choose_splits(int N, int K) {
-  const int units = K / 256;  // splits are multiples of 256 in K
+  const int units = K / 256;
   const int colblocks = N / 64;
-  int target = (4096 + colblocks - 1) / colblocks;
   int best = units;
   for (int s = 1; s <= units; ++s)
-    if (units % s == 0 && s >= target) {
+    if (units % s == 0 && (int64_t)s * colblocks >= 2048) {
       best = s;
       break;
     }
@@ -103,7 +125,7 @@ int choose_splits(int N, int K) {
 int64_t skinny_partial_elems(int N, int K) { return (int64_t)choose_splits(N, K) * SK_ROWS * N; }
 
 template <class Epi>
-hipError_t launch_skinny_bf16(const bf16_t* A, int lda, const bf16_t* B, int ldb, int M, int N, int K,
+hipError_t launch_skinny_bf16(const bf16_t* A, int lda, const bf16_t* B, int M, int N, int K,
                               float* partial, int64_t partial_elems, const Epi& epi, hipStream_t stream) {
   if (M <= 0) return hipSuccess;
   if (M > SK_ROWS || K % 256 != 0 || N % 128 != 0) return hipErrorInvalidValue;
@@ -111,7 +133,7 @@ hipError_t launch_skinny_bf16(const bf16_t* A, int lda, const bf16_t* B, int ldb
   if ((int64_t)ns * SK_ROWS * N > partial_elems) return hipErrorInvalidValue;
   const int kc = K / ns;
   dim3 grid((N / 64 + 3) / 4, ns);
-  hipLaunchKernelGGL(skinny_partial_kernel, grid, dim3(256), 0, stream, A, lda, B, ldb, M, N, kc, partial);
+  hipLaunchKernelGGL(skinny_partial_kernel, grid, dim3(256), 0, stream, A, lda, B, K, M, N, kc, partial);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t work = (int64_t)M * (N / 2);
@@ -120,13 +142,13 @@ hipError_t launch_skinny_bf16(const bf16_t* A, int lda, const bf16_t* B, int ldb
   return hipGetLastError();
 }
 
-template hipError_t launch_skinny_bf16<EpiQKV<bf16_t>>(const bf16_t*, int, const bf16_t*, int, int, int, int, float*,
+template hipError_t launch_skinny_bf16<EpiQKV<bf16_t>>(const bf16_t*, int, const bf16_t*, int, int, int, float*,
                                                        int64_t, const EpiQKV<bf16_t>&, hipStream_t);
-template hipError_t launch_skinny_bf16<EpiResidual>(const bf16_t*, int, const bf16_t*, int, int, int, int, float*,
+template hipError_t launch_skinny_bf16<EpiResidual>(const bf16_t*, int, const bf16_t*, int, int, int, float*,
                                                     int64_t, const EpiResidual&, hipStream_t);
-template hipError_t launch_skinny_bf16<EpiSwiGLU<bf16_t>>(const bf16_t*, int, const bf16_t*, int, int, int, int,
+template hipError_t launch_skinny_bf16<EpiSwiGLU<bf16_t>>(const bf16_t*, int, const bf16_t*, int, int, int,
                                                           float*, int64_t, const EpiSwiGLU<bf16_t>&, hipStream_t);
-template hipError_t launch_skinny_bf16<EpiStoreF32>(const bf16_t*, int, const bf16_t*, int, int, int, int, float*,
+template hipError_t launch_skinny_bf16<EpiStoreF32>(const bf16_t*, int, const bf16_t*, int, int, int, float*,
                                                     int64_t, const EpiStoreF32&, hipStream_t);
-template hipError_t launch_skinny_bf16<EpiStore<bf16_t>>(const bf16_t*, int, const bf16_t*, int, int, int, int,
+template hipError_t launch_skinny_bf16<EpiStore<bf16_t>>(const bf16_t*, int, const bf16_t*, int, int, int,
                                                          float*, int64_t, const EpiStore<bf16_t>&, hipStream_t);
