@@ -169,44 +169,58 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
     }
 
-    // online softmax per query column
+    // Online softmax per query column.  Scores stay raw; the scale c =
+    // log2(e)/sqrt(dh) enters the exponent, p = 2^(c*s - m).  The running
+    // offset m only moves when a column's tile maximum exceeds it by more
+    // than kLazy (then every column of the wave rescales); otherwise p <=
+    // 2^kLazy, which fp32 sums and bf16 probabilities hold exactly as well.
+    // softmax(s) does not depend on the offset, so this is the same
+    // function; it saves the rescale of the output accumulators on most
+    // tiles.  Masking (causal diagonal, prompt end) only on the tiles that
+    // need it.
+    constexpr float kLazy = 8.0f;
     bf16x8_t pf[QT][4];
 #pragma unroll
     for (int s = 0; s < QT; ++s) {
       const int qi = q0 + s * 32 + (lane & 31);
       const bool need_mask = (k0 + FA_KT - 1 > q0 + s * 32) || (k0 + FA_KT > N);
-      float mt = -INFINITY;
+      if (need_mask) {
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int key = k0 + st * 32 + 8 * (v >> 2) + 4 * hh + (v & 3);
+            if (key > qi || key >= N) sacc[s][st][v] = -INFINITY;
+          }
+      }
+      float mt = sacc[s][0][0];
 #pragma unroll
       for (int st = 0; st < 2; ++st)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          float x = sacc[s][st][v] * scale_log2;
-          if (need_mask) {
-            int key = k0 + st * 32 + 8 * (v >> 2) + 4 * hh + (v & 3);
-            if (key > qi || key >= N) x = -INFINITY;
-          }
-          sacc[s][st][v] = x;
-          mt = fmaxf(mt, x);
-        }
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-      const float m_new = fmaxf(m_run[s], mt);
-      const float alpha = exp2f(m_run[s] - m_new);
-      m_run[s] = m_new;
+        for (int v = 0; v < 16; ++v) mt = fmaxf(mt, sacc[s][st][v]);
+      mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * scale_log2;
+      if (__builtin_amdgcn_ballot_w64(mt > m_run[s] + kLazy) != 0) {
+        const float m_new = fmaxf(m_run[s], mt);
+        const float alpha = __builtin_amdgcn_exp2f(m_run[s] - m_new);
+        m_run[s] = m_new;
+        l_run[s] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) oacc[s][dt][v] *= alpha;
+      }
+      const float mneg = -m_run[s];
       float ls = 0.f;
 #pragma unroll
       for (int st = 0; st < 2; ++st)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          float p = exp2f(sacc[s][st][v] - m_new);
+          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[s][st][v], scale_log2, mneg));
           sacc[s][st][v] = p;
           ls += p;
         }
       ls += __shfl_xor(ls, 32, 64);
-      l_run[s] = l_run[s] * alpha + ls;
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) oacc[s][dt][v] *= alpha;
+      l_run[s] += ls;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         const int st = kk >> 1, vb = 8 * (kk & 1);

@@ -69,6 +69,16 @@ def test_llama8b_l24_acrosskv4_b32_sampled():
     _check_sampled(w, batch, [17])
 
 
+def test_small_model_long_context():
+    """Attention over long prompts against the full oracle: a 3-layer model (d=512, 8/2 heads of 128, l=2) on an
+    8192-token and a 3000-token prompt; every KV slot and both logits rows (the last token attends over all keys of
+    the skipped layer)."""
+    w = si.small_workload("long8k", n_layers=3, d_model=512, n_q_heads=8, n_kv_heads=2, head_dim=128, ffn_dim=512,
+                          vocab=1024, l=2, g=1, lengths=(8192, 3000), seed=31, weight_seed=131)
+    batch = si.make_batch(w)
+    _check_sampled(w, batch, [0, 1])
+
+
 def test_midsize_split_tail_gemms():
     """d_model 4096 over 5000 tokens: the O, gate/up and down GEMMs have 320 tiles on 256 CUs, so their
     last wave runs as K-split partial tiles plus the fixed-order reduction."""
