@@ -1,9 +1,9 @@
 // Attention kernels.
 //
-// 1. attn_prefill_kernel (bf16, MFMA): causal GQA flash attention of the
+// 1. attn_prefill8_kernel (bf16, MFMA): causal GQA flash attention of the
 //    prompt tokens of layers 1..l, reading K/V from the paged cache.
-//    A workgroup = 4 wave64s = 4 query heads of one kv-head group, for
-//    32*QT consecutive query positions of one prompt.  Per 64-key tile:
+//    A workgroup = 8 wave64s = 4 query heads of one kv-head group x two
+//    32-query blocks of one prompt (64 queries).  Per 64-key tile:
 //      S^T (keys x queries) = K Q^T   with A = K from LDS, B = Q^T from
 //                                     registers (v_mfma_f32_32x32x16_bf16);
 //      each lane then owns one query column, so the online-softmax max and
@@ -19,14 +19,12 @@
 //    ([64 keys][128 dims], 16-byte chunk c of key row r at c ^ (r & 15)).
 //    O^T is transposed through LDS at the end and written 8 bytes per lane
 //    into the panel layout of the O projection's A operand.
-//    K/V tiles move global -> LDS directly (global_load_lds_dwordx4) into a
-//    two-stage ring, the next tile's loads in flight while the current one
-//    is computed; the prompt's block ids are staged in LDS so no load waits
-//    on a block-table read.  Keys past the prompt (or causally masked) get
+//    K/V tiles move global -> LDS directly (global_load_lds_dwordx4) into
+//    two-stage rings (64 KB); the block ids of the next tiles are fetched
+//    one iteration ahead.  Keys past the prompt (or causally masked) get
 //    probability exactly 0, so the cache contents loaded for them only need
 //    to be finite, which the cache guarantees (zero-filled at creation,
-//    written only with results).  Two workgroups fit per CU (<= 256 VGPRs,
-//    66 KB LDS).
+//    written only with results).  One workgroup per CU (256 VGPRs per wave).
 //
 // 2. attn_rows_kernel + attn_combine_kernel (fp32 or bf16, vector ALU):
 //    attention of an explicit list of query rows (the last prompt token of
@@ -45,7 +43,6 @@ typedef s16x4_t short4_lds_t;
 constexpr int FA_DH = 128;
 constexpr int FA_KT = 64;  // keys per tile
 
-constexpr int FA_BTW = 32;  // block-table entries staged in LDS at a time (8 key tiles)
 
 SKV_DEV void wait_loads_then_barrier() {
   __builtin_amdgcn_sched_barrier(0);
@@ -53,195 +50,166 @@ SKV_DEV void wait_loads_then_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int QT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_prefill_kernel(
+// Prefill attention: one workgroup = the 4 q heads of one kv group x 64
+// queries (two 32-query blocks, 8 waves, two per SIMD), so every K/V tile is
+// loaded once for 8 waves.  K and V move through two-stage rings; within a
+// wave the score MFMAs of tile t+1 are issued before the softmax of tile t,
+// so the vector ALU work of one tile overlaps the matrix-core work of the
+// next.
+SKV_DEV void f8_qk(const bf16_t* sk, const bf16x8_t* qf, int lane, f32x16_t* sacc) {
+  const int hh = lane >> 5;
+  sacc[0] = sacc[1] = f32x16_t{0};
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    const int ch = ks * 2 + hh;
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const int key = st * 32 + (lane & 31);
+      bf16x8_t kf = as_bf16x8(*reinterpret_cast<const u32x4_t*>(sk + key * FA_DH + ((ch ^ (key & 15)) << 3)));
+      sacc[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc[st], 0, 0, 0);
+    }
+  }
+}
+
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_prefill8_kernel(
     const bf16_t* __restrict__ q, CacheSlot<bf16_t> cache, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ bt, int max_blocks, int hq, int rep, float scale_log2, bf16_t* __restrict__ o) {
-  // double-buffered K and V tiles, [64 keys][128 dims] each, filled by
-  // direct global -> LDS loads
-  __shared__ __attribute__((aligned(1024))) bf16_t sK[2][FA_KT * FA_DH];
-  __shared__ __attribute__((aligned(1024))) bf16_t sV[2][FA_KT * FA_DH];
-  __shared__ int32_t sBT[FA_BTW];
+  // buffers 0, 1: K ring; 2, 3: V ring ([64 keys][128 dims] each); the
+  // whole 64 KB stages the output at the end
+  __shared__ __attribute__((aligned(1024))) bf16_t smem[4][FA_KT * FA_DH];
 
   const int b = blockIdx.y;
   const int tok0 = cu[b];
   const int N = cu[b + 1] - tok0;
-  const int QB = 32 * QT;
-  const int nqb = (N + QB - 1) / QB;
+  const int nqb = (N + 63) / 64;
   const int qb = gridDim.x - 1 - blockIdx.x;  // longest rows first
   if (qb >= nqb) return;
-  const int q0 = qb * QB;
+  const int q0w = qb * 64;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hh = lane >> 5;
-  const int h = blockIdx.z * 4 + wave;
+  const int h = blockIdx.z * 4 + (wave & 3);
+  const int q0 = q0w + (wave >> 2) * 32;  // this wave's 32 queries
   const int g = (blockIdx.z * 4) / rep;
   const int hkv = cache.hkv;
   const int dq = hq * FA_DH;
 
-  const int kend = min(N, q0 + QB);
+  const int kend = min(N, q0w + 64);
   const int ntiles = (kend + FA_KT - 1) / FA_KT;
   const int nblk_need = (kend + kBlockSize - 1) / kBlockSize;
   const int32_t* btb = bt + (int64_t)b * max_blocks;
 
-  // Block ids of tiles t0 .. t0+7.  Entries past the keys this workgroup
-  // needs (causally masked or beyond the prompt) repeat block 0, a valid
-  // block of the prompt, so every load stays inside the cache.
-  auto stage_block_ids = [&](int t0) {
-    if (tid < FA_BTW) {
-      const int i = tid;
-      const int bi = t0 * (FA_KT / kBlockSize) + i;
-      sBT[i] = btb[bi < nblk_need ? bi : 0];
-    }
-  };
-  stage_block_ids(0);
-
-  // Q^T fragments: lane holds query (lane & 31), dims ks*16 + hh*8 .. +8
-  bf16x8_t qf[QT][8];
-#pragma unroll
-  for (int s = 0; s < QT; ++s) {
-    int qi = min(q0 + s * 32 + (lane & 31), N - 1);
+  bf16x8_t qf[8];
+  {
+    const int qi = min(q0 + (lane & 31), N - 1);
     const bf16_t* qp = q + (int64_t)(tok0 + qi) * dq + h * FA_DH + hh * 8;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) qf[s][ks] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(qp + ks * 16));
+    for (int ks = 0; ks < 8; ++ks) qf[ks] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(qp + ks * 16));
   }
 
-  f32x16_t oacc[QT][4];
-  float m_run[QT], l_run[QT];
+  // Tile loads: wave w moves 16-key block r = w/2, key rows (w%2)*8 .. +8
+  // of it, for K and for V (two 1 KB instructions each).  Lane l's 16 bytes
+  // land at tile row (instruction base + l/16), physical chunk l%16, so it
+  // fetches logical chunk (l%16) ^ (row & 15).  Entries past the keys this
+  // workgroup needs read block 0, a valid block of the prompt.
+  const int r_blk = wave >> 1;
+  int src_off[2];
 #pragma unroll
-  for (int s = 0; s < QT; ++s) {
-    m_run[s] = -INFINITY;
-    l_run[s] = 0.f;
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) oacc[s][dt] = f32x16_t{0};
+  for (int i = 0; i < 2; ++i) {
+    const int lrow = (wave & 1) * 8 + i * 4 + (lane >> 4);  // key row within the 16-key block
+    src_off[i] = lrow * FA_DH + (((lane & 15) ^ lrow) << 3);
   }
-  __syncthreads();
-
-  // Tile loads: per 16-key block r of the tile, wave w moves key rows
-  // w*4 .. w*4+3 of K and of V (1 KB each, one instruction).  Lane l's 16
-  // bytes land at LDS row w*4 + l/16, physical chunk l%16, so it fetches the
-  // logical chunk (l%16) ^ (row & 15): the XOR swizzle of the tile layout.
-  const int lrow = wave * 4 + (lane >> 4);
-  const int lane_off = lrow * FA_DH + (((lane & 15) ^ lrow) << 3);
-  auto issue_tile = [&](int t, int buf) {
-    const int wb = (t * (FA_KT / kBlockSize)) % FA_BTW;
+  auto block_of = [&](int t) {
+    const int bi = t * (FA_KT / kBlockSize) + r_blk;
+    return btb[bi < nblk_need ? bi : 0];
+  };
+  auto issue = [&](const bf16_t* base_ptr, int blk, int buf) {
+    const bf16_t* src = base_ptr + ((int64_t)blk * hkv + g) * (kBlockSize * FA_DH);
+    typedef __attribute__((address_space(3))) void* lds_ptr;
 #pragma unroll
-    for (int r = 0; r < FA_KT / kBlockSize; ++r) {
-      const int64_t base = ((int64_t)sBT[wb + r] * hkv + g) * (kBlockSize * FA_DH) + lane_off;
-      typedef __attribute__((address_space(3))) void* lds_ptr;
-      __builtin_amdgcn_global_load_lds(cache.k + base, (lds_ptr)(&sK[buf][(r * 16 + wave * 4) * FA_DH]), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(cache.v + base, (lds_ptr)(&sV[buf][(r * 16 + wave * 4) * FA_DH]), 16, 0, 0);
+    for (int i = 0; i < 2; ++i) {
+      const bf16_t* sp = src + src_off[i];
+      __builtin_amdgcn_global_load_lds(sp, (lds_ptr)(&smem[buf][(r_blk * 16 + (wave & 1) * 8 + i * 4) * FA_DH]), 16, 0,
+                                       0);
     }
   };
 
-  issue_tile(0, 0);
-  wait_loads_then_barrier();
+  f32x16_t oacc[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) oacc[dt] = f32x16_t{0};
+  float m_run = -INFINITY, l_run = 0.f;
+  constexpr float kLazy = 8.0f;
 
-  for (int kt = 0; kt < ntiles; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < ntiles) {
-      if ((kt + 1) % (FA_BTW / (FA_KT / kBlockSize)) == 0) {  // next window of block ids
-        stage_block_ids(kt + 1);
-        __syncthreads();
-      }
-      issue_tile(kt + 1, cur ^ 1);
-    }
-    const int k0 = kt * FA_KT;
-    const bf16_t* sk = sK[cur];
-    const bf16_t* sv = sV[cur];
-
-    // S^T = K Q^T, two 32-key subtiles
-    f32x16_t sacc[QT][2];
-#pragma unroll
-    for (int s = 0; s < QT; ++s) sacc[s][0] = sacc[s][1] = f32x16_t{0};
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      const int key = st * 32 + (lane & 31);
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const int ch = ks * 2 + hh;
-        bf16x8_t kf = as_bf16x8(*reinterpret_cast<const u32x4_t*>(sk + key * FA_DH + ((ch ^ (key & 15)) << 3)));
-#pragma unroll
-        for (int s = 0; s < QT; ++s)
-          sacc[s][st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s][ks], sacc[s][st], 0, 0, 0);
-      }
-    }
-
-    // Online softmax per query column.  Scores stay raw; the scale c =
-    // log2(e)/sqrt(dh) enters the exponent, p = 2^(c*s - m).  The running
-    // offset m only moves when a column's tile maximum exceeds it by more
-    // than kLazy (then every column of the wave rescales); otherwise p <=
-    // 2^kLazy, which fp32 sums and bf16 probabilities hold exactly as well.
-    // softmax(s) does not depend on the offset, so this is the same
-    // function; it saves the rescale of the output accumulators on most
-    // tiles.  Masking (causal diagonal, prompt end) only on the tiles that
-    // need it.
-    constexpr float kLazy = 8.0f;
-    bf16x8_t pf[QT][4];
-#pragma unroll
-    for (int s = 0; s < QT; ++s) {
-      const int qi = q0 + s * 32 + (lane & 31);
-      const bool need_mask = (k0 + FA_KT - 1 > q0 + s * 32) || (k0 + FA_KT > N);
-      if (need_mask) {
-#pragma unroll
-        for (int st = 0; st < 2; ++st)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int key = k0 + st * 32 + 8 * (v >> 2) + 4 * hh + (v & 3);
-            if (key > qi || key >= N) sacc[s][st][v] = -INFINITY;
-          }
-      }
-      float mt = sacc[s][0][0];
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) mt = fmaxf(mt, sacc[s][st][v]);
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * scale_log2;
-      if (__builtin_amdgcn_ballot_w64(mt > m_run[s] + kLazy) != 0) {
-        const float m_new = fmaxf(m_run[s], mt);
-        const float alpha = __builtin_amdgcn_exp2f(m_run[s] - m_new);
-        m_run[s] = m_new;
-        l_run[s] *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) oacc[s][dt][v] *= alpha;
-      }
-      const float mneg = -m_run[s];
-      float ls = 0.f;
+  // Softmax of tile t in two parts.  Scores stay raw; the scale c =
+  // log2(e)/sqrt(dh) enters the exponent, p = 2^(c*s - m).  The running
+  // offset m only moves when a column's tile maximum exceeds it by more than
+  // kLazy (then every column of the wave rescales); otherwise p <= 2^kLazy,
+  // which fp32 sums and bf16 probabilities hold exactly as well.
+  // softmax(s) does not depend on the offset, so this is the same function;
+  // it saves the rescale of the output accumulators on most tiles.
+  // soft_prep masks (diagonal / prompt-end tiles only), takes the column
+  // maxima and moves the offset if needed; exp_pv turns the scores into bf16
+  // probabilities and accumulates O^T += V^T P^T from V buffer vb.  Only
+  // soft_prep branches, so exp_pv and the next tile's score MFMAs form one
+  // straight block the scheduler can interleave.
+  auto soft_prep = [&](int t, f32x16_t* sacc) {
+    const int k0 = t * FA_KT;
+    const int qi = q0 + (lane & 31);
+    if ((k0 + FA_KT - 1 > q0) || (k0 + FA_KT > N)) {
 #pragma unroll
       for (int st = 0; st < 2; ++st)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[s][st][v], scale_log2, mneg));
-          sacc[s][st][v] = p;
-          ls += p;
+          const int key = k0 + st * 32 + 8 * (v >> 2) + 4 * hh + (v & 3);
+          if (key > qi || key >= N) sacc[st][v] = -INFINITY;
         }
-      ls += __shfl_xor(ls, 32, 64);
-      l_run[s] += ls;
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int st = kk >> 1, vb = 8 * (kk & 1);
-        u32x4_t w;
-        w.x = pack_bf16x2(sacc[s][st][vb + 0], sacc[s][st][vb + 1]);
-        w.y = pack_bf16x2(sacc[s][st][vb + 2], sacc[s][st][vb + 3]);
-        w.z = pack_bf16x2(sacc[s][st][vb + 4], sacc[s][st][vb + 5]);
-        w.w = pack_bf16x2(sacc[s][st][vb + 6], sacc[s][st][vb + 7]);
-        pf[s][kk] = as_bf16x8(w);
-      }
     }
-
-    // O^T += V^T P^T.  Transposing reads: lane l = 16 grp + 4 a + b points
-    // at key kk*16 + 4*(l/32) + a (and +8), dims dbase + 4b .. +3, and
-    // receives keys kk*16 + 4*(l/32) + 0..3 (and +8) of dim dbase + l%16.
+    float mt = sacc[0][0];
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) mt = fmaxf(mt, sacc[st][v]);
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * scale_log2;
+    if (__builtin_amdgcn_ballot_w64(mt > m_run + kLazy) != 0) {
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) oacc[dt][v] *= alpha;
+    }
+  };
+  auto exp_pv = [&](const f32x16_t* sacc, int vb) {
+    const float mneg = -m_run;
+    float ls = 0.f;
+    bf16x8_t pf[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int st = kk >> 1, vb8 = 8 * (kk & 1);
+      float p[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        p[e] = __builtin_amdgcn_exp2f(fmaf(sacc[st][vb8 + e], scale_log2, mneg));
+        ls += p[e];
+      }
+      pf[kk] = as_bf16x8(u32x4_t{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                                 pack_bf16x2(p[6], p[7])});
+    }
+    ls += __shfl_xor(ls, 32, 64);
+    l_run += ls;
+    const bf16_t* sv = smem[2 + vb];
     const int tj = lane & 15, ta = tj >> 2, tb = tj & 3;
+    // key steps outer, dims inner: consecutive MFMAs feed four independent
+    // accumulators
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-      const int d = dt * 32 + 16 * ((lane >> 4) & 1) + 4 * tb;
+    for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
+      for (int dt = 0; dt < 4; ++dt) {
+        const int d = dt * 32 + 16 * ((lane >> 4) & 1) + 4 * tb;
         const int k1 = kk * 16 + 4 * hh + ta, k2 = k1 + 8;
         typedef __attribute__((address_space(3))) short4_lds_t* lds_s4p;
         s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -250,44 +218,87 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             (lds_s4p)(sv + k2 * FA_DH + (((d >> 3) ^ (k2 & 15)) << 3) + (d & 7)));
         u32x2_t lo2 = __builtin_bit_cast(u32x2_t, lo), hi2 = __builtin_bit_cast(u32x2_t, hi);
         bf16x8_t vf = as_bf16x8(u32x4_t{lo2.x, lo2.y, hi2.x, hi2.y});
-#pragma unroll
-        for (int s = 0; s < QT; ++s)
-          oacc[s][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[s][kk], oacc[s][dt], 0, 0, 0);
+        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kk], oacc[dt], 0, 0, 0);
       }
     }
+  };
 
+  // Pipeline.  Iteration t < ntiles - 1: loads of K(t+2) (into the buffer
+  // K(t) used) and V(t+1) (into V(t-1)'s) go out; the scores of tile t+1
+  // are computed from K(t+1) (landed at the end of iteration t-1) while the
+  // softmax and P.V of tile t run; then every wave waits for its loads and
+  // the workgroup synchronises.  Loads for tiles past the end read block 0
+  // of the prompt (in bounds, unused), so they need no branch.  The last
+  // tile only runs its softmax and P.V.  Stage parity is unrolled so the two
+  // score accumulators stay in registers.
+  // blk1 / blk2: block ids of tiles t+1 / t+2, fetched one iteration ahead
+  // so no load waits on a block-table read
+  int blk1 = block_of(1), blk2 = block_of(2);
+  issue(cache.k, block_of(0), 0);
+  issue(cache.v, block_of(0), 2);
+  issue(cache.k, blk1, 1);
+  wait_loads_then_barrier();
+  f32x16_t sa[2], sb[2];
+  f8_qk(smem[0], qf, lane, sa);
+  wait_loads_then_barrier();  // every wave has read K(0) before its buffer takes K(2)
+  auto full = [&](int t, f32x16_t* cur, f32x16_t* nxt) {
+    const int blk3 = block_of(t + 3);
+    issue(cache.k, blk2, t & 1);
+    issue(cache.v, blk1, 2 + ((t + 1) & 1));
+    soft_prep(t, cur);
+    f8_qk(smem[(t + 1) & 1], qf, lane, nxt);
+    exp_pv(cur, t & 1);
     wait_loads_then_barrier();
+    blk1 = blk2;
+    blk2 = blk3;
+  };
+  auto last = [&](int t, f32x16_t* cur) {
+    soft_prep(t, cur);
+    exp_pv(cur, t & 1);
+  };
+  const int n1 = ntiles - 1;  // iterations that also compute the next tile's scores
+  int t = 0;
+  for (; t + 1 < n1; t += 2) {
+    full(t, sa, sb);
+    full(t + 1, sb, sa);
   }
+  if (t < n1) {
+    full(t, sa, sb);
+    last(t + 1, sb);
+  } else {
+    last(t, sa);
+  }
+  wait_loads_then_barrier();  // all P.V reads done before the buffers stage the output
 
   // normalise and write: O^T -> LDS [32 q][128 d] per wave (8-byte quads
   // swizzled by q) -> panel rows (a row's 128 dims are four 64-byte runs)
-  bf16_t* so = &sK[0][0] + wave * (32 * FA_DH);
-#pragma unroll
-  for (int s = 0; s < QT; ++s) {
-    const float inv = 1.0f / l_run[s];
+  bf16_t* so = &smem[0][0] + wave * (32 * FA_DH);
+  {
+    const float inv = 1.0f / l_run;
     const int ql = lane & 31;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
       for (int vq = 0; vq < 4; ++vq) {
-        const int u = dt * 8 + vq * 2 + hh;  // quad of dims dt*32 + 8*vq + 4*hh .. +3
+        const int u = dt * 8 + vq * 2 + hh;
         u32x2_t w;
-        w.x = pack_bf16x2(oacc[s][dt][vq * 4 + 0] * inv, oacc[s][dt][vq * 4 + 1] * inv);
-        w.y = pack_bf16x2(oacc[s][dt][vq * 4 + 2] * inv, oacc[s][dt][vq * 4 + 3] * inv);
+        w.x = pack_bf16x2(oacc[dt][vq * 4 + 0] * inv, oacc[dt][vq * 4 + 1] * inv);
+        w.y = pack_bf16x2(oacc[dt][vq * 4 + 2] * inv, oacc[dt][vq * 4 + 3] * inv);
         *reinterpret_cast<u32x2_t*>(so + ql * FA_DH + ((u ^ ql) << 2)) = w;
       }
-    __syncthreads();
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int it = 0; it < 16; ++it) {
-      const int idx = it * 64 + lane;
-      const int ql2 = idx >> 5, u = idx & 31;
-      const int qi = q0 + s * 32 + ql2;
-      if (qi < N) {
-        u32x2_t w = *reinterpret_cast<const u32x2_t*>(so + ql2 * FA_DH + ((u ^ ql2) << 2));
-        *reinterpret_cast<u32x2_t*>(o + panel_off(tok0 + qi, h * FA_DH + u * 4, dq)) = w;
-      }
+  for (int it = 0; it < 16; ++it) {
+    const int idx = it * 64 + lane;
+    const int ql2 = idx >> 5, u = idx & 31;
+    const int qi = q0 + ql2;
+    if (qi < N) {
+      u32x2_t w = *reinterpret_cast<const u32x2_t*>(so + ql2 * FA_DH + ((u ^ ql2) << 2));
+      *reinterpret_cast<u32x2_t*>(o + panel_off(tok0 + qi, h * FA_DH + u * 4, dq)) = w;
     }
-    __syncthreads();
   }
 }
 
@@ -483,11 +494,10 @@ hipError_t launch_attn_prefill_bf16(const bf16_t* q, CacheSlot<bf16_t> cache, co
                                     const int32_t* block_tables, int max_blocks, int batch, int max_seqlen, int hq,
                                     bf16_t* o, hipStream_t stream) {
   if (batch <= 0 || max_seqlen <= 0) return hipSuccess;
-  constexpr int QT = 1;
   const int rep = hq / cache.hkv;
-  dim3 grid((max_seqlen + 32 * QT - 1) / (32 * QT), batch, hq / 4);
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)FA_DH);
-  hipLaunchKernelGGL(attn_prefill_kernel<QT>, grid, dim3(256), 0, stream, q, cache, cu_seqlens, block_tables,
+  dim3 grid((max_seqlen + 63) / 64, batch, hq / 4);
+  hipLaunchKernelGGL(attn_prefill8_kernel, grid, dim3(512), 0, stream, q, cache, cu_seqlens, block_tables,
                      max_blocks, hq, rep, scale_log2, o);
   return hipGetLastError();
 }
