@@ -8,7 +8,10 @@ path: layers 1..l for all prompt tokens, the fused skipped-layer KV GEMM,
 the last-token path through layers l+1..L and the LM head), inputs and
 weights already resident in HBM.  Prints one JSON line.  The same batch is
 then also timed through the unmodified model (l = L, same kernels), so the
-line carries the SwiftKV / full-depth wall-clock ratio next to the FLOP ratio.
+line carries the SwiftKV / full-depth wall-clock ratio next to the FLOP ratio,
+and (bf16) through skv_step: one decode token per prompt after its prefill
+(weight-streaming, HBM-bound) and the same prompts prefilled in chunks of 256
+tokens per prompt per call.
 """
 from __future__ import annotations
 
@@ -87,6 +90,48 @@ def copy_calibration(mib: int):
                                            "bytes_written_per_launch": n * 4}}), flush=True)
 
 
+def decode_tables(batch, extra: int):
+    """Block tables of the batch with `extra` fresh blocks appended to every prompt's row (ids after the
+    prefill's), so decode tokens after the prompts have room."""
+    B = len(batch.lengths)
+    bs = batch.block_size
+    width = max(-(-int(n) // bs) for n in batch.lengths) + extra
+    bt = np.full((B, width), -1, dtype=np.int32)
+    for b, n in enumerate(batch.lengths):
+        nb = -(-int(n) // bs)
+        bt[b, :nb] = batch.block_tables[b, :nb]
+        bt[b, nb:nb + extra] = batch.num_blocks + b * extra + np.arange(extra)
+    return bt
+
+
+def decode_bytes(cfg, ctx_lens) -> float:
+    """Algorithmic HBM bytes of one SwiftKV decode step (bf16): every weight read once (layers 1..l with their
+    K/V rows, layers l+1..L with Q only, the folded skipped-layer K/V rows, the LM head) plus every cached K/V
+    row the new tokens attend to."""
+    d, dh, hq, hkv, f, V = cfg.d_model, cfg.head_dim, cfg.n_q_heads, cfg.n_kv_heads, cfg.ffn_dim, cfg.vocab
+    L, l, g = cfg.n_layers, cfg.swiftkv_l, cfg.acrosskv_g
+    dq, dkv = hq * dh, hkv * dh
+    G = -(-(L - l) // g)
+    w = l * d * (dq + 2 * dkv) + (L - l) * d * dq + G * 2 * dkv * d + L * (dq * d + 3 * d * f) + V * d
+    kv = L * sum(int(c) + 1 for c in ctx_lens) * 2 * dkv
+    return 2.0 * (w + kv)
+
+
+def time_calls(fn, steps, warmup, stream):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -96,6 +141,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-full-depth", action="store_true",
                     help="skip timing the same batch through all layers (l = L) with the same kernels")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip timing a decode step and a chunked prefill over the same prompts")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 3 fp32 device copies of MIB MiB each (reference for FETCH_SIZE/WRITE_SIZE)")
     args = ap.parse_args()
@@ -118,9 +165,11 @@ def main():
     log(f"[bench] workload {w.name}: {B} prompts, {T} tokens, lengths {list(batch.lengths)}")
     cached = CachedLayers() if not args.no_cpu_baseline else None
     t0 = time.time()
-    model = runner.load_seeded_model(w, T, B, batch.max_seqlen, layer_hook=cached.hook if cached else None)
+    extra = 4  # blocks per prompt beyond its prefill, for the decode measurement
+    model = runner.load_seeded_model(w, T, B, batch.max_seqlen + extra * batch.block_size,
+                                     layer_hook=cached.hook if cached else None)
     log(f"[bench] weights generated and loaded in {time.time() - t0:.1f} s")
-    cache = runner.Cache(model, batch.num_blocks)
+    cache = runner.Cache(model, batch.num_blocks + B * extra)
     db = runner.device_batch(batch)
     logits = torch.empty((B, w.shape.vocab), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
@@ -188,6 +237,40 @@ def main():
                      "avg_launch_ms": round(avg_launch_ms, 4), "launches": prof["launches"],
                      "flops_per_launch": flops_per_launch},
     }
+    if not args.no_decode and w.dtype == "bf16":
+        # one decode token per prompt right after its prefill (positions N_b, context N_b + 1), the same step
+        # repeated; then the same prompts prefilled as chunks of at most 256 tokens per prompt per call
+        runner.prefill(model, cache, db, logits, stream)
+        dbt = decode_tables(batch, extra)
+        nxt = si.randint(w.input_seed, 7, B, w.shape.vocab)
+        ds = runner.device_step(nxt, [1] * B, batch.lengths, dbt)
+        ms_dec = time_calls(lambda: runner.step(model, cache, ds, logits, stream), args.steps, args.warmup, stream)
+        by = decode_bytes(model.cfg, batch.lengths)
+        log(f"[bench] decode step ({B} tokens): {ms_dec:.3f} ms")
+        res["decode_step"] = {
+            "tokens": B, "context_tokens": int(sum(batch.lengths)) + B, "ms_per_step": round(ms_dec, 4),
+            "tokens_per_s": round(B / (ms_dec / 1e3), 1), "bound": "hbm",
+            "algorithmic_bytes": by, "achieved_GBs": round(by / (ms_dec / 1e3) / 1e9, 1),
+            "peak_GBs": MI355X_HBM_GBS, "frac": round(by / (ms_dec / 1e3) / 1e9 / MI355X_HBM_GBS, 4)}
+        chunk = 256
+        calls, ctx = [], np.zeros(B, dtype=np.int64)
+        while (ctx < batch.lengths).any():
+            live = [b for b in range(B) if ctx[b] < batch.lengths[b]]
+            ns = [int(min(chunk, batch.lengths[b] - ctx[b])) for b in live]
+            toks = np.concatenate([batch.tokens[b][ctx[b]:ctx[b] + n] for b, n in zip(live, ns)])
+            calls.append((runner.device_step(toks, ns, ctx[live], batch.block_tables[live]), len(live)))
+            ctx[live] += ns
+        lgc = [torch.empty((nl, w.shape.vocab), dtype=torch.float32, device="cuda") for _, nl in calls]
+
+        def chunked():
+            for (dsc, _), lg in zip(calls, lgc):
+                runner.step(model, cache, dsc, lg, stream)
+        ms_ch = time_calls(chunked, args.steps, args.warmup, stream)
+        log(f"[bench] chunked prefill ({len(calls)} calls of <= {chunk} tokens per prompt): {ms_ch:.3f} ms")
+        res["chunked_prefill"] = {
+            "chunk_tokens_per_prompt": chunk, "calls": len(calls), "ms_per_prefill": round(ms_ch, 4),
+            "tokens_per_s": round(T / (ms_ch / 1e3), 1), "time_vs_one_shot": round(ms_ch / ms, 4),
+            "actual_tflops": round(swift / (ms_ch / 1e3) / 1e12, 2)}
     if not args.no_full_depth and w.swiftkv_l < w.shape.n_layers:
         # the unmodified model (every layer for every prompt token), same weights, batch and kernels: the
         # wall-clock ratio to compare with the FLOP ratio

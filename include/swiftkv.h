@@ -167,6 +167,40 @@ typedef struct {
  * outside [0, num_blocks) or too few blocks; HIP on launch failure. */
 skv_status skv_prefill(skv_model* m, skv_kv_cache* c, const skv_batch* batch, float* logits, void* stream);
 
+/* A batch of sequences that may already hold cached positions: sequence b
+ * has ctx_lens[b] positions in the cache (written by earlier calls with the
+ * same block-table entries) and brings the new tokens
+ * tokens.cu_seqlens[b]..[b+1], at positions ctx_lens[b] onwards.  Its block
+ * table must cover ctx_lens[b] + (new tokens) positions.  tokens.max_seqlen
+ * bounds the new tokens of one sequence; ctx_lens[b] + new tokens must not
+ * exceed the model's max_seqlen.  Both ctx arrays NULL = no cached
+ * positions (the call is then a prefill). */
+typedef struct {
+  skv_batch tokens;
+  const int32_t* ctx_lens_host; /* host   [batch] */
+  const int32_t* ctx_lens;      /* device [batch], same values */
+} skv_step_batch;
+
+/* One forward pass over a mixed batch of prompt chunks and decode tokens
+ * (section 3.5 "Optimized Implementation for Inference"; "Inference
+ * Implementation in Production Serving Frameworks", chunked prefill):
+ *  1. every new token runs layers 1..l, attending to its sequence's cached
+ *     positions and to the new tokens up to its own; its K/V go to slots
+ *     0..l-1 at its position;
+ *  2. the K/V of slots l..l+G-1 (every skipped layer / AcrossKV group) are
+ *     computed from x_{l+1} of every new token, as in skv_prefill;
+ *  3. the last new token of each sequence runs layers l+1..L, attending at
+ *     layer j to all ctx + new positions of its slot;
+ *  4. logits[b, :] = RMSNorm(y_b; final gain) W_lm^T, the next-token logits
+ *     after that token (a decode token's, a final prompt chunk's first
+ *     generated token; a caller ignores the row of an unfinished chunk).
+ * A decode token is a sequence with one new token.  Splitting a prompt into
+ * chunks fed one call after another yields the cache and final logits of
+ * skv_prefill over the whole prompt.  Same asynchrony, ownership and errors
+ * as skv_prefill, plus INVALID_ARG for a negative ctx_lens entry or only one
+ * of the two ctx arrays given. */
+skv_status skv_step(skv_model* m, skv_kv_cache* c, const skv_step_batch* batch, float* logits, void* stream);
+
 /* Closed-form FLOPs of a prefill over prompts of the given lengths (host
  * array).  full = the unmodified model (all layers for every token, LM head
  * for the last token); swiftkv = layers 1..l for every token, one K/V

@@ -33,6 +33,12 @@ input of layer i, l = number of unskipped layers, g = AcrossKV group size):
      SwiftKV cache of each layer (all N positions, its own included).
   5. logits = RMSNorm(y; final gain) @ W_lm^T for that last token.
 
+swiftkv_step extends this to a mixed batch ([P1] "Inference Implementation
+in Production Serving Frameworks"; [P2] section 3.5): each sequence may hold
+cached positions already (a prompt chunk after earlier chunks, a decode
+token); its new tokens run steps 2-3 attending to the cache as well, and its
+last new token runs step 4 and 5.
+
 Readings where the pages are silent (each one is listed in the design doc):
   * Llama block: pre-norm RMSNorm, GQA attention with RoPE (rotate-half,
     inv_freq_i = theta^(-2i/dh), no frequency scaling), SwiGLU MLP
@@ -52,7 +58,8 @@ counted.
 Parity of this oracle is pinned by tests/test_oracle_pins.py against an
 independent library Llama (l = L), an incremental one-token-at-a-time decode,
 the pages' printed FLOP (Table 1) and KV-memory figures, and closed-form
-identities.
+identities; the step by tests/test_oracle_step_pins.py (chunked = one-shot
+prefill, decode at l = L = standard decode, batch independence, FLOPs).
 """
 from __future__ import annotations
 
@@ -356,6 +363,107 @@ def swiftkv_prefill(dims: Dims, weights: WeightSource, prompts: Sequence[np.ndar
     return OracleResult(kv, logits, fc.total, xs)
 
 
+def attention_with_past(q: np.ndarray, k: np.ndarray, v: np.ndarray, q_pos: np.ndarray,
+                        fc: Optional[FlopCounter]) -> np.ndarray:
+    """GQA attention of queries at absolute positions q_pos over cached keys/values.
+
+    q [n,hq,dh]; k/v [m,hkv,dh] hold positions 0..m-1.  Query row i sees the
+    keys at positions 0..q_pos[i] (causal, earlier calls' positions
+    included).  Returns [n, hq*dh].
+    """
+    n, hq, dh = q.shape
+    rep = hq // k.shape[1]
+    scale = q.dtype.type(1.0 / math.sqrt(dh))
+    visible = np.arange(k.shape[0])[None, :] <= np.asarray(q_pos)[:, None]
+    out = np.empty((n, hq, dh), dtype=q.dtype)
+    for h in range(hq):
+        g = h // rep
+        s = (q[:, h, :] @ k[:, g, :].T) * scale
+        out[:, h, :] = softmax_rows(np.where(visible, s, -np.inf)) @ v[:, g, :]
+    if fc is not None:
+        fc.add(4 * dh * hq * int(np.sum(np.asarray(q_pos) + 1)))
+    return out.reshape(n, hq * dh)
+
+
+@dataclass
+class StepResult:
+    kv: List[Dict[int, Tuple[np.ndarray, np.ndarray]]]   # per sequence: slot -> (K, V) over all ctx + n positions
+    logits: np.ndarray                                    # [B, vocab], after each sequence's last new token
+    flops: int
+
+
+def swiftkv_step(dims: Dims, weights: WeightSource, past: Sequence[Dict[int, Tuple[np.ndarray, np.ndarray]]],
+                 new_tokens: Sequence[np.ndarray], l: int, g: int = 1, dtype=np.float32) -> StepResult:
+    """One forward pass over a mixed batch of prompt chunks and decode tokens.
+
+    Source: [P1] "Inference Implementation in Production Serving Frameworks"
+    (mixed batches, chunked prefill) and [P2] section 3.5: every token of
+    the batch, prefill chunk or decode token, runs layers 1..l with its
+    early-layer KV stored normally; right after layer l the KV of every
+    skipped layer is computed from x_{l+1} of every new token; only the
+    tokens that continue (the decode tokens; here the last new token of
+    every sequence, which also yields a finished prompt's first logits) run
+    layers l+1..L, attending to the cache.
+
+    ``past[b]`` maps each KV slot to sequence b's cached (K, V) over
+    positions 0..C_b-1 (an empty dict: C_b = 0); ``new_tokens[b]`` are its
+    new tokens at positions C_b, C_b+1, ...  Returns the extended caches
+    (new arrays; ``past`` is not modified) and the logits after each
+    sequence's last new token.
+    """
+    L, eps = dims.n_layers, dims.rms_eps
+    if not 0 <= l <= L or g < 1:
+        raise ValueError("bad l or g")
+    if len(past) != len(new_tokens) or any(len(t) < 1 for t in new_tokens):
+        raise ValueError("one non-empty token run per sequence")
+    fc = FlopCounter()
+    nslot = kv_slots(L, l, g)
+    empty = np.zeros((0, dims.n_kv_heads, dims.head_dim), dtype)
+    kv = [{s: past[b].get(s, (empty, empty)) for s in range(nslot)} for b in range(len(past))]
+    ctx = [kv[b][0][0].shape[0] for b in range(len(past))]
+    for b in range(len(past)):
+        if any(kv[b][s][0].shape[0] != ctx[b] for s in range(nslot)):
+            raise ValueError("every slot of a sequence must hold the same positions")
+    xs = [weights.embed[np.asarray(t)].astype(dtype) for t in new_tokens]
+    pos = [ctx[b] + np.arange(len(new_tokens[b])) for b in range(len(past))]
+
+    for i in range(1, l + 1):                      # layers 1..l: every new token
+        W = weights.layer(i)
+        for b in range(len(past)):
+            q, k, v = qkv_projection(xs[b], W, pos[b], dims, fc)
+            K = np.concatenate([kv[b][i - 1][0], k], axis=0)
+            V = np.concatenate([kv[b][i - 1][1], v], axis=0)
+            kv[b][i - 1] = (K, V)
+            x = xs[b] + matmul_wt(attention_with_past(q, K, V, pos[b], fc), W["wo"], fc)
+            xs[b] = mlp_residual(x, W, dims, fc)
+
+    ys = [x[-1:].copy() for x in xs]
+    for j in range(l + 1, L + 1):
+        W = weights.layer(j)
+        s = slot_of_layer(j, L, l, g)
+        if representative(j, l, g) == j:           # KV of the skipped layers from x_{l+1}
+            for b in range(len(past)):
+                n = xs[b].shape[0]
+                a = rmsnorm(xs[b], W["attn_norm"], eps)
+                k = matmul_wt(a, W["wk"], fc).reshape(n, dims.n_kv_heads, dims.head_dim)
+                v = matmul_wt(a, W["wv"], fc).reshape(n, dims.n_kv_heads, dims.head_dim)
+                kv[b][s] = (np.concatenate([kv[b][s][0], rope(k, pos[b], dims.rope_theta)], axis=0),
+                            np.concatenate([kv[b][s][1], v], axis=0))
+        for b in range(len(past)):                 # the continuing token
+            K, V = kv[b][s]
+            p_last = int(pos[b][-1])
+            a = rmsnorm(ys[b], W["attn_norm"], eps)
+            q = matmul_wt(a, W["wq"], fc).reshape(1, dims.n_q_heads, dims.head_dim)
+            q = rope(q, np.array([p_last]), dims.rope_theta)
+            o = attention_with_past(q, K, V, np.array([p_last]), fc)
+            y = ys[b] + matmul_wt(o, W["wo"], fc)
+            ys[b] = mlp_residual(y, W, dims, fc)
+
+    logits = np.concatenate(
+        [matmul_wt(rmsnorm(y, weights.final_norm, eps), weights.lm_head, fc) for y in ys], axis=0)
+    return StepResult(kv, logits, fc.total)
+
+
 def standard_incremental_decode(dims: Dims, weights: WeightSource, prompt: np.ndarray, dtype=np.float32):
     """Unmodified model run one token at a time with a growing KV cache.
 
@@ -406,6 +514,26 @@ def prefill_flops(dims: Dims, l: int, g: int, lengths: Sequence[int]) -> Tuple[i
         swift += (l * layer_full + G * n * 4 * d * dkv
                   + (L - l) * (2 * d * dq + 2 * dq * d + 6 * d * f + 4 * n * dh * hq) + 2 * d * V)
     return full, swift
+
+
+def step_flops(dims: Dims, l: int, g: int, ctx: Sequence[int], new: Sequence[int]) -> int:
+    """SwiftKV FLOPs of one mixed-batch step: sequence b holds ctx[b] cached
+    positions and brings new[b] tokens.  Layers 1..l for every new token
+    (token at position p attends p+1 keys), one K/V projection per AcrossKV
+    group for every new token, layers l+1..L and the LM head for the last
+    new token (attending ctx + new keys)."""
+    d, dq, dkv, f, V, L = dims.d_model, dims.dq, dims.dkv, dims.ffn_dim, dims.vocab, dims.n_layers
+    hq, dh = dims.n_q_heads, dims.head_dim
+    G = n_groups(L, l, g)
+    total = 0
+    for c, n in zip(ctx, new):
+        c, n = int(c), int(n)
+        t = c + n
+        keys = (t * (t + 1) - c * (c + 1)) // 2          # sum of p + 1 over the new positions
+        total += l * (n * (2 * d * dq + 2 * dq * d + 6 * d * f + 4 * d * dkv) + 4 * dh * hq * keys)
+        total += G * n * 4 * d * dkv
+        total += (L - l) * (2 * d * dq + 2 * dq * d + 6 * d * f + 4 * t * dh * hq) + 2 * d * V
+    return total
 
 
 def per_token_breakdown(dims: Dims, l: int, g: int, attn_per_layer_flops: float = 0.0) -> Dict[str, float]:

@@ -43,8 +43,13 @@ class skv_batch(Structure):
                 ("token_ids", c_void_p), ("cu_seqlens", c_void_p), ("block_tables", c_void_p)]
 
 
+class skv_step_batch(Structure):
+    _fields_ = [("tokens", skv_batch), ("ctx_lens_host", c_void_p), ("ctx_lens", c_void_p)]
+
+
 EXPORTED = ["skv_model_create", "skv_model_load_globals", "skv_model_load_layer", "skv_model_destroy",
             "skv_kv_cache_create", "skv_kv_cache_destroy", "skv_num_kv_slots", "skv_kv_cache_view", "skv_prefill",
+            "skv_step",
             "skv_flops", "skv_profile_enable", "skv_profile_read", "skv_last_error"]
 
 _lib = None
@@ -76,6 +81,7 @@ def lib():
         L.skv_num_kv_slots.restype = c_int32
         L.skv_kv_cache_view.argtypes = [vp, c_int32, POINTER(skv_tensor_view), POINTER(skv_tensor_view)]
         L.skv_prefill.argtypes = [vp, vp, POINTER(skv_batch), vp, vp]
+        L.skv_step.argtypes = [vp, vp, POINTER(skv_step_batch), vp, vp]
         L.skv_flops.argtypes = [POINTER(skv_model_config), vp, c_int32, POINTER(c_double), POINTER(c_double)]
         L.skv_profile_enable.argtypes = [vp, c_int32, c_int32]
         L.skv_profile_read.argtypes = [vp, POINTER(c_double), POINTER(c_int64), POINTER(c_double), POINTER(c_double)]
@@ -150,6 +156,10 @@ def skv_kv_cache_view(cache: int, layer: int):
 
 def skv_prefill(model: int, cache: int, batch: skv_batch, logits_ptr: int, stream: int = 0) -> None:
     check(lib().skv_prefill(model, cache, ctypes.byref(batch), logits_ptr, stream))
+
+
+def skv_step(model: int, cache: int, batch: skv_step_batch, logits_ptr: int, stream: int = 0) -> None:
+    check(lib().skv_step(model, cache, ctypes.byref(batch), logits_ptr, stream))
 
 
 def skv_flops(cfg: skv_model_config, seqlens) -> tuple:

@@ -28,6 +28,10 @@ skv_status fail(skv_status s, const std::string& msg) {
   } while (0)
 
 int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// bf16 batches of at most this many new tokens take the row path through
+// layers 1..l (run_step).
+constexpr int kRowPathMax = kSkinnyMaxRows;
 size_t round_up(size_t a, size_t b) { return (a + b - 1) / b * b; }
 
 }  // namespace
@@ -289,10 +293,13 @@ skv_status skv_model_create(const skv_model_config* cfg, skv_model** out) {
   ALLOC(m->last_row, B * 4);
   ALLOC(m->iota, B * 4);
   ALLOC(m->y, B * d * 4);
-  ALLOC(m->ya, B * d * E);
-  ALLOC(m->yq, B * dq * E);
-  ALLOC(m->yo, B * dq * E);
-  ALLOC(m->yh, B * f * E);
+  // row-major buffers: the last tokens, and (bf16) the new tokens of a
+  // batch small enough for the row path
+  const size_t RY = m->bf16 ? std::max(B, std::min(T, (size_t)kRowPathMax)) : B;
+  ALLOC(m->ya, RY * d * E);
+  ALLOC(m->yq, RY * dq * E);
+  ALLOC(m->yo, RY * dq * E);
+  ALLOC(m->yh, RY * f * E);
   if (m->bf16) {
     int64_t pe = 0;
     pe = std::max(pe, skinny_partial_elems((int)dq, (int)d));
@@ -300,9 +307,11 @@ skv_status skv_model_create(const skv_model_config* cfg, skv_model** out) {
     pe = std::max(pe, skinny_partial_elems((int)(2 * f), (int)d));
     pe = std::max(pe, skinny_partial_elems((int)d, (int)f));
     pe = std::max(pe, skinny_partial_elems((int)V, (int)d));
+    pe = std::max(pe, skinny_partial_elems((int)(dq + 2 * dkv), (int)d));
+    if (m->G > 0) pe = std::max(pe, skinny_partial_elems((int)(m->G * 2 * dkv), (int)d));
     m->partial_elems = pe;
     ALLOC(m->partial, (size_t)pe * 4);
-    m->attn_ws_elems = attn_rows_ws_elems((int)B, c.max_seqlen, c.n_q_heads, c.head_dim);
+    m->attn_ws_elems = attn_rows_ws_elems((int)RY, c.max_seqlen, c.n_q_heads, c.head_dim);
   } else {
     m->attn_ws_elems = attn_rows_ws_elems((int)std::max(T, B), c.max_seqlen, c.n_q_heads, c.head_dim);
   }
@@ -544,9 +553,18 @@ skv_status skv_profile_read(skv_model* m, double* total_ms, int64_t* launches, d
 
 namespace {
 
+// Host-side facts about one call's batch (validated before anything is enqueued).
+struct StepInfo {
+  const int32_t* ctx_dev = nullptr;  // device [batch] cached positions per sequence, NULL = none
+  int max_new = 0;                   // longest run of new tokens
+  int max_total = 0;                 // longest cached + new
+  double attn_flops = 0;             // 4 * keys * dh * hq summed over the new tokens
+  double ctx_tokens = 0;             // keys attended by the last tokens, summed
+};
+
 template <typename T>
-skv_status run_prefill(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, float* logits, int max_len,
-                       hipStream_t s) {
+skv_status run_step(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, const StepInfo& si, float* logits,
+                    hipStream_t s) {
   const auto& c = m->cfg;
   const int T_ = bt->total_tokens, B = bt->batch, d = c.d_model, dq = m->dq, dkv = m->dkv, f = c.ffn_dim,
             V = c.vocab, dh = c.head_dim, hq = c.n_q_heads, l = c.swiftkv_l, L = c.n_layers;
@@ -565,28 +583,73 @@ skv_status run_prefill(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, floa
                         c.n_kv_heads, dh};
   };
   constexpr bool kBf16 = sizeof(T) == 2;
+  // bf16 batches of at most kRowPathMax new tokens (decode steps, short
+  // chunks) run layers 1..l like the last-token path: row-major
+  // activations, the split-K skinny GEMM and per-row attention, instead of
+  // 256-row GEMM tiles that would be mostly padding.
+  const bool rows_path = kBf16 && T_ <= kRowPathMax;
 
   // algorithmic work of the attention and last-token rows, for the profiling hook
-  double attn_flops = 0, ctx_tokens = 0;
-  for (int b = 0; b < B; ++b) {
-    const double n = bt->cu_seqlens_host[b + 1] - bt->cu_seqlens_host[b];
-    attn_flops += 2.0 * n * (n + 1) * dh * hq;
-    ctx_tokens += n;
-  }
   const double attn_bytes = (double)T_ * (2.0 * dq + 2.0 * dkv) * E;
   const double n_deep = L - l;
-  const double last_flops = n_deep * (B * (4.0 * d * dq + 6.0 * d * f) + 4.0 * ctx_tokens * dh * hq) + 2.0 * d * V * B;
-  const double last_bytes = n_deep * ((2.0 * dq * d + 3.0 * f * d) * E + ctx_tokens * 2.0 * dkv * E) + (double)V * d * E;
+  const double last_flops = n_deep * (B * (4.0 * d * dq + 6.0 * d * f) + 4.0 * si.ctx_tokens * dh * hq) + 2.0 * d * V * B;
+  const double last_bytes = n_deep * ((2.0 * dq * d + 3.0 * f * d) * E + si.ctx_tokens * 2.0 * dkv * E) + (double)V * d * E;
 
-  SKV_HIP(launch_meta(bt->cu_seqlens, bt->block_tables, B, bt->max_blocks_per_seq, kc->num_blocks, T_, m->pos,
-                      m->slot, m->last_pos, m->last_row, s));
-  if (!kBf16) SKV_HIP(launch_token_seq(bt->cu_seqlens, B, T_, m->seq, s));
+  SKV_HIP(launch_meta(bt->cu_seqlens, si.ctx_dev, bt->block_tables, B, bt->max_blocks_per_seq, kc->num_blocks, T_,
+                      m->pos, m->slot, m->last_pos, m->last_row, s));
+  if (!kBf16 || rows_path) SKV_HIP(launch_token_seq(bt->cu_seqlens, B, T_, m->seq, s));
   SKV_HIP(launch_embed<T>(bt->token_ids, (const T*)m->embed, V, d, T_, m->x, s));
 
-  // ---- layers 1..l for every prompt token
+  // One layer over a few rows held row-major (the last tokens at layers
+  // l+1..L; every new token of a short bf16 batch at layers 1..l).  x: the
+  // rows' residual stream; with_kv: the QKV product also yields K/V, written
+  // to cache slot cs at slot[row].
+  auto row_layer = [&](const LayerDev& Ly, CacheSlot<T> cs, int rows, float* x, const int32_t* row_seq,
+                       const int32_t* row_pos, const int32_t* slot, bool with_kv, int max_ctx) -> skv_status {
+    SKV_HIP(launch_rmsnorm<T>(x, nullptr, Ly.attn_norm, rows, d, c.rms_eps, ya, s));
+    const int nq = with_kv ? dq + 2 * dkv : dq;
+    EpiQKV<T> eq{yq, cs, row_pos, slot, m->rope_cos, m->rope_sin, dq, dkv, dh, P};
+    EpiResidual er{x, d, kBf16 ? 64 : 16};
+    EpiSwiGLU<T> esw{yh, f, m->p_mlp};
+    if constexpr (kBf16) {
+      SKV_HIP(launch_skinny_bf16((const bf16_t*)ya, d, (const bf16_t*)Ly.wqkv, Ly.panel_rows, rows, nq, d, m->partial,
+                                 m->partial_elems, eq, s));
+    } else if (P == 16) {
+      SKV_HIP((launch_gemm_f32<16>((const float*)ya, d, (const float*)Ly.wqkv, d, rows, nq, d, eq, s)));
+    } else if (P == 32) {
+      SKV_HIP((launch_gemm_f32<32>((const float*)ya, d, (const float*)Ly.wqkv, d, rows, nq, d, eq, s)));
+    } else {
+      SKV_HIP((launch_gemm_f32<64>((const float*)ya, d, (const float*)Ly.wqkv, d, rows, nq, d, eq, s)));
+    }
+    SKV_HIP(launch_attn_rows<T>(yq, cs, row_seq, row_pos, bt->block_tables, bt->max_blocks_per_seq, rows, max_ctx, hq,
+                                m->attn_ws, yo, s));
+    if constexpr (kBf16) {
+      SKV_HIP(launch_skinny_bf16((const bf16_t*)yo, dq, (const bf16_t*)Ly.wo, Ly.panel_rows, rows, d, dq, m->partial,
+                                 m->partial_elems, er, s));
+    } else {
+      SKV_HIP((launch_gemm_f32<16>((const float*)yo, dq, (const float*)Ly.wo, dq, rows, d, dq, er, s)));
+    }
+    SKV_HIP(launch_rmsnorm<T>(x, nullptr, Ly.ffn_norm, rows, d, c.rms_eps, ya, s));
+    if constexpr (kBf16) {
+      SKV_HIP(launch_skinny_bf16((const bf16_t*)ya, d, (const bf16_t*)Ly.wgu, Ly.panel_rows, rows, 2 * f, d, m->partial,
+                                 m->partial_elems, esw, s));
+      SKV_HIP(launch_skinny_bf16((const bf16_t*)yh, f, (const bf16_t*)Ly.wdown, Ly.panel_rows, rows, d, f, m->partial,
+                                 m->partial_elems, er, s));
+    } else {
+      SKV_HIP((launch_gemm_f32<16>((const float*)ya, d, (const float*)Ly.wgu, d, rows, 2 * f, d, esw, s)));
+      SKV_HIP((launch_gemm_f32<16>((const float*)yh, f, (const float*)Ly.wdown, f, rows, d, f, er, s)));
+    }
+    return SKV_OK;
+  };
+
+  // ---- layers 1..l for every new token
   for (int i = 1; i <= l; ++i) {
     const LayerDev& Ly = m->layers[i - 1];
     CacheSlot<T> cs = slot_of(i - 1);
+    if (rows_path) {
+      SKV_TRY(row_layer(Ly, cs, T_, m->x, m->seq, m->pos, m->slot, true, si.max_total));
+      continue;
+    }
     {
       Prof p(m, SKV_K_RMSNORM, s, 0, (double)T_ * d * (4 + E));
       if constexpr (kBf16)
@@ -608,13 +671,13 @@ skv_status run_prefill(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, floa
         SKV_HIP((launch_gemm_f32<64>((const float*)act, d, (const float*)Ly.wqkv, d, T_, N, d, epi, s)));
     }
     {
-      Prof p(m, SKV_K_ATTN_PREFILL, s, attn_flops, attn_bytes);
+      Prof p(m, SKV_K_ATTN_PREFILL, s, si.attn_flops, attn_bytes);
       if constexpr (kBf16)
-        SKV_HIP(launch_attn_prefill_bf16((const bf16_t*)qbuf, cs, bt->cu_seqlens, bt->block_tables,
-                                         bt->max_blocks_per_seq, B, max_len, hq, (bf16_t*)obuf, s));
+        SKV_HIP(launch_attn_prefill_bf16((const bf16_t*)qbuf, cs, bt->cu_seqlens, si.ctx_dev, bt->block_tables,
+                                         bt->max_blocks_per_seq, B, si.max_new, hq, (bf16_t*)obuf, s));
       else
-        SKV_HIP(launch_attn_rows<T>(qbuf, cs, m->seq, m->pos, bt->block_tables, bt->max_blocks_per_seq, T_, max_len,
-                                    hq, m->attn_ws, obuf, s));
+        SKV_HIP(launch_attn_rows<T>(qbuf, cs, m->seq, m->pos, bt->block_tables, bt->max_blocks_per_seq, T_,
+                                    si.max_total, hq, m->attn_ws, obuf, s));
     }
     {
       EpiResidual epi{m->x, d, kBf16 ? 64 : 16};
@@ -656,69 +719,42 @@ skv_status run_prefill(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, floa
     {
       Prof p(m, SKV_K_RMSNORM, s, 0, (double)T_ * d * (4 + E));
       // x * r, gains folded into W~
-      if constexpr (kBf16)
+      if (kBf16 && !rows_path)
         SKV_HIP(launch_rmsnorm_panel(m->x, nullptr, T_, d, c.rms_eps, (bf16_t*)act, s));
       else
-        SKV_HIP(launch_rmsnorm<T>(m->x, nullptr, nullptr, T_, d, c.rms_eps, act, s));
+        SKV_HIP(launch_rmsnorm<T>(m->x, nullptr, nullptr, T_, d, c.rms_eps, rows_path ? ya : act, s));
     }
     CacheSlot<T> first = slot_of(l);
     const int N = m->G * 2 * dkv;
     EpiKVSkip<T> epi{first.k, first.v, kc->slot_elems, m->pos, m->slot, m->rope_cos, m->rope_sin, dkv, dh, P,
                      c.n_kv_heads};
     Prof p(m, SKV_K_GEMM_KVSKIP, s, 2.0 * T_ * N * d, gemm_bytes(T_, N, d, E, E));
-    if constexpr (kBf16)
-      SKV_HIP(launch_gemm_bf16((const bf16_t*)act, (const bf16_t*)m->wkv_skip, T_, N, d, epi, m->gemm_ws, m->gemm_ws_elems, s));
-    else if (P == 16)
+    if constexpr (kBf16) {
+      if (rows_path)
+        SKV_HIP(launch_skinny_bf16((const bf16_t*)ya, d, (const bf16_t*)m->wkv_skip, kPanelRows, T_, N, d, m->partial,
+                                   m->partial_elems, epi, s));
+      else
+        SKV_HIP(launch_gemm_bf16((const bf16_t*)act, (const bf16_t*)m->wkv_skip, T_, N, d, epi, m->gemm_ws,
+                                 m->gemm_ws_elems, s));
+    } else if (P == 16) {
       SKV_HIP((launch_gemm_f32<16>((const float*)act, d, (const float*)m->wkv_skip, d, T_, N, d, epi, s)));
-    else if (P == 32)
+    } else if (P == 32) {
       SKV_HIP((launch_gemm_f32<32>((const float*)act, d, (const float*)m->wkv_skip, d, T_, N, d, epi, s)));
-    else
+    } else {
       SKV_HIP((launch_gemm_f32<64>((const float*)act, d, (const float*)m->wkv_skip, d, T_, N, d, epi, s)));
+    }
   }
 
-  // ---- last prompt token of each prompt through layers l+1..L, then the LM head
+  // ---- last new token of each sequence through layers l+1..L, then the LM head
   Prof plast(m, SKV_K_LAST_TOKEN, s, last_flops, last_bytes);
   SKV_HIP(launch_gather_rows(m->x, m->last_row, B, d, m->y, s));
-  for (int j = l + 1; j <= L; ++j) {
-    const LayerDev& Ly = m->layers[j - 1];
-    CacheSlot<T> cs = slot_of(slot_of_layer(c, j));
-    SKV_HIP(launch_rmsnorm<T>(m->y, nullptr, Ly.attn_norm, B, d, c.rms_eps, ya, s));
-    EpiQKV<T> eq{yq, cs, m->last_pos, nullptr, m->rope_cos, m->rope_sin, dq, dkv, dh, P};
-    EpiResidual er{m->y, d, kBf16 ? 64 : 16};
-    EpiSwiGLU<T> esw{yh, f, m->p_mlp};
-    if constexpr (kBf16) {
-      SKV_HIP(launch_skinny_bf16((const bf16_t*)ya, d, (const bf16_t*)Ly.wqkv, B, dq, d, m->partial,
-                                 m->partial_elems, eq, s));
-    } else if (P == 16) {
-      SKV_HIP((launch_gemm_f32<16>((const float*)ya, d, (const float*)Ly.wqkv, d, B, dq, d, eq, s)));
-    } else if (P == 32) {
-      SKV_HIP((launch_gemm_f32<32>((const float*)ya, d, (const float*)Ly.wqkv, d, B, dq, d, eq, s)));
-    } else {
-      SKV_HIP((launch_gemm_f32<64>((const float*)ya, d, (const float*)Ly.wqkv, d, B, dq, d, eq, s)));
-    }
-    SKV_HIP(launch_attn_rows<T>(yq, cs, m->iota, m->last_pos, bt->block_tables, bt->max_blocks_per_seq, B, max_len,
-                                hq, m->attn_ws, yo, s));
-    if constexpr (kBf16) {
-      SKV_HIP(launch_skinny_bf16((const bf16_t*)yo, dq, (const bf16_t*)Ly.wo, B, d, dq, m->partial,
-                                 m->partial_elems, er, s));
-    } else {
-      SKV_HIP((launch_gemm_f32<16>((const float*)yo, dq, (const float*)Ly.wo, dq, B, d, dq, er, s)));
-    }
-    SKV_HIP(launch_rmsnorm<T>(m->y, nullptr, Ly.ffn_norm, B, d, c.rms_eps, ya, s));
-    if constexpr (kBf16) {
-      SKV_HIP(launch_skinny_bf16((const bf16_t*)ya, d, (const bf16_t*)Ly.wgu, B, 2 * f, d, m->partial,
-                                 m->partial_elems, esw, s));
-      SKV_HIP(launch_skinny_bf16((const bf16_t*)yh, f, (const bf16_t*)Ly.wdown, B, d, f, m->partial,
-                                 m->partial_elems, er, s));
-    } else {
-      SKV_HIP((launch_gemm_f32<16>((const float*)ya, d, (const float*)Ly.wgu, d, B, 2 * f, d, esw, s)));
-      SKV_HIP((launch_gemm_f32<16>((const float*)yh, f, (const float*)Ly.wdown, f, B, d, f, er, s)));
-    }
-  }
+  for (int j = l + 1; j <= L; ++j)
+    SKV_TRY(row_layer(m->layers[j - 1], slot_of(slot_of_layer(c, j)), B, m->y, m->iota, m->last_pos, nullptr, false,
+                      si.max_total));
   SKV_HIP(launch_rmsnorm<T>(m->y, nullptr, m->final_norm, B, d, c.rms_eps, ya, s));
   EpiStoreF32 el{logits, V, kBf16 ? 64 : 16};
   if constexpr (kBf16)
-    SKV_HIP(launch_skinny_bf16((const bf16_t*)ya, d, (const bf16_t*)m->lm_head, B, V, d, m->partial,
+    SKV_HIP(launch_skinny_bf16((const bf16_t*)ya, d, (const bf16_t*)m->lm_head, kSkinnyPanelRows, B, V, d, m->partial,
                                m->partial_elems, el, s));
   else
     SKV_HIP((launch_gemm_f32<16>((const float*)ya, d, (const float*)m->lm_head, d, B, V, d, el, s)));
@@ -727,8 +763,12 @@ skv_status run_prefill(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, floa
 
 }  // namespace
 
-extern "C" skv_status skv_prefill(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, float* logits,
-                                  void* stream) {
+namespace {
+
+// Shared argument checks of skv_prefill / skv_step; ctx_host NULL = no
+// cached positions.
+skv_status check_and_run(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, const int32_t* ctx_host,
+                         const int32_t* ctx_dev, float* logits, void* stream) {
   if (!m || !kc || !bt || !logits) return fail(SKV_ERR_INVALID_ARG, "NULL argument");
   if (kc->m != m) return fail(SKV_ERR_INVALID_ARG, "cache was created for another model");
   const auto& c = m->cfg;
@@ -745,22 +785,45 @@ extern "C" skv_status skv_prefill(skv_model* m, skv_kv_cache* kc, const skv_batc
   const int32_t* cu = bt->cu_seqlens_host;
   if (cu[0] != 0 || cu[B] != bt->total_tokens)
     return fail(SKV_ERR_INVALID_ARG, "cu_seqlens must start at 0 and end at total_tokens");
-  int max_len = 0;
+  const double dh = c.head_dim, hq = c.n_q_heads;
+  StepInfo si;
+  si.ctx_dev = ctx_dev;
   for (int b = 0; b < B; ++b) {
     const int n = cu[b + 1] - cu[b];
-    if (n < 1) return fail(SKV_ERR_INVALID_ARG, "prompt " + std::to_string(b) + " is empty");
-    if (n > c.max_seqlen) return fail(SKV_ERR_INVALID_ARG, "prompt longer than max_seqlen");
-    const int nb = ceil_div(n, kc->block_size);
+    const int cx = ctx_host ? ctx_host[b] : 0;
+    if (n < 1) return fail(SKV_ERR_INVALID_ARG, "sequence " + std::to_string(b) + " brings no token");
+    if (cx < 0) return fail(SKV_ERR_INVALID_ARG, "negative cached length");
+    if ((int64_t)cx + n > c.max_seqlen) return fail(SKV_ERR_INVALID_ARG, "sequence longer than max_seqlen");
+    const int tot = cx + n;
+    const int nb = ceil_div(tot, kc->block_size);
     if (nb > bt->max_blocks_per_seq) return fail(SKV_ERR_INVALID_ARG, "block table too small");
     for (int i = 0; i < nb; ++i) {
       const int blk = bt->block_tables_host[(int64_t)b * bt->max_blocks_per_seq + i];
       if (blk < 0 || blk >= kc->num_blocks)
         return fail(SKV_ERR_INVALID_ARG, "block table entry outside [0, num_blocks)");
     }
-    max_len = std::max(max_len, n);
+    si.max_new = std::max(si.max_new, n);
+    si.max_total = std::max(si.max_total, tot);
+    si.attn_flops += 2.0 * dh * hq * ((double)tot * (tot + 1) - (double)cx * (cx + 1));
+    si.ctx_tokens += tot;
   }
-  if (bt->max_seqlen < max_len) return fail(SKV_ERR_INVALID_ARG, "max_seqlen smaller than the longest prompt");
+  if (bt->max_seqlen < si.max_new) return fail(SKV_ERR_INVALID_ARG, "max_seqlen smaller than the longest run");
   hipStream_t s = (hipStream_t)stream;
-  if (m->bf16) return run_prefill<bf16_t>(m, kc, bt, logits, max_len, s);
-  return run_prefill<float>(m, kc, bt, logits, max_len, s);
+  if (m->bf16) return run_step<bf16_t>(m, kc, bt, si, logits, s);
+  return run_step<float>(m, kc, bt, si, logits, s);
+}
+
+}  // namespace
+
+extern "C" skv_status skv_prefill(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, float* logits,
+                                  void* stream) {
+  return check_and_run(m, kc, bt, nullptr, nullptr, logits, stream);
+}
+
+extern "C" skv_status skv_step(skv_model* m, skv_kv_cache* kc, const skv_step_batch* sb, float* logits,
+                               void* stream) {
+  if (!sb) return fail(SKV_ERR_INVALID_ARG, "NULL argument");
+  if (!sb->ctx_lens_host != !sb->ctx_lens)
+    return fail(SKV_ERR_INVALID_ARG, "ctx_lens_host and ctx_lens must both be set or both be NULL");
+  return check_and_run(m, kc, &sb->tokens, sb->ctx_lens_host, sb->ctx_lens, logits, stream);
 }

@@ -1,7 +1,9 @@
 // Attention kernels.
 //
 // 1. attn_prefill8_kernel (bf16, MFMA): causal GQA flash attention of the
-//    prompt tokens of layers 1..l, reading K/V from the paged cache.
+//    prompt tokens of layers 1..l, reading K/V from the paged cache.  A
+//    sequence's new tokens may follow positions already cached (a prompt
+//    chunk, a decode token): they attend to those as well as to each other.
 //    A workgroup = 8 wave64s = 4 query heads of one kv-head group x two
 //    32-query blocks of one prompt (64 queries).  Per 64-key tile:
 //      S^T (keys x queries) = K Q^T   with A = K from LDS, B = Q^T from
@@ -73,14 +75,17 @@ SKV_DEV void f8_qk(const bf16_t* sk, const bf16x8_t* qf, int lane, f32x16_t* sac
 
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_prefill8_kernel(
     const bf16_t* __restrict__ q, CacheSlot<bf16_t> cache, const int32_t* __restrict__ cu,
-    const int32_t* __restrict__ bt, int max_blocks, int hq, int rep, float scale_log2, bf16_t* __restrict__ o) {
+    const int32_t* __restrict__ ctx, const int32_t* __restrict__ bt, int max_blocks, int hq, int rep,
+    float scale_log2, bf16_t* __restrict__ o) {
   // buffers 0, 1: K ring; 2, 3: V ring ([64 keys][128 dims] each); the
   // whole 64 KB stages the output at the end
   __shared__ __attribute__((aligned(1024))) bf16_t smem[4][FA_KT * FA_DH];
 
   const int b = blockIdx.y;
   const int tok0 = cu[b];
-  const int N = cu[b + 1] - tok0;
+  const int N = cu[b + 1] - tok0;  // new queries, at positions C .. C + N - 1
+  const int C = ctx ? ctx[b] : 0;  // positions cached before them
+  const int NK = C + N;            // keys
   const int nqb = (N + 63) / 64;
   const int qb = gridDim.x - 1 - blockIdx.x;  // longest rows first
   if (qb >= nqb) return;
@@ -96,7 +101,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int hkv = cache.hkv;
   const int dq = hq * FA_DH;
 
-  const int kend = min(N, q0w + 64);
+  const int kend = min(NK, C + q0w + 64);
   const int ntiles = (kend + FA_KT - 1) / FA_KT;
   const int nblk_need = (kend + kBlockSize - 1) / kBlockSize;
   const int32_t* btb = bt + (int64_t)b * max_blocks;
@@ -156,14 +161,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // straight block the scheduler can interleave.
   auto soft_prep = [&](int t, f32x16_t* sacc) {
     const int k0 = t * FA_KT;
-    const int qi = q0 + (lane & 31);
-    if ((k0 + FA_KT - 1 > q0) || (k0 + FA_KT > N)) {
+    const int qi = C + q0 + (lane & 31);  // the column's position
+    if ((k0 + FA_KT - 1 > C + q0) || (k0 + FA_KT > NK)) {
 #pragma unroll
       for (int st = 0; st < 2; ++st)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int key = k0 + st * 32 + 8 * (v >> 2) + 4 * hh + (v & 3);
-          if (key > qi || key >= N) sacc[st][v] = -INFINITY;
+          if (key > qi || key >= NK) sacc[st][v] = -INFINITY;
         }
     }
     float mt = sacc[0][0];
@@ -491,13 +496,13 @@ __global__ void attn_combine_kernel(const float* __restrict__ ws, int hq, int dh
 }  // namespace
 
 hipError_t launch_attn_prefill_bf16(const bf16_t* q, CacheSlot<bf16_t> cache, const int32_t* cu_seqlens,
-                                    const int32_t* block_tables, int max_blocks, int batch, int max_seqlen, int hq,
-                                    bf16_t* o, hipStream_t stream) {
-  if (batch <= 0 || max_seqlen <= 0) return hipSuccess;
+                                    const int32_t* ctx_lens, const int32_t* block_tables, int max_blocks, int batch,
+                                    int max_new, int hq, bf16_t* o, hipStream_t stream) {
+  if (batch <= 0 || max_new <= 0) return hipSuccess;
   const int rep = hq / cache.hkv;
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)FA_DH);
-  dim3 grid((max_seqlen + 63) / 64, batch, hq / 4);
-  hipLaunchKernelGGL(attn_prefill8_kernel, grid, dim3(512), 0, stream, q, cache, cu_seqlens, block_tables,
+  dim3 grid((max_new + 63) / 64, batch, hq / 4);
+  hipLaunchKernelGGL(attn_prefill8_kernel, grid, dim3(512), 0, stream, q, cache, cu_seqlens, ctx_lens, block_tables,
                      max_blocks, hq, rep, scale_log2, o);
   return hipGetLastError();
 }

@@ -8,9 +8,9 @@
 
 namespace {
 
-__global__ void meta_kernel(const int32_t* __restrict__ cu, const int32_t* __restrict__ bt, int batch,
-                            int max_blocks, int num_blocks, int T, int32_t* __restrict__ pos,
-                            int32_t* __restrict__ slot, int32_t* __restrict__ last_pos,
+__global__ void meta_kernel(const int32_t* __restrict__ cu, const int32_t* __restrict__ ctx,
+                            const int32_t* __restrict__ bt, int batch, int max_blocks, int num_blocks, int T,
+                            int32_t* __restrict__ pos, int32_t* __restrict__ slot, int32_t* __restrict__ last_pos,
                             int32_t* __restrict__ last_row) {
   int t = blockIdx.x * blockDim.x + threadIdx.x;
   if (t < T) {
@@ -22,14 +22,14 @@ __global__ void meta_kernel(const int32_t* __restrict__ cu, const int32_t* __res
       else
         hi = mid;
     }
-    int p = t - cu[lo];
+    int p = (ctx ? ctx[lo] : 0) + t - cu[lo];
     pos[t] = p;
     int bi = p / kBlockSize;
     int blk = bi < max_blocks ? bt[(int64_t)lo * max_blocks + bi] : -1;
     slot[t] = (blk >= 0 && blk < num_blocks) ? blk * kBlockSize + (p % kBlockSize) : -1;
   }
   if (t < batch) {
-    last_pos[t] = cu[t + 1] - cu[t] - 1;
+    last_pos[t] = (ctx ? ctx[t] : 0) + cu[t + 1] - cu[t] - 1;
     last_row[t] = cu[t + 1] - 1;
   }
 }
@@ -198,12 +198,12 @@ int grid_for(int64_t n) {
 
 }  // namespace
 
-hipError_t launch_meta(const int32_t* cu_seqlens, const int32_t* block_tables, int batch, int max_blocks,
-                       int num_blocks, int total_tokens, int32_t* pos, int32_t* slot, int32_t* last_pos,
-                       int32_t* last_row, hipStream_t stream) {
+hipError_t launch_meta(const int32_t* cu_seqlens, const int32_t* ctx_lens, const int32_t* block_tables, int batch,
+                       int max_blocks, int num_blocks, int total_tokens, int32_t* pos, int32_t* slot,
+                       int32_t* last_pos, int32_t* last_row, hipStream_t stream) {
   int n = total_tokens > batch ? total_tokens : batch;
-  hipLaunchKernelGGL(meta_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, cu_seqlens, block_tables, batch,
-                     max_blocks, num_blocks, total_tokens, pos, slot, last_pos, last_row);
+  hipLaunchKernelGGL(meta_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, cu_seqlens, ctx_lens, block_tables,
+                     batch, max_blocks, num_blocks, total_tokens, pos, slot, last_pos, last_row);
   return hipGetLastError();
 }
 

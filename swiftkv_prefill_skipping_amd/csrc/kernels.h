@@ -22,20 +22,27 @@ template <int P, class Epi>
 hipError_t launch_gemm_f32(const float* A, int lda, const float* B, int ldb, int M, int N, int K, const Epi& epi,
                            hipStream_t stream);
 
+// Rows one skinny product takes at most.
+constexpr int kSkinnyMaxRows = 32;
+
 // Skinny bf16 product for the last-token path (M <= 32 rows): split-K MFMA
 // partial sums into `partial` [splits, 32, N] fp32, then a finalize pass
 // that reduces them in fixed order and applies the epilogue (pair distance
 // 64).  A is row-major [M, lda]; B [N, K] is in the panel layout with
-// 64-row panels.  Requires K % 256 == 0, N % 128 == 0.
+// panels of panel_rows (kSkinnyPanelRows or kPanelRows) rows.  Requires
+// K % 256 == 0, N % 128 == 0.
 template <class Epi>
-hipError_t launch_skinny_bf16(const bf16_t* A, int lda, const bf16_t* B, int M, int N, int K,
+hipError_t launch_skinny_bf16(const bf16_t* A, int lda, const bf16_t* B, int panel_rows, int M, int N, int K,
                               float* partial, int64_t partial_elems, const Epi& epi, hipStream_t stream);
 int64_t skinny_partial_elems(int N, int K);
 
-// Per-token metadata: pos[t], slot[t], and last_pos[b] = len_b - 1, last_row[b] = cu[b+1] - 1.
-hipError_t launch_meta(const int32_t* cu_seqlens, const int32_t* block_tables, int batch, int max_blocks,
-                       int num_blocks, int total_tokens, int32_t* pos, int32_t* slot, int32_t* last_pos,
-                       int32_t* last_row, hipStream_t stream);
+// Per-token metadata of a batch whose sequence b already holds ctx_b cached
+// positions (ctx_lens NULL: all zero) and brings the tokens cu[b]..cu[b+1]:
+// pos[t] = ctx_b + t - cu[b], slot[t] = its cache slot, and
+// last_pos[b] = ctx_b + len_b - 1, last_row[b] = cu[b+1] - 1.
+hipError_t launch_meta(const int32_t* cu_seqlens, const int32_t* ctx_lens, const int32_t* block_tables, int batch,
+                       int max_blocks, int num_blocks, int total_tokens, int32_t* pos, int32_t* slot,
+                       int32_t* last_pos, int32_t* last_row, hipStream_t stream);
 
 // x[t, :] = E[tok[t], :] as fp32.
 template <typename T>
@@ -58,10 +65,12 @@ hipError_t launch_gather_rows(const float* x, const int32_t* rows_idx, int rows,
 
 // Causal GQA flash attention for prompt tokens (bf16, MFMA): q [T, hq, dh],
 // K/V from one cache slot, o [T, hq * dh] in the panel layout (panel_off with
-// hq * dh columns).  head_dim 128, hq/hkv % 4 == 0.
+// hq * dh columns).  Sequence b's tokens cu[b]..cu[b+1] sit at positions
+// ctx_b.. (ctx_lens NULL: 0) and attend to every cached position up to their
+// own.  max_new = the longest cu run.  head_dim 128, hq/hkv % 4 == 0.
 hipError_t launch_attn_prefill_bf16(const bf16_t* q, CacheSlot<bf16_t> cache, const int32_t* cu_seqlens,
-                                    const int32_t* block_tables, int max_blocks, int batch, int max_seqlen, int hq,
-                                    bf16_t* o, hipStream_t stream);
+                                    const int32_t* ctx_lens, const int32_t* block_tables, int max_blocks, int batch,
+                                    int max_new, int hq, bf16_t* o, hipStream_t stream);
 
 // Attention for a list of query rows, each attending to positions
 // [0, ctx) of its prompt (ctx = pos + 1), split over key chunks with a

@@ -3,9 +3,10 @@
 // kernel is laid out for bandwidth.  Each wave64 owns 64 output columns and
 // one K split; A (activations, tiny and L2 resident) and B (weights) are
 // read 16 bytes per lane straight into v_mfma_f32_16x16x32_bf16 operands.
-// B is stored in 64-row panels of [64][32] blocks, so the wave's 64 columns
-// are one panel and each load instruction (16 rows x 32 k) reads 1 KB of
-// contiguous memory; a wave streams one contiguous run of its panel.
+// B is stored in panels of pr rows (64 for the last-token weights, 256 for
+// the weights the prompt-token GEMMs also read) of [pr][32] blocks; the
+// wave's 64 columns sit in one panel and each load instruction (16 rows x
+// 32 k) reads 1 KB of contiguous memory.
 // Split-K partial sums land in an fp32 buffer [splits, 32, N] and a second
 // pass adds them in fixed split order (deterministic) and applies the
 // epilogue on column pairs (col, col + 64).
@@ -15,7 +16,7 @@
 
 namespace {
 
-constexpr int SK_ROWS = 32;
+constexpr int SK_ROWS = kSkinnyMaxRows;
 
 // U k-steps of 32 per loop trip: all U x 4 weight loads (and the few
 // activation loads) are issued before the MFMAs that consume them, so each
@@ -23,8 +24,8 @@ constexpr int SK_ROWS = 32;
 constexpr int SK_U = 4;
 
 __global__ __launch_bounds__(256) void skinny_partial_kernel(const bf16_t* __restrict__ A, int lda,
-                                                             const bf16_t* __restrict__ B, int K, int M, int N,
-                                                             int kc, float* __restrict__ partial) {
+                                                             const bf16_t* __restrict__ B, int K, int pr, int M,
+                                                             int N, int kc, float* __restrict__ partial) {
   const int lane = threadIdx.x & 63;
   const int cb = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (cb * 64 >= N) return;
@@ -39,9 +40,11 @@ __global__ __launch_bounds__(256) void skinny_partial_kernel(const bf16_t* __res
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0, 0, 0, 0};
 
-  // panel cb, k-block kbeg/32 onwards: block b at + b * 2048, row r at + r * 32
-  constexpr int kBlk = kSkinnyPanelRows * kPanelCols;
-  const bf16_t* bpanel = B + ((int64_t)cb * (K / kPanelCols) + kbeg / kPanelCols) * kBlk;
+  // columns cb*64 .. +64 sit in panel p at rows r0 ..; k-block kb of the
+  // panel starts at (p * K/32 + kb) * pr * 32, row r at + r * 32
+  const int64_t blk = (int64_t)pr * kPanelCols;
+  const int p = cb * 64 / pr, r0 = cb * 64 - p * pr;
+  const bf16_t* bpanel = B + ((int64_t)p * (K / kPanelCols) + kbeg / kPanelCols) * blk + r0 * kPanelCols;
   const bf16_t* bp[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) bp[j] = bpanel + (j * 16 + r16) * kPanelCols + kq;
@@ -54,7 +57,7 @@ __global__ __launch_bounds__(256) void skinny_partial_kernel(const bf16_t* __res
 #pragma unroll
     for (int u = 0; u < SK_U; ++u)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) b[u][j] = *reinterpret_cast<const u32x4_t*>(bp[j] + (int64_t)(k / 32 + u) * kBlk);
+      for (int j = 0; j < 4; ++j) b[u][j] = *reinterpret_cast<const u32x4_t*>(bp[j] + (int64_t)(k / 32 + u) * blk);
 #pragma unroll
     for (int u = 0; u < SK_U; ++u) {
       a0[u] = a0ok ? *reinterpret_cast<const u32x4_t*>(ap0 + k + u * 32) : u32x4_t{0, 0, 0, 0};
@@ -125,15 +128,17 @@ int choose_splits(int N, int K) {
 int64_t skinny_partial_elems(int N, int K) { return (int64_t)choose_splits(N, K) * SK_ROWS * N; }
 
 template <class Epi>
-hipError_t launch_skinny_bf16(const bf16_t* A, int lda, const bf16_t* B, int M, int N, int K,
+hipError_t launch_skinny_bf16(const bf16_t* A, int lda, const bf16_t* B, int panel_rows, int M, int N, int K,
                               float* partial, int64_t partial_elems, const Epi& epi, hipStream_t stream) {
   if (M <= 0) return hipSuccess;
-  if (M > SK_ROWS || K % 256 != 0 || N % 128 != 0) return hipErrorInvalidValue;
+  if (M > SK_ROWS || K % 256 != 0 || N % 128 != 0 || (panel_rows != kSkinnyPanelRows && panel_rows != kPanelRows))
+    return hipErrorInvalidValue;
   const int ns = choose_splits(N, K);
   if ((int64_t)ns * SK_ROWS * N > partial_elems) return hipErrorInvalidValue;
   const int kc = K / ns;
   dim3 grid((N / 64 + 3) / 4, ns);
-  hipLaunchKernelGGL(skinny_partial_kernel, grid, dim3(256), 0, stream, A, lda, B, K, M, N, kc, partial);
+  hipLaunchKernelGGL(skinny_partial_kernel, grid, dim3(256), 0, stream, A, lda, B, K, panel_rows, M, N, kc,
+                     partial);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t work = (int64_t)M * (N / 2);
@@ -142,13 +147,15 @@ hipError_t launch_skinny_bf16(const bf16_t* A, int lda, const bf16_t* B, int M, 
   return hipGetLastError();
 }
 
-template hipError_t launch_skinny_bf16<EpiQKV<bf16_t>>(const bf16_t*, int, const bf16_t*, int, int, int, float*,
+template hipError_t launch_skinny_bf16<EpiQKV<bf16_t>>(const bf16_t*, int, const bf16_t*, int, int, int, int, float*,
                                                        int64_t, const EpiQKV<bf16_t>&, hipStream_t);
-template hipError_t launch_skinny_bf16<EpiResidual>(const bf16_t*, int, const bf16_t*, int, int, int, float*,
+template hipError_t launch_skinny_bf16<EpiResidual>(const bf16_t*, int, const bf16_t*, int, int, int, int, float*,
                                                     int64_t, const EpiResidual&, hipStream_t);
-template hipError_t launch_skinny_bf16<EpiSwiGLU<bf16_t>>(const bf16_t*, int, const bf16_t*, int, int, int,
+template hipError_t launch_skinny_bf16<EpiSwiGLU<bf16_t>>(const bf16_t*, int, const bf16_t*, int, int, int, int,
                                                           float*, int64_t, const EpiSwiGLU<bf16_t>&, hipStream_t);
-template hipError_t launch_skinny_bf16<EpiStoreF32>(const bf16_t*, int, const bf16_t*, int, int, int, float*,
+template hipError_t launch_skinny_bf16<EpiStoreF32>(const bf16_t*, int, const bf16_t*, int, int, int, int, float*,
                                                     int64_t, const EpiStoreF32&, hipStream_t);
-template hipError_t launch_skinny_bf16<EpiStore<bf16_t>>(const bf16_t*, int, const bf16_t*, int, int, int,
+template hipError_t launch_skinny_bf16<EpiKVSkip<bf16_t>>(const bf16_t*, int, const bf16_t*, int, int, int, int,
+                                                          float*, int64_t, const EpiKVSkip<bf16_t>&, hipStream_t);
+template hipError_t launch_skinny_bf16<EpiStore<bf16_t>>(const bf16_t*, int, const bf16_t*, int, int, int, int,
                                                          float*, int64_t, const EpiStore<bf16_t>&, hipStream_t);

@@ -172,3 +172,43 @@ def prefill(model: Model, cache: Cache, db: DeviceBatch, logits=None, stream=Non
     s = stream if stream is not None else torch.cuda.current_stream()
     L.skv_prefill(model.handle, cache.handle, db.struct, logits.data_ptr(), s.cuda_stream)
     return logits
+
+
+@dataclass
+class DeviceStep:
+    """A mixed batch in device memory: new tokens per sequence plus cached lengths."""
+    tokens: DeviceBatch
+    ctx_dev: object
+    ctx_host: np.ndarray
+    struct: L.skv_step_batch
+
+
+def device_step(token_ids, new_lens, ctx_lens, block_tables) -> DeviceStep:
+    """Device copies of a step batch: sequence b brings new_lens[b] of the
+    packed token_ids after ctx_lens[b] cached positions; block_tables [B, m]."""
+    torch = _torch()
+    new_lens = np.asarray(new_lens, dtype=np.int32)
+    cu = np.zeros(len(new_lens) + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(new_lens)
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    ctx = np.ascontiguousarray(ctx_lens, dtype=np.int32)
+    tok = torch.as_tensor(np.asarray(token_ids, dtype=np.int32)).cuda()
+    cu_d = torch.as_tensor(cu).cuda()
+    bt_d = torch.as_tensor(bt.reshape(-1)).cuda()
+    ctx_d = torch.as_tensor(ctx).cuda()
+    inner = L.skv_batch(len(new_lens), int(cu[-1]), int(new_lens.max()), bt.shape[1], cu.ctypes.data, bt.ctypes.data,
+                        tok.data_ptr(), cu_d.data_ptr(), bt_d.data_ptr())
+    db = DeviceBatch(None, tok, cu_d, bt_d, cu, bt, inner)
+    st = L.skv_step_batch(inner, ctx.ctypes.data, ctx_d.data_ptr())
+    return DeviceStep(db, ctx_d, ctx, st)
+
+
+def step(model: Model, cache: Cache, ds: DeviceStep, logits=None, stream=None):
+    """Enqueue skv_step on `stream` (torch stream; default = current) and return the logits tensor."""
+    torch = _torch()
+    B = ds.struct.tokens.batch
+    if logits is None:
+        logits = torch.empty((B, model.cfg.vocab), dtype=torch.float32, device="cuda")
+    s = stream if stream is not None else torch.cuda.current_stream()
+    L.skv_step(model.handle, cache.handle, ds.struct, logits.data_ptr(), s.cuda_stream)
+    return logits

@@ -1,0 +1,147 @@
+"""Mixed-batch steps on the GPU (skv_step) against the oracle's swiftkv_step.
+
+A schedule is a list of calls; each call brings, for some sequences, their
+next n tokens after what earlier calls cached (a prompt chunk, a whole
+prompt, or a single decode token).  The GPU and the oracle run the same
+schedule in lockstep; every call's logits rows and, at the end, every KV
+slot of every sequence (all positions) are compared with the parity metric
+max |gpu - oracle| / max |oracle|: 1e-4 for fp32 models, 2e-2 for bf16.
+
+Batches of at most 32 new tokens (bf16) take the row path through layers
+1..l; larger ones the tiled GEMMs and the MFMA attention with cached
+prefixes.  The schedules below exercise both, chunk starts that are not
+multiples of the 16-token block or the 64-key tile, single-token rows inside
+large batches, and AcrossKV / l = 0 / l = L.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import skv_inputs as si
+from oracle import swiftkv_oracle as O
+from tests.helpers import CachedLayers, dims_of, max_rel, oracle_weights
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"fp32": 1e-4, "bf16": 2e-2}
+
+
+def _say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def run_schedule(w, final_lengths, schedule, shuffle=True, label=""):
+    import torch
+    from swiftkv_prefill_skipping_amd import runner
+    from tests.test_gpu_parity import gpu_kv
+    batch = si.make_batch(w, lengths=list(final_lengths), shuffle=shuffle)
+    B = len(final_lengths)
+    max_new = max(sum(n for _, n in call) for call in schedule)
+    cached = CachedLayers()
+    model = runner.load_seeded_model(w, max_new, max(len(c) for c in schedule), int(max(final_lengths)),
+                                     layer_hook=cached.hook)
+    cache = runner.Cache(model, batch.num_blocks)
+    W = oracle_weights(w, cached)
+    dims = dims_of(w.shape)
+    tol = TOL[w.dtype]
+    ctx = [0] * B
+    past = [{} for _ in range(B)]
+    worst = 0.0
+    for ci, call in enumerate(schedule):
+        seqs = [s for s, _ in call]
+        runs = [batch.tokens[s][ctx[s]:ctx[s] + n] for s, n in call]
+        assert all(len(r) == n for r, (_, n) in zip(runs, call)), "schedule runs past a prompt"
+        _say(f"[step] {label} call {ci}: " + ", ".join(f"seq {s} ctx {ctx[s]} +{n}" for s, n in call))
+        ds = runner.device_step(np.concatenate(runs), [n for _, n in call], [ctx[s] for s in seqs],
+                                batch.block_tables[seqs])
+        lg = runner.step(model, cache, ds)
+        torch.cuda.synchronize()
+        lg = lg.cpu().numpy()
+        r = O.swiftkv_step(dims, W, [past[s] for s in seqs], runs, w.swiftkv_l, w.acrosskv_g)
+        for i, (s, n) in enumerate(call):
+            e = max_rel(lg[i], r.logits[i])
+            worst = max(worst, e)
+            assert e < tol, f"{label} call {ci} seq {s} logits: {e:.3e}"
+            past[s] = r.kv[i]
+            ctx[s] += n
+    assert ctx == [int(n) for n in final_lengths], "schedule must cover every prompt"
+    for b in range(B):
+        gkv = gpu_kv(cache, w, batch, b)
+        assert set(gkv) == set(past[b])
+        for s in gkv:
+            for t, name in ((0, "K"), (1, "V")):
+                e = max_rel(gkv[s][t], past[b][s][t])
+                worst = max(worst, e)
+                assert e < tol, f"{label} seq {b} slot {s} {name}: {e:.3e}"
+    _say(f"[step] {label}: worst max-rel error {worst:.3e} (bar {tol})")
+    return model, cache
+
+
+def test_chunked_prefill_large_batches_bf16():
+    """Chunks of 40..150 tokens after cached prefixes of 0, 40, 100, 101 and 251 positions (tiled path), with a
+    single-token row and a fresh prompt riding in one batch."""
+    w = si.small_workload("step_chunks", l=2, g=1, lengths=(300, 77, 5), seed=41)
+    sched = [[(0, 100), (1, 40)],
+             [(0, 1), (1, 37), (2, 5)],
+             [(0, 150)],
+             [(0, 49)]]
+    run_schedule(w, (300, 77, 5), sched, label="chunks")
+
+
+@pytest.mark.parametrize("l,g", [(2, 1), (1, 2), (0, 1), (4, 1)], ids=["l2", "l1_g2", "l0", "lL"])
+def test_decode_steps_bf16(l, g):
+    """A prefill, then five decode steps of one token per sequence (row path through layers 1..l)."""
+    w = si.small_workload(f"step_decode_{l}_{g}", l=l, g=g, lengths=(205, 134, 69), seed=43)
+    sched = [[(0, 200), (1, 129), (2, 64)]] + [[(0, 1), (1, 1), (2, 1)]] * 5
+    run_schedule(w, (205, 134, 69), sched, label=f"decode l={l} g={g}")
+
+
+def test_row_path_chunks_and_decode_bf16():
+    """Small mixed batches: a 20-token chunk with two decode tokens, a 32-token chunk (the largest row-path batch),
+    then 33 tokens (the smallest tiled batch) after a cached prefix."""
+    w = si.small_workload("step_rows", l=2, g=1, lengths=(135, 81, 34), seed=47)
+    sched = [[(0, 50), (1, 80), (2, 33)],
+             [(0, 20), (1, 1), (2, 1)],
+             [(0, 32)],
+             [(0, 33)]]
+    run_schedule(w, (135, 81, 34), sched, label="rows")
+
+
+def test_chunks_and_decode_fp32():
+    w = si.small_workload("step_fp32", n_layers=5, d_model=128, n_q_heads=4, n_kv_heads=2, head_dim=32, ffn_dim=176,
+                          vocab=512, dtype="fp32", l=2, g=2, lengths=(90, 41), seed=49)
+    sched = [[(0, 30), (1, 40)],
+             [(0, 55), (1, 1)],
+             [(0, 1)],
+             [(0, 4)]]
+    run_schedule(w, (90, 41), sched, label="fp32")
+
+
+def test_step_host_side_errors():
+    import torch
+    from swiftkv_prefill_skipping_amd import _lib as L, runner
+    w = si.small_workload("step_errs", l=1, g=1, lengths=(40, 20), seed=53)
+    batch = si.make_batch(w)
+    model = runner.load_seeded_model(w, 64, 2, 48)
+    cache = runner.Cache(model, batch.num_blocks)
+    logits = torch.empty((2, w.shape.vocab), dtype=torch.float32, device="cuda")
+    toks = np.zeros(2, dtype=np.int32)
+
+    def call(ctx, bt=batch.block_tables):
+        ds = runner.device_step(toks, [1, 1], ctx, bt)
+        L.skv_step(model.handle, cache.handle, ds.struct, logits.data_ptr(), 0)
+        return ds
+
+    with pytest.raises(L.SkvError):
+        call([48, 0])                          # position 48 is past max_seqlen 48
+    with pytest.raises(L.SkvError):
+        call([-1, 0])                          # negative cached length
+    with pytest.raises(L.SkvError):
+        call([0, 32])                          # sequence 1 would need a third block; its table has two
+    ds = runner.device_step(toks, [1, 1], [3, 3], batch.block_tables)
+    half = L.skv_step_batch(ds.struct.tokens, ds.ctx_host.ctypes.data, 0)
+    with pytest.raises(L.SkvError):            # only one of the two ctx arrays
+        L.skv_step(model.handle, cache.handle, half, logits.data_ptr(), 0)
+    call([3, 3])                               # a good call still works
+    torch.cuda.synchronize()
