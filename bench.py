@@ -132,6 +132,47 @@ def time_calls(fn, steps, warmup, stream):
     return e0.elapsed_time(e1) / steps
 
 
+def measure_decode(model, cache, w, batch, extra, logits, stream, args):
+    """One decode token per prompt at position N_b (context N_b + 1), the same step repeated."""
+    import skv_inputs as si
+    from swiftkv_prefill_skipping_amd import runner
+    B = len(batch.lengths)
+    dbt = decode_tables(batch, extra)
+    nxt = si.randint(w.input_seed, 7, B, w.shape.vocab)
+    ds = runner.device_step(nxt, [1] * B, batch.lengths, dbt)
+    ms_dec = time_calls(lambda: runner.step(model, cache, ds, logits, stream), args.steps, args.warmup, stream)
+    by = decode_bytes(model.cfg, batch.lengths)
+    log(f"[bench] decode step ({B} tokens): {ms_dec:.3f} ms")
+    return {"tokens": B, "context_tokens": int(sum(batch.lengths)) + B, "ms_per_step": round(ms_dec, 4),
+            "tokens_per_s": round(B / (ms_dec / 1e3), 1), "bound": "hbm", "algorithmic_bytes": by,
+            "achieved_GBs": round(by / (ms_dec / 1e3) / 1e9, 1), "peak_GBs": MI355X_HBM_GBS,
+            "frac": round(by / (ms_dec / 1e3) / 1e9 / MI355X_HBM_GBS, 4)}
+
+
+def measure_chunked(model, cache, w, batch, stream, args, ms_one_shot, swift_flops, chunk=256):
+    """The batch's prompts prefilled through skv_step, at most `chunk` tokens per prompt per call."""
+    import torch
+    from swiftkv_prefill_skipping_amd import runner
+    B, T = len(batch.lengths), batch.total_tokens
+    calls, ctx = [], np.zeros(B, dtype=np.int64)
+    while (ctx < batch.lengths).any():
+        live = [b for b in range(B) if ctx[b] < batch.lengths[b]]
+        ns = [int(min(chunk, batch.lengths[b] - ctx[b])) for b in live]
+        toks = np.concatenate([batch.tokens[b][ctx[b]:ctx[b] + n] for b, n in zip(live, ns)])
+        calls.append(runner.device_step(toks, ns, ctx[live], batch.block_tables[live]))
+        ctx[live] += ns
+    lgc = [torch.empty((c.struct.tokens.batch, w.shape.vocab), dtype=torch.float32, device="cuda") for c in calls]
+
+    def chunked():
+        for c, lg in zip(calls, lgc):
+            runner.step(model, cache, c, lg, stream)
+    ms_ch = time_calls(chunked, args.steps, args.warmup, stream)
+    log(f"[bench] chunked prefill ({len(calls)} calls of <= {chunk} tokens per prompt): {ms_ch:.3f} ms")
+    return {"chunk_tokens_per_prompt": chunk, "calls": len(calls), "ms_per_prefill": round(ms_ch, 4),
+            "tokens_per_s": round(T / (ms_ch / 1e3), 1), "time_vs_one_shot": round(ms_ch / ms_one_shot, 4),
+            "actual_tflops": round(swift_flops / (ms_ch / 1e3) / 1e12, 2)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -143,6 +184,8 @@ def main():
                     help="skip timing the same batch through all layers (l = L) with the same kernels")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip timing a decode step and a chunked prefill over the same prompts")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="only time decode steps (for kernel traces of the decode path)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 3 fp32 device copies of MIB MiB each (reference for FETCH_SIZE/WRITE_SIZE)")
     args = ap.parse_args()
@@ -173,6 +216,12 @@ def main():
     db = runner.device_batch(batch)
     logits = torch.empty((B, w.shape.vocab), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
+
+    if args.decode_only:
+        # decode steps alone, over the cache as created (zero K/V: the same work as after a prefill)
+        print(json.dumps({"workload": w.name, "decode_step": measure_decode(model, cache, w, batch, extra, logits,
+                                                                            stream, args)}), flush=True)
+        return
 
     for i in range(args.warmup):
         runner.prefill(model, cache, db, logits, stream)
@@ -238,39 +287,9 @@ def main():
                      "flops_per_launch": flops_per_launch},
     }
     if not args.no_decode and w.dtype == "bf16":
-        # one decode token per prompt right after its prefill (positions N_b, context N_b + 1), the same step
-        # repeated; then the same prompts prefilled as chunks of at most 256 tokens per prompt per call
         runner.prefill(model, cache, db, logits, stream)
-        dbt = decode_tables(batch, extra)
-        nxt = si.randint(w.input_seed, 7, B, w.shape.vocab)
-        ds = runner.device_step(nxt, [1] * B, batch.lengths, dbt)
-        ms_dec = time_calls(lambda: runner.step(model, cache, ds, logits, stream), args.steps, args.warmup, stream)
-        by = decode_bytes(model.cfg, batch.lengths)
-        log(f"[bench] decode step ({B} tokens): {ms_dec:.3f} ms")
-        res["decode_step"] = {
-            "tokens": B, "context_tokens": int(sum(batch.lengths)) + B, "ms_per_step": round(ms_dec, 4),
-            "tokens_per_s": round(B / (ms_dec / 1e3), 1), "bound": "hbm",
-            "algorithmic_bytes": by, "achieved_GBs": round(by / (ms_dec / 1e3) / 1e9, 1),
-            "peak_GBs": MI355X_HBM_GBS, "frac": round(by / (ms_dec / 1e3) / 1e9 / MI355X_HBM_GBS, 4)}
-        chunk = 256
-        calls, ctx = [], np.zeros(B, dtype=np.int64)
-        while (ctx < batch.lengths).any():
-            live = [b for b in range(B) if ctx[b] < batch.lengths[b]]
-            ns = [int(min(chunk, batch.lengths[b] - ctx[b])) for b in live]
-            toks = np.concatenate([batch.tokens[b][ctx[b]:ctx[b] + n] for b, n in zip(live, ns)])
-            calls.append((runner.device_step(toks, ns, ctx[live], batch.block_tables[live]), len(live)))
-            ctx[live] += ns
-        lgc = [torch.empty((nl, w.shape.vocab), dtype=torch.float32, device="cuda") for _, nl in calls]
-
-        def chunked():
-            for (dsc, _), lg in zip(calls, lgc):
-                runner.step(model, cache, dsc, lg, stream)
-        ms_ch = time_calls(chunked, args.steps, args.warmup, stream)
-        log(f"[bench] chunked prefill ({len(calls)} calls of <= {chunk} tokens per prompt): {ms_ch:.3f} ms")
-        res["chunked_prefill"] = {
-            "chunk_tokens_per_prompt": chunk, "calls": len(calls), "ms_per_prefill": round(ms_ch, 4),
-            "tokens_per_s": round(T / (ms_ch / 1e3), 1), "time_vs_one_shot": round(ms_ch / ms, 4),
-            "actual_tflops": round(swift / (ms_ch / 1e3) / 1e12, 2)}
+        res["decode_step"] = measure_decode(model, cache, w, batch, extra, logits, stream, args)
+        res["chunked_prefill"] = measure_chunked(model, cache, w, batch, stream, args, ms, swift)
     if not args.no_full_depth and w.swiftkv_l < w.shape.n_layers:
         # the unmodified model (every layer for every prompt token), same weights, batch and kernels: the
         # wall-clock ratio to compare with the FLOP ratio
