@@ -220,12 +220,81 @@ def mlp_residual(x: np.ndarray, W: Dict[str, np.ndarray], dims: Dims, fc: Option
 
 
 def decoder_layer(x: np.ndarray, W: Dict[str, np.ndarray], pos: np.ndarray, dims: Dims,
-                  fc: Optional[FlopCounter], store: Callable = _keep):
-    """Standard pre-norm layer over all n positions of one prompt.  Returns (x_next, K, V)."""
+                  fc: Optional[FlopCounter], store: Callable = _keep, kv_cache: Callable = _keep):
+    """Standard pre-norm layer over all n positions of one prompt.  Returns (x_next, K, V).
+
+    ``kv_cache`` maps K and V to what the cache holds (identity, or the FP8
+    round trip); attention reads the cached values."""
     q, k, v = qkv_projection(x, W, pos, dims, fc, store)
+    k, v = kv_cache(k), kv_cache(v)
     o = store(causal_gqa_attention(q, k, v, fc))
     x = x + matmul_wt(o, W["wo"], fc)
     return mlp_residual(x, W, dims, fc, store), k, v
+
+
+# ----------------------------------------------------------------------------
+# FP8 KV cache (per-token scale), [S] "Complementarity with KV quantization"
+# (Appendix B.1, Table B.1)
+# ----------------------------------------------------------------------------
+
+E4M3_MAX = 448.0
+
+
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    """Value of OCP FP8 E4M3 codes (sign, 4 exponent bits with bias 7, 3
+    mantissa bits; exponent 0 is subnormal, m * 2^-9; no infinities;
+    S.1111.111 is NaN) as float32."""
+    c = np.asarray(codes).astype(np.int64)
+    e = (c >> 3) & 15
+    m = (c & 7).astype(np.float64)
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * 2.0 ** (e - 7))
+    mag = np.where((c & 0x7F) == 0x7F, np.nan, mag)
+    return np.where(c & 0x80, -mag, mag).astype(np.float32)
+
+
+def e4m3_encode(y: np.ndarray) -> np.ndarray:
+    """E4M3 code nearest to each float32 value, ties to even; |y| <= 448."""
+    y = np.asarray(y, dtype=np.float32)
+    a = np.abs(y).astype(np.float64)                 # exact
+    if np.any(a > E4M3_MAX):
+        raise ValueError("value outside the E4M3 range")
+    sub = np.rint(a * 512.0)                          # subnormal step 2^-9; 8 = the smallest normal's code
+    mant, ex = np.frexp(a)                            # a = mant * 2^ex, mant in [0.5, 1)
+    e = ex - 1                                        # a = (2 mant) 2^e
+    m = np.rint((2.0 * mant - 1.0) * 8.0)             # exact products; rint rounds ties to even
+    up = m == 8
+    e = np.where(up, e + 1, e)
+    m = np.where(up, 0, m)
+    normal = (e + 7) * 8 + m
+    code = np.where(a < 2.0 ** -6, sub, normal).astype(np.int64)
+    return (code | np.where(np.signbit(y), 0x80, 0)).astype(np.uint8)
+
+
+def fp8_quantize_rows(x: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Per-token FP8: each row (one token's K or V over all kv heads) gets
+    scale = max|row| / 448 and codes = E4M3(row * (1 / scale)), every step a
+    single float32 operation (division, reciprocal, product, clamp to +-448),
+    so the code decisions are those of float32 arithmetic.  A zero row has
+    scale 0 and zero codes."""
+    x = np.asarray(x, dtype=np.float32)
+    amax = np.max(np.abs(x), axis=1)
+    scale = amax / np.float32(E4M3_MAX)
+    inv = np.where(scale > 0, np.float32(1.0) / np.where(scale > 0, scale, np.float32(1.0)), np.float32(0.0))
+    y = np.clip(x * inv.astype(np.float32)[:, None], -E4M3_MAX, E4M3_MAX).astype(np.float32)
+    return e4m3_encode(y), scale.astype(np.float32)
+
+
+def fp8_dequantize_rows(codes: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    """codes * scale per row, float32."""
+    return (e4m3_decode(codes) * np.asarray(scale, dtype=np.float32)[:, None]).astype(np.float32)
+
+
+def fp8_kv_roundtrip(t: np.ndarray) -> np.ndarray:
+    """What a per-token FP8 cache hands back for K or V [n, hkv, dh]."""
+    n = t.shape[0]
+    flat = np.asarray(t, dtype=np.float32).reshape(n, -1)
+    c, sc = fp8_quantize_rows(flat)
+    return fp8_dequantize_rows(c, sc).reshape(t.shape).astype(t.dtype)
 
 
 # ----------------------------------------------------------------------------
@@ -304,7 +373,7 @@ class OracleResult:
 
 
 def swiftkv_prefill(dims: Dims, weights: WeightSource, prompts: Sequence[np.ndarray], l: int, g: int = 1,
-                    dtype=np.float32, store: Optional[Callable] = None) -> OracleResult:
+                    dtype=np.float32, store: Optional[Callable] = None, kv_fp8: bool = False) -> OracleResult:
     """SwiftKV prefill of a batch of independent prompts (steps 1-5 of the module docstring).
 
     Layers are visited in increasing order exactly once (layer-major), so a
@@ -316,8 +385,12 @@ def swiftkv_prefill(dims: Dims, weights: WeightSource, prompts: Sequence[np.ndar
     output.  With a bf16 rounding function this evaluates the same definition
     with bf16 storage (the precision the pages serve in), which measures how
     far bf16 storage alone moves each output from the plain evaluation.
+
+    ``kv_fp8``: the cache holds per-token FP8 K and V (fp8_kv_roundtrip);
+    every attention reads those values and ``kv`` returns them.
     """
     st = store if store is not None else _keep
+    kq = fp8_kv_roundtrip if kv_fp8 else _keep
     L = dims.n_layers
     if not 0 <= l <= L:
         raise ValueError(f"swiftkv l={l} outside 0..{L}")
@@ -334,7 +407,7 @@ def swiftkv_prefill(dims: Dims, weights: WeightSource, prompts: Sequence[np.ndar
     for i in range(1, l + 1):                                                     # step 2
         W = weights.layer(i)
         for b in range(len(prompts)):
-            xs[b], k, v = decoder_layer(xs[b], W, pos[b], dims, fc, st)
+            xs[b], k, v = decoder_layer(xs[b], W, pos[b], dims, fc, st, kq)
             kv[b][i - 1] = (k, v)
 
     ys = [x[-1:].copy() for x in xs]                                              # last token rows
@@ -347,7 +420,7 @@ def swiftkv_prefill(dims: Dims, weights: WeightSource, prompts: Sequence[np.ndar
                 a = st(rmsnorm(xs[b], W["attn_norm"], eps))
                 k = matmul_wt(a, W["wk"], fc).reshape(n, dims.n_kv_heads, dims.head_dim)
                 v = matmul_wt(a, W["wv"], fc).reshape(n, dims.n_kv_heads, dims.head_dim)
-                kv[b][s] = (st(rope(k, pos[b], dims.rope_theta)), st(v))
+                kv[b][s] = (kq(st(rope(k, pos[b], dims.rope_theta))), kq(st(v)))
         for b in range(len(prompts)):                                             # step 4
             n = xs[b].shape[0]
             K, V = kv[b][s]
@@ -393,7 +466,8 @@ class StepResult:
 
 
 def swiftkv_step(dims: Dims, weights: WeightSource, past: Sequence[Dict[int, Tuple[np.ndarray, np.ndarray]]],
-                 new_tokens: Sequence[np.ndarray], l: int, g: int = 1, dtype=np.float32) -> StepResult:
+                 new_tokens: Sequence[np.ndarray], l: int, g: int = 1, dtype=np.float32,
+                 kv_fp8: bool = False) -> StepResult:
     """One forward pass over a mixed batch of prompt chunks and decode tokens.
 
     Source: [P1] "Inference Implementation in Production Serving Frameworks"
@@ -409,9 +483,12 @@ def swiftkv_step(dims: Dims, weights: WeightSource, past: Sequence[Dict[int, Tup
     positions 0..C_b-1 (an empty dict: C_b = 0); ``new_tokens[b]`` are its
     new tokens at positions C_b, C_b+1, ...  Returns the extended caches
     (new arrays; ``past`` is not modified) and the logits after each
-    sequence's last new token.
+    sequence's last new token.  ``kv_fp8``: the cache holds per-token FP8
+    values (fp8_kv_roundtrip of each new token's K and V); ``past`` then
+    holds such values too.
     """
     L, eps = dims.n_layers, dims.rms_eps
+    kq = fp8_kv_roundtrip if kv_fp8 else _keep
     if not 0 <= l <= L or g < 1:
         raise ValueError("bad l or g")
     if len(past) != len(new_tokens) or any(len(t) < 1 for t in new_tokens):
@@ -431,8 +508,8 @@ def swiftkv_step(dims: Dims, weights: WeightSource, past: Sequence[Dict[int, Tup
         W = weights.layer(i)
         for b in range(len(past)):
             q, k, v = qkv_projection(xs[b], W, pos[b], dims, fc)
-            K = np.concatenate([kv[b][i - 1][0], k], axis=0)
-            V = np.concatenate([kv[b][i - 1][1], v], axis=0)
+            K = np.concatenate([kv[b][i - 1][0], kq(k)], axis=0)
+            V = np.concatenate([kv[b][i - 1][1], kq(v)], axis=0)
             kv[b][i - 1] = (K, V)
             x = xs[b] + matmul_wt(attention_with_past(q, K, V, pos[b], fc), W["wo"], fc)
             xs[b] = mlp_residual(x, W, dims, fc)
@@ -447,8 +524,8 @@ def swiftkv_step(dims: Dims, weights: WeightSource, past: Sequence[Dict[int, Tup
                 a = rmsnorm(xs[b], W["attn_norm"], eps)
                 k = matmul_wt(a, W["wk"], fc).reshape(n, dims.n_kv_heads, dims.head_dim)
                 v = matmul_wt(a, W["wv"], fc).reshape(n, dims.n_kv_heads, dims.head_dim)
-                kv[b][s] = (np.concatenate([kv[b][s][0], rope(k, pos[b], dims.rope_theta)], axis=0),
-                            np.concatenate([kv[b][s][1], v], axis=0))
+                kv[b][s] = (np.concatenate([kv[b][s][0], kq(rope(k, pos[b], dims.rope_theta))], axis=0),
+                            np.concatenate([kv[b][s][1], kq(v)], axis=0))
         for b in range(len(past)):                 # the continuing token
             K, V = kv[b][s]
             p_last = int(pos[b][-1])
@@ -555,6 +632,9 @@ def per_token_breakdown(dims: Dims, l: int, g: int, attn_per_layer_flops: float 
     }
 
 
-def kv_memory_fraction(L: int, l: int, g: int) -> float:
-    """KV memory relative to the unmodified model: (l + (L-l)/g) / L (AcrossKV memory formula)."""
-    return kv_slots(L, l, g) / L
+def kv_memory_fraction(L: int, l: int, g: int, kv_bits: int = 16) -> float:
+    """KV memory relative to the unmodified model with a 16-bit cache:
+    (l + (L-l)/g) / L (AcrossKV memory formula) times kv_bits / 16 (an FP8
+    cache halves every entry; the per-token scales are not counted, as in
+    the pages' figures)."""
+    return kv_slots(L, l, g) / L * kv_bits / 16
