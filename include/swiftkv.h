@@ -46,7 +46,19 @@ typedef enum {
   SKV_ERR_UNSUPPORTED = -4  /* valid but not implemented for this shape/dtype */
 } skv_status;
 
-typedef enum { SKV_BF16 = 0, SKV_FP32 = 1 } skv_dtype;
+typedef enum { SKV_BF16 = 0, SKV_FP32 = 1, SKV_FP8_E4M3 = 2 /* cache views only */ } skv_dtype;
+
+/* What the KV cache stores (Appendix B.1 / Table B.1: AcrossKV combined
+ * with a per-token FP8 KV cache).
+ * SKV_KV_MODEL: K/V in the model dtype.
+ * SKV_KV_FP8: OCP FP8 E4M3 codes (bias 7, largest finite value 448) plus
+ * one fp32 scale per token position, per KV slot, for K and V separately:
+ * scale = max|x| / 448 over the token's K (or V) row across all kv heads,
+ * code = E4M3 round-to-nearest-even of x * (1 / scale) clamped to +-448
+ * (each step one fp32 operation); the cached value is code * scale.  Every
+ * attention (prompt tokens and last tokens alike) reads the cached values.
+ * bf16 models only, n_kv_heads * head_dim <= 1024. */
+typedef enum { SKV_KV_MODEL = 0, SKV_KV_FP8 = 1 } skv_kv_dtype;
 
 /* Model description.  The transformation is the one of section 3.4:
  * swiftkv_l = number of layers every prompt token runs (0..n_layers;
@@ -68,6 +80,7 @@ typedef struct {
   int32_t acrosskv_g;
   int32_t dtype; /* skv_dtype */
   int32_t max_tokens, max_batch, max_seqlen;
+  int32_t kv_dtype; /* skv_kv_dtype */
 } skv_model_config;
 
 typedef struct skv_model skv_model;
@@ -124,11 +137,19 @@ typedef struct {
 
 /* K and V of layer `layer` (1-based).  Layers of one AcrossKV group return
  * the same memory.  Layout of both: [num_blocks, n_kv_heads, block_size,
- * head_dim].  Token position p of a prompt with block table row bt lives in
+ * head_dim]; dtype = the model's, or SKV_FP8_E4M3 (codes) with an FP8
+ * cache.  Token position p of a prompt with block table row bt lives in
  * block bt[p / block_size] at offset p % block_size.  K holds RoPE-rotated
  * keys.  Positions of a prompt's last block beyond its length keep whatever
  * they held (zero after creation); they must stay finite. */
 skv_status skv_kv_cache_view(const skv_kv_cache* c, int32_t layer, skv_tensor_view* k, skv_tensor_view* v);
+
+/* Per-token scales of layer `layer`'s K and V in an FP8 cache: fp32
+ * [num_blocks, block_size], position p at [bt[p / block_size], p %
+ * block_size]; the value of a K element is its code's E4M3 value times the
+ * K scale of its position.  INVALID_ARG if the cache is not FP8. */
+skv_status skv_kv_cache_scales(const skv_kv_cache* c, int32_t layer, skv_tensor_view* k_scale,
+                               skv_tensor_view* v_scale);
 
 /* A batch of independent prompts packed back to back (varlen).
  * cu_seqlens[b]..cu_seqlens[b+1] are prompt b's tokens; every prompt has at

@@ -289,10 +289,21 @@ def fp8_dequantize_rows(codes: np.ndarray, scale: np.ndarray) -> np.ndarray:
     return (e4m3_decode(codes) * np.asarray(scale, dtype=np.float32)[:, None]).astype(np.float32)
 
 
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    """float32 values rounded to the nearest bfloat16 (ties to even), returned as float32."""
+    b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = ((b + 0x7FFF + ((b >> 16) & 1)) & 0xFFFF0000).astype(np.uint32)
+    return r.view(np.float32).reshape(np.shape(x))
+
+
 def fp8_kv_roundtrip(t: np.ndarray) -> np.ndarray:
-    """What a per-token FP8 cache hands back for K or V [n, hkv, dh]."""
+    """What a per-token FP8 cache hands back for K or V [n, hkv, dh].
+
+    The quantiser takes the values a bf16 inference path holds (the pages
+    serve in bf16), so each K/V value is rounded to bf16 first; the code
+    decisions are then float32 arithmetic on bf16 inputs."""
     n = t.shape[0]
-    flat = np.asarray(t, dtype=np.float32).reshape(n, -1)
+    flat = bf16_round(np.asarray(t, dtype=np.float32).reshape(n, -1))
     c, sc = fp8_quantize_rows(flat)
     return fp8_dequantize_rows(c, sc).reshape(t.shape).astype(t.dtype)
 

@@ -13,7 +13,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libswiftkv.so")
 
 SKV_OK, SKV_ERR_INVALID_ARG, SKV_ERR_OOM, SKV_ERR_HIP, SKV_ERR_UNSUPPORTED = 0, -1, -2, -3, -4
-SKV_BF16, SKV_FP32 = 0, 1
+SKV_BF16, SKV_FP32, SKV_FP8_E4M3 = 0, 1, 2
+SKV_KV_MODEL, SKV_KV_FP8 = 0, 1
 (SKV_K_GEMM_QKV, SKV_K_ATTN_PREFILL, SKV_K_GEMM_O, SKV_K_GEMM_GATEUP, SKV_K_GEMM_DOWN, SKV_K_GEMM_KVSKIP,
  SKV_K_RMSNORM, SKV_K_LAST_TOKEN) = range(8)
 KERNEL_CLASS_NAMES = ["gemm_qkv", "attn_prefill", "gemm_o", "gemm_gateup", "gemm_down", "gemm_kvskip", "rmsnorm",
@@ -24,7 +25,7 @@ class skv_model_config(Structure):
     _fields_ = [("n_layers", c_int32), ("d_model", c_int32), ("n_q_heads", c_int32), ("n_kv_heads", c_int32),
                 ("head_dim", c_int32), ("ffn_dim", c_int32), ("vocab", c_int32), ("rope_theta", c_float),
                 ("rms_eps", c_float), ("swiftkv_l", c_int32), ("acrosskv_g", c_int32), ("dtype", c_int32),
-                ("max_tokens", c_int32), ("max_batch", c_int32), ("max_seqlen", c_int32)]
+                ("max_tokens", c_int32), ("max_batch", c_int32), ("max_seqlen", c_int32), ("kv_dtype", c_int32)]
 
 
 class skv_layer_weights(Structure):
@@ -48,7 +49,7 @@ class skv_step_batch(Structure):
 
 
 EXPORTED = ["skv_model_create", "skv_model_load_globals", "skv_model_load_layer", "skv_model_destroy",
-            "skv_kv_cache_create", "skv_kv_cache_destroy", "skv_num_kv_slots", "skv_kv_cache_view", "skv_prefill",
+            "skv_kv_cache_create", "skv_kv_cache_destroy", "skv_num_kv_slots", "skv_kv_cache_view", "skv_kv_cache_scales", "skv_prefill",
             "skv_step",
             "skv_flops", "skv_profile_enable", "skv_profile_read", "skv_last_error"]
 
@@ -80,6 +81,7 @@ def lib():
         L.skv_num_kv_slots.argtypes = [vp]
         L.skv_num_kv_slots.restype = c_int32
         L.skv_kv_cache_view.argtypes = [vp, c_int32, POINTER(skv_tensor_view), POINTER(skv_tensor_view)]
+        L.skv_kv_cache_scales.argtypes = [vp, c_int32, POINTER(skv_tensor_view), POINTER(skv_tensor_view)]
         L.skv_prefill.argtypes = [vp, vp, POINTER(skv_batch), vp, vp]
         L.skv_step.argtypes = [vp, vp, POINTER(skv_step_batch), vp, vp]
         L.skv_flops.argtypes = [POINTER(skv_model_config), vp, c_int32, POINTER(c_double), POINTER(c_double)]
@@ -110,9 +112,9 @@ def _ptr(a) -> int:
 
 
 def make_config(n_layers, d_model, n_q_heads, n_kv_heads, head_dim, ffn_dim, vocab, rope_theta, rms_eps, swiftkv_l,
-                acrosskv_g, dtype, max_tokens, max_batch, max_seqlen) -> skv_model_config:
+                acrosskv_g, dtype, max_tokens, max_batch, max_seqlen, kv_dtype=SKV_KV_MODEL) -> skv_model_config:
     return skv_model_config(n_layers, d_model, n_q_heads, n_kv_heads, head_dim, ffn_dim, vocab, rope_theta, rms_eps,
-                            swiftkv_l, acrosskv_g, dtype, max_tokens, max_batch, max_seqlen)
+                            swiftkv_l, acrosskv_g, dtype, max_tokens, max_batch, max_seqlen, kv_dtype)
 
 
 def skv_model_create(cfg: skv_model_config) -> int:
@@ -151,6 +153,12 @@ def skv_num_kv_slots(model: int) -> int:
 def skv_kv_cache_view(cache: int, layer: int):
     k, v = skv_tensor_view(), skv_tensor_view()
     check(lib().skv_kv_cache_view(cache, layer, ctypes.byref(k), ctypes.byref(v)))
+    return k, v
+
+
+def skv_kv_cache_scales(cache: int, layer: int):
+    k, v = skv_tensor_view(), skv_tensor_view()
+    check(lib().skv_kv_cache_scales(cache, layer, ctypes.byref(k), ctypes.byref(v)))
     return k, v
 
 

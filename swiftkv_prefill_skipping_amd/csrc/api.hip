@@ -88,6 +88,13 @@ struct skv_model {
   int32_t* last_pos = nullptr;
   int32_t* last_row = nullptr;
   int32_t* iota = nullptr;
+  // FP8 KV cache: new K/V rows (bf16) staged in the cache layout with the
+  // token index as physical slot, then quantised into the cache
+  bool kv8 = false;
+  bf16_t* kv_stage = nullptr;
+  int64_t stage_group = 0;  // elements per group (K then V)
+  int64_t stage_v = 0;      // offset of V within a group
+  int32_t* tok_iota = nullptr;
   float* y = nullptr;
   void* ya = nullptr;
   void* yq = nullptr;
@@ -112,6 +119,9 @@ struct skv_kv_cache {
   void* k;
   void* v;
   int64_t slot_elems;
+  bool fp8 = false;
+  float* ks = nullptr;  // FP8: per-token scales [n_slots][num_blocks * block_size]
+  float* vs = nullptr;
 };
 
 namespace {
@@ -146,6 +156,11 @@ skv_status validate_config(const skv_model_config* c) {
     return fail(SKV_ERR_INVALID_ARG, "swiftkv_l must lie in 0..n_layers");
   if (c->acrosskv_g < 1) return fail(SKV_ERR_INVALID_ARG, "acrosskv_g must be >= 1");
   if (c->dtype != SKV_BF16 && c->dtype != SKV_FP32) return fail(SKV_ERR_INVALID_ARG, "unknown dtype");
+  if (c->kv_dtype != SKV_KV_MODEL && c->kv_dtype != SKV_KV_FP8) return fail(SKV_ERR_INVALID_ARG, "unknown kv_dtype");
+  if (c->kv_dtype == SKV_KV_FP8 && c->dtype != SKV_BF16)
+    return fail(SKV_ERR_UNSUPPORTED, "the FP8 KV cache needs a bf16 model");
+  if (c->kv_dtype == SKV_KV_FP8 && (int64_t)c->n_kv_heads * c->head_dim > 1024)
+    return fail(SKV_ERR_UNSUPPORTED, "the FP8 KV cache needs n_kv_heads * head_dim <= 1024");
   if (c->max_tokens < 1 || c->max_batch < 1 || c->max_seqlen < 1)
     return fail(SKV_ERR_INVALID_ARG, "max_tokens, max_batch and max_seqlen must be positive");
   if (!(c->rope_theta > 0.f) || !(c->rms_eps >= 0.f)) return fail(SKV_ERR_INVALID_ARG, "bad rope_theta or rms_eps");
@@ -320,6 +335,14 @@ skv_status skv_model_create(const skv_model_config* cfg, skv_model** out) {
     m->gemm_ws_elems = gemm_bf16_ws_elems();
     ALLOC(m->gemm_ws, (size_t)m->gemm_ws_elems * 4);
   }
+  m->kv8 = c.kv_dtype == SKV_KV_FP8;
+  if (m->kv8) {
+    const size_t T16 = round_up(T, kBlockSize);
+    m->stage_v = (int64_t)(T16 * dkv);
+    m->stage_group = 2 * m->stage_v;
+    ALLOC(m->kv_stage, (size_t)std::max(m->G, 1) * m->stage_group * 2);
+    ALLOC(m->tok_iota, T * 4);
+  }
 #undef ALLOC
 
   // the panel padding rows of the activations are read (never stored) by
@@ -342,6 +365,12 @@ skv_status skv_model_create(const skv_model_config* cfg, skv_model** out) {
     if (hipMemcpy(m->rope_cos, cs.data(), cs.size() * 4, hipMemcpyHostToDevice) != hipSuccess ||
         hipMemcpy(m->rope_sin, sn.data(), sn.size() * 4, hipMemcpyHostToDevice) != hipSuccess)
       return bail(fail(SKV_ERR_HIP, "uploading RoPE tables failed"));
+    if (m->kv8) {
+      std::vector<int32_t> ti(T);
+      for (size_t t = 0; t < T; ++t) ti[t] = (int32_t)t;
+      if (hipMemcpy(m->tok_iota, ti.data(), T * 4, hipMemcpyHostToDevice) != hipSuccess)
+        return bail(fail(SKV_ERR_HIP, "uploading token indices failed"));
+    }
     std::vector<int32_t> io(B);
     for (size_t b = 0; b < B; ++b) io[b] = (int32_t)b;
     if (hipMemcpy(m->iota, io.data(), B * 4, hipMemcpyHostToDevice) != hipSuccess)
@@ -480,7 +509,9 @@ skv_status skv_kv_cache_create(const skv_model* m, int32_t num_blocks, int32_t b
   if (num_blocks < 1) return fail(SKV_ERR_INVALID_ARG, "num_blocks must be positive");
   const int n_slots = skv_num_kv_slots(m);
   const int64_t slot_elems = (int64_t)num_blocks * m->cfg.n_kv_heads * block_size * m->cfg.head_dim;
-  const size_t bytes = (size_t)slot_elems * n_slots * m->esz;
+  const bool fp8 = m->kv8;
+  const size_t bytes = (size_t)slot_elems * n_slots * (fp8 ? 1 : m->esz);
+  const size_t sbytes = fp8 ? (size_t)n_slots * num_blocks * block_size * 4 : 0;
   void *k = nullptr, *v = nullptr;
   if (hipMalloc(&k, bytes) != hipSuccess) {
     (void)hipGetLastError();
@@ -491,13 +522,28 @@ skv_status skv_kv_cache_create(const skv_model* m, int32_t num_blocks, int32_t b
     (void)hipFree(k);
     return fail(SKV_ERR_OOM, "KV cache allocation failed");
   }
+  float *ks = nullptr, *vs = nullptr;
+  if (fp8 && (hipMalloc(&ks, sbytes) != hipSuccess || hipMalloc(&vs, sbytes) != hipSuccess)) {
+    (void)hipGetLastError();
+    (void)hipFree(k);
+    (void)hipFree(v);
+    if (ks) (void)hipFree(ks);
+    return fail(SKV_ERR_OOM, "KV cache scale allocation failed");
+  }
   if (hipMemset(k, 0, bytes) != hipSuccess || hipMemset(v, 0, bytes) != hipSuccess ||
+      (fp8 && (hipMemset(ks, 0, sbytes) != hipSuccess || hipMemset(vs, 0, sbytes) != hipSuccess)) ||
       hipDeviceSynchronize() != hipSuccess) {
     (void)hipFree(k);
     (void)hipFree(v);
+    if (ks) (void)hipFree(ks);
+    if (vs) (void)hipFree(vs);
     return fail(SKV_ERR_HIP, "KV cache clear failed");
   }
-  *out = new skv_kv_cache{m, num_blocks, block_size, n_slots, k, v, slot_elems};
+  skv_kv_cache* kc = new skv_kv_cache{m, num_blocks, block_size, n_slots, k, v, slot_elems};
+  kc->fp8 = fp8;
+  kc->ks = ks;
+  kc->vs = vs;
+  *out = kc;
   return SKV_OK;
 }
 
@@ -505,6 +551,8 @@ void skv_kv_cache_destroy(skv_kv_cache* c) {
   if (!c) return;
   (void)hipFree(c->k);
   (void)hipFree(c->v);
+  if (c->ks) (void)hipFree(c->ks);
+  if (c->vs) (void)hipFree(c->vs);
   delete c;
 }
 
@@ -514,9 +562,22 @@ skv_status skv_kv_cache_view(const skv_kv_cache* c, int32_t layer, skv_tensor_vi
   if (layer < 1 || layer > cfg.n_layers) return fail(SKV_ERR_INVALID_ARG, "layer outside 1..n_layers");
   const int s = slot_of_layer(cfg, layer);
   const int64_t nb = c->num_blocks, hkv = cfg.n_kv_heads, bs = c->block_size, dh = cfg.head_dim;
-  const size_t off = (size_t)s * c->slot_elems * c->m->esz;
-  *k = skv_tensor_view{(char*)c->k + off, cfg.dtype, 4, {nb, hkv, bs, dh}, {hkv * bs * dh, bs * dh, dh, 1}};
-  *v = skv_tensor_view{(char*)c->v + off, cfg.dtype, 4, {nb, hkv, bs, dh}, {hkv * bs * dh, bs * dh, dh, 1}};
+  const size_t off = (size_t)s * c->slot_elems * (c->fp8 ? 1 : c->m->esz);
+  const int32_t dt = c->fp8 ? SKV_FP8_E4M3 : cfg.dtype;
+  *k = skv_tensor_view{(char*)c->k + off, dt, 4, {nb, hkv, bs, dh}, {hkv * bs * dh, bs * dh, dh, 1}};
+  *v = skv_tensor_view{(char*)c->v + off, dt, 4, {nb, hkv, bs, dh}, {hkv * bs * dh, bs * dh, dh, 1}};
+  return SKV_OK;
+}
+
+skv_status skv_kv_cache_scales(const skv_kv_cache* c, int32_t layer, skv_tensor_view* k, skv_tensor_view* v) {
+  if (!c || !k || !v) return fail(SKV_ERR_INVALID_ARG, "NULL argument");
+  if (!c->fp8) return fail(SKV_ERR_INVALID_ARG, "the cache holds no FP8 scales");
+  const auto& cfg = c->m->cfg;
+  if (layer < 1 || layer > cfg.n_layers) return fail(SKV_ERR_INVALID_ARG, "layer outside 1..n_layers");
+  const int64_t nb = c->num_blocks, bs = c->block_size;
+  const size_t off = (size_t)slot_of_layer(cfg, layer) * nb * bs;
+  *k = skv_tensor_view{c->ks + off, SKV_FP32, 2, {nb, bs, 0, 0}, {bs, 1, 0, 0}};
+  *v = skv_tensor_view{c->vs + off, SKV_FP32, 2, {nb, bs, 0, 0}, {bs, 1, 0, 0}};
   return SKV_OK;
 }
 
@@ -583,6 +644,21 @@ skv_status run_step(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, const S
                         c.n_kv_heads, dh};
   };
   constexpr bool kBf16 = sizeof(T) == 2;
+  // FP8 cache: K/V epilogues write the staging area (physical slot = token
+  // index), kv_quant moves the rows into the cache, attention reads codes
+  const bool kv8 = kc->fp8;
+  const int64_t nb16 = (int64_t)kc->num_blocks * kBlockSize;
+  auto slot8_of = [&](int s_) {
+    return Fp8Slot{(uint8_t*)kc->k + (int64_t)s_ * kc->slot_elems, (uint8_t*)kc->v + (int64_t)s_ * kc->slot_elems,
+                   kc->ks + s_ * nb16, kc->vs + s_ * nb16, c.n_kv_heads, dh};
+  };
+  const CacheSlot<T> stage{(T*)m->kv_stage, (T*)m->kv_stage + m->stage_v, c.n_kv_heads, dh};
+  const int32_t* kv_slot = kv8 ? m->tok_iota : m->slot;  // where the K/V epilogues write
+  auto quantize = [&](int rows, int ngroups, int first_slot) -> skv_status {
+    SKV_HIP(launch_kv_quant(m->kv_stage, m->stage_group, m->stage_v, rows, ngroups, m->slot, slot8_of(first_slot),
+                            kc->slot_elems, nb16, s));
+    return SKV_OK;
+  };
   // bf16 batches of at most kRowPathMax new tokens (decode steps, short
   // chunks) run layers 1..l like the last-token path: row-major
   // activations, the split-K skinny GEMM and per-row attention, instead of
@@ -604,11 +680,12 @@ skv_status run_step(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, const S
   // l+1..L; every new token of a short bf16 batch at layers 1..l).  x: the
   // rows' residual stream; with_kv: the QKV product also yields K/V, written
   // to cache slot cs at slot[row].
-  auto row_layer = [&](const LayerDev& Ly, CacheSlot<T> cs, int rows, float* x, const int32_t* row_seq,
-                       const int32_t* row_pos, const int32_t* slot, bool with_kv, int max_ctx) -> skv_status {
+  auto row_layer = [&](const LayerDev& Ly, int cache_slot, int rows, float* x, const int32_t* row_seq,
+                       const int32_t* row_pos, bool with_kv, int max_ctx) -> skv_status {
+    const CacheSlot<T> cs = slot_of(cache_slot);
     SKV_HIP(launch_rmsnorm<T>(x, nullptr, Ly.attn_norm, rows, d, c.rms_eps, ya, s));
     const int nq = with_kv ? dq + 2 * dkv : dq;
-    EpiQKV<T> eq{yq, cs, row_pos, slot, m->rope_cos, m->rope_sin, dq, dkv, dh, P};
+    EpiQKV<T> eq{yq, kv8 ? stage : cs, row_pos, with_kv ? kv_slot : nullptr, m->rope_cos, m->rope_sin, dq, dkv, dh, P};
     EpiResidual er{x, d, kBf16 ? 64 : 16};
     EpiSwiGLU<T> esw{yh, f, m->p_mlp};
     if constexpr (kBf16) {
@@ -621,8 +698,15 @@ skv_status run_step(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, const S
     } else {
       SKV_HIP((launch_gemm_f32<64>((const float*)ya, d, (const float*)Ly.wqkv, d, rows, nq, d, eq, s)));
     }
-    SKV_HIP(launch_attn_rows<T>(yq, cs, row_seq, row_pos, bt->block_tables, bt->max_blocks_per_seq, rows, max_ctx, hq,
-                                m->attn_ws, yo, s));
+    if (with_kv && kv8) SKV_TRY(quantize(rows, 1, cache_slot));
+    if (kv8) {
+      if constexpr (kBf16)
+        SKV_HIP(launch_attn_rows_fp8((const bf16_t*)yq, slot8_of(cache_slot), row_seq, row_pos, bt->block_tables,
+                                     bt->max_blocks_per_seq, rows, max_ctx, hq, m->attn_ws, (bf16_t*)yo, s));
+    } else {
+      SKV_HIP(launch_attn_rows<T>(yq, cs, row_seq, row_pos, bt->block_tables, bt->max_blocks_per_seq, rows, max_ctx,
+                                  hq, m->attn_ws, yo, s));
+    }
     if constexpr (kBf16) {
       SKV_HIP(launch_skinny_bf16((const bf16_t*)yo, dq, (const bf16_t*)Ly.wo, Ly.panel_rows, rows, d, dq, m->partial,
                                  m->partial_elems, er, s));
@@ -647,7 +731,7 @@ skv_status run_step(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, const S
     const LayerDev& Ly = m->layers[i - 1];
     CacheSlot<T> cs = slot_of(i - 1);
     if (rows_path) {
-      SKV_TRY(row_layer(Ly, cs, T_, m->x, m->seq, m->pos, m->slot, true, si.max_total));
+      SKV_TRY(row_layer(Ly, i - 1, T_, m->x, m->seq, m->pos, true, si.max_total));
       continue;
     }
     {
@@ -659,7 +743,7 @@ skv_status run_step(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, const S
     }
     {
       const int N = dq + 2 * dkv;
-      EpiQKV<T> epi{qbuf, cs, m->pos, m->slot, m->rope_cos, m->rope_sin, dq, dkv, dh, P};
+      EpiQKV<T> epi{qbuf, kv8 ? stage : cs, m->pos, kv_slot, m->rope_cos, m->rope_sin, dq, dkv, dh, P};
       Prof p(m, SKV_K_GEMM_QKV, s, 2.0 * T_ * N * d, gemm_bytes(T_, N, d, E, E));
       if constexpr (kBf16)
         SKV_HIP(launch_gemm_bf16((const bf16_t*)act, (const bf16_t*)Ly.wqkv, T_, N, d, epi, m->gemm_ws, m->gemm_ws_elems, s));
@@ -670,9 +754,15 @@ skv_status run_step(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, const S
       else
         SKV_HIP((launch_gemm_f32<64>((const float*)act, d, (const float*)Ly.wqkv, d, T_, N, d, epi, s)));
     }
+    if (kv8) SKV_TRY(quantize(T_, 1, i - 1));
     {
       Prof p(m, SKV_K_ATTN_PREFILL, s, si.attn_flops, attn_bytes);
-      if constexpr (kBf16)
+      if (kv8) {
+        if constexpr (kBf16)
+          SKV_HIP(launch_attn_prefill_fp8((const bf16_t*)qbuf, slot8_of(i - 1), bt->cu_seqlens, si.ctx_dev,
+                                          bt->block_tables, bt->max_blocks_per_seq, B, si.max_new, hq, (bf16_t*)obuf,
+                                          s));
+      } else if constexpr (kBf16)
         SKV_HIP(launch_attn_prefill_bf16((const bf16_t*)qbuf, cs, bt->cu_seqlens, si.ctx_dev, bt->block_tables,
                                          bt->max_blocks_per_seq, B, si.max_new, hq, (bf16_t*)obuf, s));
       else
@@ -724,10 +814,10 @@ skv_status run_step(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, const S
       else
         SKV_HIP(launch_rmsnorm<T>(m->x, nullptr, nullptr, T_, d, c.rms_eps, rows_path ? ya : act, s));
     }
-    CacheSlot<T> first = slot_of(l);
+    CacheSlot<T> first = kv8 ? stage : slot_of(l);
     const int N = m->G * 2 * dkv;
-    EpiKVSkip<T> epi{first.k, first.v, kc->slot_elems, m->pos, m->slot, m->rope_cos, m->rope_sin, dkv, dh, P,
-                     c.n_kv_heads};
+    EpiKVSkip<T> epi{first.k, first.v, kv8 ? m->stage_group : kc->slot_elems, m->pos, kv_slot, m->rope_cos,
+                     m->rope_sin, dkv, dh, P, c.n_kv_heads};
     Prof p(m, SKV_K_GEMM_KVSKIP, s, 2.0 * T_ * N * d, gemm_bytes(T_, N, d, E, E));
     if constexpr (kBf16) {
       if (rows_path)
@@ -743,14 +833,14 @@ skv_status run_step(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, const S
     } else {
       SKV_HIP((launch_gemm_f32<64>((const float*)act, d, (const float*)m->wkv_skip, d, T_, N, d, epi, s)));
     }
+    if (kv8) SKV_TRY(quantize(T_, m->G, l));
   }
 
   // ---- last new token of each sequence through layers l+1..L, then the LM head
   Prof plast(m, SKV_K_LAST_TOKEN, s, last_flops, last_bytes);
   SKV_HIP(launch_gather_rows(m->x, m->last_row, B, d, m->y, s));
   for (int j = l + 1; j <= L; ++j)
-    SKV_TRY(row_layer(m->layers[j - 1], slot_of(slot_of_layer(c, j)), B, m->y, m->iota, m->last_pos, nullptr, false,
-                      si.max_total));
+    SKV_TRY(row_layer(m->layers[j - 1], slot_of_layer(c, j), B, m->y, m->iota, m->last_pos, false, si.max_total));
   SKV_HIP(launch_rmsnorm<T>(m->y, nullptr, m->final_norm, B, d, c.rms_eps, ya, s));
   EpiStoreF32 el{logits, V, kBf16 ? 64 : 16};
   if constexpr (kBf16)

@@ -28,6 +28,10 @@
 //    to be finite, which the cache guarantees (zero-filled at creation,
 //    written only with results).  One workgroup per CU (256 VGPRs per wave).
 //
+//    With a per-token FP8 cache the tiles move through registers instead and
+//    are dequantised (code * the key's scale, rounded to bf16) on the way
+//    into the same LDS layout.
+//
 // 2. attn_rows_kernel + attn_combine_kernel (fp32 or bf16, vector ALU):
 //    attention of an explicit list of query rows (the last prompt token of
 //    each prompt at layers l+1..L; every token for fp32 models), split over
@@ -73,8 +77,13 @@ SKV_DEV void f8_qk(const bf16_t* sk, const bf16x8_t* qf, int lane, f32x16_t* sac
   }
 }
 
+// F8: K/V tiles come from the per-token FP8 cache c8 and move through
+// registers: each thread fetches 16 codes of one key and its scale, and
+// writes code * scale as bf16 into the same LDS layout the direct loads
+// produce; everything after the tile loads is shared.
+template <bool F8>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_prefill8_kernel(
-    const bf16_t* __restrict__ q, CacheSlot<bf16_t> cache, const int32_t* __restrict__ cu,
+    const bf16_t* __restrict__ q, CacheSlot<bf16_t> cache, Fp8Slot c8, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ ctx, const int32_t* __restrict__ bt, int max_blocks, int hq, int rep,
     float scale_log2, bf16_t* __restrict__ o) {
   // buffers 0, 1: K ring; 2, 3: V ring ([64 keys][128 dims] each); the
@@ -129,6 +138,28 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   auto block_of = [&](int t) {
     const int bi = t * (FA_KT / kBlockSize) + r_blk;
     return btb[bi < nblk_need ? bi : 0];
+  };
+  // FP8 tiles: thread tid moves key fk = tid / 8 of the tile (block row
+  // r_blk, as above), dims fq * 16 .. + 16: two 16-byte bf16 chunks after
+  // dequantisation, placed at the swizzled chunk positions
+  const int fk = tid >> 3, fq = tid & 7;
+  auto fetch8 = [&](const uint8_t* codes, const float* scales, int blk, u32x4_t& w, float& sc) {
+    const int64_t row = ((int64_t)blk * hkv + g) * kBlockSize + (fk & 15);
+    w = *reinterpret_cast<const u32x4_t*>(codes + row * FA_DH + fq * 16);
+    sc = scales[(int64_t)blk * kBlockSize + (fk & 15)];
+  };
+  auto store8 = [&](const u32x4_t& w, float sc, int buf) {
+    float x[16];
+    decode16_e4m3(w, x);
+    u32x4_t lo, hi;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      lo[e] = pack_bf16x2(x[2 * e] * sc, x[2 * e + 1] * sc);
+      hi[e] = pack_bf16x2(x[8 + 2 * e] * sc, x[8 + 2 * e + 1] * sc);
+    }
+    bf16_t* row = &smem[buf][fk * FA_DH];
+    *reinterpret_cast<u32x4_t*>(row + (((2 * fq) ^ (fk & 15)) << 3)) = lo;
+    *reinterpret_cast<u32x4_t*>(row + (((2 * fq + 1) ^ (fk & 15)) << 3)) = hi;
   };
   auto issue = [&](const bf16_t* base_ptr, int blk, int buf) {
     const bf16_t* src = base_ptr + ((int64_t)blk * hkv + g) * (kBlockSize * FA_DH);
@@ -239,20 +270,43 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // blk1 / blk2: block ids of tiles t+1 / t+2, fetched one iteration ahead
   // so no load waits on a block-table read
   int blk1 = block_of(1), blk2 = block_of(2);
-  issue(cache.k, block_of(0), 0);
-  issue(cache.v, block_of(0), 2);
-  issue(cache.k, blk1, 1);
+  u32x4_t wk, wv;  // FP8: codes of K(t+2) / V(t+1) in flight through registers
+  float sk, sv;
+  if constexpr (F8) {
+    const int blk0 = block_of(0);
+    fetch8(c8.k, c8.ks, blk0, wk, sk);
+    fetch8(c8.v, c8.vs, blk0, wv, sv);
+    store8(wk, sk, 0);
+    store8(wv, sv, 2);
+    fetch8(c8.k, c8.ks, blk1, wk, sk);
+    store8(wk, sk, 1);
+  } else {
+    issue(cache.k, block_of(0), 0);
+    issue(cache.v, block_of(0), 2);
+    issue(cache.k, blk1, 1);
+  }
   wait_loads_then_barrier();
   f32x16_t sa[2], sb[2];
   f8_qk(smem[0], qf, lane, sa);
   wait_loads_then_barrier();  // every wave has read K(0) before its buffer takes K(2)
   auto full = [&](int t, f32x16_t* cur, f32x16_t* nxt) {
     const int blk3 = block_of(t + 3);
-    issue(cache.k, blk2, t & 1);
-    issue(cache.v, blk1, 2 + ((t + 1) & 1));
+    if constexpr (F8) {
+      fetch8(c8.k, c8.ks, blk2, wk, sk);
+      fetch8(c8.v, c8.vs, blk1, wv, sv);
+    } else {
+      issue(cache.k, blk2, t & 1);
+      issue(cache.v, blk1, 2 + ((t + 1) & 1));
+    }
     soft_prep(t, cur);
     f8_qk(smem[(t + 1) & 1], qf, lane, nxt);
     exp_pv(cur, t & 1);
+    if constexpr (F8) {
+      // K(t) and V(t-1), whose buffers these take, were last read in the
+      // previous iteration
+      store8(wk, sk, t & 1);
+      store8(wv, sv, 2 + ((t + 1) & 1));
+    }
     wait_loads_then_barrier();
     blk1 = blk2;
     blk2 = blk3;
@@ -317,13 +371,15 @@ constexpr int RW_HG = 4;       // q heads handled per pass over the chunk
 // kv head.  Writes (max, sum, unnormalised o) per head for the combine pass.
 // Lanes read key and value rows as 16-byte slices: LPK lanes cover one row
 // (DH elements), so one wave load instruction covers 64/LPK whole rows.
-template <typename T, int DH>
-__global__ __launch_bounds__(256) void attn_rows_kernel(const T* __restrict__ q, CacheSlot<T> cache,
+// F8: K/V come from the per-token FP8 cache c8 (codes times the token's
+// scale, in fp32); otherwise from `cache` in the activation type.
+template <typename T, int DH, bool F8>
+__global__ __launch_bounds__(256) void attn_rows_kernel(const T* __restrict__ q, CacheSlot<T> cache, Fp8Slot c8,
                                                         const int32_t* __restrict__ row_seq,
                                                         const int32_t* __restrict__ row_pos,
                                                         const int32_t* __restrict__ bt, int max_blocks, int hq,
                                                         int nchunks, float scale, float* __restrict__ ws) {
-  constexpr int VEC = 16 / (int)sizeof(T);  // elements per lane load
+  constexpr int VEC = F8 ? 16 : 16 / (int)sizeof(T);  // elements per lane load
   constexpr int LPK = DH / VEC;             // lanes per key row
   constexpr int KPI = 64 / LPK;             // key rows per wave load
   constexpr int ITERS = 64 / KPI;           // loads per wave per chunk
@@ -378,10 +434,16 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const T* __restrict__ q,
 #pragma unroll
       for (int hh = 0; hh < RW_HG; ++hh) part[hh] = 0.f;
       if (kk < nk) {
-        const T* kr = cache.k + kv_index(sl_s[kk], g, d0, hkv, DH);
-        const u32x4_t raw = *reinterpret_cast<const u32x4_t*>(kr);
         float kv[VEC];
-        unpack16<T>(raw, kv);
+        if constexpr (F8) {
+          const int sl = sl_s[kk];
+          decode16_e4m3(*reinterpret_cast<const u32x4_t*>(c8.k + kv_index(sl, g, d0, hkv, DH)), kv);
+          const float sc = c8.ks[sl];
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) kv[e] *= sc;
+        } else {
+          unpack16<T>(*reinterpret_cast<const u32x4_t*>(cache.k + kv_index(sl_s[kk], g, d0, hkv, DH)), kv);
+        }
 #pragma unroll
         for (int hh = 0; hh < RW_HG; ++hh) {
           if (h0 + hh < rep) {
@@ -433,10 +495,16 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const T* __restrict__ q,
     for (int it = 0; it < ITERS; ++it) {
       const int kk = kw + it * KPI + sub;
       if (kk < nk) {
-        const T* vr = cache.v + kv_index(sl_s[kk], g, d0, hkv, DH);
-        const u32x4_t raw = *reinterpret_cast<const u32x4_t*>(vr);
         float vv[VEC];
-        unpack16<T>(raw, vv);
+        if constexpr (F8) {
+          const int sl = sl_s[kk];
+          decode16_e4m3(*reinterpret_cast<const u32x4_t*>(c8.v + kv_index(sl, g, d0, hkv, DH)), vv);
+          const float sc = c8.vs[sl];
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) vv[e] *= sc;
+        } else {
+          unpack16<T>(*reinterpret_cast<const u32x4_t*>(cache.v + kv_index(sl_s[kk], g, d0, hkv, DH)), vv);
+        }
 #pragma unroll
         for (int hh = 0; hh < RW_HG; ++hh) {
           const float p = ps[hh][kk];
@@ -502,8 +570,22 @@ hipError_t launch_attn_prefill_bf16(const bf16_t* q, CacheSlot<bf16_t> cache, co
   const int rep = hq / cache.hkv;
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)FA_DH);
   dim3 grid((max_new + 63) / 64, batch, hq / 4);
-  hipLaunchKernelGGL(attn_prefill8_kernel, grid, dim3(512), 0, stream, q, cache, cu_seqlens, ctx_lens, block_tables,
-                     max_blocks, hq, rep, scale_log2, o);
+  hipLaunchKernelGGL(attn_prefill8_kernel<false>, grid, dim3(512), 0, stream, q, cache, Fp8Slot{}, cu_seqlens,
+                     ctx_lens, block_tables, max_blocks, hq, rep, scale_log2, o);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_prefill_fp8(const bf16_t* q, Fp8Slot cache, const int32_t* cu_seqlens, const int32_t* ctx_lens,
+                                   const int32_t* block_tables, int max_blocks, int batch, int max_new, int hq,
+                                   bf16_t* o, hipStream_t stream) {
+  if (batch <= 0 || max_new <= 0) return hipSuccess;
+  if (cache.dh != FA_DH) return hipErrorInvalidValue;
+  const int rep = hq / cache.hkv;
+  const float scale_log2 = 1.4426950408889634f / sqrtf((float)FA_DH);
+  dim3 grid((max_new + 63) / 64, batch, hq / 4);
+  hipLaunchKernelGGL(attn_prefill8_kernel<true>, grid, dim3(512), 0, stream, q,
+                     CacheSlot<bf16_t>{nullptr, nullptr, cache.hkv, cache.dh}, cache, cu_seqlens, ctx_lens,
+                     block_tables, max_blocks, hq, rep, scale_log2, o);
   return hipGetLastError();
 }
 
@@ -512,25 +594,27 @@ int64_t attn_rows_ws_elems(int rows, int max_ctx, int hq, int dh) {
   return (int64_t)rows * hq * nchunks * (dh + 2);
 }
 
-template <typename T>
-hipError_t launch_attn_rows(const T* q, CacheSlot<T> cache, const int32_t* row_seq, const int32_t* row_pos,
-                            const int32_t* block_tables, int max_blocks, int rows, int max_ctx, int hq, float* ws,
-                            T* o, hipStream_t stream) {
+namespace {
+
+template <typename T, bool F8>
+hipError_t attn_rows_impl(const T* q, CacheSlot<T> cache, Fp8Slot c8, const int32_t* row_seq, const int32_t* row_pos,
+                          const int32_t* block_tables, int max_blocks, int rows, int max_ctx, int hq, float* ws, T* o,
+                          hipStream_t stream) {
   if (rows <= 0) return hipSuccess;
   const int nchunks = (max_ctx + RW_CH - 1) / RW_CH;
   const float scale = 1.0f / sqrtf((float)cache.dh);
   const dim3 grid(rows, cache.hkv, nchunks);
   switch (cache.dh) {
     case 128:
-      hipLaunchKernelGGL((attn_rows_kernel<T, 128>), grid, dim3(256), 0, stream, q, cache, row_seq, row_pos,
+      hipLaunchKernelGGL((attn_rows_kernel<T, 128, F8>), grid, dim3(256), 0, stream, q, cache, c8, row_seq, row_pos,
                          block_tables, max_blocks, hq, nchunks, scale, ws);
       break;
     case 64:
-      hipLaunchKernelGGL((attn_rows_kernel<T, 64>), grid, dim3(256), 0, stream, q, cache, row_seq, row_pos,
+      hipLaunchKernelGGL((attn_rows_kernel<T, 64, F8>), grid, dim3(256), 0, stream, q, cache, c8, row_seq, row_pos,
                          block_tables, max_blocks, hq, nchunks, scale, ws);
       break;
     case 32:
-      hipLaunchKernelGGL((attn_rows_kernel<T, 32>), grid, dim3(256), 0, stream, q, cache, row_seq, row_pos,
+      hipLaunchKernelGGL((attn_rows_kernel<T, 32, F8>), grid, dim3(256), 0, stream, q, cache, c8, row_seq, row_pos,
                          block_tables, max_blocks, hq, nchunks, scale, ws);
       break;
     default:
@@ -540,6 +624,24 @@ hipError_t launch_attn_rows(const T* q, CacheSlot<T> cache, const int32_t* row_s
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(attn_combine_kernel<T>, dim3(rows, hq), dim3(RW_MAXDH), 0, stream, ws, hq, cache.dh, nchunks, o);
   return hipGetLastError();
+}
+
+}  // namespace
+
+template <typename T>
+hipError_t launch_attn_rows(const T* q, CacheSlot<T> cache, const int32_t* row_seq, const int32_t* row_pos,
+                            const int32_t* block_tables, int max_blocks, int rows, int max_ctx, int hq, float* ws,
+                            T* o, hipStream_t stream) {
+  return attn_rows_impl<T, false>(q, cache, Fp8Slot{}, row_seq, row_pos, block_tables, max_blocks, rows, max_ctx, hq,
+                                  ws, o, stream);
+}
+
+hipError_t launch_attn_rows_fp8(const bf16_t* q, Fp8Slot cache, const int32_t* row_seq, const int32_t* row_pos,
+                                const int32_t* block_tables, int max_blocks, int rows, int max_ctx, int hq, float* ws,
+                                bf16_t* o, hipStream_t stream) {
+  if (cache.dh != 128) return hipErrorInvalidValue;
+  return attn_rows_impl<bf16_t, true>(q, CacheSlot<bf16_t>{nullptr, nullptr, cache.hkv, cache.dh}, cache, row_seq,
+                                      row_pos, block_tables, max_blocks, rows, max_ctx, hq, ws, o, stream);
 }
 
 template hipError_t launch_attn_rows<float>(const float*, CacheSlot<float>, const int32_t*, const int32_t*,

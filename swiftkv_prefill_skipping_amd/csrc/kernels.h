@@ -5,6 +5,7 @@
 
 #include "common.h"
 #include "epilogues.h"
+#include "fp8.h"
 
 // C[M,N] = A[M,K] B[N,K]^T on MFMA (bf16 in, fp32 accumulate), pair distance 64.
 // A and B are in the panel layout (panel_off; row counts rounded up to 256,
@@ -72,6 +73,11 @@ hipError_t launch_attn_prefill_bf16(const bf16_t* q, CacheSlot<bf16_t> cache, co
                                     const int32_t* ctx_lens, const int32_t* block_tables, int max_blocks, int batch,
                                     int max_new, int hq, bf16_t* o, hipStream_t stream);
 
+// The same attention with K/V from a per-token FP8 cache slot.
+hipError_t launch_attn_prefill_fp8(const bf16_t* q, Fp8Slot cache, const int32_t* cu_seqlens, const int32_t* ctx_lens,
+                                   const int32_t* block_tables, int max_blocks, int batch, int max_new, int hq,
+                                   bf16_t* o, hipStream_t stream);
+
 // Attention for a list of query rows, each attending to positions
 // [0, ctx) of its prompt (ctx = pos + 1), split over key chunks with a
 // combine pass.  Used for the last-token path and for fp32 prompt tokens.
@@ -82,10 +88,24 @@ hipError_t launch_attn_rows(const T* q, CacheSlot<T> cache, const int32_t* row_s
                             const int32_t* block_tables, int max_blocks, int rows, int max_ctx, int hq, float* ws,
                             T* o, hipStream_t stream);
 int64_t attn_rows_ws_elems(int rows, int max_ctx, int hq, int dh);
+// The same with K/V from a per-token FP8 cache slot (bf16 queries, dh 128).
+hipError_t launch_attn_rows_fp8(const bf16_t* q, Fp8Slot cache, const int32_t* row_seq, const int32_t* row_pos,
+                                const int32_t* block_tables, int max_blocks, int rows, int max_ctx, int hq, float* ws,
+                                bf16_t* o, hipStream_t stream);
 
 // For fp32 prompt-token attention: row_seq[t] for every token.
 hipError_t launch_token_seq(const int32_t* cu_seqlens, int batch, int total_tokens, int32_t* seq,
                             hipStream_t stream);
+
+// Per-token FP8 quantisation of T new tokens' K/V rows.  stage: bf16 rows in
+// the cache layout with physical slot = token index (group g's K at
+// stage + g * stage_group_stride, V at + stage_v_offset); ngroups
+// destination slots dst0, dst0 + 1 slot, ... (codes dst_slot_stride bytes
+// apart, scales dst_scale_stride floats apart); slot[t] = the token's
+// physical slot (-1: skipped).  hkv * dh <= 1024, dh % 16 == 0.
+hipError_t launch_kv_quant(const bf16_t* stage, int64_t stage_group_stride, int64_t stage_v_offset, int T,
+                           int ngroups, const int32_t* slot, Fp8Slot dst0, int64_t dst_slot_stride,
+                           int64_t dst_scale_stride, hipStream_t stream);
 
 // Weight repacking at load time.
 template <typename T>

@@ -32,10 +32,12 @@ def _torch():
     return torch
 
 
-def config_from(shape, dtype: str, l: int, g: int, max_tokens: int, max_batch: int, max_seqlen: int):
+def config_from(shape, dtype: str, l: int, g: int, max_tokens: int, max_batch: int, max_seqlen: int,
+                kv_fp8: bool = False):
     return L.make_config(shape.n_layers, shape.d_model, shape.n_q_heads, shape.n_kv_heads, shape.head_dim,
                          shape.ffn_dim, shape.vocab, shape.rope_theta, shape.rms_eps, l, g,
-                         L.SKV_BF16 if dtype == "bf16" else L.SKV_FP32, max_tokens, max_batch, max_seqlen)
+                         L.SKV_BF16 if dtype == "bf16" else L.SKV_FP32, max_tokens, max_batch, max_seqlen,
+                         L.SKV_KV_FP8 if kv_fp8 else L.SKV_KV_MODEL)
 
 
 class Model:
@@ -67,7 +69,8 @@ class Model:
             pass
 
 
-def load_seeded_model(workload, max_tokens: int, max_batch: int, max_seqlen: int, layer_hook=None) -> Model:
+def load_seeded_model(workload, max_tokens: int, max_batch: int, max_seqlen: int, layer_hook=None,
+                      kv_fp8: bool = False) -> Model:
     """Create a model for `workload` and load its seeded weights layer by layer.
 
     layer_hook(i, weights) (optional) sees each layer's host arrays after
@@ -75,7 +78,8 @@ def load_seeded_model(workload, max_tokens: int, max_batch: int, max_seqlen: int
     """
     import skv_inputs as si
     s = workload.shape
-    cfg = config_from(s, workload.dtype, workload.swiftkv_l, workload.acrosskv_g, max_tokens, max_batch, max_seqlen)
+    cfg = config_from(s, workload.dtype, workload.swiftkv_l, workload.acrosskv_g, max_tokens, max_batch, max_seqlen,
+                      kv_fp8)
     m = Model(cfg)
     gw = si.global_weights(s, workload.dtype)
     m.load_globals(gw["embed"], gw["final_norm"], gw["lm_head"])
@@ -103,7 +107,7 @@ class Cache:
     def _copy_view(self, v: L.skv_tensor_view):
         torch = _torch()
         shape = tuple(v.shape[i] for i in range(v.ndim))
-        dt = torch.uint16 if v.dtype == L.SKV_BF16 else torch.float32
+        dt = {L.SKV_BF16: torch.uint16, L.SKV_FP32: torch.float32, L.SKV_FP8_E4M3: torch.uint8}[v.dtype]
         t = torch.empty(shape, dtype=dt, device="cuda")
         nbytes = t.numel() * t.element_size()
         torch.cuda.synchronize()
@@ -113,9 +117,26 @@ class Cache:
         return t.view(torch.bfloat16) if v.dtype == L.SKV_BF16 else t
 
     def read_layer(self, layer: int):
-        """Device copies of (K, V) of a layer, each [num_blocks, hkv, block_size, dh]."""
+        """Device copies of (K, V) of a layer, each [num_blocks, hkv, block_size, dh]; an FP8 cache's values are
+        decoded (code value times the position's scale, fp32)."""
         k, v = self.view(layer)
-        return self._copy_view(k), self._copy_view(v)
+        kt, vt = self._copy_view(k), self._copy_view(v)
+        if k.dtype != L.SKV_FP8_E4M3:
+            return kt, vt
+        torch = _torch()
+        ks, vs = (self._copy_view(x) for x in L.skv_kv_cache_scales(self.handle, layer))
+
+        def dec(codes, sc):
+            val = codes.cpu().view(torch.float8_e4m3fn).float()              # E4M3 values (host conversion)
+            return (val * sc.cpu()[:, None, :, None]).to(codes.device)
+        return dec(kt, ks), dec(vt, vs)
+
+    def read_codes(self, layer: int):
+        """Host copies of an FP8 cache layer: (K codes, V codes) uint8 [num_blocks, hkv, block_size, dh] and
+        (K scales, V scales) fp32 [num_blocks, block_size]."""
+        k, v = self.view(layer)
+        ks, vs = L.skv_kv_cache_scales(self.handle, layer)
+        return tuple(self._copy_view(x).cpu().numpy() for x in (k, v, ks, vs))
 
     def close(self):
         if self.handle:

@@ -1,0 +1,129 @@
+"""Per-token FP8 KV cache on the GPU (Appendix B.1 / Table B.1 of the SwiftKV
+paper: AcrossKV composed with FP8 KV quantisation).
+
+* Quantiser, bit-exact: the first layer's K/V (and with l = 0 every skipped
+  slot's) are computed identically by a bf16-cache and an FP8-cache model on
+  the same batch, so the FP8 cache's codes and scales must equal the oracle's
+  quantiser applied to the bf16 cache's values, bit for bit.
+* Whole path: prefill and mixed-batch steps with the FP8 cache against the
+  oracle evaluated with the same cache (kv_fp8=True).  A GPU value computed
+  in another order may round to the neighbouring code, so every cached
+  element must lie within one E4M3 step of the oracle's plus twice the bf16
+  bar, and each logits row within the bf16 bar plus one E4M3 step of the
+  largest value (2e-2 + 1/14).
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import skv_inputs as si
+from oracle import swiftkv_oracle as O
+from tests.helpers import CachedLayers, dims_of, max_rel, oracle_weights
+from tests.test_gpu_step import FP8_LOGITS_TOL, fp8_kv_check, run_schedule
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def _logical_rows(arr, block_row, n):
+    """[num_blocks, hkv, 16, dh] (or scales [num_blocks, 16]) -> position order for the first n positions."""
+    bs = 16
+    nb = -(-n // bs)
+    sel = arr[np.asarray(block_row[:nb], dtype=np.int64)]
+    if sel.ndim == 2:
+        return sel.reshape(nb * bs)[:n]
+    return sel.transpose(0, 2, 1, 3).reshape(nb * bs, sel.shape[1], sel.shape[3])[:n]
+
+
+@pytest.mark.parametrize("l", [2, 0])
+def test_fp8_quantizer_matches_oracle_bit_exactly(l):
+    import torch
+    from swiftkv_prefill_skipping_amd import runner
+    w = si.small_workload(f"fp8_bits_l{l}", l=l, g=1, lengths=(150, 37, 64), seed=61, shuffle=True)
+    batch = si.make_batch(w)
+    T, B = batch.total_tokens, len(batch.lengths)
+    _say(f"[fp8] quantiser bit-exactness, l={l}")
+    m16 = runner.load_seeded_model(w, T, B, batch.max_seqlen)
+    c16 = runner.Cache(m16, batch.num_blocks)
+    m8 = runner.load_seeded_model(w, T, B, batch.max_seqlen, kv_fp8=True)
+    c8 = runner.Cache(m8, batch.num_blocks)
+    db = runner.device_batch(batch)
+    runner.prefill(m16, c16, db)
+    runner.prefill(m8, c8, db)
+    torch.cuda.synchronize()
+    layers = [1] if l > 0 else list(range(1, w.shape.n_layers + 1))
+    checked = 0
+    for j in layers:
+        k16, v16 = c16.read_layer(j)
+        kc, vc, ks, vs = c8.read_codes(j)
+        k16, v16 = k16.float().cpu().numpy(), v16.float().cpu().numpy()
+        for b in range(B):
+            n = int(batch.lengths[b])
+            for x16, codes, scales in ((k16, kc, ks), (v16, vc, vs)):
+                rows = _logical_rows(x16, batch.block_tables[b], n).reshape(n, -1)
+                want_c, want_s = O.fp8_quantize_rows(rows)
+                got_c = _logical_rows(codes, batch.block_tables[b], n).reshape(n, -1)
+                got_s = _logical_rows(scales, batch.block_tables[b], n)
+                assert np.array_equal(got_s.view(np.uint32), want_s.view(np.uint32)), f"layer {j} prompt {b} scales"
+                assert np.array_equal(got_c, want_c), f"layer {j} prompt {b} codes"
+                checked += rows.size
+    _say(f"[fp8] {checked} codes bit-exact")
+
+
+def _fp8_prefill_case(w, prompts):
+    import torch
+    from swiftkv_prefill_skipping_amd import runner
+    from tests.test_gpu_parity import gpu_kv
+    batch = si.make_batch(w)
+    cached = CachedLayers()
+    model = runner.load_seeded_model(w, batch.total_tokens, len(batch.lengths), batch.max_seqlen,
+                                     layer_hook=cached.hook, kv_fp8=True)
+    cache = runner.Cache(model, batch.num_blocks)
+    lg = runner.prefill(model, cache, runner.device_batch(batch))
+    torch.cuda.synchronize()
+    lg = lg.cpu().numpy()
+    ores = O.swiftkv_prefill(dims_of(w.shape), oracle_weights(w, cached), [batch.tokens[b] for b in prompts],
+                             w.swiftkv_l, w.acrosskv_g, kv_fp8=True)
+    worst_l, worst_kv, errs = 0.0, 0.0, []
+    for ob, b in enumerate(prompts):
+        e = max_rel(lg[b], ores.logits[ob])
+        worst_l = max(worst_l, e)
+        errs.append(e)
+        assert e < FP8_LOGITS_TOL, f"prompt {b} logits {e:.3e}"
+        gkv = gpu_kv(cache, w, batch, b)
+        for s in gkv:
+            for t, name in ((0, "K"), (1, "V")):
+                ok, e, mr = fp8_kv_check(gkv[s][t], ores.kv[ob][s][t])
+                worst_kv = max(worst_kv, e)
+                assert ok, f"prompt {b} slot {s} {name}: {e:.2f} of the bound (max-rel {mr:.3e})"
+    _say(f"[fp8] {w.name}: logits {' '.join(f'{e:.2e}' for e in errs)}; K/V worst {worst_kv:.2f} of the bound")
+
+
+FP8_CASES = [
+    ("l2_ragged", dict(l=2, g=1, lengths=(100, 37, 300, 1, 64))),
+    ("l1_acrosskv_g2", dict(l=1, g=2, lengths=(150, 33))),
+    ("l2_acrosskv_g2_shuffled", dict(l=2, g=2, lengths=(333, 65), shuffle=True)),
+    ("l0", dict(l=0, g=1, lengths=(77, 130))),
+]
+
+
+@pytest.mark.parametrize("name,kw", FP8_CASES, ids=[c[0] for c in FP8_CASES])
+def test_fp8_prefill_matches_oracle(name, kw):
+    w = si.small_workload("fp8_" + name, seed=63, **kw)
+    _say(f"[fp8] prefill {name}")
+    _fp8_prefill_case(w, list(range(len(w.fixed_lengths))))
+
+
+def test_fp8_chunks_and_decode():
+    """Mixed batches with the FP8 cache: tiled path with cached prefixes, row path (decode tokens, a short
+    chunk), AcrossKV."""
+    w = si.small_workload("fp8_step", l=2, g=2, lengths=(220, 90, 40), seed=67)
+    sched = [[(0, 100), (1, 60)],
+             [(0, 1), (1, 20), (2, 40)],
+             [(0, 118), (1, 1)],
+             [(0, 1), (1, 9)]]
+    run_schedule(w, (220, 90, 40), sched, label="fp8 step", kv_fp8=True)

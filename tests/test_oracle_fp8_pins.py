@@ -78,6 +78,16 @@ def test_per_token_quantizer_error_bound_and_scale():
         assert np.max(np.abs(O.e4m3_decode(codes[r]))) == 448.0     # the row maximum maps to +-448
 
 
+def test_bf16_rounding_matches_library():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(9)
+    x = (rng.standard_normal(50000) * np.exp(rng.uniform(-30, 30, 50000))).astype(np.float32)
+    ties = (np.arange(1, 2000, dtype=np.uint32) << 16 | 0x8000).view(np.float32)   # exact halfway cases
+    x = np.concatenate([x, ties, -ties, np.float32([0.0, -0.0, 1.0])])
+    lib = torch.from_numpy(x).to(torch.bfloat16).float().numpy()
+    assert np.array_equal(O.bf16_round(x).view(np.uint32), lib.view(np.uint32))
+
+
 def test_fp8_kv_memory_reductions_printed_by_the_pages():
     gold = json.load(open(os.path.join(GOLDEN, "fp8_kv_memory.json")))
     L, l = gold["n_layers"], gold["l"]
