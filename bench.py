@@ -11,7 +11,8 @@ then also timed through the unmodified model (l = L, same kernels), so the
 line carries the SwiftKV / full-depth wall-clock ratio next to the FLOP ratio,
 and (bf16) through skv_step: one decode token per prompt after its prefill
 (weight-streaming, HBM-bound) and the same prompts prefilled in chunks of 256
-tokens per prompt per call.
+tokens per prompt per call; finally prefill and decode with a per-token FP8
+KV cache.
 """
 from __future__ import annotations
 
@@ -60,20 +61,22 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(workload, batch, cached, budget_prompt=None):
-    """Time the oracle on one prompt of the batch (the shortest) on the host cores."""
+def cpu_baseline(workload, batch, cached, n_prompts=2):
+    """Time the oracle on the host cores over the batch's shortest prompts (about 10 s of work at the 8B shape)."""
     from threadpoolctl import threadpool_info
     from oracle import swiftkv_oracle as O
     from tests.helpers import dims_of, oracle_weights
-    b = int(np.argmin(batch.lengths)) if budget_prompt is None else budget_prompt
+    sel = [int(b) for b in np.argsort(batch.lengths, kind="stable")[:n_prompts]]
     W = oracle_weights(workload, cached)
     t0 = time.perf_counter()
-    O.swiftkv_prefill(dims_of(workload.shape), W, [batch.tokens[b]], workload.swiftkv_l, workload.acrosskv_g)
+    O.swiftkv_prefill(dims_of(workload.shape), W, [batch.tokens[b] for b in sel], workload.swiftkv_l,
+                      workload.acrosskv_g)
     dt = time.perf_counter() - t0
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    n = int(batch.lengths[b])
+    n = int(sum(int(batch.lengths[b]) for b in sel))
     return {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"prompt {b} of the batch ({n} tokens), fp32 NumPy oracle, {dt:.1f} s wall"}
+            "sample": f"prompts {sel} of the batch ({n} tokens) through the whole path, fp32 NumPy oracle, "
+                      f"{dt:.1f} s wall"}
 
 
 def copy_calibration(mib: int):
@@ -173,6 +176,35 @@ def measure_chunked(model, cache, w, batch, stream, args, ms_one_shot, swift_flo
             "actual_tflops": round(swift_flops / (ms_ch / 1e3) / 1e12, 2)}
 
 
+def measure_fp8(w, batch, db, logits, stream, args, extra, ms_bf16, dec_bf16):
+    """The same batch with a per-token FP8 KV cache: prefill and decode step times, KV bytes."""
+    import torch
+    from swiftkv_prefill_skipping_amd import runner
+    T, B = batch.total_tokens, len(batch.lengths)
+    t0 = time.time()
+    m8 = runner.load_seeded_model(w, T, B, batch.max_seqlen + extra * batch.block_size, kv_fp8=True)
+    c8 = runner.Cache(m8, batch.num_blocks + B * extra)
+    log(f"[bench] FP8-cache model loaded in {time.time() - t0:.1f} s")
+    ms8 = time_calls(lambda: runner.prefill(m8, c8, db, logits, stream), args.steps, args.warmup, stream)
+    log(f"[bench] FP8 KV cache: prefill {ms8:.3f} ms/step")
+    out = {"ms_per_step": round(ms8, 4), "tokens_per_s": round(T / (ms8 / 1e3), 1),
+           "time_vs_bf16_cache": round(ms8 / ms_bf16, 4)}
+    if dec_bf16 is not None:
+        runner.prefill(m8, c8, db, logits, stream)
+        d8 = measure_decode(m8, c8, w, batch, extra, logits, stream, args)
+        out["decode_ms_per_step"] = d8["ms_per_step"]
+        out["decode_time_vs_bf16_cache"] = round(d8["ms_per_step"] / dec_bf16["ms_per_step"], 4)
+    s = w.shape
+    slots = w.swiftkv_l + -(-(s.n_layers - w.swiftkv_l) // w.acrosskv_g)
+    per_tok_bf16 = slots * 2 * s.n_kv_heads * s.head_dim * 2
+    per_tok_fp8 = slots * 2 * (s.n_kv_heads * s.head_dim + 4)
+    out["kv_bytes_per_token"] = {"bf16": per_tok_bf16, "fp8_with_scales": per_tok_fp8,
+                                 "full_model_bf16": s.n_layers * 2 * s.n_kv_heads * s.head_dim * 2}
+    c8.close()
+    m8.close()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -184,6 +216,8 @@ def main():
                     help="skip timing the same batch through all layers (l = L) with the same kernels")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip timing a decode step and a chunked prefill over the same prompts")
+    ap.add_argument("--no-fp8", action="store_true",
+                    help="skip timing the same batch with a per-token FP8 KV cache")
     ap.add_argument("--decode-only", action="store_true",
                     help="only time decode steps (for kernel traces of the decode path)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -290,6 +324,10 @@ def main():
         runner.prefill(model, cache, db, logits, stream)
         res["decode_step"] = measure_decode(model, cache, w, batch, extra, logits, stream, args)
         res["chunked_prefill"] = measure_chunked(model, cache, w, batch, stream, args, ms, swift)
+    if not args.no_fp8 and w.dtype == "bf16":
+        model.close()
+        cache.close()
+        res["fp8_kv_cache"] = measure_fp8(w, batch, db, logits, stream, args, extra, ms, res.get("decode_step"))
     if not args.no_full_depth and w.swiftkv_l < w.shape.n_layers:
         # the unmodified model (every layer for every prompt token), same weights, batch and kernels: the
         # wall-clock ratio to compare with the FLOP ratio
