@@ -48,6 +48,7 @@ struct LayerDev {
   void* wgu = nullptr;   // [2f, d], gate/up interleaved in blocks of P_mlp rows
   void* wdown = nullptr; // [d, f]
   int panel_rows = 0;    // 0: row-major; else the panel height of the layout
+  bool gain_folded = false;  // attn / ffn RMSNorm gains folded into wqkv / wgu (bf16, layers <= l)
   bool loaded = false;
 };
 
@@ -102,6 +103,10 @@ struct skv_model {
   void* yh = nullptr;
   float* partial = nullptr;
   int64_t partial_elems = 0;
+  // bf16 prompt-token path: RMSNorm factor per token row, and the partial
+  // sums of squares [T, d/16] the residual epilogues leave for it
+  float* rrow = nullptr;
+  float* ssp = nullptr;
   float* attn_ws = nullptr;
   int64_t attn_ws_elems = 0;
   float* gemm_ws = nullptr;  // split partial tiles of the GEMMs
@@ -334,6 +339,8 @@ skv_status skv_model_create(const skv_model_config* cfg, skv_model** out) {
   if (m->bf16) {
     m->gemm_ws_elems = gemm_bf16_ws_elems();
     ALLOC(m->gemm_ws, (size_t)m->gemm_ws_elems * 4);
+    ALLOC(m->rrow, T * 4);
+    ALLOC(m->ssp, T * (d / 16) * 4);
   }
   m->kv8 = c.kv_dtype == SKV_KV_FP8;
   if (m->kv8) {
@@ -452,9 +459,15 @@ skv_status skv_model_load_layer(skv_model* m, int32_t layer, const skv_layer_wei
     SKV_TRY(copy_in(dst + dq * d * E, w->wk, dkv * d * E, "wk"));
     SKV_TRY(copy_in(dst + (dq + dkv) * d * E, w->wv, dkv * d * E, "wv"));
     if (L.panel_rows) {
+      // the prompt-token GEMMs take un-normalised rows and scale the
+      // products by the row's RMSNorm factor: fold the gain into the rows
+      // (W diag(gamma)), exact in real arithmetic
+      SKV_HIP(launch_fold_rows<bf16_t>((const bf16_t*)m->staging, (const bf16_t*)m->gamma_stage, (int)(dq + 2 * dkv),
+                                       (int)d, (bf16_t*)m->staging, 0));
       SKV_HIP(launch_to_panels((const bf16_t*)m->staging, (int)(dq + 2 * dkv), (int)d, L.panel_rows,
                                (bf16_t*)L.wqkv, 0));
       SKV_HIP(hipDeviceSynchronize());
+      L.gain_folded = true;
     }
   } else {
     SKV_TRY(load_matrix(m, L.wqkv, w->wq, dq, d, L.panel_rows, "wq"));
@@ -491,6 +504,12 @@ skv_status skv_model_load_layer(skv_model* m, int32_t layer, const skv_layer_wei
   else
     SKV_HIP(launch_interleave<float>((const float*)m->staging, (const float*)m->staging + f * d, (int)f, (int)d,
                                      m->p_mlp, (float*)L.wgu, 0));
+  if (L.gain_folded) {
+    SKV_HIP(hipDeviceSynchronize());
+    SKV_TRY(gain_to_f32(m, w->ffn_norm, L.ffn_norm, "ffn_norm"));  // gamma_stage = ffn gain
+    SKV_HIP(launch_fold_rows<bf16_t>((const bf16_t*)L.wgu, (const bf16_t*)m->gamma_stage, (int)(2 * f), (int)d,
+                                     (bf16_t*)L.wgu, 0));
+  }
   if (L.panel_rows) {
     SKV_HIP(launch_to_panels((const bf16_t*)L.wgu, (int)(2 * f), (int)d, L.panel_rows, (bf16_t*)m->staging, 0));
     SKV_HIP(hipMemcpyAsync(L.wgu, m->staging, round_up(2 * f, 256) * d * E, hipMemcpyDeviceToDevice, 0));
@@ -683,7 +702,8 @@ skv_status run_step(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, const S
   auto row_layer = [&](const LayerDev& Ly, int cache_slot, int rows, float* x, const int32_t* row_seq,
                        const int32_t* row_pos, bool with_kv, int max_ctx) -> skv_status {
     const CacheSlot<T> cs = slot_of(cache_slot);
-    SKV_HIP(launch_rmsnorm<T>(x, nullptr, Ly.attn_norm, rows, d, c.rms_eps, ya, s));
+    // (gains folded into the weights of layers <= l: plain x * r here)
+    SKV_HIP(launch_rmsnorm<T>(x, nullptr, Ly.gain_folded ? nullptr : Ly.attn_norm, rows, d, c.rms_eps, ya, s));
     const int nq = with_kv ? dq + 2 * dkv : dq;
     EpiQKV<T> eq{yq, kv8 ? stage : cs, row_pos, with_kv ? kv_slot : nullptr, m->rope_cos, m->rope_sin, dq, dkv, dh, P};
     EpiResidual er{x, d, kBf16 ? 64 : 16};
@@ -713,7 +733,7 @@ skv_status run_step(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, const S
     } else {
       SKV_HIP((launch_gemm_f32<16>((const float*)yo, dq, (const float*)Ly.wo, dq, rows, d, dq, er, s)));
     }
-    SKV_HIP(launch_rmsnorm<T>(x, nullptr, Ly.ffn_norm, rows, d, c.rms_eps, ya, s));
+    SKV_HIP(launch_rmsnorm<T>(x, nullptr, Ly.gain_folded ? nullptr : Ly.ffn_norm, rows, d, c.rms_eps, ya, s));
     if constexpr (kBf16) {
       SKV_HIP(launch_skinny_bf16((const bf16_t*)ya, d, (const bf16_t*)Ly.wgu, Ly.panel_rows, rows, 2 * f, d, m->partial,
                                  m->partial_elems, esw, s));
@@ -726,6 +746,22 @@ skv_status run_step(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, const S
     return SKV_OK;
   };
 
+  // bf16 prompt-token GEMMs take un-normalised bf16 rows (`act`) and apply
+  // the row's RMSNorm factor (rrow) in their epilogues; the gains sit in the
+  // weights.  The residual epilogues write the next act and the partial sums
+  // of squares for rrow.  Here: x_1's.
+  const bool panel_path = kBf16 && !rows_path;
+  auto next_rrow = [&]() -> skv_status {
+    Prof p(m, SKV_K_RMSNORM, s, 0, (double)T_ * d / 16 * 4 + T_ * 4.0);
+    SKV_HIP(launch_rms_from_partials(m->ssp, T_, d, c.rms_eps, m->rrow, s));
+    return SKV_OK;
+  };
+  if (panel_path && (l > 0 || m->G > 0)) {
+    Prof p(m, SKV_K_RMSNORM, s, 0, (double)T_ * d * (4 + E));
+    SKV_HIP(launch_rows_rms_panel(m->x, T_, d, c.rms_eps, (bf16_t*)act, m->rrow, s));
+  }
+  const float* rrow = panel_path ? m->rrow : nullptr;
+
   // ---- layers 1..l for every new token
   for (int i = 1; i <= l; ++i) {
     const LayerDev& Ly = m->layers[i - 1];
@@ -734,16 +770,13 @@ skv_status run_step(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, const S
       SKV_TRY(row_layer(Ly, i - 1, T_, m->x, m->seq, m->pos, true, si.max_total));
       continue;
     }
-    {
+    if constexpr (!kBf16) {
       Prof p(m, SKV_K_RMSNORM, s, 0, (double)T_ * d * (4 + E));
-      if constexpr (kBf16)
-        SKV_HIP(launch_rmsnorm_panel(m->x, Ly.attn_norm, T_, d, c.rms_eps, (bf16_t*)act, s));
-      else
-        SKV_HIP(launch_rmsnorm<T>(m->x, nullptr, Ly.attn_norm, T_, d, c.rms_eps, act, s));
+      SKV_HIP(launch_rmsnorm<T>(m->x, nullptr, Ly.attn_norm, T_, d, c.rms_eps, act, s));
     }
     {
       const int N = dq + 2 * dkv;
-      EpiQKV<T> epi{qbuf, kv8 ? stage : cs, m->pos, kv_slot, m->rope_cos, m->rope_sin, dq, dkv, dh, P};
+      EpiQKV<T> epi{qbuf, kv8 ? stage : cs, m->pos, kv_slot, m->rope_cos, m->rope_sin, dq, dkv, dh, P, rrow};
       Prof p(m, SKV_K_GEMM_QKV, s, 2.0 * T_ * N * d, gemm_bytes(T_, N, d, E, E));
       if constexpr (kBf16)
         SKV_HIP(launch_gemm_bf16((const bf16_t*)act, (const bf16_t*)Ly.wqkv, T_, N, d, epi, m->gemm_ws, m->gemm_ws_elems, s));
@@ -770,24 +803,23 @@ skv_status run_step(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, const S
                                     si.max_total, hq, m->attn_ws, obuf, s));
     }
     {
-      EpiResidual epi{m->x, d, kBf16 ? 64 : 16};
+      EpiResidual epi{m->x, d, kBf16 ? 64 : 16, kBf16 ? (bf16_t*)act : nullptr, kBf16 ? m->ssp : nullptr};
       Prof p(m, SKV_K_GEMM_O, s, 2.0 * T_ * d * dq, gemm_bytes(T_, d, dq, E, 8));
       if constexpr (kBf16)
         SKV_HIP(launch_gemm_bf16((const bf16_t*)obuf, (const bf16_t*)Ly.wo, T_, d, dq, epi, m->gemm_ws, m->gemm_ws_elems, s));
       else
         SKV_HIP((launch_gemm_f32<16>((const float*)obuf, dq, (const float*)Ly.wo, dq, T_, d, dq, epi, s)));
     }
-    {
+    if constexpr (kBf16) {
+      SKV_TRY(next_rrow());
+    } else {
       Prof p(m, SKV_K_RMSNORM, s, 0, (double)T_ * d * (4 + E));
-      if constexpr (kBf16)
-        SKV_HIP(launch_rmsnorm_panel(m->x, Ly.ffn_norm, T_, d, c.rms_eps, (bf16_t*)act, s));
-      else
-        SKV_HIP(launch_rmsnorm<T>(m->x, nullptr, Ly.ffn_norm, T_, d, c.rms_eps, act, s));
+      SKV_HIP(launch_rmsnorm<T>(m->x, nullptr, Ly.ffn_norm, T_, d, c.rms_eps, act, s));
     }
     {
       Prof p(m, SKV_K_GEMM_GATEUP, s, 2.0 * T_ * 2 * f * d, gemm_bytes(T_, 2.0 * f, d, E, 0) + (double)T_ * f * E);
       if constexpr (kBf16) {
-        EpiSwiGLUPanel epi{(bf16_t*)hbuf, f, m->p_mlp};
+        EpiSwiGLUPanel epi{(bf16_t*)hbuf, f, m->p_mlp, rrow};
         SKV_HIP(launch_gemm_bf16((const bf16_t*)act, (const bf16_t*)Ly.wgu, T_, 2 * f, d, epi, m->gemm_ws, m->gemm_ws_elems, s));
       } else {
         EpiSwiGLU<T> epi{hbuf, f, m->p_mlp};
@@ -795,29 +827,27 @@ skv_status run_step(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, const S
       }
     }
     {
-      EpiResidual epi{m->x, d, kBf16 ? 64 : 16};
+      EpiResidual epi{m->x, d, kBf16 ? 64 : 16, kBf16 ? (bf16_t*)act : nullptr, kBf16 ? m->ssp : nullptr};
       Prof p(m, SKV_K_GEMM_DOWN, s, 2.0 * T_ * d * f, gemm_bytes(T_, d, f, E, 8));
       if constexpr (kBf16)
         SKV_HIP(launch_gemm_bf16((const bf16_t*)hbuf, (const bf16_t*)Ly.wdown, T_, d, f, epi, m->gemm_ws, m->gemm_ws_elems, s));
       else
         SKV_HIP((launch_gemm_f32<16>((const float*)hbuf, f, (const float*)Ly.wdown, f, T_, d, f, epi, s)));
     }
+    if constexpr (kBf16) SKV_TRY(next_rrow());
   }
 
   // ---- boundary: KV of every skipped layer / AcrossKV group from x_{l+1}
   if (m->G > 0) {
-    {
+    if (!panel_path) {
+      // x * r, gains folded into W~ (the panel path has act = bf16(x_{l+1}) and rrow already)
       Prof p(m, SKV_K_RMSNORM, s, 0, (double)T_ * d * (4 + E));
-      // x * r, gains folded into W~
-      if (kBf16 && !rows_path)
-        SKV_HIP(launch_rmsnorm_panel(m->x, nullptr, T_, d, c.rms_eps, (bf16_t*)act, s));
-      else
-        SKV_HIP(launch_rmsnorm<T>(m->x, nullptr, nullptr, T_, d, c.rms_eps, rows_path ? ya : act, s));
+      SKV_HIP(launch_rmsnorm<T>(m->x, nullptr, nullptr, T_, d, c.rms_eps, rows_path ? ya : act, s));
     }
     CacheSlot<T> first = kv8 ? stage : slot_of(l);
     const int N = m->G * 2 * dkv;
     EpiKVSkip<T> epi{first.k, first.v, kv8 ? m->stage_group : kc->slot_elems, m->pos, kv_slot, m->rope_cos,
-                     m->rope_sin, dkv, dh, P, c.n_kv_heads};
+                     m->rope_sin, dkv, dh, P, c.n_kv_heads, rrow};
     Prof p(m, SKV_K_GEMM_KVSKIP, s, 2.0 * T_ * N * d, gemm_bytes(T_, N, d, E, E));
     if constexpr (kBf16) {
       if (rows_path)

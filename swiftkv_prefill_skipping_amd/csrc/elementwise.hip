@@ -135,6 +135,41 @@ __global__ __launch_bounds__(256) void rmsnorm_panel_kernel(const float* __restr
   }
 }
 
+// Un-normalised GEMM input of a row plus its RMSNorm factor: y = bf16(x) in
+// the panel layout, r[row] = 1 / sqrt(mean(x^2) + eps).  One wave per row.
+__global__ __launch_bounds__(256) void rows_rms_panel_kernel(const float* __restrict__ x, int rows, int d, float eps,
+                                                             bf16_t* __restrict__ y, float* __restrict__ r_out) {
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  const float* xr = x + (int64_t)r * d;
+  float ss = 0.f;
+  for (int c = lane * 8; c < d; c += 512) {
+    float v[8];
+    load8(xr + c, v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss += v[e] * v[e];
+    store8(y + panel_off(r, c, d), v);
+  }
+  ss = warp_sum(ss);
+  if (lane == 0) r_out[r] = 1.0f / sqrtf(ss / (float)d + eps);
+}
+
+// r[row] = 1 / sqrt(sum of the row's `units` partial sums of squares / d + eps).
+// One wave per row: lane l adds partials l, l+64, ... in order, then a fixed
+// butterfly across lanes (deterministic).
+__global__ __launch_bounds__(256) void rms_from_partials_kernel(const float* __restrict__ ss, int rows, int units,
+                                                                int d, float eps, float* __restrict__ r_out) {
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;  // whole waves
+  const float* p = ss + (int64_t)r * units;
+  float t = 0.f;
+  for (int u = lane; u < units; u += 64) t += p[u];
+  t = warp_sum(t);
+  if (lane == 0) r_out[r] = 1.0f / sqrtf(t / (float)d + eps);
+}
+
 // Row-major [rows, K] -> panel layout with panels of pr rows, eight
 // elements (16 bytes) per thread in destination order; rows beyond `rows`
 // (panel padding) become zero.
@@ -235,6 +270,22 @@ hipError_t launch_rmsnorm_panel(const float* x, const float* gamma, int rows, in
   if (rows <= 0) return hipSuccess;
   if (d % kPanelCols || d > 512 * kNormMaxChunks) return hipErrorInvalidValue;
   hipLaunchKernelGGL(rmsnorm_panel_kernel, dim3((rows + 3) / 4), dim3(256), 0, stream, x, gamma, rows, d, eps, y);
+  return hipGetLastError();
+}
+
+hipError_t launch_rows_rms_panel(const float* x, int rows, int d, float eps, bf16_t* y, float* r,
+                                 hipStream_t stream) {
+  if (rows <= 0) return hipSuccess;
+  if (d % kPanelCols) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(rows_rms_panel_kernel, dim3((rows + 3) / 4), dim3(256), 0, stream, x, rows, d, eps, y, r);
+  return hipGetLastError();
+}
+
+hipError_t launch_rms_from_partials(const float* ss, int rows, int d, float eps, float* r, hipStream_t stream) {
+  if (rows <= 0) return hipSuccess;
+  if (d % 16) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(rms_from_partials_kernel, dim3((rows + 3) / 4), dim3(256), 0, stream, ss, rows, d / 16, d, eps,
+                     r);
   return hipGetLastError();
 }
 

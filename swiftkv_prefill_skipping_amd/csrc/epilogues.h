@@ -63,10 +63,17 @@ struct EpiStore {
 };
 
 // Residual add into the fp32 residual stream: x += o W^T  (O and down projections).
+// Optionally (act != NULL, vec8 only) it also hands the next projection its
+// input: act = bf16 of the new x in the panel layout, and ss = the sum of
+// squares of each eight-pair unit's 16 new x values at [row * ld/16 +
+// (col / 2P) * P/8 + (col % 2P) / 8], from which the row's RMSNorm factor
+// is summed in fixed order.
 struct EpiResidual {
   float* x;
   int ld;
   int P;
+  bf16_t* act = nullptr;
+  float* ss = nullptr;
   SKV_DEV void operator()(int row, int col, float v0, float v1) const {
     float* p = x + (int64_t)row * ld + col;
     p[0] += v0;
@@ -93,6 +100,14 @@ struct EpiResidual {
     }
     store8(p, y0);
     store8(p + P, y1);
+    if (act) {
+      store8(act + panel_off(row, col, ld), y0);
+      store8(act + panel_off(row, col + P, ld), y1);
+      float q = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) q += y0[e] * y0[e] + y1[e] * y1[e];
+      ss[(int64_t)row * (ld / 16) + (col / (2 * P)) * (P / 8) + (col % (2 * P)) / 8] = q;
+    }
   }
   SKV_DEV void vec8(int row, int col, const float* a, const float* b) const { vec8(row, col, a, b, pre8(row, col)); }
 };
@@ -123,16 +138,21 @@ struct EpiSwiGLU {
 // SwiGLU for the prompt-token GEMM: h is written in the panel layout
 // (panel_off with F columns), where it is the A operand of the down
 // projection.  Gate/up columns interleaved in blocks of P as in EpiSwiGLU.
+// rs (optional): per-row factor applied to gate and up first (the RMSNorm
+// factor of an input that reached the GEMM un-normalised).
 struct EpiSwiGLUPanel {
   bf16_t* h;
   int F;
   int P;
-  SKV_DEV void vec8(int row, int col, const float* g, const float* u) const {
+  const float* rs = nullptr;
+  SKV_DEV float scale(int row) const { return rs ? rs[row] : 1.0f; }
+  SKV_DEV void vec8(int row, int col, const float* g, const float* u) const { vec8s(row, col, g, u, scale(row)); }
+  SKV_DEV void vec8s(int row, int col, const float* g, const float* u, float sr) const {
     int blk = col / (2 * P);
     int c = col - blk * 2 * P;
     float y[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) y[e] = silu_f(g[e]) * u[e];
+    for (int e = 0; e < 8; ++e) y[e] = silu_f(g[e] * sr) * (u[e] * sr);
     store8(h + panel_off(row, blk * P + c, F), y);
   }
 };
@@ -166,7 +186,12 @@ struct EpiQKV {
   const float* rope_cos;  // [max_pos, P]
   const float* rope_sin;
   int dq, dkv, dh, P;
+  const float* rs = nullptr;  // optional per-row factor (RMSNorm of an un-normalised input)
   SKV_DEV void operator()(int row, int col, float v0, float v1) const {
+    if (rs) {
+      v0 *= rs[row];
+      v1 *= rs[row];
+    }
     if (col < dq) {
       int i = col % dh;
       int p = pos[row];
@@ -194,7 +219,17 @@ struct EpiQKV {
       cache.v[kv_index(sl, h, i + P, cache.hkv, dh)] = from_f32<T>(v1);
     }
   }
-  SKV_DEV void vec8(int row, int col, const float* a, const float* b) const {
+  SKV_DEV float scale(int row) const { return rs ? rs[row] : 1.0f; }
+  SKV_DEV void vec8(int row, int col, const float* a_in, const float* b_in) const {
+    vec8s(row, col, a_in, b_in, scale(row));
+  }
+  SKV_DEV void vec8s(int row, int col, const float* a_in, const float* b_in, float sr) const {
+    float a[8], b[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      a[e] = a_in[e] * sr;
+      b[e] = b_in[e] * sr;
+    }
     float y0[8], y1[8];
     if (col < dq) {
       rope8(a, b, rope_cos, rope_sin, pos[row], P, col % dh, y0, y1);
@@ -231,9 +266,14 @@ struct EpiKVSkip {
   const float* rope_cos;
   const float* rope_sin;
   int dkv, dh, P, hkv;
+  const float* rs = nullptr;  // optional per-row factor (the row-rms of x_{l+1})
   SKV_DEV void operator()(int row, int col, float a, float b) const {
     int sl = slot[row];
     if (sl < 0) return;
+    if (rs) {
+      a *= rs[row];
+      b *= rs[row];
+    }
     int g = col / (2 * dkv);
     int c = col - g * 2 * dkv;
     if (c < dkv) {
@@ -252,9 +292,19 @@ struct EpiKVSkip {
       vp[kv_index(sl, h, i + P, hkv, dh)] = from_f32<T>(b);
     }
   }
-  SKV_DEV void vec8(int row, int col, const float* a, const float* b) const {
+  SKV_DEV float scale(int row) const { return rs ? rs[row] : 1.0f; }
+  SKV_DEV void vec8(int row, int col, const float* a_in, const float* b_in) const {
+    vec8s(row, col, a_in, b_in, scale(row));
+  }
+  SKV_DEV void vec8s(int row, int col, const float* a_in, const float* b_in, float sr) const {
     int sl = slot[row];
     if (sl < 0) return;
+    float a[8], b[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      a[e] = a_in[e] * sr;
+      b[e] = b_in[e] * sr;
+    }
     int g = col / (2 * dkv);
     int c = col - g * 2 * dkv;
     if (c < dkv) {

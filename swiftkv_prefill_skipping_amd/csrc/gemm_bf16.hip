@@ -119,6 +119,24 @@ struct EpiAhead {
     e.vec8(row, col, a, b);
   }
 };
+// Epilogues that scale each row by a factor they read (the RMSNorm factor
+// of an un-normalised input) load it one pass ahead as well.
+template <class Epi>
+struct EpiAheadScaled {
+  struct Pre {
+    float sr;
+  };
+  static SKV_DEV Pre load(const Epi& e, int row, int) { return {e.scale(row)}; }
+  static SKV_DEV void apply(const Epi& e, int row, int col, const float* a, const float* b, const Pre& p) {
+    e.vec8s(row, col, a, b, p.sr);
+  }
+};
+template <>
+struct EpiAhead<EpiSwiGLUPanel> : EpiAheadScaled<EpiSwiGLUPanel> {};
+template <>
+struct EpiAhead<EpiQKV<bf16_t>> : EpiAheadScaled<EpiQKV<bf16_t>> {};
+template <>
+struct EpiAhead<EpiKVSkip<bf16_t>> : EpiAheadScaled<EpiKVSkip<bf16_t>> {};
 template <>
 struct EpiAhead<EpiResidual> {
   using Pre = EpiResidual::Pre;

@@ -60,6 +60,14 @@ hipError_t launch_rmsnorm(const float* x, const int32_t* rows_idx, const float* 
 hipError_t launch_rmsnorm_panel(const float* x, const float* gamma, int rows, int d, float eps, bf16_t* y,
                                 hipStream_t stream);
 
+// Un-normalised input of the next projection: y = bf16(x) in the panel
+// layout (d columns, d % 32 == 0) and r[row] = 1 / sqrt(mean x^2 + eps).
+hipError_t launch_rows_rms_panel(const float* x, int rows, int d, float eps, bf16_t* y, float* r,
+                                 hipStream_t stream);
+// r[row] from the d/16 partial sums of squares per row that EpiResidual
+// writes (summed in a fixed order); d % 16 == 0.
+hipError_t launch_rms_from_partials(const float* ss, int rows, int d, float eps, float* r, hipStream_t stream);
+
 // y[r, :] = x[rows_idx[r], :]  (fp32 rows)
 hipError_t launch_gather_rows(const float* x, const int32_t* rows_idx, int rows, int d, float* y,
                               hipStream_t stream);

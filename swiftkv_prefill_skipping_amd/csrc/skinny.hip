@@ -99,11 +99,27 @@ __global__ void skinny_finalize_kernel(const float* __restrict__ partial, int M,
   const int row = (int)(idx / half);
   const int j = (int)(idx % half);
   const int col = (j / 64) * 128 + (j % 64);
+  // splits summed in order; eight at a time so their loads are in flight together
+  const float* p = partial + (int64_t)row * N + col;
+  const int64_t ss = (int64_t)SK_ROWS * N;
   float v0 = 0.f, v1 = 0.f;
-  for (int s = 0; s < nsplit; ++s) {
-    const float* p = partial + ((int64_t)s * SK_ROWS + row) * N + col;
-    v0 += p[0];
-    v1 += p[64];
+  int s = 0;
+  for (; s + 8 <= nsplit; s += 8) {
+    float a[8], b[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      a[u] = p[(s + u) * ss];
+      b[u] = p[(s + u) * ss + 64];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      v0 += a[u];
+      v1 += b[u];
+    }
+  }
+  for (; s < nsplit; ++s) {
+    v0 += p[s * ss];
+    v1 += p[s * ss + 64];
   }
   epi(row, col, v0, v1);
 }
