@@ -96,45 +96,6 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
   }
 }
 
-// RMSNorm into the panel layout: one wave per row, lane l holding columns
-// [8l + 512i, 8l + 512i + 8) (those below d) in registers, so x is read
-// once.  A store instruction writes 16 bytes per lane: 64-byte runs, one
-// per 32-column block, which the next row's wave completes to full lines.
-constexpr int kNormMaxChunks = 16;  // d <= 8192
-__global__ __launch_bounds__(256) void rmsnorm_panel_kernel(const float* __restrict__ x,
-                                                            const float* __restrict__ gamma, int rows, int d,
-                                                            float eps, bf16_t* __restrict__ y) {
-  const int lane = threadIdx.x & 63;
-  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (r >= rows) return;  // whole waves
-  const int nch = (d + 511) / 512;
-  const float* xr = x + (int64_t)r * d + lane * 8;
-  float v[kNormMaxChunks][8];
-  float ss = 0.f;
-#pragma unroll
-  for (int i = 0; i < kNormMaxChunks; ++i) {
-    if (i < nch && lane * 8 + i * 512 < d) {
-      load8(xr + i * 512, v[i]);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) ss += v[i][e] * v[i][e];
-    }
-  }
-  ss = warp_sum(ss);
-  const float inv = 1.0f / sqrtf(ss / (float)d + eps);
-#pragma unroll
-  for (int i = 0; i < kNormMaxChunks; ++i) {
-    if (i < nch && lane * 8 + i * 512 < d) {
-      const int c = lane * 8 + i * 512;
-      float g[8] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
-      if (gamma) load8(gamma + c, g);
-      float o[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] = v[i][e] * inv * g[e];
-      store8(y + panel_off(r, c, d), o);
-    }
-  }
-}
-
 // Un-normalised GEMM input of a row plus its RMSNorm factor: y = bf16(x) in
 // the panel layout, r[row] = 1 / sqrt(mean(x^2) + eps).  One wave per row.
 __global__ __launch_bounds__(256) void rows_rms_panel_kernel(const float* __restrict__ x, int rows, int d, float eps,
@@ -262,14 +223,6 @@ hipError_t launch_rmsnorm(const float* x, const int32_t* rows_idx, const float* 
                           T* y, hipStream_t stream) {
   if (rows <= 0) return hipSuccess;
   hipLaunchKernelGGL(rmsnorm_kernel<T>, dim3(rows), dim3(256), 0, stream, x, rows_idx, gamma, d, eps, y);
-  return hipGetLastError();
-}
-
-hipError_t launch_rmsnorm_panel(const float* x, const float* gamma, int rows, int d, float eps, bf16_t* y,
-                                hipStream_t stream) {
-  if (rows <= 0) return hipSuccess;
-  if (d % kPanelCols || d > 512 * kNormMaxChunks) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(rmsnorm_panel_kernel, dim3((rows + 3) / 4), dim3(256), 0, stream, x, gamma, rows, d, eps, y);
   return hipGetLastError();
 }
 

@@ -55,11 +55,6 @@ template <typename T>
 hipError_t launch_rmsnorm(const float* x, const int32_t* rows_idx, const float* gamma, int rows, int d, float eps,
                           T* y, hipStream_t stream);
 
-// Same RMSNorm for rows 0..rows-1 of x into bf16 y in the panel layout
-// (panel_off with d columns); d % 32 == 0 and d <= 8192.
-hipError_t launch_rmsnorm_panel(const float* x, const float* gamma, int rows, int d, float eps, bf16_t* y,
-                                hipStream_t stream);
-
 // Un-normalised input of the next projection: y = bf16(x) in the panel
 // layout (d columns, d % 32 == 0) and r[row] = 1 / sqrt(mean x^2 + eps).
 hipError_t launch_rows_rms_panel(const float* x, int rows, int d, float eps, bf16_t* y, float* r,
