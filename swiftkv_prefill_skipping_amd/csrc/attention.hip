@@ -90,13 +90,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // whole 64 KB stages the output at the end
   __shared__ __attribute__((aligned(1024))) bf16_t smem[4][FA_KT * FA_DH];
 
-  const int b = blockIdx.y;
+  // grid: x = (prompt, head group), y = query tile counted from the last, so
+  // workgroups are dispatched longest first across the whole batch
+  const int ngrp = hq / 4;
+  const int b = blockIdx.x / ngrp;
+  const int zg = blockIdx.x - b * ngrp;
   const int tok0 = cu[b];
   const int N = cu[b + 1] - tok0;  // new queries, at positions C .. C + N - 1
   const int C = ctx ? ctx[b] : 0;  // positions cached before them
   const int NK = C + N;            // keys
   const int nqb = (N + 63) / 64;
-  const int qb = gridDim.x - 1 - blockIdx.x;  // longest rows first
+  const int qb = gridDim.y - 1 - blockIdx.y;
   if (qb >= nqb) return;
   const int q0w = qb * 64;
 
@@ -104,9 +108,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hh = lane >> 5;
-  const int h = blockIdx.z * 4 + (wave & 3);
+  const int h = zg * 4 + (wave & 3);
   const int q0 = q0w + (wave >> 2) * 32;  // this wave's 32 queries
-  const int g = (blockIdx.z * 4) / rep;
+  const int g = (zg * 4) / rep;
   const int hkv = cache.hkv;
   const int dq = hq * FA_DH;
 
@@ -569,7 +573,7 @@ hipError_t launch_attn_prefill_bf16(const bf16_t* q, CacheSlot<bf16_t> cache, co
   if (batch <= 0 || max_new <= 0) return hipSuccess;
   const int rep = hq / cache.hkv;
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)FA_DH);
-  dim3 grid((max_new + 63) / 64, batch, hq / 4);
+  dim3 grid(batch * (hq / 4), (max_new + 63) / 64);
   hipLaunchKernelGGL(attn_prefill8_kernel<false>, grid, dim3(512), 0, stream, q, cache, Fp8Slot{}, cu_seqlens,
                      ctx_lens, block_tables, max_blocks, hq, rep, scale_log2, o);
   return hipGetLastError();
@@ -582,7 +586,7 @@ hipError_t launch_attn_prefill_fp8(const bf16_t* q, Fp8Slot cache, const int32_t
   if (cache.dh != FA_DH) return hipErrorInvalidValue;
   const int rep = hq / cache.hkv;
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)FA_DH);
-  dim3 grid((max_new + 63) / 64, batch, hq / 4);
+  dim3 grid(batch * (hq / 4), (max_new + 63) / 64);
   hipLaunchKernelGGL(attn_prefill8_kernel<true>, grid, dim3(512), 0, stream, q,
                      CacheSlot<bf16_t>{nullptr, nullptr, cache.hkv, cache.dh}, cache, cu_seqlens, ctx_lens,
                      block_tables, max_blocks, hq, rep, scale_log2, o);
