@@ -50,6 +50,18 @@ constexpr int FA_DH = 128;
 constexpr int FA_KT = 64;  // keys per tile
 
 
+// x combined with lane (l ^ 32)'s value through gfx950's v_permlane32_swap:
+// the swap leaves lane l holding (value of lane l & 31, value of lane l | 32),
+// so both halves see the pair in the same order
+SKV_DEV float xor32_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+SKV_DEV float xor32_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 SKV_DEV void wait_loads_then_barrier() {
   __builtin_amdgcn_sched_barrier(0);
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -211,7 +223,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int st = 0; st < 2; ++st)
 #pragma unroll
       for (int v = 0; v < 16; ++v) mt = fmaxf(mt, sacc[st][v]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * scale_log2;
+    mt = xor32_max(mt) * scale_log2;
     if (__builtin_amdgcn_ballot_w64(mt > m_run + kLazy) != 0) {
       const float m_new = fmaxf(m_run, mt);
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -239,7 +251,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       pf[kk] = as_bf16x8(u32x4_t{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
                                  pack_bf16x2(p[6], p[7])});
     }
-    ls += __shfl_xor(ls, 32, 64);
+    ls = xor32_sum(ls);
     l_run += ls;
     const bf16_t* sv = smem[2 + vb];
     const int tj = lane & 15, ta = tj >> 2, tb = tj & 3;
