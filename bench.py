@@ -61,8 +61,8 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(workload, batch, cached, n_prompts=2):
-    """Time the oracle on the host cores over the batch's shortest prompts (about 10 s of work at the 8B shape)."""
+def cpu_baseline(workload, batch, cached, n_prompts=3):
+    """Time the oracle on the host cores over the batch's three shortest prompts (10-15 s of work at the 8B shape)."""
     from threadpoolctl import threadpool_info
     from oracle import swiftkv_oracle as O
     from tests.helpers import dims_of, oracle_weights

@@ -804,7 +804,7 @@ skv_status run_step(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, const S
     }
     {
       EpiResidual epi{m->x, d, kBf16 ? 64 : 16, kBf16 ? (bf16_t*)act : nullptr, kBf16 ? m->ssp : nullptr};
-      Prof p(m, SKV_K_GEMM_O, s, 2.0 * T_ * d * dq, gemm_bytes(T_, d, dq, E, 8));
+      Prof p(m, SKV_K_GEMM_O, s, 2.0 * T_ * d * dq, gemm_bytes(T_, d, dq, E, kBf16 ? 8 + 2 + 0.25 : 8));
       if constexpr (kBf16)
         SKV_HIP(launch_gemm_bf16((const bf16_t*)obuf, (const bf16_t*)Ly.wo, T_, d, dq, epi, m->gemm_ws, m->gemm_ws_elems, s));
       else
@@ -828,7 +828,7 @@ skv_status run_step(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, const S
     }
     {
       EpiResidual epi{m->x, d, kBf16 ? 64 : 16, kBf16 ? (bf16_t*)act : nullptr, kBf16 ? m->ssp : nullptr};
-      Prof p(m, SKV_K_GEMM_DOWN, s, 2.0 * T_ * d * f, gemm_bytes(T_, d, f, E, 8));
+      Prof p(m, SKV_K_GEMM_DOWN, s, 2.0 * T_ * d * f, gemm_bytes(T_, d, f, E, kBf16 ? 8 + 2 + 0.25 : 8));
       if constexpr (kBf16)
         SKV_HIP(launch_gemm_bf16((const bf16_t*)hbuf, (const bf16_t*)Ly.wdown, T_, d, f, epi, m->gemm_ws, m->gemm_ws_elems, s));
       else
