@@ -478,7 +478,7 @@ class StepResult:
 
 def swiftkv_step(dims: Dims, weights: WeightSource, past: Sequence[Dict[int, Tuple[np.ndarray, np.ndarray]]],
                  new_tokens: Sequence[np.ndarray], l: int, g: int = 1, dtype=np.float32,
-                 kv_fp8: bool = False) -> StepResult:
+                 kv_fp8: bool = False, store: Optional[Callable] = None) -> StepResult:
     """One forward pass over a mixed batch of prompt chunks and decode tokens.
 
     Source: [P1] "Inference Implementation in Production Serving Frameworks"
@@ -496,10 +496,12 @@ def swiftkv_step(dims: Dims, weights: WeightSource, past: Sequence[Dict[int, Tup
     (new arrays; ``past`` is not modified) and the logits after each
     sequence's last new token.  ``kv_fp8``: the cache holds per-token FP8
     values (fp8_kv_roundtrip of each new token's K and V); ``past`` then
-    holds such values too.
+    holds such values too.  ``store``: as in swiftkv_prefill (the stored
+    tensors rounded, e.g. to bf16).
     """
     L, eps = dims.n_layers, dims.rms_eps
     kq = fp8_kv_roundtrip if kv_fp8 else _keep
+    st = store if store is not None else _keep
     if not 0 <= l <= L or g < 1:
         raise ValueError("bad l or g")
     if len(past) != len(new_tokens) or any(len(t) < 1 for t in new_tokens):
@@ -518,12 +520,12 @@ def swiftkv_step(dims: Dims, weights: WeightSource, past: Sequence[Dict[int, Tup
     for i in range(1, l + 1):                      # layers 1..l: every new token
         W = weights.layer(i)
         for b in range(len(past)):
-            q, k, v = qkv_projection(xs[b], W, pos[b], dims, fc)
+            q, k, v = qkv_projection(xs[b], W, pos[b], dims, fc, st)
             K = np.concatenate([kv[b][i - 1][0], kq(k)], axis=0)
             V = np.concatenate([kv[b][i - 1][1], kq(v)], axis=0)
             kv[b][i - 1] = (K, V)
-            x = xs[b] + matmul_wt(attention_with_past(q, K, V, pos[b], fc), W["wo"], fc)
-            xs[b] = mlp_residual(x, W, dims, fc)
+            x = xs[b] + matmul_wt(st(attention_with_past(q, K, V, pos[b], fc)), W["wo"], fc)
+            xs[b] = mlp_residual(x, W, dims, fc, st)
 
     ys = [x[-1:].copy() for x in xs]
     for j in range(l + 1, L + 1):
@@ -532,23 +534,23 @@ def swiftkv_step(dims: Dims, weights: WeightSource, past: Sequence[Dict[int, Tup
         if representative(j, l, g) == j:           # KV of the skipped layers from x_{l+1}
             for b in range(len(past)):
                 n = xs[b].shape[0]
-                a = rmsnorm(xs[b], W["attn_norm"], eps)
+                a = st(rmsnorm(xs[b], W["attn_norm"], eps))
                 k = matmul_wt(a, W["wk"], fc).reshape(n, dims.n_kv_heads, dims.head_dim)
                 v = matmul_wt(a, W["wv"], fc).reshape(n, dims.n_kv_heads, dims.head_dim)
-                kv[b][s] = (np.concatenate([kv[b][s][0], kq(rope(k, pos[b], dims.rope_theta))], axis=0),
-                            np.concatenate([kv[b][s][1], kq(v)], axis=0))
+                kv[b][s] = (np.concatenate([kv[b][s][0], kq(st(rope(k, pos[b], dims.rope_theta)))], axis=0),
+                            np.concatenate([kv[b][s][1], kq(st(v))], axis=0))
         for b in range(len(past)):                 # the continuing token
             K, V = kv[b][s]
             p_last = int(pos[b][-1])
-            a = rmsnorm(ys[b], W["attn_norm"], eps)
+            a = st(rmsnorm(ys[b], W["attn_norm"], eps))
             q = matmul_wt(a, W["wq"], fc).reshape(1, dims.n_q_heads, dims.head_dim)
-            q = rope(q, np.array([p_last]), dims.rope_theta)
-            o = attention_with_past(q, K, V, np.array([p_last]), fc)
+            q = st(rope(q, np.array([p_last]), dims.rope_theta))
+            o = st(attention_with_past(q, K, V, np.array([p_last]), fc))
             y = ys[b] + matmul_wt(o, W["wo"], fc)
-            ys[b] = mlp_residual(y, W, dims, fc)
+            ys[b] = mlp_residual(y, W, dims, fc, st)
 
     logits = np.concatenate(
-        [matmul_wt(rmsnorm(y, weights.final_norm, eps), weights.lm_head, fc) for y in ys], axis=0)
+        [matmul_wt(st(rmsnorm(y, weights.final_norm, eps)), weights.lm_head, fc) for y in ys], axis=0)
     return StepResult(kv, logits, fc.total)
 
 

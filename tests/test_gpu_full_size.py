@@ -69,6 +69,75 @@ def test_llama8b_l24_acrosskv4_b32_sampled():
     _check_sampled(w, batch, [17])
 
 
+def test_llama8b_decode_step_and_fp8_cache_sampled():
+    """The bench workload's decode step and FP8 cache at full size: the whole batch prefilled on the GPU, one
+    decode token per prompt (skv_step); the shortest prompt's decode logits against the oracle's step after its
+    prefill.  Then the same batch with the per-token FP8 cache: that prompt's prefill logits and the K/V of a
+    prompt-token slot and of a skipped slot against the oracle with the FP8 cache.  Bars as for the prefill (G18
+    fallback to the bf16-storage evaluation) and, for the FP8 cache, the FP8 bars of tests/test_gpu_step."""
+    import torch
+    from swiftkv_prefill_skipping_amd import runner
+    from tests.test_gpu_step import FP8_LOGITS_TOL, fp8_kv_check
+    w = si.WORKLOADS["llama8b_l16_b16"]
+    batch = si.make_batch(w)
+    B = len(batch.lengths)
+    b = int(np.argmin(batch.lengths))
+    n = int(batch.lengths[b])
+    extra = 2
+    bt = np.full((B, batch.block_tables.shape[1] + extra), -1, dtype=np.int32)
+    for i, ln in enumerate(batch.lengths):
+        nb = -(-int(ln) // 16)
+        bt[i, :nb] = batch.block_tables[i, :nb]
+        bt[i, nb:nb + extra] = batch.num_blocks + i * extra + np.arange(extra)
+    nxt = si.randint(w.input_seed, 7, B, w.shape.vocab)
+    dims = dims_of(w.shape)
+    t0 = time.time()
+    cached = CachedLayers()
+    model = runner.load_seeded_model(w, batch.total_tokens, B, batch.max_seqlen + 16 * extra, layer_hook=cached.hook)
+    cache = runner.Cache(model, batch.num_blocks + B * extra)
+    db = runner.device_batch(batch)
+    ds = runner.device_step(nxt, [1] * B, batch.lengths, bt)
+    runner.prefill(model, cache, db)
+    lg = runner.step(model, cache, ds)
+    torch.cuda.synchronize()
+    lg = lg.cpu().numpy()
+    assert np.isfinite(lg).all()
+    _say(f"[full] decode step of {B} tokens after the prefill done ({time.time() - t0:.1f} s); oracle on prompt {b}")
+    W = oracle_weights(w, cached)
+    res = {}
+    for mode, store in (("fp32", None), ("bf16-storage", round_bf16)):
+        kw = {} if store is None else {"store": store}
+        pre = O.swiftkv_prefill(dims, W, [batch.tokens[b]], w.swiftkv_l, w.acrosskv_g, **kw)
+        res[mode] = O.swiftkv_step(dims, W, [pre.kv[0]], [nxt[b:b + 1]], w.swiftkv_l, w.acrosskv_g, **kw)
+    e = max_rel(lg[b], res["fp32"].logits[0])
+    e_ref = max_rel(res["bf16-storage"].logits[0], res["fp32"].logits[0])
+    _say(f"[full] decode logits of prompt {b}: {e:.3e} (bf16-storage evaluation {e_ref:.3e})")
+    assert e < 2e-2 or e <= 1.5 * e_ref, (e, e_ref)
+    model.close()
+    cache.close()
+
+    t1 = time.time()
+    m8 = runner.load_seeded_model(w, batch.total_tokens, B, batch.max_seqlen, kv_fp8=True)
+    c8 = runner.Cache(m8, batch.num_blocks)
+    lg8 = runner.prefill(m8, c8, db)
+    torch.cuda.synchronize()
+    lg8 = lg8.cpu().numpy()
+    _say(f"[full] FP8-cache prefill done ({time.time() - t1:.1f} s)")
+    o8 = O.swiftkv_prefill(dims, W, [batch.tokens[b]], w.swiftkv_l, w.acrosskv_g, kv_fp8=True)
+    o8b = O.swiftkv_prefill(dims, W, [batch.tokens[b]], w.swiftkv_l, w.acrosskv_g, kv_fp8=True, store=round_bf16)
+    e8 = max_rel(lg8[b], o8.logits[0])
+    e8_ref = max_rel(o8b.logits[0], o8.logits[0])
+    _say(f"[full] FP8 prefill logits of prompt {b}: {e8:.3e} (bf16-storage evaluation {e8_ref:.3e})")
+    assert e8 < FP8_LOGITS_TOL or e8 <= 1.5 * e8_ref, (e8, e8_ref)
+    gkv = gpu_kv(c8, w, batch, b)
+    for s in (0, w.swiftkv_l - 1, w.swiftkv_l, max(gkv)):
+        for t, name in ((0, "K"), (1, "V")):
+            tol = max(2e-2, 1.5 * max_rel(o8b.kv[0][s][t], o8.kv[0][s][t]))
+            ok, r, mr = fp8_kv_check(gkv[s][t], o8.kv[0][s][t], tol=tol)
+            _say(f"[full] FP8 slot {s} {name}: {r:.2f} of the bound (max-rel {mr:.2e}, tol {tol:.2e})")
+            assert ok, (s, name, r, mr)
+
+
 def test_small_model_long_context():
     """Attention over long prompts against the full oracle: a 3-layer model (d=512, 8/2 heads of 128, l=2) on an
     8192-token and a 3000-token prompt; every KV slot and both logits rows (the last token attends over all keys of

@@ -126,3 +126,13 @@ def test_step_flop_counter_matches_closed_form(l, g):
     assert r.flops == O.step_flops(dims, l, g, [6, 0], [4, 7])
     # without cached positions the step is a prefill
     assert O.step_flops(dims, l, g, [0, 0], [10, 7]) == O.prefill_flops(dims, l, g, [10, 7])[1]
+
+
+def test_step_storage_hook_identity_is_plain():
+    dims = tiny_dims()
+    W = tiny_weights(dims, dtype=np.float32)
+    ps = prompts_for(dims, [11, 5], seed=13)
+    past = O.swiftkv_prefill(dims, W, [ps[0][:8]], 2, 1).kv[0]
+    a = O.swiftkv_step(dims, W, [past, {}], [ps[0][8:], ps[1]], 2, 1)
+    b = O.swiftkv_step(dims, W, [past, {}], [ps[0][8:], ps[1]], 2, 1, store=lambda t: t)
+    assert np.array_equal(a.logits, b.logits)
