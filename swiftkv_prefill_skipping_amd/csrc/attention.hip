@@ -62,6 +62,48 @@ SKV_DEV float xor32_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+SKV_DEV float xor16_sum(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+template <int CTRL>
+SKV_DEV float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+// x + (value of lane l ^ off) without going through LDS: DPP within a row of
+// 16 lanes (quad permutes for 1 and 2, row rotate by 8 for 8) and the
+// gfx950 permlane swaps across rows.  uniform4: lanes already agree within
+// aligned groups of 4 (a butterfly that started at 1), so the half-row
+// mirror stands in for xor 4.
+SKV_DEV float xor_add(float x, int off, bool uniform4) {
+  switch (off) {
+    case 1: return x + dpp_f<0xB1>(x);
+    case 2: return x + dpp_f<0x4E>(x);
+    case 4: return uniform4 ? x + dpp_f<0x141>(x) : x + __shfl_xor(x, 4, 64);
+    case 8: return x + dpp_f<0x128>(x);
+    case 16: return xor16_sum(x);
+    case 32: return xor32_sum(x);
+    default: return x + __shfl_xor(x, off, 64);
+  }
+}
+
+// Whole-wave max / sum through the same DPP and permlane steps (offsets
+// 1, 2, 4, 8, 16, 32); every lane ends with the result.
+SKV_DEV float wave_max_x(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));
+  v = fmaxf(v, dpp_f<0x4E>(v));
+  v = fmaxf(v, dpp_f<0x141>(v));
+  v = fmaxf(v, dpp_f<0x128>(v));
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return xor32_max(v);
+}
+SKV_DEV float wave_sum_x(float v) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) v = xor_add(v, off, true);
+  return v;
+}
+
 SKV_DEV void wait_loads_then_barrier() {
   __builtin_amdgcn_sched_barrier(0);
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -471,7 +513,7 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const T* __restrict__ q,
 #pragma unroll
       for (int hh = 0; hh < RW_HG; ++hh) {
 #pragma unroll
-        for (int off = 1; off < LPK; off <<= 1) part[hh] += __shfl_xor(part[hh], off);
+        for (int off = 1; off < LPK; off <<= 1) part[hh] = xor_add(part[hh], off, true);
       }
       if (lane % LPK == 0) {
 #pragma unroll
@@ -484,7 +526,7 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const T* __restrict__ q,
     float mh[RW_HG];
 #pragma unroll
     for (int hh = 0; hh < RW_HG; ++hh) {
-      float m = warp_max(ps[hh][tid]);
+      float m = wave_max_x(ps[hh][tid]);
       if (lane == 0) red[hh][w] = m;
     }
     __syncthreads();
@@ -496,7 +538,7 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const T* __restrict__ q,
       const float x = ps[hh][tid];
       const float p = x == -INFINITY ? 0.f : __expf(x - mh[hh]);
       ps[hh][tid] = p;
-      const float sm = warp_sum(p);
+      const float sm = wave_sum_x(p);
       if (lane == 0) red[hh][w] = sm;
     }
     __syncthreads();
@@ -535,7 +577,7 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const T* __restrict__ q,
 #pragma unroll
       for (int e = 0; e < VEC; ++e)
 #pragma unroll
-        for (int off = LPK; off < 64; off <<= 1) acc[hh][e] += __shfl_xor(acc[hh][e], off);
+        for (int off = LPK; off < 64; off <<= 1) acc[hh][e] = xor_add(acc[hh][e], off, false);
     if (sub == 0) {
 #pragma unroll
       for (int hh = 0; hh < RW_HG; ++hh)
