@@ -606,9 +606,12 @@ __global__ void attn_combine_kernel(const float* __restrict__ ws, int hq, int dh
   if (d >= dh) return;
   const int stride = dh + 2;
   const float* w = ws + ((int64_t)r * hq + h) * nchunks * stride;
+  // chunks in order; unrolled so a long context keeps several loads in flight
   float m = -INFINITY;
+#pragma unroll 8
   for (int c = 0; c < nchunks; ++c) m = fmaxf(m, w[c * stride]);
   float l = 0.f, acc = 0.f;
+#pragma unroll 8
   for (int c = 0; c < nchunks; ++c) {
     float mc = w[c * stride];
     if (mc == -INFINITY) continue;
