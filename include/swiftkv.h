@@ -110,7 +110,10 @@ skv_status skv_model_load_globals(skv_model* m, const void* embed, const void* f
  * interleaved; for an AcrossKV representative j > l, its input-RMSNorm gain
  * folded into its K and V rows (W~ = W_KV diag(gamma_j), exact in real
  * arithmetic: RMSNorm(x; gamma) W^T = r (x (W diag gamma)^T) with
- * r = 1/sqrt(mean x^2 + eps)).  Synchronous. */
+ * r = 1/sqrt(mean x^2 + eps)).  bf16 models fold the same way the attention
+ * gain of an unskipped layer into its Q/K/V rows and its MLP gain into its
+ * gate/up rows (the prompt-token projections then scale by r in their
+ * epilogues).  Synchronous. */
 skv_status skv_model_load_layer(skv_model* m, int32_t layer, const skv_layer_weights* w);
 
 /* Free everything the model owns.  Accepts NULL. */
