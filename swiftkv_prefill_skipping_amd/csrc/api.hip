@@ -331,9 +331,9 @@ skv_status skv_model_create(const skv_model_config* cfg, skv_model** out) {
     if (m->G > 0) pe = std::max(pe, skinny_partial_elems((int)(m->G * 2 * dkv), (int)d));
     m->partial_elems = pe;
     ALLOC(m->partial, (size_t)pe * 4);
-    m->attn_ws_elems = attn_rows_ws_elems((int)RY, c.max_seqlen, c.n_q_heads, c.head_dim);
+    m->attn_ws_elems = attn_rows_ws_elems((int)RY, c.max_seqlen, c.n_q_heads, c.head_dim, true);
   } else {
-    m->attn_ws_elems = attn_rows_ws_elems((int)std::max(T, B), c.max_seqlen, c.n_q_heads, c.head_dim);
+    m->attn_ws_elems = attn_rows_ws_elems((int)std::max(T, B), c.max_seqlen, c.n_q_heads, c.head_dim, false);
   }
   ALLOC(m->attn_ws, (size_t)m->attn_ws_elems * 4);
   if (m->bf16) {

@@ -32,10 +32,11 @@
 //    are dequantised (code * the key's scale, rounded to bf16) on the way
 //    into the same LDS layout.
 //
-// 2. attn_rows_kernel + attn_combine_kernel (fp32 or bf16, vector ALU):
-//    attention of an explicit list of query rows (the last prompt token of
-//    each prompt at layers l+1..L; every token for fp32 models), split over
-//    256-key chunks with a fixed-order combine.
+// 2. attn_rows_kernel / attn_dec_kernel + attn_combine_kernel (vector
+//    ALU): attention of an explicit list of query rows (the last prompt
+//    token of each prompt at layers l+1..L, decode rows; every token for
+//    fp32 models), split over key chunks (64 keys for bf16 rows of head_dim
+//    128, 256 otherwise) with a fixed-order combine.
 #include <math.h>
 
 #include "common.h"
@@ -600,6 +601,188 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const T* __restrict__ q,
   }
 }
 
+// bf16 rows with head_dim 128 (the decode and last-token rows): one wave
+// per 64-key chunk of one row and kv head, four independent waves per
+// workgroup, no workgroup barrier.  Every K and V load of the chunk is
+// issued before any result is consumed (keys past the context read slot 0
+// and are masked), so a wave waits for memory about twice, not per key.
+//  * block ids: the chunk spans four 16-key blocks, uniform across the wave.
+//  * scores: lane (k, j) = (lane / 4, lane % 4) takes key pass*16 + k and
+//    dims 32 j .. + 32 (four 16-byte loads), bf16 pair dot products
+//    (v_dot2c_f32_bf16) against the row's q, then a quad reduction; the
+//    chunk's softmax statistics reduce across the 16 key lanes and the
+//    probabilities go to wave-local LDS.
+//  * P.V: lane (b, c) = (lane / 16, lane % 16) takes the 16 keys of block b,
+//    dims 8 c .. + 8 (one 16-byte load per key), for all four heads; a
+//    reduce-scatter over the four blocks with the permlane swaps leaves
+//    head b's sums in the lanes of block b.
+// Writes (max, sum, unnormalised o) per head and chunk like attn_rows_kernel.
+constexpr int DC_KEYS = 64;
+__global__ __launch_bounds__(256) void attn_dec_kernel(const bf16_t* __restrict__ q, CacheSlot<bf16_t> cache,
+                                                       const int32_t* __restrict__ row_seq,
+                                                       const int32_t* __restrict__ row_pos,
+                                                       const int32_t* __restrict__ bt, int max_blocks, int hq,
+                                                       int nchunks, float scale, float* __restrict__ ws) {
+  constexpr int DH = 128;
+  __shared__ f32x4_t ps_s[4][DC_KEYS];  // [wave][key] -> probabilities of the wave's four heads
+  const int r = blockIdx.x, g = blockIdx.y;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int c = blockIdx.z * 4 + wave;
+  if (c >= nchunks) return;
+  const int hkv = cache.hkv;
+  const int rep = hq / hkv;
+  const int ctx = row_pos[r] + 1;
+  const int seq = row_seq[r];
+  const int stride = DH + 2;
+  float* wsr = ws + ((int64_t)r * hq + g * rep) * nchunks * stride + (int64_t)c * stride;
+  const int kbeg = c * DC_KEYS;
+  if (kbeg >= ctx) {  // empty chunk
+    if (lane < rep) {
+      wsr[(int64_t)lane * nchunks * stride] = -INFINITY;
+      wsr[(int64_t)lane * nchunks * stride + 1] = 0.f;
+    }
+    return;
+  }
+  const int nk = min(DC_KEYS, ctx - kbeg);
+  int blk[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) blk[b] = kbeg + 16 * b < ctx ? bt[(int64_t)seq * max_blocks + kbeg / kBlockSize + b] : 0;
+  const int kq = lane >> 2, j = lane & 3;   // score layout
+  const int vb = lane >> 4, vc = lane & 15;  // P.V layout
+  const int vblk = vb == 0 ? blk[0] : vb == 1 ? blk[1] : vb == 2 ? blk[2] : blk[3];
+  for (int h0 = 0; h0 < rep; h0 += RW_HG) {
+    const int nh = min(RW_HG, rep - h0);
+    // K of the lane's four keys (issued first), then q of heads h0 .. h0 + 3.
+    // The bf16 pairs for v_dot2c_f32_bf16 are taken from bf16x8 vectors by
+    // shufflevector: hipcc 7.2 lowers a bit_cast of a u32x4 element to bf16x2
+    // feeding the dot2 builtin to element 0 of the vector every time.
+    bf16x8_t kv[4][4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const bf16_t* kr = cache.k + kv_index(blk[p] * kBlockSize + kq, g, j * 32, hkv, DH);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) kv[p][i] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(kr + i * 8));
+    }
+    bf16x8_t qv[RW_HG][4];
+#pragma unroll
+    for (int hh = 0; hh < RW_HG; ++hh)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        qv[hh][i] = as_bf16x8(hh < nh ? *reinterpret_cast<const u32x4_t*>(q + ((int64_t)r * hq + g * rep + h0 + hh) * DH + j * 32 + i * 8)
+                                      : u32x4_t{0u, 0u, 0u, 0u});
+    float sc[4][RW_HG];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      float acc[RW_HG] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int hh = 0; hh < RW_HG; ++hh) {
+          const bf16x8_t kx = kv[p][i], qx = qv[hh][i];
+          float a = acc[hh];
+          a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(kx, kx, 0, 1), __builtin_shufflevector(qx, qx, 0, 1), a, false);
+          a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(kx, kx, 2, 3), __builtin_shufflevector(qx, qx, 2, 3), a, false);
+          a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(kx, kx, 4, 5), __builtin_shufflevector(qx, qx, 4, 5), a, false);
+          a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(kx, kx, 6, 7), __builtin_shufflevector(qx, qx, 6, 7), a, false);
+          acc[hh] = a;
+        }
+#pragma unroll
+      for (int hh = 0; hh < RW_HG; ++hh) {
+        float a = xor_add(acc[hh], 1, true);
+        a = xor_add(a, 2, true);
+        sc[p][hh] = p * 16 + kq < nk ? a * scale : -INFINITY;  // a select: garbage past the context never propagates
+      }
+    }
+    // V of the lane's 16 keys, in flight while the softmax runs
+    bf16x8_t vv[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      vv[i] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(cache.v + kv_index(vblk * kBlockSize + i, g, vc * 8, hkv, DH)));
+    // softmax statistics over the chunk, per head (lanes of a quad agree)
+    float mh[RW_HG], lh[RW_HG];
+    f32x4_t pe[4];
+#pragma unroll
+    for (int hh = 0; hh < RW_HG; ++hh) {
+      float m = fmaxf(fmaxf(sc[0][hh], sc[1][hh]), fmaxf(sc[2][hh], sc[3][hh]));
+      m = fmaxf(m, dpp_f<0x141>(m));
+      m = fmaxf(m, dpp_f<0x128>(m));
+      {
+        auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+        m = fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
+      }
+      m = xor32_max(m);
+      float l = 0.f;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const float e = sc[p][hh] == -INFINITY ? 0.f : __expf(sc[p][hh] - m);
+        l += e;
+        pe[p][hh] = e;
+      }
+      l = xor_add(l, 4, true);
+      l = xor_add(l, 8, true);
+      l = xor_add(l, 16, true);
+      l = xor_add(l, 32, true);
+      mh[hh] = m;
+      lh[hh] = l;
+    }
+    if (j == 0) {
+#pragma unroll
+      for (int p = 0; p < 4; ++p) ps_s[wave][p * 16 + kq] = pe[p];
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's probabilities are in LDS
+    // o[hh][8 vc .. + 8] over the 16 keys of block vb
+    float o[RW_HG][8];
+#pragma unroll
+    for (int hh = 0; hh < RW_HG; ++hh)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[hh][e] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const f32x4_t pk = ps_s[wave][vb * 16 + i];  // zero past the context
+      const bool live = vb * 16 + i < nk;
+      const u32x4_t raw = __builtin_bit_cast(u32x4_t, vv[i]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t w2 = live ? raw[e] : 0u;  // no 0 * NaN from slots past the context
+        const float v0 = __uint_as_float(w2 << 16), v1 = __uint_as_float(w2 & 0xffff0000u);
+#pragma unroll
+        for (int hh = 0; hh < RW_HG; ++hh) {
+          o[hh][2 * e] = fmaf(pk[hh], v0, o[hh][2 * e]);
+          o[hh][2 * e + 1] = fmaf(pk[hh], v1, o[hh][2 * e + 1]);
+        }
+      }
+    }
+    // reduce-scatter over the four blocks: heads (0, 1) | (2, 3) across
+    // lane ^ 32, then head 0 | 1 (2 | 3) across lane ^ 16
+    float t2[2][8], u[8];
+#pragma unroll
+    for (int hp = 0; hp < 2; ++hp)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(o[hp][e]), __float_as_uint(o[hp + 2][e]), false, false);
+        t2[hp][e] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+      }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(t2[0][e]), __float_as_uint(t2[1][e]), false, false);
+      u[e] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    }
+    if (vb < nh) {
+      float* w = wsr + (int64_t)(h0 + vb) * nchunks * stride + 2 + vc * 8;
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) *reinterpret_cast<f32x2_t*>(w + e) = f32x2_t{u[e], u[e + 1]};
+    }
+    if (lane < nh) {
+      float* w = wsr + (int64_t)(h0 + lane) * nchunks * stride;
+      const float mv = lane == 0 ? mh[0] : lane == 1 ? mh[1] : lane == 2 ? mh[2] : mh[3];
+      const float lv = lane == 0 ? lh[0] : lane == 1 ? lh[1] : lane == 2 ? lh[2] : lh[3];
+      w[0] = mv;
+      w[1] = lv;
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // LDS reads of this head group done before the next overwrites ps_s
+  }
+}
+
 template <typename T>
 __global__ void attn_combine_kernel(const float* __restrict__ ws, int hq, int dh, int nchunks, T* __restrict__ o) {
   const int r = blockIdx.x, h = blockIdx.y, d = threadIdx.x;
@@ -650,8 +833,10 @@ hipError_t launch_attn_prefill_fp8(const bf16_t* q, Fp8Slot cache, const int32_t
   return hipGetLastError();
 }
 
-int64_t attn_rows_ws_elems(int rows, int max_ctx, int hq, int dh) {
-  int nchunks = (max_ctx + RW_CH - 1) / RW_CH;
+int64_t attn_rows_ws_elems(int rows, int max_ctx, int hq, int dh, bool bf16_rows) {
+  // bf16 rows of head_dim 128 use attn_dec_kernel's 64-key chunks
+  const int ch = bf16_rows && dh == 128 ? DC_KEYS : RW_CH;
+  int nchunks = (max_ctx + ch - 1) / ch;
   return (int64_t)rows * hq * nchunks * (dh + 2);
 }
 
@@ -662,8 +847,19 @@ hipError_t attn_rows_impl(const T* q, CacheSlot<T> cache, Fp8Slot c8, const int3
                           const int32_t* block_tables, int max_blocks, int rows, int max_ctx, int hq, float* ws, T* o,
                           hipStream_t stream) {
   if (rows <= 0) return hipSuccess;
-  const int nchunks = (max_ctx + RW_CH - 1) / RW_CH;
   const float scale = 1.0f / sqrtf((float)cache.dh);
+  if constexpr (sizeof(T) == 2 && !F8) {
+    if (cache.dh == 128) {
+      const int nch = (max_ctx + DC_KEYS - 1) / DC_KEYS;
+      hipLaunchKernelGGL(attn_dec_kernel, dim3(rows, cache.hkv, (nch + 3) / 4), dim3(256), 0, stream, q, cache,
+                         row_seq, row_pos, block_tables, max_blocks, hq, nch, scale, ws);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(attn_combine_kernel<T>, dim3(rows, hq), dim3(RW_MAXDH), 0, stream, ws, hq, cache.dh, nch, o);
+      return hipGetLastError();
+    }
+  }
+  const int nchunks = (max_ctx + RW_CH - 1) / RW_CH;
   const dim3 grid(rows, cache.hkv, nchunks);
   switch (cache.dh) {
     case 128:

@@ -90,7 +90,7 @@ template <typename T>
 hipError_t launch_attn_rows(const T* q, CacheSlot<T> cache, const int32_t* row_seq, const int32_t* row_pos,
                             const int32_t* block_tables, int max_blocks, int rows, int max_ctx, int hq, float* ws,
                             T* o, hipStream_t stream);
-int64_t attn_rows_ws_elems(int rows, int max_ctx, int hq, int dh);
+int64_t attn_rows_ws_elems(int rows, int max_ctx, int hq, int dh, bool bf16_rows);
 // The same with K/V from a per-token FP8 cache slot (bf16 queries, dh 128).
 hipError_t launch_attn_rows_fp8(const bf16_t* q, Fp8Slot cache, const int32_t* row_seq, const int32_t* row_pos,
                                 const int32_t* block_tables, int max_blocks, int rows, int max_ctx, int hq, float* ws,
