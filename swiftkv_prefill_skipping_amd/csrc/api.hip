@@ -48,7 +48,7 @@ struct LayerDev {
   void* wgu = nullptr;   // [2f, d], gate/up interleaved in blocks of P_mlp rows
   void* wdown = nullptr; // [d, f]
   int panel_rows = 0;    // 0: row-major; else the panel height of the layout
-  bool gain_folded = false;  // attn / ffn RMSNorm gains folded into wqkv / wgu (bf16, layers <= l)
+  bool gain_folded = false;  // attn / ffn RMSNorm gains folded into wqkv / wgu (every bf16 layer)
   bool loaded = false;
 };
 
@@ -107,6 +107,9 @@ struct skv_model {
   // sums of squares [T, d/16] the residual epilogues leave for it
   float* rrow = nullptr;
   float* ssp = nullptr;
+  // bf16 row path: partial sums of squares [RY, d/128] of the rows whose
+  // bf16 copy `ya` holds (the skinny products fold the RMSNorm in)
+  float* rss = nullptr;
   float* attn_ws = nullptr;
   int64_t attn_ws_elems = 0;
   float* gemm_ws = nullptr;  // split partial tiles of the GEMMs
@@ -320,6 +323,7 @@ skv_status skv_model_create(const skv_model_config* cfg, skv_model** out) {
   ALLOC(m->yq, RY * dq * E);
   ALLOC(m->yo, RY * dq * E);
   ALLOC(m->yh, RY * f * E);
+  if (m->bf16) ALLOC(m->rss, RY * (d / 128) * 4);
   if (m->bf16) {
     int64_t pe = 0;
     pe = std::max(pe, skinny_partial_elems((int)dq, (int)d));
@@ -417,8 +421,10 @@ static skv_status gain_to_f32(skv_model* m, const void* src, float* dst, const c
 // Copy a row-major host/device matrix into `dst`, either as is
 // (panel_rows == 0) or through the staging buffer into the panel layout,
 // in chunks of whole panels that fit the staging buffer.
+// fold_gain (panel layouts): scale column c by the gain in gamma_stage
+// first (W diag(gamma)).
 static skv_status load_matrix(skv_model* m, void* dst, const void* src, size_t rows, size_t cols, int panel_rows,
-                              const char* what) {
+                              const char* what, bool fold_gain = false) {
   const size_t row_bytes = cols * m->esz;
   if (!panel_rows) return copy_in(dst, src, rows * row_bytes, what);
   if (!src) return fail(SKV_ERR_INVALID_ARG, std::string(what) + " is NULL");
@@ -427,6 +433,9 @@ static skv_status load_matrix(skv_model* m, void* dst, const void* src, size_t r
   for (size_t r0 = 0; r0 < rows; r0 += chunk) {
     const size_t n = std::min(chunk, rows - r0);
     SKV_TRY(copy_in(m->staging, (const char*)src + r0 * row_bytes, n * row_bytes, what));
+    if (fold_gain)
+      SKV_HIP(launch_fold_rows<bf16_t>((const bf16_t*)m->staging, (const bf16_t*)m->gamma_stage, (int)n, (int)cols,
+                                       (bf16_t*)m->staging, 0));
     SKV_HIP(launch_to_panels((const bf16_t*)m->staging, (int)n, (int)cols, panel_rows,
                              (bf16_t*)dst + r0 * cols, 0));
     SKV_HIP(hipDeviceSynchronize());
@@ -438,8 +447,10 @@ skv_status skv_model_load_globals(skv_model* m, const void* embed, const void* f
   if (!m) return fail(SKV_ERR_INVALID_ARG, "model is NULL");
   const size_t d = m->cfg.d_model, V = m->cfg.vocab;
   SKV_TRY(copy_in(m->embed, embed, V * d * m->esz, "embed"));
-  SKV_TRY(load_matrix(m, m->lm_head, lm_head, V, d, m->bf16 ? kSkinnyPanelRows : 0, "lm_head"));
-  SKV_TRY(gain_to_f32(m, final_norm, m->final_norm, "final_norm"));
+  SKV_TRY(gain_to_f32(m, final_norm, m->final_norm, "final_norm"));  // leaves gamma_stage = final gain
+  // bf16: the LM head takes bf16(y) and scales its products by the row's
+  // RMSNorm factor, so the final gain goes into its columns
+  SKV_TRY(load_matrix(m, m->lm_head, lm_head, V, d, m->bf16 ? kSkinnyPanelRows : 0, "lm_head", m->bf16));
   m->globals_loaded = true;
   return SKV_OK;
 }
@@ -470,7 +481,9 @@ skv_status skv_model_load_layer(skv_model* m, int32_t layer, const skv_layer_wei
       L.gain_folded = true;
     }
   } else {
-    SKV_TRY(load_matrix(m, L.wqkv, w->wq, dq, d, L.panel_rows, "wq"));
+    // (bf16) the attention gain goes into wq's columns as for layers <= l
+    SKV_TRY(load_matrix(m, L.wqkv, w->wq, dq, d, L.panel_rows, "wq", L.panel_rows != 0));
+    L.gain_folded = L.panel_rows != 0;
     if (is_representative(c, layer)) {
       // fold this layer's input-RMSNorm gain into its K and V rows (in place
       // in the staging buffer), then store them as this group's block of the
@@ -694,6 +707,7 @@ skv_status run_step(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, const S
                       m->pos, m->slot, m->last_pos, m->last_row, s));
   if (!kBf16 || rows_path) SKV_HIP(launch_token_seq(bt->cu_seqlens, B, T_, m->seq, s));
   SKV_HIP(launch_embed<T>(bt->token_ids, (const T*)m->embed, V, d, T_, m->x, s));
+  if (kBf16 && rows_path) SKV_HIP(launch_rows_act_ss(m->x, nullptr, T_, d, nullptr, (bf16_t*)ya, m->rss, s));
 
   // One layer over a few rows held row-major (the last tokens at layers
   // l+1..L; every new token of a short bf16 batch at layers 1..l).  x: the
@@ -702,21 +716,30 @@ skv_status run_step(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, const S
   auto row_layer = [&](const LayerDev& Ly, int cache_slot, int rows, float* x, const int32_t* row_seq,
                        const int32_t* row_pos, bool with_kv, int max_ctx) -> skv_status {
     const CacheSlot<T> cs = slot_of(cache_slot);
-    // (gains folded into the weights of layers <= l: plain x * r here)
-    SKV_HIP(launch_rmsnorm<T>(x, nullptr, Ly.gain_folded ? nullptr : Ly.attn_norm, rows, d, c.rms_eps, ya, s));
     const int nq = with_kv ? dq + 2 * dkv : dq;
     EpiQKV<T> eq{yq, kv8 ? stage : cs, row_pos, with_kv ? kv_slot : nullptr, m->rope_cos, m->rope_sin, dq, dkv, dh, P};
-    EpiResidual er{x, d, kBf16 ? 64 : 16};
     EpiSwiGLU<T> esw{yh, f, m->p_mlp};
+    // bf16: ya holds bf16(x) and rss its partial sums of squares on entry
+    // and on exit; the gains sit in the weights, and each normalised
+    // product scales by 1 / rms(x) in its finalize pass
+    SkinnyRowNorm rn_in, rn_out;
     if constexpr (kBf16) {
+      rn_in.ss_in = m->rss;
+      rn_in.nparts = (int)(d / 128);
+      rn_in.inv_d = 1.0f / (float)d;
+      rn_in.eps = c.rms_eps;
+      rn_out.ss_out = m->rss;
       SKV_HIP(launch_skinny_bf16((const bf16_t*)ya, d, (const bf16_t*)Ly.wqkv, Ly.panel_rows, rows, nq, d, m->partial,
-                                 m->partial_elems, eq, s));
-    } else if (P == 16) {
-      SKV_HIP((launch_gemm_f32<16>((const float*)ya, d, (const float*)Ly.wqkv, d, rows, nq, d, eq, s)));
-    } else if (P == 32) {
-      SKV_HIP((launch_gemm_f32<32>((const float*)ya, d, (const float*)Ly.wqkv, d, rows, nq, d, eq, s)));
+                                 m->partial_elems, eq, s, rn_in));
     } else {
-      SKV_HIP((launch_gemm_f32<64>((const float*)ya, d, (const float*)Ly.wqkv, d, rows, nq, d, eq, s)));
+      SKV_HIP(launch_rmsnorm<T>(x, nullptr, Ly.attn_norm, rows, d, c.rms_eps, ya, s));
+      if (P == 16) {
+        SKV_HIP((launch_gemm_f32<16>((const float*)ya, d, (const float*)Ly.wqkv, d, rows, nq, d, eq, s)));
+      } else if (P == 32) {
+        SKV_HIP((launch_gemm_f32<32>((const float*)ya, d, (const float*)Ly.wqkv, d, rows, nq, d, eq, s)));
+      } else {
+        SKV_HIP((launch_gemm_f32<64>((const float*)ya, d, (const float*)Ly.wqkv, d, rows, nq, d, eq, s)));
+      }
     }
     if (with_kv && kv8) SKV_TRY(quantize(rows, 1, cache_slot));
     if (kv8) {
@@ -728,18 +751,17 @@ skv_status run_step(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, const S
                                   hq, m->attn_ws, yo, s));
     }
     if constexpr (kBf16) {
+      EpiResidualRow er{x, d, (bf16_t*)ya};
       SKV_HIP(launch_skinny_bf16((const bf16_t*)yo, dq, (const bf16_t*)Ly.wo, Ly.panel_rows, rows, d, dq, m->partial,
-                                 m->partial_elems, er, s));
-    } else {
-      SKV_HIP((launch_gemm_f32<16>((const float*)yo, dq, (const float*)Ly.wo, dq, rows, d, dq, er, s)));
-    }
-    SKV_HIP(launch_rmsnorm<T>(x, nullptr, Ly.gain_folded ? nullptr : Ly.ffn_norm, rows, d, c.rms_eps, ya, s));
-    if constexpr (kBf16) {
+                                 m->partial_elems, er, s, rn_out));
       SKV_HIP(launch_skinny_bf16((const bf16_t*)ya, d, (const bf16_t*)Ly.wgu, Ly.panel_rows, rows, 2 * f, d, m->partial,
-                                 m->partial_elems, esw, s));
+                                 m->partial_elems, esw, s, rn_in));
       SKV_HIP(launch_skinny_bf16((const bf16_t*)yh, f, (const bf16_t*)Ly.wdown, Ly.panel_rows, rows, d, f, m->partial,
-                                 m->partial_elems, er, s));
+                                 m->partial_elems, er, s, rn_out));
     } else {
+      EpiResidual er{x, d, 16};
+      SKV_HIP((launch_gemm_f32<16>((const float*)yo, dq, (const float*)Ly.wo, dq, rows, d, dq, er, s)));
+      SKV_HIP(launch_rmsnorm<T>(x, nullptr, Ly.ffn_norm, rows, d, c.rms_eps, ya, s));
       SKV_HIP((launch_gemm_f32<16>((const float*)ya, d, (const float*)Ly.wgu, d, rows, 2 * f, d, esw, s)));
       SKV_HIP((launch_gemm_f32<16>((const float*)yh, f, (const float*)Ly.wdown, f, rows, d, f, er, s)));
     }
@@ -839,10 +861,10 @@ skv_status run_step(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, const S
 
   // ---- boundary: KV of every skipped layer / AcrossKV group from x_{l+1}
   if (m->G > 0) {
-    if (!panel_path) {
-      // x * r, gains folded into W~ (the panel path has act = bf16(x_{l+1}) and rrow already)
+    if constexpr (!kBf16) {
+      // x * r, gains folded into W~ (bf16: act / ya already hold bf16(x_{l+1}), with rrow / rss)
       Prof p(m, SKV_K_RMSNORM, s, 0, (double)T_ * d * (4 + E));
-      SKV_HIP(launch_rmsnorm<T>(m->x, nullptr, nullptr, T_, d, c.rms_eps, rows_path ? ya : act, s));
+      SKV_HIP(launch_rmsnorm<T>(m->x, nullptr, nullptr, T_, d, c.rms_eps, act, s));
     }
     CacheSlot<T> first = kv8 ? stage : slot_of(l);
     const int N = m->G * 2 * dkv;
@@ -850,9 +872,15 @@ skv_status run_step(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, const S
                      m->rope_sin, dkv, dh, P, c.n_kv_heads, rrow};
     Prof p(m, SKV_K_GEMM_KVSKIP, s, 2.0 * T_ * N * d, gemm_bytes(T_, N, d, E, E));
     if constexpr (kBf16) {
-      if (rows_path)
+      if (rows_path) {
+        SkinnyRowNorm rn;
+        rn.ss_in = m->rss;
+        rn.nparts = (int)(d / 128);
+        rn.inv_d = 1.0f / (float)d;
+        rn.eps = c.rms_eps;
         SKV_HIP(launch_skinny_bf16((const bf16_t*)ya, d, (const bf16_t*)m->wkv_skip, kPanelRows, T_, N, d, m->partial,
-                                   m->partial_elems, epi, s));
+                                   m->partial_elems, epi, s, rn));
+      }
       else
         SKV_HIP(launch_gemm_bf16((const bf16_t*)act, (const bf16_t*)m->wkv_skip, T_, N, d, epi, m->gemm_ws,
                                  m->gemm_ws_elems, s));
@@ -868,16 +896,26 @@ skv_status run_step(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, const S
 
   // ---- last new token of each sequence through layers l+1..L, then the LM head
   Prof plast(m, SKV_K_LAST_TOKEN, s, last_flops, last_bytes);
-  SKV_HIP(launch_gather_rows(m->x, m->last_row, B, d, m->y, s));
+  if constexpr (kBf16)
+    SKV_HIP(launch_rows_act_ss(m->x, m->last_row, B, d, m->y, (bf16_t*)ya, m->rss, s));
+  else
+    SKV_HIP(launch_gather_rows(m->x, m->last_row, B, d, m->y, s));
   for (int j = l + 1; j <= L; ++j)
     SKV_TRY(row_layer(m->layers[j - 1], slot_of_layer(c, j), B, m->y, m->iota, m->last_pos, false, si.max_total));
-  SKV_HIP(launch_rmsnorm<T>(m->y, nullptr, m->final_norm, B, d, c.rms_eps, ya, s));
   EpiStoreF32 el{logits, V, kBf16 ? 64 : 16};
-  if constexpr (kBf16)
+  if constexpr (kBf16) {
+    // final RMSNorm folded in: ya = bf16(y), its partials in rss, the gain in the LM head
+    SkinnyRowNorm rn;
+    rn.ss_in = m->rss;
+    rn.nparts = (int)(d / 128);
+    rn.inv_d = 1.0f / (float)d;
+    rn.eps = c.rms_eps;
     SKV_HIP(launch_skinny_bf16((const bf16_t*)ya, d, (const bf16_t*)m->lm_head, kSkinnyPanelRows, B, V, d, m->partial,
-                               m->partial_elems, el, s));
-  else
+                               m->partial_elems, el, s, rn));
+  } else {
+    SKV_HIP(launch_rmsnorm<T>(m->y, nullptr, m->final_norm, B, d, c.rms_eps, ya, s));
     SKV_HIP((launch_gemm_f32<16>((const float*)ya, d, (const float*)m->lm_head, d, B, V, d, el, s)));
+  }
   return SKV_OK;
 }
 

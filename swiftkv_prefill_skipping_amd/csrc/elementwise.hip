@@ -157,6 +157,25 @@ __global__ void gather_rows_kernel(const float* __restrict__ x, const int32_t* _
   for (int c = threadIdx.x; c < d; c += blockDim.x) yr[c] = xr[c];
 }
 
+// One row per workgroup; a half-wave (32 lanes x 4 values) covers one
+// 128-column unit of the sums of squares.
+__global__ __launch_bounds__(256) void rows_act_ss_kernel(const float* __restrict__ x, const int32_t* __restrict__ idx,
+                                                          int d, float* __restrict__ y, bf16_t* __restrict__ act,
+                                                          float* __restrict__ ss) {
+  const int r = blockIdx.x;
+  const float* xr = x + (int64_t)(idx ? idx[r] : r) * d;
+  for (int c = threadIdx.x * 4; c < d; c += 1024) {
+    const float4 v = *reinterpret_cast<const float4*>(xr + c);
+    if (y) *reinterpret_cast<float4*>(y + (int64_t)r * d + c) = v;
+    const u32x2_t packed{pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w)};
+    *reinterpret_cast<u32x2_t*>(act + (int64_t)r * d + c) = packed;
+    float q = v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) q += __shfl_xor(q, o, 64);
+    if ((threadIdx.x & 31) == 0) ss[(int64_t)r * (d / 128) + c / 128] = q;
+  }
+}
+
 template <typename T>
 __global__ void fold_rows_kernel(const T* __restrict__ W, const T* __restrict__ gamma, int rows, int cols,
                                  T* __restrict__ out) {
@@ -255,6 +274,14 @@ hipError_t launch_gather_rows(const float* x, const int32_t* rows_idx, int rows,
                               hipStream_t stream) {
   if (rows <= 0) return hipSuccess;
   hipLaunchKernelGGL(gather_rows_kernel, dim3(rows), dim3(256), 0, stream, x, rows_idx, d, y);
+  return hipGetLastError();
+}
+
+hipError_t launch_rows_act_ss(const float* x, const int32_t* rows_idx, int rows, int d, float* y, bf16_t* act,
+                              float* ss, hipStream_t stream) {
+  if (rows <= 0) return hipSuccess;
+  if (d % 128) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(rows_act_ss_kernel, dim3(rows), dim3(256), 0, stream, x, rows_idx, d, y, act, ss);
   return hipGetLastError();
 }
 

@@ -112,6 +112,27 @@ struct EpiResidual {
   SKV_DEV void vec8(int row, int col, const float* a, const float* b) const { vec8(row, col, a, b, pre8(row, col)); }
 };
 
+// Residual add for the skinny (row-major, at most 32 rows) products:
+// x += o W^T on the column pair (col, col + 64), act = bf16 of the new x in
+// the same row-major layout (the next projection's un-normalised input),
+// and the pair's sum of squares handed back to the finalize pass, which
+// reduces it over the wave's 128 columns.
+struct EpiResidualRow {
+  float* x;
+  int ld;
+  bf16_t* act;
+  SKV_DEV float operator()(int row, int col, float v0, float v1) const {
+    float* p = x + (int64_t)row * ld + col;
+    const float y0 = p[0] + v0, y1 = p[64] + v1;
+    p[0] = y0;
+    p[64] = y1;
+    bf16_t* a = act + (int64_t)row * ld + col;
+    a[0] = from_f32<bf16_t>(y0);
+    a[64] = from_f32<bf16_t>(y1);
+    return y0 * y0 + y1 * y1;
+  }
+};
+
 // SwiGLU on gate/up rows interleaved in blocks of P: GEMM column
 // b*2P + c (c < P) is gate feature b*P + c, column b*2P + P + c is up
 // feature b*P + c.  h = silu(gate) * up.

@@ -32,9 +32,23 @@ constexpr int kSkinnyMaxRows = 32;
 // 64).  A is row-major [M, lda]; B [N, K] is in the panel layout with
 // panels of panel_rows (kSkinnyPanelRows or kPanelRows) rows.  Requires
 // K % 256 == 0, N % 128 == 0.
+//
+// Row RMSNorm folded into the product (rn.ss_in != NULL): A holds bf16(x)
+// of rows whose gains sit in B, and rn.ss_in [M, nparts] holds partial sums
+// of squares of x; the finalize scales each row's products by
+// 1 / sqrt(sum * inv_d + eps) before the epilogue.  EpiResidualRow writes
+// the new rows' partials (one per 128 columns) to rn.ss_out [M, N / 128].
+struct SkinnyRowNorm {
+  const float* ss_in = nullptr;
+  int nparts = 0;
+  float inv_d = 0.f;
+  float eps = 0.f;
+  float* ss_out = nullptr;
+};
 template <class Epi>
 hipError_t launch_skinny_bf16(const bf16_t* A, int lda, const bf16_t* B, int panel_rows, int M, int N, int K,
-                              float* partial, int64_t partial_elems, const Epi& epi, hipStream_t stream);
+                              float* partial, int64_t partial_elems, const Epi& epi, hipStream_t stream,
+                              SkinnyRowNorm rn = SkinnyRowNorm{});
 int64_t skinny_partial_elems(int N, int K);
 
 // Per-token metadata of a batch whose sequence b already holds ctx_b cached
@@ -66,6 +80,12 @@ hipError_t launch_rms_from_partials(const float* ss, int rows, int d, float eps,
 // y[r, :] = x[rows_idx[r], :]  (fp32 rows)
 hipError_t launch_gather_rows(const float* x, const int32_t* rows_idx, int rows, int d, float* y,
                               hipStream_t stream);
+// The skinny products' un-normalised input: act[r, :] = bf16(x[src, :]) and
+// ss[r, c] = sum of x[src, 128 c .. 128 c + 128]^2, with src = rows_idx[r]
+// (rows_idx NULL: src = r); y (optional) receives a copy of the fp32 row.
+// d % 128 == 0.
+hipError_t launch_rows_act_ss(const float* x, const int32_t* rows_idx, int rows, int d, float* y, bf16_t* act,
+                              float* ss, hipStream_t stream);
 
 // Causal GQA flash attention for prompt tokens (bf16, MFMA): q [T, hq, dh],
 // K/V from one cache slot, o [T, hq * dh] in the panel layout (panel_off with

@@ -10,6 +10,8 @@
 // Split-K partial sums land in an fp32 buffer [splits, 32, N] and a second
 // pass adds them in fixed split order (deterministic) and applies the
 // epilogue on column pairs (col, col + 64).
+#include <type_traits>
+
 #include "common.h"
 #include "epilogues.h"
 #include "kernels.h"
@@ -92,13 +94,20 @@ __global__ __launch_bounds__(256) void skinny_partial_kernel(const bf16_t* __res
 }
 
 template <class Epi>
-__global__ void skinny_finalize_kernel(const float* __restrict__ partial, int M, int N, int nsplit, Epi epi) {
+__global__ void skinny_finalize_kernel(const float* __restrict__ partial, int M, int N, int nsplit, Epi epi,
+                                       SkinnyRowNorm rn) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t half = N / 2;
-  if (idx >= (int64_t)M * half) return;
+  if (idx >= (int64_t)M * half) return;  // whole waves: half is a multiple of 64
   const int row = (int)(idx / half);
   const int j = (int)(idx % half);
   const int col = (j / 64) * 128 + (j % 64);
+  const int lane = threadIdx.x & 63;
+  // the row's RMSNorm partials (a wave's 64 threads share its row), loaded
+  // with the splits
+  float t = 0.f;
+  if (rn.ss_in)
+    for (int i = lane; i < rn.nparts; i += 64) t += rn.ss_in[(int64_t)row * rn.nparts + i];
   // splits summed in order; eight at a time so their loads are in flight together
   const float* p = partial + (int64_t)row * N + col;
   const int64_t ss = (int64_t)SK_ROWS * N;
@@ -121,7 +130,17 @@ __global__ void skinny_finalize_kernel(const float* __restrict__ partial, int M,
     v0 += p[s * ss];
     v1 += p[s * ss + 64];
   }
-  epi(row, col, v0, v1);
+  if (rn.ss_in) {  // the input was bf16(x) with the gain in the weights: scale by 1 / rms(x)
+    const float r = 1.0f / sqrtf(warp_sum(t) * rn.inv_d + rn.eps);
+    v0 *= r;
+    v1 *= r;
+  }
+  if constexpr (std::is_same<Epi, EpiResidualRow>::value) {
+    const float q = warp_sum(epi(row, col, v0, v1));
+    if (lane == 0) rn.ss_out[(int64_t)row * (N / 128) + col / 128] = q;
+  } else {
+    epi(row, col, v0, v1);
+  }
 }
 
 // K splits (each a multiple of 256 columns): the fewest that still give
@@ -148,10 +167,13 @@ int64_t skinny_partial_elems(int N, int K) { return (int64_t)choose_splits(N, K)
 
 template <class Epi>
 hipError_t launch_skinny_bf16(const bf16_t* A, int lda, const bf16_t* B, int panel_rows, int M, int N, int K,
-                              float* partial, int64_t partial_elems, const Epi& epi, hipStream_t stream) {
+                              float* partial, int64_t partial_elems, const Epi& epi, hipStream_t stream,
+                              SkinnyRowNorm rn) {
   if (M <= 0) return hipSuccess;
   if (M > SK_ROWS || K % 256 != 0 || N % 128 != 0 || (panel_rows != kSkinnyPanelRows && panel_rows != kPanelRows))
     return hipErrorInvalidValue;
+  if (rn.ss_in && (rn.nparts <= 0 || !(rn.inv_d > 0.f))) return hipErrorInvalidValue;
+  if (std::is_same<Epi, EpiResidualRow>::value && !rn.ss_out) return hipErrorInvalidValue;
   const int ns = choose_splits(N, K);
   if ((int64_t)ns * SK_ROWS * N > partial_elems) return hipErrorInvalidValue;
   const int kc = K / ns;
@@ -162,19 +184,21 @@ hipError_t launch_skinny_bf16(const bf16_t* A, int lda, const bf16_t* B, int pan
   if (e != hipSuccess) return e;
   const int64_t work = (int64_t)M * (N / 2);
   hipLaunchKernelGGL(skinny_finalize_kernel<Epi>, dim3((unsigned)((work + 255) / 256)), dim3(256), 0, stream, partial,
-                     M, N, ns, epi);
+                     M, N, ns, epi, rn);
   return hipGetLastError();
 }
 
 template hipError_t launch_skinny_bf16<EpiQKV<bf16_t>>(const bf16_t*, int, const bf16_t*, int, int, int, int, float*,
-                                                       int64_t, const EpiQKV<bf16_t>&, hipStream_t);
+                                                       int64_t, const EpiQKV<bf16_t>&, hipStream_t, SkinnyRowNorm);
 template hipError_t launch_skinny_bf16<EpiResidual>(const bf16_t*, int, const bf16_t*, int, int, int, int, float*,
-                                                    int64_t, const EpiResidual&, hipStream_t);
+                                                    int64_t, const EpiResidual&, hipStream_t, SkinnyRowNorm);
 template hipError_t launch_skinny_bf16<EpiSwiGLU<bf16_t>>(const bf16_t*, int, const bf16_t*, int, int, int, int,
-                                                          float*, int64_t, const EpiSwiGLU<bf16_t>&, hipStream_t);
+                                                          float*, int64_t, const EpiSwiGLU<bf16_t>&, hipStream_t, SkinnyRowNorm);
 template hipError_t launch_skinny_bf16<EpiStoreF32>(const bf16_t*, int, const bf16_t*, int, int, int, int, float*,
-                                                    int64_t, const EpiStoreF32&, hipStream_t);
+                                                    int64_t, const EpiStoreF32&, hipStream_t, SkinnyRowNorm);
 template hipError_t launch_skinny_bf16<EpiKVSkip<bf16_t>>(const bf16_t*, int, const bf16_t*, int, int, int, int,
-                                                          float*, int64_t, const EpiKVSkip<bf16_t>&, hipStream_t);
+                                                          float*, int64_t, const EpiKVSkip<bf16_t>&, hipStream_t, SkinnyRowNorm);
 template hipError_t launch_skinny_bf16<EpiStore<bf16_t>>(const bf16_t*, int, const bf16_t*, int, int, int, int,
-                                                         float*, int64_t, const EpiStore<bf16_t>&, hipStream_t);
+                                                         float*, int64_t, const EpiStore<bf16_t>&, hipStream_t, SkinnyRowNorm);
+template hipError_t launch_skinny_bf16<EpiResidualRow>(const bf16_t*, int, const bf16_t*, int, int, int, int, float*,
+                                                       int64_t, const EpiResidualRow&, hipStream_t, SkinnyRowNorm);
