@@ -7,5 +7,7 @@ if ROOT not in sys.path:
 
 
 def pytest_configure(config):
+    from tests import helpers
+    helpers.CAPMAN = config.pluginmanager.getplugin("capturemanager")
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     config.addinivalue_line("markers", "slow: long-running (full-size workloads)")

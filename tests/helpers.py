@@ -1,6 +1,8 @@
 """Shared helpers of the tests: seeded inputs -> oracle inputs, error metrics."""
 from __future__ import annotations
 
+import sys
+
 import numpy as np
 
 import skv_inputs as si
@@ -43,3 +45,17 @@ def max_rel(got, ref) -> float:
     if den == 0.0:
         return float(np.max(np.abs(got))) if got.size else 0.0
     return float(np.max(np.abs(got - ref)) / den)
+
+
+# pytest's capture manager (set by conftest.py): progress lines bypass output
+# capture, so a long GPU test shows it is alive while it runs
+CAPMAN = None
+
+
+def say(*a):
+    """Print a progress line to the real stderr, past pytest's capture."""
+    if CAPMAN is not None:
+        with CAPMAN.global_and_fixture_disabled():
+            print(*a, file=sys.stderr, flush=True)
+    else:
+        print(*a, file=sys.stderr, flush=True)

@@ -19,14 +19,14 @@ import pytest
 
 import skv_inputs as si
 from oracle import swiftkv_oracle as O
-from tests.helpers import CachedLayers, dims_of, max_rel, oracle_weights
+from tests.helpers import CachedLayers, dims_of, max_rel, oracle_weights, say
 from tests.test_gpu_step import FP8_LOGITS_TOL, fp8_kv_check, run_schedule
 
 pytestmark = pytest.mark.gpu
 
 
 def _say(*a):
-    print(*a, file=sys.stderr, flush=True)
+    say(*a)
 
 
 def _logical_rows(arr, block_row, n):

@@ -19,7 +19,7 @@ import pytest
 
 import skv_inputs as si
 from oracle import swiftkv_oracle as O
-from tests.helpers import CachedLayers, dims_of, max_rel, oracle_weights
+from tests.helpers import CachedLayers, dims_of, max_rel, oracle_weights, say
 from tests.test_gpu_parity import compare, gpu_kv, run_gpu
 
 pytestmark = pytest.mark.gpu
@@ -30,7 +30,7 @@ def round_bf16(x):
 
 
 def _say(*a):
-    print(*a, file=sys.stderr, flush=True)
+    say(*a)
 
 
 def _check_sampled(w, batch, prompts, tol=2e-2):

@@ -5,13 +5,14 @@ KV slot of every checked prompt (positions 0..N-1) and for each checked
 prompt's logits row.  Bars: 1e-4 for fp32 models, 2e-2 for bf16 models.
 """
 import sys
+import time
 
 import numpy as np
 import pytest
 
 import skv_inputs as si
 from oracle import swiftkv_oracle as O
-from tests.helpers import CachedLayers, dims_of, max_rel, oracle_weights
+from tests.helpers import CachedLayers, dims_of, max_rel, oracle_weights, say
 
 pytestmark = pytest.mark.gpu
 
@@ -19,15 +20,22 @@ TOL = {"fp32": 1e-4, "bf16": 2e-2}
 
 
 def _say(*a):
-    print(*a, file=sys.stderr, flush=True)
+    say(*a)
 
 
 def run_gpu(w, batch, max_tokens=None, max_seqlen=None, cached=None, num_blocks=None):
     import torch
     from swiftkv_prefill_skipping_amd import runner
     T, B = batch.total_tokens, len(batch.lengths)
-    model = runner.load_seeded_model(w, max_tokens or T, max(B, 1), max_seqlen or batch.max_seqlen,
-                                     layer_hook=cached.hook if cached is not None else None)
+    t0 = time.time()
+
+    def hook(i, lw):  # progress every 16 layers (a full-size load takes minutes)
+        if i % 16 == 0:
+            _say(f"[load] {w.name}: {i} of {w.shape.n_layers} layers loaded ({time.time() - t0:.0f} s)")
+        if cached is not None:
+            cached.hook(i, lw)
+
+    model = runner.load_seeded_model(w, max_tokens or T, max(B, 1), max_seqlen or batch.max_seqlen, layer_hook=hook)
     cache = runner.Cache(model, num_blocks or batch.num_blocks)
     db = runner.device_batch(batch)
     logits = runner.prefill(model, cache, db)

@@ -20,7 +20,7 @@ import pytest
 
 import skv_inputs as si
 from oracle import swiftkv_oracle as O
-from tests.helpers import CachedLayers, dims_of, max_rel, oracle_weights
+from tests.helpers import CachedLayers, dims_of, max_rel, oracle_weights, say
 
 pytestmark = pytest.mark.gpu
 
@@ -28,7 +28,7 @@ TOL = {"fp32": 1e-4, "bf16": 2e-2}
 
 
 def _say(*a):
-    print(*a, file=sys.stderr, flush=True)
+    say(*a)
 
 
 def fp8_kv_check(got, ref, tol=2e-2):
