@@ -20,9 +20,10 @@
 // 16 bank groups: the fragment reads are conflict free.
 //
 // Schedule: each k-stage is two k-substeps of 16 MFMAs; the fragment reads
-// of the next substep are interleaved with the MFMAs of the current one.
-// One workgroup barrier per stage publishes the next stage and frees the
-// current buffer, whose next load goes out right after it.
+// of the next substep are interleaved with the first 8 MFMAs of the current
+// one.  One workgroup barrier per stage publishes the next stage and frees
+// the current buffer, whose next load goes out in two halves, one in each
+// of the following two substeps, between their last 8 MFMAs.
 //
 // Epilogue: the accumulators go through LDS (each wave stages 32 rows x 128
 // columns of fp32 at a time in a padded, conflict-free layout), so the
@@ -211,11 +212,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(const bf16_t* __
     const int row = (wave * LH + i) * RPI + lane / CH;
     g_off[i] = row * BK + (((lane % CH) ^ swizzle<CH>(row)) << 3);
   }
-  auto gload = [&](int buf, int stage_idx) {
+  // loads i0 .. i1-1 of stage stage_idx (two instructions each, A and B)
+  auto gload_part = [&](int buf, int stage_idx, int i0, int i1) {
     typedef __attribute__((address_space(3))) void* lds_ptr;
     const int64_t so = (int64_t)stage_idx * (BM * BK);
 #pragma unroll
-    for (int i = 0; i < LH; ++i) {
+    for (int i = i0; i < i1; ++i) {
       const int grp = wave * LH + i;
       const bf16_t* sa = a_panel + so + g_off[i];
       const bf16_t* sb = b_panel + so + g_off[i];
@@ -223,6 +225,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(const bf16_t* __
       __builtin_amdgcn_global_load_lds(sb, (lds_ptr)(&smem[buf][BM * BK + grp * RPI * BK]), 16, 0, 0);
     }
   };
+  auto gload = [&](int buf, int stage_idx) { gload_part(buf, stage_idx, 0, LH); };
 
   f32x16_t acc[4][4];
 #pragma unroll
@@ -258,56 +261,54 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(const bf16_t* __
   };
 
   const int nk = ke - kb;
-  // one k-substep: 16 MFMAs on fragment slot `slot`, with the 8 fragment
-  // reads of the next substep interleaved between the first 8 of them
-  auto step = [&](int slot, int buf, int kk_next) {
-    fload(buf, kk_next, slot ^ 1);
-    compute(slot);
+  static_assert(NSUB == 2 && LH % 2 == 0, "two k-substeps per stage, loads in two halves");
+
+  // Pipeline: all NBUF buffers are filled up front.  The barrier in the
+  // middle of stage s publishes stage s+1 (every wave has landed its share)
+  // and frees the buffer of stage s (its last fragments are in registers).
+  // Stage s+NBUF then goes into that buffer in two halves: the first during
+  // the second k-substep of stage s, the second during the first k-substep
+  // of stage s+1, so each substep's 16 MFMAs carry LPW/2 direct loads and
+  // the load issue never bunches up behind the barrier.  At the barrier of
+  // stage s the loads issued after stage s+1's are those of stages s+2 and
+  // s+3 (LPW each), whenever both exist; near the end the wait drains all.
+  // The flags are constants at each call site, so every stage body is one
+  // straight-line block and the group barriers interleave its loads and LDS
+  // reads with the MFMAs.
+  //   load_a: first half of stage s+NBUF, after the barrier
+  //   load_b: second half of stage s+NBUF-1, before the barrier
+  auto stage = [&](int s, bool load_a, bool load_b, bool next) {
+    const int cur = s % NBUF;
+    // substep 0: the fragments of substep 1 are read between its first 8
+    // MFMAs, the second half of the previous stage's load between the rest
+    fload(cur, 1, 1);
+    if (load_b) gload_part((s + NBUF - 1) % NBUF, kb + s + NBUF - 1, LH / 2, LH);
+    compute(0);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  // Wait until this wave's loads of stage s+1 have landed while those of
-  // the `after` later stages may still be in flight, then a workgroup
-  // barrier: every wave's share of stage s+1 is then in LDS, and every wave
-  // has finished reading the buffer of stage s.
-  auto wait_then_barrier = [&](int after) {
-    constexpr int L = StageShape<BK>::LPW;
-    if (after <= 0) wait_vm_then_barrier<0>();
-    else if (after == 1) wait_vm_then_barrier<L>();
-    else if (after == 2) wait_vm_then_barrier<2 * L>();
-    else if (after == 3) wait_vm_then_barrier<3 * L>();
-    else wait_vm_then_barrier<4 * L>();
-  };
-
-  // Pipeline: all NBUF buffers are filled up front.  At the end of stage s
-  // (after the barrier that publishes stage s+1) the buffer of stage s is
-  // free and receives stage s+NBUF, while the last k-substep of stage s runs
-  // and the first fragments of stage s+1 are read.  The flags are constants
-  // at each call site, so every stage body is one straight-line block and
-  // the group barriers interleave its loads and LDS reads with the MFMAs.
-  auto stage = [&](int s, bool load, bool next) {
-    const int cur = s % NBUF;
+    if (load_b) {
 #pragma unroll
-    for (int kk = 0; kk < StageShape<BK>::NSUB - 1; ++kk) step(kk & 1, cur, kk + 1);
+      for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, LPW / 8, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
+    } else {
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
     if (next) {
-      if (load) wait_vm_then_barrier<(NBUF - 2) * StageShape<BK>::LPW>();
+      if (load_a || load_b) wait_vm_then_barrier<2 * LPW>();
       else wait_vm_then_barrier<0>();
     }
-    if (load) gload(cur, kb + s + NBUF);
+    // substep 1: the next stage's first fragments, then the first half of
+    // stage s+NBUF into the freed buffer
     if (next) fload((s + 1) % NBUF, 0, 0);
+    if (load_a) gload_part(cur, kb + s + NBUF, 0, LH / 2);
     compute(1);
-    if (load) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x020, StageShape<BK>::LPW / 8, 0);
-      }
-    }
     if (next) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -315,17 +316,30 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(const bf16_t* __
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
     }
+    if (load_a) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, LPW / 8, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
+    }
     __builtin_amdgcn_sched_barrier(0);
   };
   const int pre = min(NBUF, nk);
   for (int p = 0; p < pre; ++p) gload(p, kb + p);
-  wait_then_barrier(pre - 1);
+  if (pre == 1) wait_vm_then_barrier<0>();
+  else if (pre == 2) wait_vm_then_barrier<LPW>();
+  else if (pre == 3) wait_vm_then_barrier<2 * LPW>();
+  else wait_vm_then_barrier<3 * LPW>();
   fload(0, 0, 0);
   __builtin_amdgcn_sched_barrier(0);
   int s = 0;
-  for (; s < nk - NBUF; ++s) stage(s, true, true);
-  for (; s < nk - 1; ++s) stage(s, false, true);
-  stage(s, false, false);
+  if (nk > NBUF) stage(s++, true, false, true);
+  for (; s < nk - NBUF; ++s) stage(s, true, true, true);
+  if (s >= 1 && s == nk - NBUF) stage(s++, false, true, true);
+  for (; s < nk - 1; ++s) stage(s, false, false, true);
+  stage(s, false, false, false);
 
   // Epilogue through LDS.  The last stage's reads are complete in every wave
   // after this barrier, so the stage buffers can be reused.
@@ -419,7 +433,8 @@ int num_cus() {
 
 }  // namespace
 
-int64_t gemm_bf16_ws_elems() { return (int64_t)num_cus() * BM * BN; }
+// room for 2 partial tiles per CU (128 MB on 256 CUs)
+int64_t gemm_bf16_ws_elems() { return (int64_t)2 * num_cus() * BM * BN; }
 
 template <int NBUF, class Epi>
 hipError_t launch_gemm_cfg(const bf16_t* A, const bf16_t* B, int M, int N, int K, const Epi& epi, float* ws,
@@ -430,15 +445,31 @@ hipError_t launch_gemm_cfg(const bf16_t* A, const bf16_t* B, int M, int N, int K
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   const int P = num_cus();
   const int nk = K / BK;
-  // a partly filled last wave of whole tiles is replaced by K-split units
-  // that fill every CU (at least 2 k-stages per unit)
+  // A partly filled last wave of whole tiles (or a launch of fewer tiles
+  // than CUs) is replaced by K-split units.  The split count s minimises the
+  // tail's time in units of one whole tile: waves of units ceil(rem*s/P),
+  // each unit taking 1/s of the tile plus a fixed cost (pipeline fill and
+  // the fp32 partial-tile store, ~10 % of a tile at K = 4096), plus the
+  // summing pass over all rem*s partial tiles (~13 % of a tile per P of
+  // them at K = 4096); measured on the MI355X at K = 4096 and 14336.  At
+  // least 2 k-stages per unit; partial tiles must fit the workspace.
   SplitPlan plan{tiles, 1, ws};
   const int rem = tiles % P;
-  if (ws != nullptr && tiles >= P && rem != 0) {
-    const int splits = min(P / rem, nk / 2);
-    if (splits >= 2 && (int64_t)rem * splits * BM * BN <= ws_elems) {
+  if (ws != nullptr && rem != 0) {
+    const double fixed = 0.10 * 4096.0 / K, sum = 0.13 * 4096.0 / K;
+    double best = 1.0;
+    int best_s = 1;
+    const int64_t cap = ws_elems / ((int64_t)BM * BN);
+    for (int s = 2; s <= nk / 2 && (int64_t)rem * s <= cap; ++s) {
+      const double cost = (double)((rem * s + P - 1) / P) * (1.0 / s + fixed) + sum * rem * s / P;
+      if (cost < best) {
+        best = cost;
+        best_s = s;
+      }
+    }
+    if (best_s >= 2) {
       plan.dp_tiles = tiles - rem;
-      plan.splits = splits;
+      plan.splits = best_s;
     }
   }
   const int grid = plan.dp_tiles + (tiles - plan.dp_tiles) * plan.splits;
