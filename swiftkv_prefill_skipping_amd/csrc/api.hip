@@ -262,7 +262,8 @@ skv_status skv_model_create(const skv_model_config* cfg, skv_model** out) {
   m->bf16 = c.dtype == SKV_BF16;
   m->esz = m->bf16 ? 2 : 4;
   m->G = ceil_div(c.n_layers - c.swiftkv_l, c.acrosskv_g);
-  m->p_mlp = m->bf16 ? 64 : 16;
+  // bf16: the interleave distance of the gate/up GEMM's SwiGLU epilogue
+  m->p_mlp = m->bf16 ? EpiSwiGLUPanel::P : 16;
   m->dq = c.n_q_heads * c.head_dim;
   m->dkv = c.n_kv_heads * c.head_dim;
   m->layers.resize(c.n_layers);
@@ -841,7 +842,7 @@ skv_status run_step(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, const S
     {
       Prof p(m, SKV_K_GEMM_GATEUP, s, 2.0 * T_ * 2 * f * d, gemm_bytes(T_, 2.0 * f, d, E, 0) + (double)T_ * f * E);
       if constexpr (kBf16) {
-        EpiSwiGLUPanel epi{(bf16_t*)hbuf, f, m->p_mlp, rrow};
+        EpiSwiGLUPanel epi{(bf16_t*)hbuf, f, rrow};
         SKV_HIP(launch_gemm_bf16((const bf16_t*)act, (const bf16_t*)Ly.wgu, T_, 2 * f, d, epi, m->gemm_ws, m->gemm_ws_elems, s));
       } else {
         EpiSwiGLU<T> epi{hbuf, f, m->p_mlp};

@@ -67,18 +67,19 @@ SKV_DEV void tile_coords(int tile, int tiles_m, int tiles_n, int& tm, int& tn) {
   tn = (tile % per_group) / gsize;
 }
 
-// Wait for this wave's direct loads and LDS reads, then a workgroup barrier.
-// (__syncthreads would add a fence; the memory clobber and the scheduling
-// barriers keep every LDS access and MFMA on its side.)
-SKV_DEV void wait_all_then_barrier() {
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-}
+// Wait for this wave's direct loads (all but the N most recent) and LDS
+// reads, then a workgroup barrier.  (__syncthreads would add a fence; the
+// memory clobber and the scheduling barriers keep every LDS access and MFMA
+// on its side.)
 template <int N>
 SKV_DEV void wait_vm_then_barrier() {
   __builtin_amdgcn_sched_barrier(0);
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+SKV_DEV void wait_lds_then_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
 }
 SKV_DEV void wait_lds() {
@@ -260,6 +261,28 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(const bf16_t* __
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[slot][j], af[slot][i], acc[i][j], 0, 0, 0);
   };
 
+  // Epilogue geometry.  unit (pass i, it): row wm*128 + i*32 + it*8 + er,
+  // columns lcol.. and lcol+64..  What the epilogue reads (residual values,
+  // row factors) for pass i+1 is loaded before pass i's stores are issued:
+  // the vector-memory counter covers stores too, so a load issued after
+  // them would make its wait cover them as well.  (Loading pass 0 during the
+  // last k-stages instead was measured slower: every CU reaches its epilogue
+  // at the same time, so those loads only move the HBM burst earlier.)
+  const int er = lane >> 3;        // row within a group of 8
+  const int ec = (lane & 7) * 8;   // first of eight columns, 0..56
+  const int wr = lane & 31;        // row written by this lane
+  const int wc = 4 * (lane >> 5);  // column offset within a group of 8
+  const int lcol = wn * 128 + ec;
+  const bool cols_ok = n0 + wn * 128 < N;
+  using Ahead = EpiAhead<Epi>;
+  typename Ahead::Pre ahead[2][4];
+  auto unit_row = [&](int i, int it) { return wm * 128 + i * 32 + it * 8 + er; };
+  auto load_pass = [&](int i) {
+#pragma clang loop unroll(full)
+    for (int it = 0; it < 4; ++it)
+      if (m0 + unit_row(i, it) < M) ahead[i & 1][it] = Ahead::load(epi, m0 + unit_row(i, it), n0 + lcol);
+  };
+
   const int nk = ke - kb;
   static_assert(NSUB == 2 && LH % 2 == 0, "two k-substeps per stage, loads in two halves");
 
@@ -341,25 +364,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(const bf16_t* __
   for (; s < nk - 1; ++s) stage(s, false, false, true);
   stage(s, false, false, false);
 
-  // Epilogue through LDS.  The last stage's reads are complete in every wave
-  // after this barrier, so the stage buffers can be reused.
-  wait_all_then_barrier();
+  // Epilogue through LDS.  Every stage load has landed (the last barrier
+  // waited for all of them); after this barrier every wave has also finished
+  // reading the last stage, so the stage buffers can be reused.
+  wait_lds_then_barrier();
   float* stg = reinterpret_cast<float*>(&smem[0][0]) + wave * kStageWave;
-  const int er = lane >> 3;        // row within a group of 8
-  const int ec = (lane & 7) * 8;   // first of eight columns, 0..56
-  const int wr = lane & 31;        // row written by this lane
-  const int wc = 4 * (lane >> 5);  // column offset within a group of 8
-  const int lcol = wn * 128 + ec;
-  const bool cols_ok = n0 + wn * 128 < N;
-  // unit (pass i, it): row wm*128 + i*32 + it*8 + er, columns lcol.. and lcol+64..
-  using Ahead = EpiAhead<Epi>;
-  typename Ahead::Pre ahead[4];
-  auto unit_row = [&](int i, int it) { return wm * 128 + i * 32 + it * 8 + er; };
-  if (!split && cols_ok) {
-#pragma clang loop unroll(full)
-    for (int it = 0; it < 4; ++it)
-      if (m0 + unit_row(0, it) < M) ahead[it] = Ahead::load(epi, m0 + unit_row(0, it), n0 + lcol);
-  }
+  if (!split && cols_ok) load_pass(0);
 #pragma clang loop unroll(full)
   for (int i = 0; i < 4; ++i) {
     // stage rows i*32 .. +32 of this wave's block: tile (i, j) value v is
@@ -371,6 +381,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(const bf16_t* __
         *reinterpret_cast<f32x4_t*>(stg + wr * kStageLd + j * 32 + 8 * g + wc) =
             f32x4_t{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
     wait_lds();
+    if (!split && cols_ok && i < 3) load_pass(i + 1);
 #pragma clang loop unroll(full)
     for (int it = 0; it < 4; ++it) {
       const int r = it * 8 + er;
@@ -383,8 +394,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(const bf16_t* __
         store8(part, a);
         store8(part + 64, b);
       } else if (cols_ok) {
-        if (m0 + lrow < M) Ahead::apply(epi, m0 + lrow, n0 + lcol, a, b, ahead[it]);
-        if (i < 3 && m0 + unit_row(i + 1, it) < M) ahead[it] = Ahead::load(epi, m0 + unit_row(i + 1, it), n0 + lcol);
+        if (m0 + lrow < M) Ahead::apply(epi, m0 + lrow, n0 + lcol, a, b, ahead[i & 1][it]);
       }
     }
     wait_lds();
