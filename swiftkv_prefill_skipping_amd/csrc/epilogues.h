@@ -183,6 +183,20 @@ struct EpiSwiGLUPanel {
       y[e] = (g[e] * u[e]) * (s2 * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g[e] * ce)));
     store8(h + panel_off(row, oc, F), y);
   }
+  // The GEMM hands this epilogue its gate/up pairs straight from the
+  // accumulator registers (a lane holds four consecutive gate columns of a
+  // row and their up partners 64 columns on), without staging them in LDS.
+  static constexpr bool kFromRegisters = true;
+  SKV_DEV void vec4s(int row, int col, const float* g, const float* u, float sr) const {
+    const int oc = (col >> 7) * P + (col & (2 * P - 1));
+    const float ce = sr * -1.4426950408889634f;
+    const float s2 = sr * sr;
+    float y[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      y[e] = (g[e] * u[e]) * (s2 * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g[e] * ce)));
+    *reinterpret_cast<u32x2_t*>(h + panel_off(row, oc, F)) = u32x2_t{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+  }
 };
 
 SKV_DEV void rope_pair(float x0, float x1, float c, float s, float& y0, float& y1) {

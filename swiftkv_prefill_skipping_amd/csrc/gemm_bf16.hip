@@ -148,11 +148,22 @@ struct EpiAhead<EpiResidual> {
   }
 };
 
-// Work split of one launch.  The first dp_tiles tiles are computed whole
-// (data parallel, grid blocks 0 .. dp_tiles-1, XCD remapped); each of the
-// remaining tiles is split along K into `splits` ranges (a partly filled
-// last wave of tiles becomes K-split units that fill every CU), one grid
-// block per range, whose fp32 partial tiles go to `ws` and are summed in
+// Epilogues with kFromRegisters take their column pairs straight from the
+// accumulators (vec4s) instead of through the LDS staging.
+template <class Epi, class = void>
+struct FromRegisters {
+  static constexpr bool value = false;
+};
+template <class Epi>
+struct FromRegisters<Epi, decltype((void)Epi::kFromRegisters)> {
+  static constexpr bool value = Epi::kFromRegisters;
+};
+
+// Work split of one GEMM.  The first dp_tiles tiles are computed whole
+// (data parallel, one launch, XCD remapped); each of the remaining tiles is
+// split along K into `splits` ranges (a partly filled last wave of tiles
+// becomes K-split units that fill every CU), one workgroup per range in a
+// second launch, whose fp32 partial tiles go to `ws` and are summed in
 // fixed order by gemm_reduce_kernel.
 struct SplitPlan {
   int dp_tiles;
@@ -160,7 +171,12 @@ struct SplitPlan {
   float* ws;
 };
 
-template <int NBUF, class Epi>
+// SPLIT selects the launch: false = the whole tiles (grid dp_tiles, XCD
+// remapped), true = the K-split units of the tail tiles (grid (tiles -
+// dp_tiles) * splits), whose fp32 partial tiles go to plan.ws.  Separate
+// kernels keep one epilogue per kernel, so neither path's register needs
+// shape the other's.
+template <int NBUF, class Epi, bool SPLIT>
 __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(const bf16_t* __restrict__ A,
                                                                  const bf16_t* __restrict__ B, int M, int N,
                                                                  int K, SplitPlan plan, Epi epi) {
@@ -174,14 +190,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(const bf16_t* __
   const int tiles_n = (N + BN - 1) / BN;
   const int nk_all = K / BK;
   const int bid = blockIdx.x;
-  const bool split = bid >= plan.dp_tiles;
+  constexpr bool split = SPLIT;
   int tile, kb, ke, unit = 0;
   if (!split) {
     tile = xcd_remap(bid, plan.dp_tiles);
     kb = 0;
     ke = nk_all;
   } else {
-    unit = bid - plan.dp_tiles;
+    unit = bid;
     tile = plan.dp_tiles + unit / plan.splits;
     const int sp = unit % plan.splits;
     kb = sp * nk_all / plan.splits;
@@ -364,6 +380,39 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(const bf16_t* __
   for (; s < nk - 1; ++s) stage(s, false, false, true);
   stage(s, false, false, false);
 
+  // Epilogues that take their pairs from registers (SwiGLU: a lane's gate
+  // columns j*32 + 8g + 4*(lane/32) + e and their up partners sit in
+  // acc[i][j] and acc[i][j+2] for j < 2) skip the LDS staging; each call
+  // writes four consecutive bf16 of a row.
+  if constexpr (FromRegisters<Epi>::value && !SPLIT) {
+    {
+      if (!cols_ok) return;
+      const int row0 = m0 + wm * 128 + (lane & 31);
+      const int col0 = n0 + wn * 128 + 4 * (lane >> 5);
+      float sr[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sr[i] = row0 + i * 32 < M ? epi.scale(row0 + i * 32) : 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (row0 + i * 32 < M) {
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const float gv[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+              const float uv[4] = {acc[i][j + 2][4 * g], acc[i][j + 2][4 * g + 1], acc[i][j + 2][4 * g + 2],
+                                   acc[i][j + 2][4 * g + 3]};
+              epi.vec4s(row0 + i * 32, col0 + j * 32 + 8 * g, gv, uv, sr[i]);
+            }
+        }
+        // one row block at a time: bounds the values copied out of the
+        // accumulators that are live at once
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      return;
+    }
+  }
+
   // Epilogue through LDS.  Every stage load has landed (the last barrier
   // waited for all of them); after this barrier every wave has also finished
   // reading the last stage, so the stage buffers can be reused.
@@ -482,10 +531,17 @@ hipError_t launch_gemm_cfg(const bf16_t* A, const bf16_t* B, int M, int N, int K
       plan.splits = best_s;
     }
   }
-  const int grid = plan.dp_tiles + (tiles - plan.dp_tiles) * plan.splits;
-  hipLaunchKernelGGL((gemm_bf16_kernel<NBUF, Epi>), dim3(grid), dim3(kThreads), 0, stream, A, B, M, N, K, plan, epi);
+  if (plan.dp_tiles > 0) {
+    hipLaunchKernelGGL((gemm_bf16_kernel<NBUF, Epi, false>), dim3(plan.dp_tiles), dim3(kThreads), 0, stream, A, B, M,
+                       N, K, plan, epi);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (plan.dp_tiles == tiles) return hipSuccess;
+  hipLaunchKernelGGL((gemm_bf16_kernel<NBUF, Epi, true>), dim3((tiles - plan.dp_tiles) * plan.splits), dim3(kThreads),
+                     0, stream, A, B, M, N, K, plan, epi);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || plan.dp_tiles == tiles) return e;
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL((gemm_reduce_kernel<Epi>), dim3(BM * 16 / 256, tiles - plan.dp_tiles), dim3(256), 0, stream, M,
                      N, plan, epi);
   return hipGetLastError();
