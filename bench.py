@@ -1,6 +1,7 @@
 """Throughput of the SwiftKV prefill on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--no-full-depth]
+                    [--no-decode] [--no-fp8] [--no-mfma-probe]
     python bench.py --copy-calibration MIB   # plain device copy of known size, for HBM counter scaling
 
 One step = one skv_prefill call over the whole batch (every row of the hot
@@ -212,6 +213,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama8b_l16_b16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-mfma-probe", action="store_true",
+                    help="skip the pure-MFMA throughput probe (random and constant operands)")
     ap.add_argument("--no-full-depth", action="store_true",
                     help="skip timing the same batch through all layers (l = L) with the same kernels")
     ap.add_argument("--no-decode", action="store_true",
@@ -356,6 +359,18 @@ def main():
             "swiftkv_time_ratio": round(ms / ms_full, 4), "swiftkv_flops_ratio": round(swift / full, 4)}
         cf.close()
         mf.close()
+    if not args.no_mfma_probe:
+        # the matrix cores alone, no memory traffic: what dense bf16 sustains on this GPU with random operands
+        # (the power limit of data like these weights) and with constant ones
+        pr = {k: L.skv_mfma_probe(k == "random_operands", 20000, stream.cuda_stream)
+              for k in ("random_operands", "constant_operands")}
+        res["mfma_probe"] = {
+            "kernel": "v_mfma_f32_32x32x16_bf16, 16 independent accumulators per wave, 4 waves per CU, no memory",
+            "cus": pr["random_operands"]["cus"], "max_clock_mhz": pr["random_operands"]["max_clock_mhz"],
+            **{k: {"tflops": round(v["tflops"], 1), "clock_mhz": round(v["clock_mhz"], 0),
+                   "frac_of_bf16_peak": round(v["tflops"] / MI355X_BF16_DENSE_TFLOPS, 4)} for k, v in pr.items()},
+            "gemm_gateup_frac_of_random_operand_probe": round(achieved / pr["random_operands"]["tflops"], 4)}
+        log(f"[bench] MFMA probe: {res['mfma_probe']}")
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on the host")
         res["cpu_baseline"] = cpu_baseline(w, batch, cached)

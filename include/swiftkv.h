@@ -258,6 +258,23 @@ skv_status skv_profile_enable(skv_model* m, int32_t kernel_class, int32_t enable
  * count, algorithmic FLOPs and algorithmic HBM bytes of those launches. */
 skv_status skv_profile_read(skv_model* m, double* total_ms, int64_t* launches, double* flops, double* bytes);
 
+/* Measurement aid, not part of the method: the dense bf16 MFMA throughput
+ * of this GPU.  Runs one workgroup of 4 waves per compute unit, each wave
+ * issuing iters x 32 v_mfma_f32_32x32x16_bf16 on 16 independent
+ * accumulators from operands held in registers (no memory traffic in the
+ * loop), once untimed and once timed with HIP events on `stream`;
+ * synchronous (returns when the timed run is done; allocates and frees
+ * its own small device buffers).  random_operands != 0 fills the operands
+ * with random sign and mantissa bits at the magnitudes of N(0, 0.02)
+ * weights, else with one constant (operand toggling sets the chip's power
+ * draw and so its clock).  Outputs: tflops (dense, 2 FLOPs per
+ * multiply-add), clock_mhz (the shader clock the loop ran at, averaged over
+ * workgroups), cus (compute units) and max_clock_mhz (the device's peak
+ * engine clock).  INVALID_ARG for iters outside [1, 2^22] or a NULL
+ * output; HIP for a failed allocation, copy or launch. */
+skv_status skv_mfma_probe(int32_t random_operands, int32_t iters, void* stream, double* tflops, double* clock_mhz,
+                          int32_t* cus, double* max_clock_mhz);
+
 /* Message of the last failure on this thread ("" if none). */
 const char* skv_last_error(void);
 

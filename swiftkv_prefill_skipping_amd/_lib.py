@@ -51,7 +51,7 @@ class skv_step_batch(Structure):
 EXPORTED = ["skv_model_create", "skv_model_load_globals", "skv_model_load_layer", "skv_model_destroy",
             "skv_kv_cache_create", "skv_kv_cache_destroy", "skv_num_kv_slots", "skv_kv_cache_view", "skv_kv_cache_scales", "skv_prefill",
             "skv_step",
-            "skv_flops", "skv_profile_enable", "skv_profile_read", "skv_last_error"]
+            "skv_flops", "skv_profile_enable", "skv_profile_read", "skv_mfma_probe", "skv_last_error"]
 
 _lib = None
 
@@ -87,6 +87,8 @@ def lib():
         L.skv_flops.argtypes = [POINTER(skv_model_config), vp, c_int32, POINTER(c_double), POINTER(c_double)]
         L.skv_profile_enable.argtypes = [vp, c_int32, c_int32]
         L.skv_profile_read.argtypes = [vp, POINTER(c_double), POINTER(c_int64), POINTER(c_double), POINTER(c_double)]
+        L.skv_mfma_probe.argtypes = [c_int32, c_int32, vp, POINTER(c_double), POINTER(c_double), POINTER(c_int32),
+                                     POINTER(c_double)]
         L.skv_last_error.argtypes = []
         L.skv_last_error.restype = c_char_p
         for name in EXPORTED:
@@ -181,6 +183,13 @@ def skv_flops(cfg: skv_model_config, seqlens) -> tuple:
 
 def skv_profile_enable(model: int, kernel_class: int, enable: bool = True) -> None:
     check(lib().skv_profile_enable(model, kernel_class, 1 if enable else 0))
+
+
+def skv_mfma_probe(random_operands: bool, iters: int, stream: int) -> dict:
+    tf, mhz, cus, mx = c_double(), c_double(), c_int32(), c_double()
+    check(lib().skv_mfma_probe(1 if random_operands else 0, iters, stream, ctypes.byref(tf), ctypes.byref(mhz),
+                               ctypes.byref(cus), ctypes.byref(mx)))
+    return {"tflops": tf.value, "clock_mhz": mhz.value, "cus": cus.value, "max_clock_mhz": mx.value}
 
 
 def skv_profile_read(model: int) -> dict:

@@ -16,7 +16,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libswiftkv.so")
-SOURCES = ["api.hip", "gemm_bf16.hip", "gemm_f32.hip", "attention.hip", "skinny.hip", "elementwise.hip", "kvquant.hip"]
+SOURCES = ["api.hip", "gemm_bf16.hip", "gemm_f32.hip", "attention.hip", "skinny.hip", "elementwise.hip", "kvquant.hip",
+           "calib.hip"]
 ARCH = os.environ.get("SKV_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -643,6 +643,67 @@ skv_status skv_profile_read(skv_model* m, double* total_ms, int64_t* launches, d
   return SKV_OK;
 }
 
+skv_status skv_mfma_probe(int32_t random_operands, int32_t iters, void* stream, double* tflops, double* clock_mhz,
+                          int32_t* cus, double* max_clock_mhz) {
+  if (iters <= 0 || iters > (1 << 22) || !tflops || !clock_mhz || !cus || !max_clock_mhz)
+    return fail(SKV_ERR_INVALID_ARG, "skv_mfma_probe: iters must be in [1, 2^22] and every output non-NULL");
+  int dev = 0, n = 0, khz = 0;
+  SKV_HIP(hipGetDevice(&dev));
+  SKV_HIP(hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev));
+  SKV_HIP(hipDeviceGetAttribute(&khz, hipDeviceAttributeClockRate, dev));
+  struct DevBuf {
+    void* p = nullptr;
+    ~DevBuf() {
+      if (p) (void)hipFree(p);
+    }
+  } in, out, clk;
+  struct Ev {
+    hipEvent_t e = nullptr;
+    ~Ev() {
+      if (e) (void)hipEventDestroy(e);
+    }
+  } e0, e1;
+  const size_t in_elems = 16 * 64 * 8;  // 16 fragments x 64 lanes x 8 bf16
+  SKV_HIP(hipMalloc(&in.p, in_elems * 2));
+  SKV_HIP(hipMalloc(&out.p, (size_t)n * 256 * 4));
+  SKV_HIP(hipMalloc(&clk.p, (size_t)n * 2 * sizeof(unsigned long long)));
+  // random operands: random sign and mantissa bits at magnitudes 2^-7 .. 2^-5
+  // (the scale of N(0, 0.02) weights); otherwise one constant value
+  std::vector<uint16_t> h(in_elems);
+  uint32_t x = 0x2545F491u;
+  for (auto& v : h) {
+    x = x * 1664525u + 1013904223u;
+    v = random_operands ? (uint16_t)(0x3c00u | ((x >> 9) & 0xffu) | ((x >> 8) & 0x8000u)) : (uint16_t)0x3c3c;
+  }
+  hipStream_t st = (hipStream_t)stream;
+  SKV_HIP(hipMemcpyAsync(in.p, h.data(), in_elems * 2, hipMemcpyHostToDevice, st));
+  SKV_HIP(hipEventCreate(&e0.e));
+  SKV_HIP(hipEventCreate(&e1.e));
+  // one untimed launch brings the clock to its steady state
+  SKV_HIP(launch_mfma_probe((const bf16x8_t*)in.p, iters, n, (float*)out.p, (unsigned long long*)clk.p, st));
+  SKV_HIP(hipEventRecord(e0.e, st));
+  SKV_HIP(launch_mfma_probe((const bf16x8_t*)in.p, iters, n, (float*)out.p, (unsigned long long*)clk.p, st));
+  SKV_HIP(hipEventRecord(e1.e, st));
+  SKV_HIP(hipEventSynchronize(e1.e));
+  float ms = 0.f;
+  SKV_HIP(hipEventElapsedTime(&ms, e0.e, e1.e));
+  std::vector<unsigned long long> c((size_t)n * 2);
+  SKV_HIP(hipMemcpy(c.data(), clk.p, c.size() * sizeof(unsigned long long), hipMemcpyDeviceToHost));
+  double mhz = 0.0;
+  int used = 0;
+  for (int g = 0; g < n; ++g)
+    if (c[2 * g + 1] > 0) {
+      mhz += (double)c[2 * g] / (double)c[2 * g + 1] * 100.0;
+      ++used;
+    }
+  const double flops = 2.0 * 32 * 32 * 16 * mfma_probe_per_iter() * (double)iters * 4 * n;
+  *tflops = ms > 0.f ? flops / ((double)ms * 1e9) : 0.0;
+  *clock_mhz = used ? mhz / used : 0.0;
+  *cus = n;
+  *max_clock_mhz = khz / 1000.0;
+  return SKV_OK;
+}
+
 }  // extern "C"
 
 namespace {

@@ -94,3 +94,11 @@ def test_step_rejects_null_arguments_without_a_device():
     with pytest.raises(L.SkvError) as e:
         L.check(L.lib().skv_step(None, None, None, None, None))
     assert e.value.status == L.SKV_ERR_INVALID_ARG
+
+
+def test_mfma_probe_rejects_bad_arguments_before_any_device_call():
+    L = _lib()
+    with pytest.raises(L.SkvError) as e:
+        L.skv_mfma_probe(True, 0, 0)
+    assert e.value.status == -1
+    assert "iters" in L.lib().skv_last_error().decode()

@@ -249,3 +249,19 @@ def test_host_side_errors():
     with pytest.raises(L.SkvError):                           # batch above max_batch
         L.skv_prefill(model.handle, cache.handle, big, logits.data_ptr(), 0)
     L.skv_prefill(model.handle, cache.handle, st, logits.data_ptr(), 0)   # the good one still works
+
+
+def test_mfma_probe_reports_plausible_figures():
+    """The pure-MFMA probe behind bench.py's mfma_probe field: positive throughput below the dense figure at the
+    reported clock, a clock within the device's range, every compute unit used."""
+    import torch
+    from swiftkv_prefill_skipping_amd import _lib as L
+    _say("[case] MFMA probe")
+    s = torch.cuda.current_stream()
+    for rnd in (True, False):
+        r = L.skv_mfma_probe(rnd, 2000, s.cuda_stream)
+        assert r["cus"] == torch.cuda.get_device_properties(0).multi_processor_count
+        assert 100.0 < r["clock_mhz"] <= r["max_clock_mhz"] * 1.05, r
+        # 4 waves x 32x32x16 MFMA (32 cycles each) per CU: 4096 FLOP per CU per clock
+        dense_at_clock = r["cus"] * 4096 * r["clock_mhz"] * 1e6 / 1e12
+        assert 0.3 * dense_at_clock < r["tflops"] < 1.05 * dense_at_clock, r
