@@ -28,7 +28,11 @@
 // Epilogue: the accumulators go through LDS (each wave stages 32 rows x 128
 // columns of fp32 at a time in a padded, conflict-free layout), so the
 // epilogue functor sees eight consecutive columns per call and every global
-// store is a whole 16-byte run.
+// store is a whole 16-byte run.  The SwiGLU epilogue skips the staging: a
+// lane already holds each gate column next to its up partner.
+//
+// A partly filled last wave of tiles is split over K into units of a second
+// launch; gemm_reduce_kernel sums their fp32 partial tiles in fixed order.
 //
 // Workgroups are dispatched round robin over the 8 XCDs; the tile index is
 // remapped so each XCD processes a contiguous run of tiles, and runs are
