@@ -271,15 +271,21 @@ def main():
     ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    # one event between consecutive steps as well, for the per-step spread
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps - 1)]
     ev0.record(stream)
     for i in range(args.steps):
         runner.prefill(model, cache, db, logits, stream)
+        if i < args.steps - 1:
+            evs[i].record(stream)
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     prof = L.skv_profile_read(model.handle)
     L.skv_profile_enable(model.handle, dominant, False)
     ms = ev0.elapsed_time(ev1) / args.steps
+    marks = [ev0] + evs + [ev1]
+    step_ms = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps))
     log(f"[bench] {args.steps} steps: {ms:.3f} ms/step (events), {wall / args.steps * 1e3:.3f} ms/step (wall)")
 
     full, swift = L.skv_flops(model.cfg, batch.lengths)
@@ -298,6 +304,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "step_ms": {"min": round(step_ms[0], 4), "median": round(float(np.median(step_ms)), 4),
+                    "max": round(step_ms[-1], 4)},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
