@@ -783,26 +783,42 @@ __global__ __launch_bounds__(256) void attn_dec_kernel(const bf16_t* __restrict_
   }
 }
 
+// One (row, head): 4 chunk groups x head_dim threads.  Group q takes chunks
+// q, q+4, ... in order; the maximum, then the weighted sums, are combined
+// across the groups in group order (fixed, deterministic).  Four groups cut
+// the serial chain of loads per thread four-fold, which matters for one
+// row over a long context (hundreds of chunks).
 template <typename T>
-__global__ void attn_combine_kernel(const float* __restrict__ ws, int hq, int dh, int nchunks, T* __restrict__ o) {
-  const int r = blockIdx.x, h = blockIdx.y, d = threadIdx.x;
-  if (d >= dh) return;
+__global__ __launch_bounds__(4 * RW_MAXDH) void attn_combine_kernel(const float* __restrict__ ws, int hq, int dh,
+                                                                    int nchunks, T* __restrict__ o) {
+  __shared__ float red_m[4], red_l[4], red_a[4][RW_MAXDH];
+  const int r = blockIdx.x, h = blockIdx.y;
+  const int d = threadIdx.x % RW_MAXDH, grp = threadIdx.x / RW_MAXDH;
   const int stride = dh + 2;
   const float* w = ws + ((int64_t)r * hq + h) * nchunks * stride;
-  // chunks in order; unrolled so a long context keeps several loads in flight
   float m = -INFINITY;
 #pragma unroll 8
-  for (int c = 0; c < nchunks; ++c) m = fmaxf(m, w[c * stride]);
+  for (int c = grp; c < nchunks; c += 4) m = fmaxf(m, w[c * stride]);
+  if (d == 0) red_m[grp] = m;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(red_m[0], red_m[1]), fmaxf(red_m[2], red_m[3]));
   float l = 0.f, acc = 0.f;
 #pragma unroll 8
-  for (int c = 0; c < nchunks; ++c) {
-    float mc = w[c * stride];
+  for (int c = grp; c < nchunks; c += 4) {
+    const float mc = w[c * stride];
     if (mc == -INFINITY) continue;
-    float e = __expf(mc - m);
+    const float e = __expf(mc - M);
     l += w[c * stride + 1] * e;
-    acc += w[c * stride + 2 + d] * e;
+    if (d < dh) acc += w[c * stride + 2 + d] * e;
   }
-  o[((int64_t)r * hq + h) * dh + d] = from_f32<T>(acc / l);
+  red_a[grp][d] = acc;
+  if (d == 0) red_l[grp] = l;
+  __syncthreads();
+  if (grp == 0 && d < dh) {
+    const float L = ((red_l[0] + red_l[1]) + red_l[2]) + red_l[3];
+    const float A = ((red_a[0][d] + red_a[1][d]) + red_a[2][d]) + red_a[3][d];
+    o[((int64_t)r * hq + h) * dh + d] = from_f32<T>(A / L);
+  }
 }
 
 }  // namespace
@@ -855,7 +871,7 @@ hipError_t attn_rows_impl(const T* q, CacheSlot<T> cache, Fp8Slot c8, const int3
                          row_seq, row_pos, block_tables, max_blocks, hq, nch, scale, ws);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
-      hipLaunchKernelGGL(attn_combine_kernel<T>, dim3(rows, hq), dim3(RW_MAXDH), 0, stream, ws, hq, cache.dh, nch, o);
+      hipLaunchKernelGGL(attn_combine_kernel<T>, dim3(rows, hq), dim3(4 * RW_MAXDH), 0, stream, ws, hq, cache.dh, nch, o);
       return hipGetLastError();
     }
   }
@@ -879,7 +895,7 @@ hipError_t attn_rows_impl(const T* q, CacheSlot<T> cache, Fp8Slot c8, const int3
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_combine_kernel<T>, dim3(rows, hq), dim3(RW_MAXDH), 0, stream, ws, hq, cache.dh, nchunks, o);
+  hipLaunchKernelGGL(attn_combine_kernel<T>, dim3(rows, hq), dim3(4 * RW_MAXDH), 0, stream, ws, hq, cache.dh, nchunks, o);
   return hipGetLastError();
 }
 
