@@ -101,22 +101,20 @@ typedef struct {
 skv_status skv_model_create(const skv_model_config* cfg, skv_model** out);
 
 /* Copy the embedding [vocab, d_model], the final RMSNorm gain [d_model] and
- * the (untied) LM head [vocab, d_model] into the model.  bf16 models fold
- * the final gain into the LM head's columns (W_lm diag(gamma)); the LM head
- * product then scales by the row's 1/rms.  Synchronous; the caller's
- * buffers may be reused when it returns. */
+ * the (untied) LM head [vocab, d_model] into the model, values unchanged.
+ * Synchronous; the caller's buffers may be reused when it returns. */
 skv_status skv_model_load_globals(skv_model* m, const void* embed, const void* final_norm, const void* lm_head);
 
 /* Copy layer `layer`'s weights into the model and repack them on the
  * device: Q/K/V rows concatenated for unskipped layers; gate and up rows
  * interleaved; for an AcrossKV representative j > l, its input-RMSNorm gain
- * folded into its K and V rows (W~ = W_KV diag(gamma_j), exact in real
- * arithmetic: RMSNorm(x; gamma) W^T = r (x (W diag gamma)^T) with
- * r = 1/sqrt(mean x^2 + eps)).  bf16 models fold the same way every
- * layer's attention gain into its Q (and, for unskipped layers, K/V) rows
- * and its MLP gain into its gate/up rows; the projections then take bf16(x)
- * and scale their products by r (in the GEMM epilogues or the skinny
- * products' finalize pass).  Synchronous. */
+ * folded into its K and V rows (W~ = W_KV diag(gamma_j), the one weight the
+ * library changes, as the skipped-layer projection is defined: exact in real
+ * arithmetic, RMSNorm(x; gamma) W^T = r (x (W diag gamma)^T) with
+ * r = 1/sqrt(mean x^2 + eps); bf16 models round W~ to bf16).  Every other
+ * weight keeps its values: bf16 projections take bf16(x * gamma) and scale
+ * their products by r (in the GEMM epilogues or the skinny products'
+ * finalize pass).  Synchronous. */
 skv_status skv_model_load_layer(skv_model* m, int32_t layer, const skv_layer_weights* w);
 
 /* Free everything the model owns.  Accepts NULL. */

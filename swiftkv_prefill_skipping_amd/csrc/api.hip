@@ -36,6 +36,7 @@ size_t round_up(size_t a, size_t b) { return (a + b - 1) / b * b; }
 
 }  // namespace
 
+
 // Weights of layers 1..l feed the prompt-token GEMMs and are kept in the
 // panel layout with 256-row panels; those of skipped layers (and the LM
 // head) feed only the last-token path and use 64-row panels (bf16 models).
@@ -48,7 +49,6 @@ struct LayerDev {
   void* wgu = nullptr;   // [2f, d], gate/up interleaved in blocks of P_mlp rows
   void* wdown = nullptr; // [d, f]
   int panel_rows = 0;    // 0: row-major; else the panel height of the layout
-  bool gain_folded = false;  // attn / ffn RMSNorm gains folded into wqkv / wgu (every bf16 layer)
   bool loaded = false;
 };
 
@@ -108,7 +108,7 @@ struct skv_model {
   float* rrow = nullptr;
   float* ssp = nullptr;
   // bf16 row path: partial sums of squares [RY, d/128] of the rows whose
-  // bf16 copy `ya` holds (the skinny products fold the RMSNorm in)
+  // bf16(x * gain) `ya` holds (the skinny products apply the RMSNorm factor)
   float* rss = nullptr;
   float* attn_ws = nullptr;
   int64_t attn_ws_elems = 0;
@@ -204,7 +204,8 @@ struct Prof {
   bool on;
   hipEvent_t a{}, b{};
   hipStream_t s;
-  Prof(skv_model* m_, int cls, hipStream_t s_, double flops, double bytes) : m(m_), on(m_->prof_class == cls), s(s_) {
+  Prof(skv_model* m_, int cls, hipStream_t s_, double flops, double bytes)
+      : m(m_), on(m_ && m_->prof_class == cls), s(s_) {
     if (on) {
       hipEventCreate(&a);
       hipEventCreate(&b);
@@ -421,11 +422,10 @@ static skv_status gain_to_f32(skv_model* m, const void* src, float* dst, const c
 
 // Copy a row-major host/device matrix into `dst`, either as is
 // (panel_rows == 0) or through the staging buffer into the panel layout,
-// in chunks of whole panels that fit the staging buffer.
-// fold_gain (panel layouts): scale column c by the gain in gamma_stage
-// first (W diag(gamma)).
+// in chunks of whole panels that fit the staging buffer.  Values are copied
+// unchanged.
 static skv_status load_matrix(skv_model* m, void* dst, const void* src, size_t rows, size_t cols, int panel_rows,
-                              const char* what, bool fold_gain = false) {
+                              const char* what) {
   const size_t row_bytes = cols * m->esz;
   if (!panel_rows) return copy_in(dst, src, rows * row_bytes, what);
   if (!src) return fail(SKV_ERR_INVALID_ARG, std::string(what) + " is NULL");
@@ -434,9 +434,6 @@ static skv_status load_matrix(skv_model* m, void* dst, const void* src, size_t r
   for (size_t r0 = 0; r0 < rows; r0 += chunk) {
     const size_t n = std::min(chunk, rows - r0);
     SKV_TRY(copy_in(m->staging, (const char*)src + r0 * row_bytes, n * row_bytes, what));
-    if (fold_gain)
-      SKV_HIP(launch_fold_rows<bf16_t>((const bf16_t*)m->staging, (const bf16_t*)m->gamma_stage, (int)n, (int)cols,
-                                       (bf16_t*)m->staging, 0));
     SKV_HIP(launch_to_panels((const bf16_t*)m->staging, (int)n, (int)cols, panel_rows,
                              (bf16_t*)dst + r0 * cols, 0));
     SKV_HIP(hipDeviceSynchronize());
@@ -448,10 +445,10 @@ skv_status skv_model_load_globals(skv_model* m, const void* embed, const void* f
   if (!m) return fail(SKV_ERR_INVALID_ARG, "model is NULL");
   const size_t d = m->cfg.d_model, V = m->cfg.vocab;
   SKV_TRY(copy_in(m->embed, embed, V * d * m->esz, "embed"));
-  SKV_TRY(gain_to_f32(m, final_norm, m->final_norm, "final_norm"));  // leaves gamma_stage = final gain
-  // bf16: the LM head takes bf16(y) and scales its products by the row's
-  // RMSNorm factor, so the final gain goes into its columns
-  SKV_TRY(load_matrix(m, m->lm_head, lm_head, V, d, m->bf16 ? kSkinnyPanelRows : 0, "lm_head", m->bf16));
+  SKV_TRY(gain_to_f32(m, final_norm, m->final_norm, "final_norm"));
+  // bf16: the LM head takes bf16(y * final gain) and scales its products by
+  // the row's RMSNorm factor
+  SKV_TRY(load_matrix(m, m->lm_head, lm_head, V, d, m->bf16 ? kSkinnyPanelRows : 0, "lm_head"));
   m->globals_loaded = true;
   return SKV_OK;
 }
@@ -471,20 +468,12 @@ skv_status skv_model_load_layer(skv_model* m, int32_t layer, const skv_layer_wei
     SKV_TRY(copy_in(dst + dq * d * E, w->wk, dkv * d * E, "wk"));
     SKV_TRY(copy_in(dst + (dq + dkv) * d * E, w->wv, dkv * d * E, "wv"));
     if (L.panel_rows) {
-      // the prompt-token GEMMs take un-normalised rows and scale the
-      // products by the row's RMSNorm factor: fold the gain into the rows
-      // (W diag(gamma)), exact in real arithmetic
-      SKV_HIP(launch_fold_rows<bf16_t>((const bf16_t*)m->staging, (const bf16_t*)m->gamma_stage, (int)(dq + 2 * dkv),
-                                       (int)d, (bf16_t*)m->staging, 0));
       SKV_HIP(launch_to_panels((const bf16_t*)m->staging, (int)(dq + 2 * dkv), (int)d, L.panel_rows,
                                (bf16_t*)L.wqkv, 0));
       SKV_HIP(hipDeviceSynchronize());
-      L.gain_folded = true;
     }
   } else {
-    // (bf16) the attention gain goes into wq's columns as for layers <= l
-    SKV_TRY(load_matrix(m, L.wqkv, w->wq, dq, d, L.panel_rows, "wq", L.panel_rows != 0));
-    L.gain_folded = L.panel_rows != 0;
+    SKV_TRY(load_matrix(m, L.wqkv, w->wq, dq, d, L.panel_rows, "wq"));
     if (is_representative(c, layer)) {
       // fold this layer's input-RMSNorm gain into its K and V rows (in place
       // in the staging buffer), then store them as this group's block of the
@@ -518,12 +507,6 @@ skv_status skv_model_load_layer(skv_model* m, int32_t layer, const skv_layer_wei
   else
     SKV_HIP(launch_interleave<float>((const float*)m->staging, (const float*)m->staging + f * d, (int)f, (int)d,
                                      m->p_mlp, (float*)L.wgu, 0));
-  if (L.gain_folded) {
-    SKV_HIP(hipDeviceSynchronize());
-    SKV_TRY(gain_to_f32(m, w->ffn_norm, L.ffn_norm, "ffn_norm"));  // gamma_stage = ffn gain
-    SKV_HIP(launch_fold_rows<bf16_t>((const bf16_t*)L.wgu, (const bf16_t*)m->gamma_stage, (int)(2 * f), (int)d,
-                                     (bf16_t*)L.wgu, 0));
-  }
   if (L.panel_rows) {
     SKV_HIP(launch_to_panels((const bf16_t*)L.wgu, (int)(2 * f), (int)d, L.panel_rows, (bf16_t*)m->staging, 0));
     SKV_HIP(hipMemcpyAsync(L.wgu, m->staging, round_up(2 * f, 256) * d * E, hipMemcpyDeviceToDevice, 0));
@@ -708,6 +691,44 @@ skv_status skv_mfma_probe(int32_t random_operands, int32_t iters, void* stream, 
 
 namespace {
 
+// Scratch of one call: the buffers the row path and the last-token path
+// write (the model's own workspace).
+struct Work {
+  float* x = nullptr;  // fp32 residual stream of the new tokens [T, d]
+  float* y = nullptr;  // last tokens' residual stream [B, d]
+  void* ya = nullptr;  // row-major bf16 / fp32 rows [RY, d], [RY, dq], [RY, dq], [RY, f]
+  void* yq = nullptr;
+  void* yo = nullptr;
+  void* yh = nullptr;
+  float* rss = nullptr;  // bf16: partial sums of squares [RY, d / 128]
+  float* partial = nullptr;  // skinny split-K partials
+  int64_t partial_elems = 0;
+  float* attn_ws = nullptr;  // row attention chunk partials
+  int32_t *pos = nullptr, *slot = nullptr, *seq = nullptr;  // [T]
+  int32_t *last_pos = nullptr, *last_row = nullptr;          // [B]
+  bool profile = true;  // the profiling hook may record events
+};
+
+Work model_work(skv_model* m) {
+  Work w;
+  w.x = m->x;
+  w.y = m->y;
+  w.ya = m->ya;
+  w.yq = m->yq;
+  w.yo = m->yo;
+  w.yh = m->yh;
+  w.rss = m->rss;
+  w.partial = m->partial;
+  w.partial_elems = m->partial_elems;
+  w.attn_ws = m->attn_ws;
+  w.pos = m->pos;
+  w.slot = m->slot;
+  w.seq = m->seq;
+  w.last_pos = m->last_pos;
+  w.last_row = m->last_row;
+  return w;
+}
+
 // Host-side facts about one call's batch (validated before anything is enqueued).
 struct StepInfo {
   const int32_t* ctx_dev = nullptr;  // device [batch] cached positions per sequence, NULL = none
@@ -719,8 +740,9 @@ struct StepInfo {
 
 template <typename T>
 skv_status run_step(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, const StepInfo& si, float* logits,
-                    hipStream_t s) {
+                    hipStream_t s, const Work& w) {
   const auto& c = m->cfg;
+  skv_model* pm = w.profile ? m : nullptr;  // the profiling hook's model (NULL: no events)
   const int T_ = bt->total_tokens, B = bt->batch, d = c.d_model, dq = m->dq, dkv = m->dkv, f = c.ffn_dim,
             V = c.vocab, dh = c.head_dim, hq = c.n_q_heads, l = c.swiftkv_l, L = c.n_layers;
   const int P = dh / 2;
@@ -729,10 +751,10 @@ skv_status run_step(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, const S
   T* qbuf = (T*)m->qbuf;
   T* obuf = (T*)m->obuf;
   T* hbuf = (T*)m->hbuf;
-  T* ya = (T*)m->ya;
-  T* yq = (T*)m->yq;
-  T* yo = (T*)m->yo;
-  T* yh = (T*)m->yh;
+  T* ya = (T*)w.ya;
+  T* yq = (T*)w.yq;
+  T* yo = (T*)w.yo;
+  T* yh = (T*)w.yh;
   auto slot_of = [&](int s_) {
     return CacheSlot<T>{(T*)kc->k + (int64_t)s_ * kc->slot_elems, (T*)kc->v + (int64_t)s_ * kc->slot_elems,
                         c.n_kv_heads, dh};
@@ -747,9 +769,9 @@ skv_status run_step(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, const S
                    kc->ks + s_ * nb16, kc->vs + s_ * nb16, c.n_kv_heads, dh};
   };
   const CacheSlot<T> stage{(T*)m->kv_stage, (T*)m->kv_stage + m->stage_v, c.n_kv_heads, dh};
-  const int32_t* kv_slot = kv8 ? m->tok_iota : m->slot;  // where the K/V epilogues write
+  const int32_t* kv_slot = kv8 ? m->tok_iota : w.slot;  // where the K/V epilogues write
   auto quantize = [&](int rows, int ngroups, int first_slot) -> skv_status {
-    SKV_HIP(launch_kv_quant(m->kv_stage, m->stage_group, m->stage_v, rows, ngroups, m->slot, slot8_of(first_slot),
+    SKV_HIP(launch_kv_quant(m->kv_stage, m->stage_group, m->stage_v, rows, ngroups, w.slot, slot8_of(first_slot),
                             kc->slot_elems, nb16, s));
     return SKV_OK;
   };
@@ -766,33 +788,44 @@ skv_status run_step(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, const S
   const double last_bytes = n_deep * ((2.0 * dq * d + 3.0 * f * d) * E + si.ctx_tokens * 2.0 * dkv * E) + (double)V * d * E;
 
   SKV_HIP(launch_meta(bt->cu_seqlens, si.ctx_dev, bt->block_tables, B, bt->max_blocks_per_seq, kc->num_blocks, T_,
-                      m->pos, m->slot, m->last_pos, m->last_row, s));
-  if (!kBf16 || rows_path) SKV_HIP(launch_token_seq(bt->cu_seqlens, B, T_, m->seq, s));
-  SKV_HIP(launch_embed<T>(bt->token_ids, (const T*)m->embed, V, d, T_, m->x, s));
-  if (kBf16 && rows_path) SKV_HIP(launch_rows_act_ss(m->x, nullptr, T_, d, nullptr, (bf16_t*)ya, m->rss, s));
+                      w.pos, w.slot, w.last_pos, w.last_row, s));
+  if (!kBf16 || rows_path) SKV_HIP(launch_token_seq(bt->cu_seqlens, B, T_, w.seq, s));
+  SKV_HIP(launch_embed<T>(bt->token_ids, (const T*)m->embed, V, d, T_, w.x, s));
+  // bf16: the gain the projections of layer j (1-based) apply to their
+  // input, folded into the bf16 copy of x that precedes them (layer L + 1:
+  // the final norm); the skipped-layer K/V projection has its gains in its
+  // weights, so the input after layer l takes none
+  auto gain_before = [&](int j) -> const float* {
+    if (j > L) return m->final_norm;
+    return m->layers[j - 1].attn_norm;
+  };
+  if (kBf16 && rows_path)
+    SKV_HIP(launch_rows_act_ss(w.x, nullptr, l > 0 ? gain_before(1) : nullptr, T_, d, nullptr, (bf16_t*)ya, w.rss,
+                               s));
 
   // One layer over a few rows held row-major (the last tokens at layers
   // l+1..L; every new token of a short bf16 batch at layers 1..l).  x: the
   // rows' residual stream; with_kv: the QKV product also yields K/V, written
-  // to cache slot cs at slot[row].
+  // to cache slot cs at slot[row]; next_gain: the gain of the RMSNorm that
+  // the rows meet after this layer (bf16).
   auto row_layer = [&](const LayerDev& Ly, int cache_slot, int rows, float* x, const int32_t* row_seq,
-                       const int32_t* row_pos, bool with_kv, int max_ctx) -> skv_status {
+                       const int32_t* row_pos, bool with_kv, int max_ctx, const float* next_gain) -> skv_status {
     const CacheSlot<T> cs = slot_of(cache_slot);
     const int nq = with_kv ? dq + 2 * dkv : dq;
     EpiQKV<T> eq{yq, kv8 ? stage : cs, row_pos, with_kv ? kv_slot : nullptr, m->rope_cos, m->rope_sin, dq, dkv, dh, P};
     EpiSwiGLU<T> esw{yh, f, m->p_mlp};
-    // bf16: ya holds bf16(x) and rss its partial sums of squares on entry
-    // and on exit; the gains sit in the weights, and each normalised
-    // product scales by 1 / rms(x) in its finalize pass
+    // bf16: ya holds bf16(x * gain) and rss the partial sums of squares of
+    // x on entry and on exit; each normalised product scales by 1 / rms(x)
+    // in its finalize pass
     SkinnyRowNorm rn_in, rn_out;
     if constexpr (kBf16) {
-      rn_in.ss_in = m->rss;
+      rn_in.ss_in = w.rss;
       rn_in.nparts = (int)(d / 128);
       rn_in.inv_d = 1.0f / (float)d;
       rn_in.eps = c.rms_eps;
-      rn_out.ss_out = m->rss;
-      SKV_HIP(launch_skinny_bf16((const bf16_t*)ya, d, (const bf16_t*)Ly.wqkv, Ly.panel_rows, rows, nq, d, m->partial,
-                                 m->partial_elems, eq, s, rn_in));
+      rn_out.ss_out = w.rss;
+      SKV_HIP(launch_skinny_bf16((const bf16_t*)ya, d, (const bf16_t*)Ly.wqkv, Ly.panel_rows, rows, nq, d, w.partial,
+                                 w.partial_elems, eq, s, rn_in));
     } else {
       SKV_HIP(launch_rmsnorm<T>(x, nullptr, Ly.attn_norm, rows, d, c.rms_eps, ya, s));
       if (P == 16) {
@@ -807,19 +840,20 @@ skv_status run_step(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, const S
     if (kv8) {
       if constexpr (kBf16)
         SKV_HIP(launch_attn_rows_fp8((const bf16_t*)yq, slot8_of(cache_slot), row_seq, row_pos, bt->block_tables,
-                                     bt->max_blocks_per_seq, rows, max_ctx, hq, m->attn_ws, (bf16_t*)yo, s));
+                                     bt->max_blocks_per_seq, rows, max_ctx, hq, w.attn_ws, (bf16_t*)yo, s));
     } else {
       SKV_HIP(launch_attn_rows<T>(yq, cs, row_seq, row_pos, bt->block_tables, bt->max_blocks_per_seq, rows, max_ctx,
-                                  hq, m->attn_ws, yo, s));
+                                  hq, w.attn_ws, yo, s));
     }
     if constexpr (kBf16) {
-      EpiResidualRow er{x, d, (bf16_t*)ya};
-      SKV_HIP(launch_skinny_bf16((const bf16_t*)yo, dq, (const bf16_t*)Ly.wo, Ly.panel_rows, rows, d, dq, m->partial,
-                                 m->partial_elems, er, s, rn_out));
-      SKV_HIP(launch_skinny_bf16((const bf16_t*)ya, d, (const bf16_t*)Ly.wgu, Ly.panel_rows, rows, 2 * f, d, m->partial,
-                                 m->partial_elems, esw, s, rn_in));
-      SKV_HIP(launch_skinny_bf16((const bf16_t*)yh, f, (const bf16_t*)Ly.wdown, Ly.panel_rows, rows, d, f, m->partial,
-                                 m->partial_elems, er, s, rn_out));
+      EpiResidualRow er_o{x, d, (bf16_t*)ya, Ly.ffn_norm};
+      EpiResidualRow er_d{x, d, (bf16_t*)ya, next_gain};
+      SKV_HIP(launch_skinny_bf16((const bf16_t*)yo, dq, (const bf16_t*)Ly.wo, Ly.panel_rows, rows, d, dq, w.partial,
+                                 w.partial_elems, er_o, s, rn_out));
+      SKV_HIP(launch_skinny_bf16((const bf16_t*)ya, d, (const bf16_t*)Ly.wgu, Ly.panel_rows, rows, 2 * f, d, w.partial,
+                                 w.partial_elems, esw, s, rn_in));
+      SKV_HIP(launch_skinny_bf16((const bf16_t*)yh, f, (const bf16_t*)Ly.wdown, Ly.panel_rows, rows, d, f, w.partial,
+                                 w.partial_elems, er_d, s, rn_out));
     } else {
       EpiResidual er{x, d, 16};
       SKV_HIP((launch_gemm_f32<16>((const float*)yo, dq, (const float*)Ly.wo, dq, rows, d, dq, er, s)));
@@ -830,19 +864,19 @@ skv_status run_step(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, const S
     return SKV_OK;
   };
 
-  // bf16 prompt-token GEMMs take un-normalised bf16 rows (`act`) and apply
-  // the row's RMSNorm factor (rrow) in their epilogues; the gains sit in the
-  // weights.  The residual epilogues write the next act and the partial sums
-  // of squares for rrow.  Here: x_1's.
+  // bf16 prompt-token GEMMs take bf16(x * gain) (`act`) and apply the row's
+  // RMSNorm factor (rrow) in their epilogues.  The residual epilogues write
+  // the next act and the partial sums of squares for rrow.  Here: x_1's.
   const bool panel_path = kBf16 && !rows_path;
   auto next_rrow = [&]() -> skv_status {
-    Prof p(m, SKV_K_RMSNORM, s, 0, (double)T_ * d / 16 * 4 + T_ * 4.0);
+    Prof p(pm, SKV_K_RMSNORM, s, 0, (double)T_ * d / 16 * 4 + T_ * 4.0);
     SKV_HIP(launch_rms_from_partials(m->ssp, T_, d, c.rms_eps, m->rrow, s));
     return SKV_OK;
   };
   if (panel_path && (l > 0 || m->G > 0)) {
-    Prof p(m, SKV_K_RMSNORM, s, 0, (double)T_ * d * (4 + E));
-    SKV_HIP(launch_rows_rms_panel(m->x, T_, d, c.rms_eps, (bf16_t*)act, m->rrow, s));
+    Prof p(pm, SKV_K_RMSNORM, s, 0, (double)T_ * d * (4 + E));
+    SKV_HIP(launch_rows_rms_panel(w.x, l > 0 ? gain_before(1) : nullptr, T_, d, c.rms_eps, false, (bf16_t*)act, m->rrow,
+                                  s));
   }
   const float* rrow = panel_path ? m->rrow : nullptr;
 
@@ -851,17 +885,17 @@ skv_status run_step(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, const S
     const LayerDev& Ly = m->layers[i - 1];
     CacheSlot<T> cs = slot_of(i - 1);
     if (rows_path) {
-      SKV_TRY(row_layer(Ly, i - 1, T_, m->x, m->seq, m->pos, true, si.max_total));
+      SKV_TRY(row_layer(Ly, i - 1, T_, w.x, w.seq, w.pos, true, si.max_total, i < l ? gain_before(i + 1) : nullptr));
       continue;
     }
     if constexpr (!kBf16) {
-      Prof p(m, SKV_K_RMSNORM, s, 0, (double)T_ * d * (4 + E));
-      SKV_HIP(launch_rmsnorm<T>(m->x, nullptr, Ly.attn_norm, T_, d, c.rms_eps, act, s));
+      Prof p(pm, SKV_K_RMSNORM, s, 0, (double)T_ * d * (4 + E));
+      SKV_HIP(launch_rmsnorm<T>(w.x, nullptr, Ly.attn_norm, T_, d, c.rms_eps, act, s));
     }
     {
       const int N = dq + 2 * dkv;
-      EpiQKV<T> epi{qbuf, kv8 ? stage : cs, m->pos, kv_slot, m->rope_cos, m->rope_sin, dq, dkv, dh, P, rrow};
-      Prof p(m, SKV_K_GEMM_QKV, s, 2.0 * T_ * N * d, gemm_bytes(T_, N, d, E, E));
+      EpiQKV<T> epi{qbuf, kv8 ? stage : cs, w.pos, kv_slot, m->rope_cos, m->rope_sin, dq, dkv, dh, P, rrow};
+      Prof p(pm, SKV_K_GEMM_QKV, s, 2.0 * T_ * N * d, gemm_bytes(T_, N, d, E, E));
       if constexpr (kBf16)
         SKV_HIP(launch_gemm_bf16((const bf16_t*)act, (const bf16_t*)Ly.wqkv, T_, N, d, epi, m->gemm_ws, m->gemm_ws_elems, s));
       else if (P == 16)
@@ -873,7 +907,7 @@ skv_status run_step(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, const S
     }
     if (kv8) SKV_TRY(quantize(T_, 1, i - 1));
     {
-      Prof p(m, SKV_K_ATTN_PREFILL, s, si.attn_flops, attn_bytes);
+      Prof p(pm, SKV_K_ATTN_PREFILL, s, si.attn_flops, attn_bytes);
       if (kv8) {
         if constexpr (kBf16)
           SKV_HIP(launch_attn_prefill_fp8((const bf16_t*)qbuf, slot8_of(i - 1), bt->cu_seqlens, si.ctx_dev,
@@ -883,12 +917,13 @@ skv_status run_step(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, const S
         SKV_HIP(launch_attn_prefill_bf16((const bf16_t*)qbuf, cs, bt->cu_seqlens, si.ctx_dev, bt->block_tables,
                                          bt->max_blocks_per_seq, B, si.max_new, hq, (bf16_t*)obuf, s));
       else
-        SKV_HIP(launch_attn_rows<T>(qbuf, cs, m->seq, m->pos, bt->block_tables, bt->max_blocks_per_seq, T_,
-                                    si.max_total, hq, m->attn_ws, obuf, s));
+        SKV_HIP(launch_attn_rows<T>(qbuf, cs, w.seq, w.pos, bt->block_tables, bt->max_blocks_per_seq, T_,
+                                    si.max_total, hq, w.attn_ws, obuf, s));
     }
     {
-      EpiResidual epi{m->x, d, kBf16 ? 64 : 16, kBf16 ? (bf16_t*)act : nullptr, kBf16 ? m->ssp : nullptr};
-      Prof p(m, SKV_K_GEMM_O, s, 2.0 * T_ * d * dq, gemm_bytes(T_, d, dq, E, kBf16 ? 8 + 2 + 0.25 : 8));
+      EpiResidual epi{w.x, d, kBf16 ? 64 : 16, kBf16 ? (bf16_t*)act : nullptr, kBf16 ? m->ssp : nullptr,
+                      kBf16 ? Ly.ffn_norm : nullptr};
+      Prof p(pm, SKV_K_GEMM_O, s, 2.0 * T_ * d * dq, gemm_bytes(T_, d, dq, E, kBf16 ? 8 + 2 + 0.25 : 8));
       if constexpr (kBf16)
         SKV_HIP(launch_gemm_bf16((const bf16_t*)obuf, (const bf16_t*)Ly.wo, T_, d, dq, epi, m->gemm_ws, m->gemm_ws_elems, s));
       else
@@ -897,11 +932,11 @@ skv_status run_step(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, const S
     if constexpr (kBf16) {
       SKV_TRY(next_rrow());
     } else {
-      Prof p(m, SKV_K_RMSNORM, s, 0, (double)T_ * d * (4 + E));
-      SKV_HIP(launch_rmsnorm<T>(m->x, nullptr, Ly.ffn_norm, T_, d, c.rms_eps, act, s));
+      Prof p(pm, SKV_K_RMSNORM, s, 0, (double)T_ * d * (4 + E));
+      SKV_HIP(launch_rmsnorm<T>(w.x, nullptr, Ly.ffn_norm, T_, d, c.rms_eps, act, s));
     }
     {
-      Prof p(m, SKV_K_GEMM_GATEUP, s, 2.0 * T_ * 2 * f * d, gemm_bytes(T_, 2.0 * f, d, E, 0) + (double)T_ * f * E);
+      Prof p(pm, SKV_K_GEMM_GATEUP, s, 2.0 * T_ * 2 * f * d, gemm_bytes(T_, 2.0 * f, d, E, 0) + (double)T_ * f * E);
       if constexpr (kBf16) {
         EpiSwiGLUPanel epi{(bf16_t*)hbuf, f, rrow};
         SKV_HIP(launch_gemm_bf16((const bf16_t*)act, (const bf16_t*)Ly.wgu, T_, 2 * f, d, epi, m->gemm_ws, m->gemm_ws_elems, s));
@@ -911,8 +946,9 @@ skv_status run_step(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, const S
       }
     }
     {
-      EpiResidual epi{m->x, d, kBf16 ? 64 : 16, kBf16 ? (bf16_t*)act : nullptr, kBf16 ? m->ssp : nullptr};
-      Prof p(m, SKV_K_GEMM_DOWN, s, 2.0 * T_ * d * f, gemm_bytes(T_, d, f, E, kBf16 ? 8 + 2 + 0.25 : 8));
+      EpiResidual epi{w.x, d, kBf16 ? 64 : 16, kBf16 ? (bf16_t*)act : nullptr, kBf16 ? m->ssp : nullptr,
+                      (kBf16 && i < l) ? gain_before(i + 1) : nullptr};
+      Prof p(pm, SKV_K_GEMM_DOWN, s, 2.0 * T_ * d * f, gemm_bytes(T_, d, f, E, kBf16 ? 8 + 2 + 0.25 : 8));
       if constexpr (kBf16)
         SKV_HIP(launch_gemm_bf16((const bf16_t*)hbuf, (const bf16_t*)Ly.wdown, T_, d, f, epi, m->gemm_ws, m->gemm_ws_elems, s));
       else
@@ -924,24 +960,24 @@ skv_status run_step(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, const S
   // ---- boundary: KV of every skipped layer / AcrossKV group from x_{l+1}
   if (m->G > 0) {
     if constexpr (!kBf16) {
-      // x * r, gains folded into W~ (bf16: act / ya already hold bf16(x_{l+1}), with rrow / rss)
-      Prof p(m, SKV_K_RMSNORM, s, 0, (double)T_ * d * (4 + E));
-      SKV_HIP(launch_rmsnorm<T>(m->x, nullptr, nullptr, T_, d, c.rms_eps, act, s));
+      // x * r, gains folded into W~ (bf16: act / ya already hold bf16(x_{l+1}) without a gain, with rrow / rss)
+      Prof p(pm, SKV_K_RMSNORM, s, 0, (double)T_ * d * (4 + E));
+      SKV_HIP(launch_rmsnorm<T>(w.x, nullptr, nullptr, T_, d, c.rms_eps, act, s));
     }
     CacheSlot<T> first = kv8 ? stage : slot_of(l);
     const int N = m->G * 2 * dkv;
-    EpiKVSkip<T> epi{first.k, first.v, kv8 ? m->stage_group : kc->slot_elems, m->pos, kv_slot, m->rope_cos,
+    EpiKVSkip<T> epi{first.k, first.v, kv8 ? m->stage_group : kc->slot_elems, w.pos, kv_slot, m->rope_cos,
                      m->rope_sin, dkv, dh, P, c.n_kv_heads, rrow};
-    Prof p(m, SKV_K_GEMM_KVSKIP, s, 2.0 * T_ * N * d, gemm_bytes(T_, N, d, E, E));
+    Prof p(pm, SKV_K_GEMM_KVSKIP, s, 2.0 * T_ * N * d, gemm_bytes(T_, N, d, E, E));
     if constexpr (kBf16) {
       if (rows_path) {
         SkinnyRowNorm rn;
-        rn.ss_in = m->rss;
+        rn.ss_in = w.rss;
         rn.nparts = (int)(d / 128);
         rn.inv_d = 1.0f / (float)d;
         rn.eps = c.rms_eps;
-        SKV_HIP(launch_skinny_bf16((const bf16_t*)ya, d, (const bf16_t*)m->wkv_skip, kPanelRows, T_, N, d, m->partial,
-                                   m->partial_elems, epi, s, rn));
+        SKV_HIP(launch_skinny_bf16((const bf16_t*)ya, d, (const bf16_t*)m->wkv_skip, kPanelRows, T_, N, d, w.partial,
+                                   w.partial_elems, epi, s, rn));
       }
       else
         SKV_HIP(launch_gemm_bf16((const bf16_t*)act, (const bf16_t*)m->wkv_skip, T_, N, d, epi, m->gemm_ws,
@@ -957,25 +993,26 @@ skv_status run_step(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, const S
   }
 
   // ---- last new token of each sequence through layers l+1..L, then the LM head
-  Prof plast(m, SKV_K_LAST_TOKEN, s, last_flops, last_bytes);
+  Prof plast(pm, SKV_K_LAST_TOKEN, s, last_flops, last_bytes);
   if constexpr (kBf16)
-    SKV_HIP(launch_rows_act_ss(m->x, m->last_row, B, d, m->y, (bf16_t*)ya, m->rss, s));
+    SKV_HIP(launch_rows_act_ss(w.x, w.last_row, gain_before(l + 1), B, d, w.y, (bf16_t*)ya, w.rss, s));
   else
-    SKV_HIP(launch_gather_rows(m->x, m->last_row, B, d, m->y, s));
+    SKV_HIP(launch_gather_rows(w.x, w.last_row, B, d, w.y, s));
   for (int j = l + 1; j <= L; ++j)
-    SKV_TRY(row_layer(m->layers[j - 1], slot_of_layer(c, j), B, m->y, m->iota, m->last_pos, false, si.max_total));
+    SKV_TRY(row_layer(m->layers[j - 1], slot_of_layer(c, j), B, w.y, m->iota, w.last_pos, false, si.max_total,
+                      gain_before(j + 1)));
   EpiStoreF32 el{logits, V, kBf16 ? 64 : 16};
   if constexpr (kBf16) {
-    // final RMSNorm folded in: ya = bf16(y), its partials in rss, the gain in the LM head
+    // final RMSNorm: ya = bf16(y * final gain), the partials of y in rss
     SkinnyRowNorm rn;
-    rn.ss_in = m->rss;
+    rn.ss_in = w.rss;
     rn.nparts = (int)(d / 128);
     rn.inv_d = 1.0f / (float)d;
     rn.eps = c.rms_eps;
-    SKV_HIP(launch_skinny_bf16((const bf16_t*)ya, d, (const bf16_t*)m->lm_head, kSkinnyPanelRows, B, V, d, m->partial,
-                               m->partial_elems, el, s, rn));
+    SKV_HIP(launch_skinny_bf16((const bf16_t*)ya, d, (const bf16_t*)m->lm_head, kSkinnyPanelRows, B, V, d, w.partial,
+                               w.partial_elems, el, s, rn));
   } else {
-    SKV_HIP(launch_rmsnorm<T>(m->y, nullptr, m->final_norm, B, d, c.rms_eps, ya, s));
+    SKV_HIP(launch_rmsnorm<T>(w.y, nullptr, m->final_norm, B, d, c.rms_eps, ya, s));
     SKV_HIP((launch_gemm_f32<16>((const float*)ya, d, (const float*)m->lm_head, d, B, V, d, el, s)));
   }
   return SKV_OK;
@@ -985,10 +1022,10 @@ skv_status run_step(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, const S
 
 namespace {
 
-// Shared argument checks of skv_prefill / skv_step; ctx_host NULL = no
-// cached positions.
-skv_status check_and_run(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, const int32_t* ctx_host,
-                         const int32_t* ctx_dev, float* logits, void* stream) {
+// Shared argument checks of skv_prefill / skv_step;
+// ctx_host NULL = no cached positions.  Fills si on success.
+skv_status check_batch(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, const int32_t* ctx_host,
+                       const int32_t* ctx_dev, float* logits, StepInfo& si) {
   if (!m || !kc || !bt || !logits) return fail(SKV_ERR_INVALID_ARG, "NULL argument");
   if (kc->m != m) return fail(SKV_ERR_INVALID_ARG, "cache was created for another model");
   const auto& c = m->cfg;
@@ -1006,7 +1043,7 @@ skv_status check_and_run(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, co
   if (cu[0] != 0 || cu[B] != bt->total_tokens)
     return fail(SKV_ERR_INVALID_ARG, "cu_seqlens must start at 0 and end at total_tokens");
   const double dh = c.head_dim, hq = c.n_q_heads;
-  StepInfo si;
+  si = StepInfo{};
   si.ctx_dev = ctx_dev;
   for (int b = 0; b < B; ++b) {
     const int n = cu[b + 1] - cu[b];
@@ -1028,9 +1065,17 @@ skv_status check_and_run(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, co
     si.ctx_tokens += tot;
   }
   if (bt->max_seqlen < si.max_new) return fail(SKV_ERR_INVALID_ARG, "max_seqlen smaller than the longest run");
+  return SKV_OK;
+}
+
+skv_status check_and_run(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, const int32_t* ctx_host,
+                         const int32_t* ctx_dev, float* logits, void* stream) {
+  StepInfo si;
+  SKV_TRY(check_batch(m, kc, bt, ctx_host, ctx_dev, logits, si));
   hipStream_t s = (hipStream_t)stream;
-  if (m->bf16) return run_step<bf16_t>(m, kc, bt, si, logits, s);
-  return run_step<float>(m, kc, bt, si, logits, s);
+  const Work w = model_work(m);
+  if (m->bf16) return run_step<bf16_t>(m, kc, bt, si, logits, s, w);
+  return run_step<float>(m, kc, bt, si, logits, s, w);
 }
 
 }  // namespace

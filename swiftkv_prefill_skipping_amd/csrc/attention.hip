@@ -117,7 +117,15 @@ SKV_DEV void wait_loads_then_barrier() {
 // wave the score MFMAs of tile t+1 are issued before the softmax of tile t,
 // so the vector ALU work of one tile overlaps the matrix-core work of the
 // next.
-SKV_DEV void f8_qk(const bf16_t* sk, const bf16x8_t* qf, int lane, f32x16_t* sacc) {
+//
+// SPLIT: q, K and V come in split-bf16 form (hi + lo parts, see bf16_hi):
+// scores = q_hi.k_hi + q_hi.k_lo + q_lo.k_hi and O += P_hi.V_hi + P_hi.V_lo
+// + P_lo.V_hi (the lo.lo products are below 2^-16 of the result), three
+// MFMAs for each one of the plain kernel; the output is written in split
+// form too.
+template <bool SPLIT>
+SKV_DEV void f8_qk(const bf16_t* sk, const bf16_t* sk_lo, const bf16x8_t* qf, const bf16x8_t* qf_lo, int lane,
+                   f32x16_t* sacc) {
   const int hh = lane >> 5;
   sacc[0] = sacc[1] = f32x16_t{0};
 #pragma unroll
@@ -128,6 +136,12 @@ SKV_DEV void f8_qk(const bf16_t* sk, const bf16x8_t* qf, int lane, f32x16_t* sac
       const int key = st * 32 + (lane & 31);
       bf16x8_t kf = as_bf16x8(*reinterpret_cast<const u32x4_t*>(sk + key * FA_DH + ((ch ^ (key & 15)) << 3)));
       sacc[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc[st], 0, 0, 0);
+      if constexpr (SPLIT) {
+        const int off = key * FA_DH + ((ch ^ (key & 15)) << 3);
+        bf16x8_t kl = as_bf16x8(*reinterpret_cast<const u32x4_t*>(sk_lo + off));
+        sacc[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kl, qf[ks], sacc[st], 0, 0, 0);
+        sacc[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf_lo[ks], sacc[st], 0, 0, 0);
+      }
     }
   }
 }
@@ -136,14 +150,16 @@ SKV_DEV void f8_qk(const bf16_t* sk, const bf16x8_t* qf, int lane, f32x16_t* sac
 // registers: each thread fetches 16 codes of one key and its scale, and
 // writes code * scale as bf16 into the same LDS layout the direct loads
 // produce; everything after the tile loads is shared.
-template <bool F8>
+template <bool F8, bool SPLIT>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_prefill8_kernel(
-    const bf16_t* __restrict__ q, CacheSlot<bf16_t> cache, Fp8Slot c8, const int32_t* __restrict__ cu,
-    const int32_t* __restrict__ ctx, const int32_t* __restrict__ bt, int max_blocks, int hq, int rep,
-    float scale_log2, bf16_t* __restrict__ o) {
-  // buffers 0, 1: K ring; 2, 3: V ring ([64 keys][128 dims] each); the
-  // whole 64 KB stages the output at the end
-  __shared__ __attribute__((aligned(1024))) bf16_t smem[4][FA_KT * FA_DH];
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ q_lo, CacheSlot<bf16_t> cache, CacheSlot<bf16_t> lo,
+    Fp8Slot c8, const int32_t* __restrict__ cu, const int32_t* __restrict__ ctx, const int32_t* __restrict__ bt,
+    int max_blocks, int hq, int rep, float scale_log2, bf16_t* __restrict__ o) {
+  static_assert(!(F8 && SPLIT), "the FP8 cache has no split form");
+  // buffers 0, 1: K ring; 2, 3: V ring ([64 keys][128 dims] each); SPLIT:
+  // 4, 5 and 6, 7 the same for the low parts.  The first 64 KB stage the
+  // output at the end (SPLIT: the low parts in the next 64 KB)
+  __shared__ __attribute__((aligned(1024))) bf16_t smem[SPLIT ? 8 : 4][FA_KT * FA_DH];
 
   // grid: x = (prompt, head group), y = query tile counted from the last, so
   // workgroups are dispatched longest first across the whole batch
@@ -174,12 +190,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int nblk_need = (kend + kBlockSize - 1) / kBlockSize;
   const int32_t* btb = bt + (int64_t)b * max_blocks;
 
-  bf16x8_t qf[8];
+  bf16x8_t qf[8], qf_lo[SPLIT ? 8 : 1];
   {
     const int qi = min(q0 + (lane & 31), N - 1);
-    const bf16_t* qp = q + (int64_t)(tok0 + qi) * dq + h * FA_DH + hh * 8;
+    const int64_t qo = (int64_t)(tok0 + qi) * dq + h * FA_DH + hh * 8;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) qf[ks] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(qp + ks * 16));
+    for (int ks = 0; ks < 8; ++ks) qf[ks] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(q + qo + ks * 16));
+    if constexpr (SPLIT) {
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) qf_lo[ks] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(q_lo + qo + ks * 16));
+    }
   }
 
   // Tile loads: wave w moves 16-key block r = w/2, key rows (w%2)*8 .. +8
@@ -281,7 +301,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   auto exp_pv = [&](const f32x16_t* sacc, int vb) {
     const float mneg = -m_run;
     float ls = 0.f;
-    bf16x8_t pf[4];
+    bf16x8_t pf[4], pf_lo[SPLIT ? 4 : 1];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       const int st = kk >> 1, vb8 = 8 * (kk & 1);
@@ -293,10 +313,18 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
       pf[kk] = as_bf16x8(u32x4_t{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
                                  pack_bf16x2(p[6], p[7])});
+      if constexpr (SPLIT) {
+        float pl[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pl[e] = bf16_lo_part(p[e]);
+        pf_lo[kk] = as_bf16x8(u32x4_t{pack_bf16x2(pl[0], pl[1]), pack_bf16x2(pl[2], pl[3]), pack_bf16x2(pl[4], pl[5]),
+                                      pack_bf16x2(pl[6], pl[7])});
+      }
     }
     ls = xor32_sum(ls);
     l_run += ls;
     const bf16_t* sv = smem[2 + vb];
+    const bf16_t* sv_lo = smem[SPLIT ? 6 + vb : 2 + vb];
     const int tj = lane & 15, ta = tj >> 2, tb = tj & 3;
     // key steps outer, dims inner: consecutive MFMAs feed four independent
     // accumulators
@@ -314,6 +342,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         u32x2_t lo2 = __builtin_bit_cast(u32x2_t, lo), hi2 = __builtin_bit_cast(u32x2_t, hi);
         bf16x8_t vf = as_bf16x8(u32x4_t{lo2.x, lo2.y, hi2.x, hi2.y});
         oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kk], oacc[dt], 0, 0, 0);
+        if constexpr (SPLIT) {
+          const int o1 = k1 * FA_DH + (((d >> 3) ^ (k1 & 15)) << 3) + (d & 7);
+          const int o2 = k2 * FA_DH + (((d >> 3) ^ (k2 & 15)) << 3) + (d & 7);
+          s16x4_t llo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4p)(sv_lo + o1));
+          s16x4_t lhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4p)(sv_lo + o2));
+          u32x2_t a2 = __builtin_bit_cast(u32x2_t, llo), b2 = __builtin_bit_cast(u32x2_t, lhi);
+          bf16x8_t vl = as_bf16x8(u32x4_t{a2.x, a2.y, b2.x, b2.y});
+          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vl, pf[kk], oacc[dt], 0, 0, 0);
+          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf_lo[kk], oacc[dt], 0, 0, 0);
+        }
       }
     }
   };
@@ -328,69 +366,93 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // score accumulators stay in registers.
   // blk1 / blk2: block ids of tiles t+1 / t+2, fetched one iteration ahead
   // so no load waits on a block-table read
-  int blk1 = block_of(1), blk2 = block_of(2);
-  u32x4_t wk, wv;  // FP8: codes of K(t+2) / V(t+1) in flight through registers
-  float sk, sv;
-  if constexpr (F8) {
-    const int blk0 = block_of(0);
-    fetch8(c8.k, c8.ks, blk0, wk, sk);
-    fetch8(c8.v, c8.vs, blk0, wv, sv);
-    store8(wk, sk, 0);
-    store8(wv, sv, 2);
-    fetch8(c8.k, c8.ks, blk1, wk, sk);
-    store8(wk, sk, 1);
-  } else {
-    issue(cache.k, block_of(0), 0);
-    issue(cache.v, block_of(0), 2);
-    issue(cache.k, blk1, 1);
-  }
-  wait_loads_then_barrier();
-  f32x16_t sa[2], sb[2];
-  f8_qk(smem[0], qf, lane, sa);
-  wait_loads_then_barrier();  // every wave has read K(0) before its buffer takes K(2)
-  auto full = [&](int t, f32x16_t* cur, f32x16_t* nxt) {
-    const int blk3 = block_of(t + 3);
-    if constexpr (F8) {
-      fetch8(c8.k, c8.ks, blk2, wk, sk);
-      fetch8(c8.v, c8.vs, blk1, wv, sv);
-    } else {
-      issue(cache.k, blk2, t & 1);
-      issue(cache.v, blk1, 2 + ((t + 1) & 1));
+  if constexpr (SPLIT) {
+    // Split form: one tile at a time (the extra q / P parts leave no
+    // registers for the next tile's scores).  Iteration t waits for tile t,
+    // then loads tile t + 1 into the buffers tile t - 1 used while it
+    // computes tile t.
+    auto issue_tile = [&](int t) {
+      const int blk = block_of(t);
+      issue(cache.k, blk, t & 1);
+      issue(cache.v, blk, 2 + (t & 1));
+      issue(lo.k, blk, 4 + (t & 1));
+      issue(lo.v, blk, 6 + (t & 1));
+    };
+    issue_tile(0);
+    for (int t = 0; t < ntiles; ++t) {
+      wait_loads_then_barrier();
+      if (t + 1 < ntiles) issue_tile(t + 1);
+      f32x16_t sa[2];
+      f8_qk<true>(smem[t & 1], smem[4 + (t & 1)], qf, qf_lo, lane, sa);
+      soft_prep(t, sa);
+      exp_pv(sa, t & 1);
     }
-    soft_prep(t, cur);
-    f8_qk(smem[(t + 1) & 1], qf, lane, nxt);
-    exp_pv(cur, t & 1);
+  } else {
+    int blk1 = block_of(1), blk2 = block_of(2);
+    u32x4_t wk, wv;  // FP8: codes of K(t+2) / V(t+1) in flight through registers
+    float sk, sv;
     if constexpr (F8) {
-      // K(t) and V(t-1), whose buffers these take, were last read in the
-      // previous iteration
-      store8(wk, sk, t & 1);
-      store8(wv, sv, 2 + ((t + 1) & 1));
+      const int blk0 = block_of(0);
+      fetch8(c8.k, c8.ks, blk0, wk, sk);
+      fetch8(c8.v, c8.vs, blk0, wv, sv);
+      store8(wk, sk, 0);
+      store8(wv, sv, 2);
+      fetch8(c8.k, c8.ks, blk1, wk, sk);
+      store8(wk, sk, 1);
+    } else {
+      issue(cache.k, block_of(0), 0);
+      issue(cache.v, block_of(0), 2);
+      issue(cache.k, blk1, 1);
     }
     wait_loads_then_barrier();
-    blk1 = blk2;
-    blk2 = blk3;
-  };
-  auto last = [&](int t, f32x16_t* cur) {
-    soft_prep(t, cur);
-    exp_pv(cur, t & 1);
-  };
-  const int n1 = ntiles - 1;  // iterations that also compute the next tile's scores
-  int t = 0;
-  for (; t + 1 < n1; t += 2) {
-    full(t, sa, sb);
-    full(t + 1, sb, sa);
-  }
-  if (t < n1) {
-    full(t, sa, sb);
-    last(t + 1, sb);
-  } else {
-    last(t, sa);
+    f32x16_t sa[2], sb[2];
+    f8_qk<false>(smem[0], smem[0], qf, qf_lo, lane, sa);
+    wait_loads_then_barrier();  // every wave has read K(0) before its buffer takes K(2)
+    auto full = [&](int t, f32x16_t* cur, f32x16_t* nxt) {
+      const int blk3 = block_of(t + 3);
+      if constexpr (F8) {
+        fetch8(c8.k, c8.ks, blk2, wk, sk);
+        fetch8(c8.v, c8.vs, blk1, wv, sv);
+      } else {
+        issue(cache.k, blk2, t & 1);
+        issue(cache.v, blk1, 2 + ((t + 1) & 1));
+      }
+      soft_prep(t, cur);
+      f8_qk<false>(smem[(t + 1) & 1], smem[0], qf, qf_lo, lane, nxt);
+      exp_pv(cur, t & 1);
+      if constexpr (F8) {
+        // K(t) and V(t-1), whose buffers these take, were last read in the
+        // previous iteration
+        store8(wk, sk, t & 1);
+        store8(wv, sv, 2 + ((t + 1) & 1));
+      }
+      wait_loads_then_barrier();
+      blk1 = blk2;
+      blk2 = blk3;
+    };
+    auto last = [&](int t, f32x16_t* cur) {
+      soft_prep(t, cur);
+      exp_pv(cur, t & 1);
+    };
+    const int n1 = ntiles - 1;  // iterations that also compute the next tile's scores
+    int t = 0;
+    for (; t + 1 < n1; t += 2) {
+      full(t, sa, sb);
+      full(t + 1, sb, sa);
+    }
+    if (t < n1) {
+      full(t, sa, sb);
+      last(t + 1, sb);
+    } else {
+      last(t, sa);
+    }
   }
   wait_loads_then_barrier();  // all P.V reads done before the buffers stage the output
 
   // normalise and write: O^T -> LDS [32 q][128 d] per wave (8-byte quads
   // swizzled by q) -> panel rows (a row's 128 dims are four 64-byte runs)
   bf16_t* so = &smem[0][0] + wave * (32 * FA_DH);
+  bf16_t* so_lo = &smem[0][0] + (SPLIT ? 4 * FA_KT * FA_DH : 0) + wave * (32 * FA_DH);
   {
     const float inv = 1.0f / l_run;
     const int ql = lane & 31;
@@ -403,11 +465,22 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         w.x = pack_bf16x2(oacc[dt][vq * 4 + 0] * inv, oacc[dt][vq * 4 + 1] * inv);
         w.y = pack_bf16x2(oacc[dt][vq * 4 + 2] * inv, oacc[dt][vq * 4 + 3] * inv);
         *reinterpret_cast<u32x2_t*>(so + ql * FA_DH + ((u ^ ql) << 2)) = w;
+        if constexpr (SPLIT) {
+          float y[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) y[e] = oacc[dt][vq * 4 + e] * inv;
+          u32x2_t wl;
+          wl.x = pack_bf16x2(bf16_lo_part(y[0]), bf16_lo_part(y[1]));
+          wl.y = pack_bf16x2(bf16_lo_part(y[2]), bf16_lo_part(y[3]));
+          *reinterpret_cast<u32x2_t*>(so_lo + ql * FA_DH + ((u ^ ql) << 2)) = wl;
+        }
       }
   }
   __builtin_amdgcn_sched_barrier(0);
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
+  // SPLIT: o has 2 dq columns, hi at column c and lo at column dq + c
+  const int ocols = SPLIT ? 2 * dq : dq;
 #pragma unroll
   for (int it = 0; it < 16; ++it) {
     const int idx = it * 64 + lane;
@@ -415,7 +488,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int qi = q0 + ql2;
     if (qi < N) {
       u32x2_t w = *reinterpret_cast<const u32x2_t*>(so + ql2 * FA_DH + ((u ^ ql2) << 2));
-      *reinterpret_cast<u32x2_t*>(o + panel_off(tok0 + qi, h * FA_DH + u * 4, dq)) = w;
+      *reinterpret_cast<u32x2_t*>(o + panel_off(tok0 + qi, h * FA_DH + u * 4, ocols)) = w;
+      if constexpr (SPLIT) {
+        u32x2_t wl = *reinterpret_cast<const u32x2_t*>(so_lo + ql2 * FA_DH + ((u ^ ql2) << 2));
+        *reinterpret_cast<u32x2_t*>(o + panel_off(tok0 + qi, dq + h * FA_DH + u * 4, ocols)) = wl;
+      }
     }
   }
 }
@@ -830,8 +907,23 @@ hipError_t launch_attn_prefill_bf16(const bf16_t* q, CacheSlot<bf16_t> cache, co
   const int rep = hq / cache.hkv;
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)FA_DH);
   dim3 grid(batch * (hq / 4), (max_new + 63) / 64);
-  hipLaunchKernelGGL(attn_prefill8_kernel<false>, grid, dim3(512), 0, stream, q, cache, Fp8Slot{}, cu_seqlens,
-                     ctx_lens, block_tables, max_blocks, hq, rep, scale_log2, o);
+  hipLaunchKernelGGL((attn_prefill8_kernel<false, false>), grid, dim3(512), 0, stream, q, nullptr, cache,
+                     CacheSlot<bf16_t>{nullptr, nullptr, cache.hkv, cache.dh}, Fp8Slot{}, cu_seqlens, ctx_lens,
+                     block_tables, max_blocks, hq, rep, scale_log2, o);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_prefill_split(const bf16_t* q, const bf16_t* q_lo, CacheSlot<bf16_t> cache,
+                                     CacheSlot<bf16_t> lo, const int32_t* cu_seqlens, const int32_t* ctx_lens,
+                                     const int32_t* block_tables, int max_blocks, int batch, int max_new, int hq,
+                                     bf16_t* o, hipStream_t stream) {
+  if (batch <= 0 || max_new <= 0) return hipSuccess;
+  if (!q_lo || !lo.k || !lo.v || lo.hkv != cache.hkv || lo.dh != cache.dh) return hipErrorInvalidValue;
+  const int rep = hq / cache.hkv;
+  const float scale_log2 = 1.4426950408889634f / sqrtf((float)FA_DH);
+  dim3 grid(batch * (hq / 4), (max_new + 63) / 64);
+  hipLaunchKernelGGL((attn_prefill8_kernel<false, true>), grid, dim3(512), 0, stream, q, q_lo, cache, lo, Fp8Slot{},
+                     cu_seqlens, ctx_lens, block_tables, max_blocks, hq, rep, scale_log2, o);
   return hipGetLastError();
 }
 
@@ -843,7 +935,8 @@ hipError_t launch_attn_prefill_fp8(const bf16_t* q, Fp8Slot cache, const int32_t
   const int rep = hq / cache.hkv;
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)FA_DH);
   dim3 grid(batch * (hq / 4), (max_new + 63) / 64);
-  hipLaunchKernelGGL(attn_prefill8_kernel<true>, grid, dim3(512), 0, stream, q,
+  hipLaunchKernelGGL((attn_prefill8_kernel<true, false>), grid, dim3(512), 0, stream, q, nullptr,
+                     CacheSlot<bf16_t>{nullptr, nullptr, cache.hkv, cache.dh},
                      CacheSlot<bf16_t>{nullptr, nullptr, cache.hkv, cache.dh}, cache, cu_seqlens, ctx_lens,
                      block_tables, max_blocks, hq, rep, scale_log2, o);
   return hipGetLastError();

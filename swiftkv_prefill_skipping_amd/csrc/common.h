@@ -25,6 +25,13 @@ SKV_DEV uint32_t pack_bf16x2(float lo, float hi) {
 }
 SKV_DEV bf16_t f32_to_bf16(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
 
+// Split-bf16 form of a float: hi = bf16(v) and lo = bf16(v - hi).  v - hi
+// is exact in fp32, so hi + lo carries 16 significant bits of v; a bf16
+// MFMA over both parts then sees the operand to about 2^-17 instead of
+// 2^-9.
+SKV_DEV float bf16_hi(float v) { return bf16_to_f32(f32_to_bf16(v)); }
+SKV_DEV float bf16_lo_part(float v) { return v - bf16_hi(v); }
+
 template <typename T>
 SKV_DEV float to_f32(T v);
 template <>

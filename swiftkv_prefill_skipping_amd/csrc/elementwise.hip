@@ -96,9 +96,12 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
   }
 }
 
-// Un-normalised GEMM input of a row plus its RMSNorm factor: y = bf16(x) in
-// the panel layout, r[row] = 1 / sqrt(mean(x^2) + eps).  One wave per row.
-__global__ __launch_bounds__(256) void rows_rms_panel_kernel(const float* __restrict__ x, int rows, int d, float eps,
+// GEMM input of a row before its RMSNorm factor, plus that factor: y =
+// bf16(x * gamma) in the panel layout (gamma NULL = 1), r[row] = 1 /
+// sqrt(mean(x^2) + eps).  One wave per row.  split: y has 2d columns, the
+// split-bf16 parts of x * gamma (hi at column c, lo at column d + c).
+__global__ __launch_bounds__(256) void rows_rms_panel_kernel(const float* __restrict__ x, const float* __restrict__ gamma,
+                                                             int rows, int d, float eps, bool split,
                                                              bf16_t* __restrict__ y, float* __restrict__ r_out) {
   const int lane = threadIdx.x & 63;
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -110,7 +113,18 @@ __global__ __launch_bounds__(256) void rows_rms_panel_kernel(const float* __rest
     load8(xr + c, v);
 #pragma unroll
     for (int e = 0; e < 8; ++e) ss += v[e] * v[e];
-    store8(y + panel_off(r, c, d), v);
+    if (gamma) {
+      float g[8];
+      load8(gamma + c, g);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] *= g[e];
+    }
+    if (split) {
+      store8(y + panel_off(r, c, 2 * d), v);
+      store8_lo(y + panel_off(r, d + c, 2 * d), v);
+    } else {
+      store8(y + panel_off(r, c, d), v);
+    }
   }
   ss = warp_sum(ss);
   if (lane == 0) r_out[r] = 1.0f / sqrtf(ss / (float)d + eps);
@@ -160,14 +174,16 @@ __global__ void gather_rows_kernel(const float* __restrict__ x, const int32_t* _
 // One row per workgroup; a half-wave (32 lanes x 4 values) covers one
 // 128-column unit of the sums of squares.
 __global__ __launch_bounds__(256) void rows_act_ss_kernel(const float* __restrict__ x, const int32_t* __restrict__ idx,
-                                                          int d, float* __restrict__ y, bf16_t* __restrict__ act,
+                                                          const float* __restrict__ gamma, int d,
+                                                          float* __restrict__ y, bf16_t* __restrict__ act,
                                                           float* __restrict__ ss) {
   const int r = blockIdx.x;
   const float* xr = x + (int64_t)(idx ? idx[r] : r) * d;
   for (int c = threadIdx.x * 4; c < d; c += 1024) {
     const float4 v = *reinterpret_cast<const float4*>(xr + c);
     if (y) *reinterpret_cast<float4*>(y + (int64_t)r * d + c) = v;
-    const u32x2_t packed{pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w)};
+    const float4 g = gamma ? *reinterpret_cast<const float4*>(gamma + c) : float4{1.f, 1.f, 1.f, 1.f};
+    const u32x2_t packed{pack_bf16x2(v.x * g.x, v.y * g.y), pack_bf16x2(v.z * g.z, v.w * g.w)};
     *reinterpret_cast<u32x2_t*>(act + (int64_t)r * d + c) = packed;
     float q = v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
 #pragma unroll
@@ -245,11 +261,12 @@ hipError_t launch_rmsnorm(const float* x, const int32_t* rows_idx, const float* 
   return hipGetLastError();
 }
 
-hipError_t launch_rows_rms_panel(const float* x, int rows, int d, float eps, bf16_t* y, float* r,
-                                 hipStream_t stream) {
+hipError_t launch_rows_rms_panel(const float* x, const float* gamma, int rows, int d, float eps, bool split, bf16_t* y,
+                                 float* r, hipStream_t stream) {
   if (rows <= 0) return hipSuccess;
   if (d % kPanelCols) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(rows_rms_panel_kernel, dim3((rows + 3) / 4), dim3(256), 0, stream, x, rows, d, eps, y, r);
+  hipLaunchKernelGGL(rows_rms_panel_kernel, dim3((rows + 3) / 4), dim3(256), 0, stream, x, gamma, rows, d, eps, split,
+                     y, r);
   return hipGetLastError();
 }
 
@@ -277,11 +294,11 @@ hipError_t launch_gather_rows(const float* x, const int32_t* rows_idx, int rows,
   return hipGetLastError();
 }
 
-hipError_t launch_rows_act_ss(const float* x, const int32_t* rows_idx, int rows, int d, float* y, bf16_t* act,
-                              float* ss, hipStream_t stream) {
+hipError_t launch_rows_act_ss(const float* x, const int32_t* rows_idx, const float* gamma, int rows, int d, float* y,
+                              bf16_t* act, float* ss, hipStream_t stream) {
   if (rows <= 0) return hipSuccess;
   if (d % 128) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(rows_act_ss_kernel, dim3(rows), dim3(256), 0, stream, x, rows_idx, d, y, act, ss);
+  hipLaunchKernelGGL(rows_act_ss_kernel, dim3(rows), dim3(256), 0, stream, x, rows_idx, gamma, d, y, act, ss);
   return hipGetLastError();
 }
 

@@ -30,6 +30,13 @@ SKV_DEV void store8(bf16_t* p, const float* v) {
   *reinterpret_cast<u32x4_t*>(p) =
       u32x4_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
 }
+// The low parts bf16(v - bf16(v)) of eight values (split-bf16 form).
+SKV_DEV void store8_lo(bf16_t* p, const float* v) {
+  float l[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) l[e] = bf16_lo_part(v[e]);
+  store8(p, l);
+}
 
 // Plain fp32 store (logits).
 struct EpiStoreF32 {
@@ -64,16 +71,19 @@ struct EpiStore {
 
 // Residual add into the fp32 residual stream: x += o W^T  (O and down projections).
 // Optionally (act != NULL, vec8 only) it also hands the next projection its
-// input: act = bf16 of the new x in the panel layout, and ss = the sum of
-// squares of each eight-pair unit's 16 new x values at [row * ld/16 +
-// (col / 2P) * P/8 + (col % 2P) / 8], from which the row's RMSNorm factor
-// is summed in fixed order.
+// input: act = bf16(x * gain) of the new x in the panel layout (gain: the
+// next RMSNorm's weights, NULL = 1), and ss = the sum of squares of each
+// eight-pair unit's 16 new x values at [row * ld/16 + (col / 2P) * P/8 +
+// (col % 2P) / 8], from which the row's RMSNorm factor is summed in fixed
+// order.  The next projection multiplies its products by that factor, so it
+// computes RMSNorm(x; gain) W^T with the weights exactly as given.
 struct EpiResidual {
   float* x;
   int ld;
   int P;
   bf16_t* act = nullptr;
   float* ss = nullptr;
+  const float* gain = nullptr;
   SKV_DEV void operator()(int row, int col, float v0, float v1) const {
     float* p = x + (int64_t)row * ld + col;
     p[0] += v0;
@@ -101,11 +111,21 @@ struct EpiResidual {
     store8(p, y0);
     store8(p + P, y1);
     if (act) {
-      store8(act + panel_off(row, col, ld), y0);
-      store8(act + panel_off(row, col + P, ld), y1);
       float q = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) q += y0[e] * y0[e] + y1[e] * y1[e];
+      if (gain) {
+        float g0[8], g1[8];
+        load8(gain + col, g0);
+        load8(gain + col + P, g1);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          y0[e] *= g0[e];
+          y1[e] *= g1[e];
+        }
+      }
+      store8(act + panel_off(row, col, ld), y0);
+      store8(act + panel_off(row, col + P, ld), y1);
       // (the bf16 GEMM's pairs are 64 apart: shifts instead of a division)
       const int u = P == 64 ? ((col >> 7) << 3) + ((col & 127) >> 3) : (col / (2 * P)) * (P / 8) + (col % (2 * P)) / 8;
       ss[(int64_t)row * (ld / 16) + u] = q;
@@ -115,22 +135,25 @@ struct EpiResidual {
 };
 
 // Residual add for the skinny (row-major, at most 32 rows) products:
-// x += o W^T on the column pair (col, col + 64), act = bf16 of the new x in
-// the same row-major layout (the next projection's un-normalised input),
-// and the pair's sum of squares handed back to the finalize pass, which
+// x += o W^T on the column pair (col, col + 64), act = bf16(x * gain) of the
+// new x in the same row-major layout (the next projection's input before
+// its RMSNorm factor; gain = the next RMSNorm's weights, NULL = 1), and the
+// pair's sum of squares of x handed back to the finalize pass, which
 // reduces it over the wave's 128 columns.
 struct EpiResidualRow {
   float* x;
   int ld;
   bf16_t* act;
+  const float* gain = nullptr;
   SKV_DEV float operator()(int row, int col, float v0, float v1) const {
     float* p = x + (int64_t)row * ld + col;
     const float y0 = p[0] + v0, y1 = p[64] + v1;
     p[0] = y0;
     p[64] = y1;
+    const float g0 = gain ? gain[col] : 1.0f, g1 = gain ? gain[col + 64] : 1.0f;
     bf16_t* a = act + (int64_t)row * ld + col;
-    a[0] = from_f32<bf16_t>(y0);
-    a[64] = from_f32<bf16_t>(y1);
+    a[0] = from_f32<bf16_t>(y0 * g0);
+    a[64] = from_f32<bf16_t>(y1 * g1);
     return y0 * y0 + y1 * y1;
   }
 };
@@ -219,6 +242,11 @@ SKV_DEV void rope8(const float* x0, const float* x1, const float* rope_cos, cons
 // key heads, [dq+dkv, dq+2dkv) value heads.  RoPE rotates q and k at the
 // token's position; q goes to a [rows, hq, dh] buffer, k and v into the
 // paged cache slot of this layer.  P = dh / 2.
+//
+// Optional split-bf16 low parts (bf16 only): q_lo receives bf16(q - bf16(q))
+// in q's layout, k_lo / v_lo the same of k and v in the cache layout (a
+// side buffer with the cache slot's geometry), for an attention that
+// computes with both parts.
 template <typename T>
 struct EpiQKV {
   T* q;
@@ -229,6 +257,15 @@ struct EpiQKV {
   const float* rope_sin;
   int dq, dkv, dh, P;
   const float* rs = nullptr;  // optional per-row factor (RMSNorm of an un-normalised input)
+  T* q_lo = nullptr;
+  T* k_lo = nullptr;
+  T* v_lo = nullptr;
+  static constexpr bool kSplit = sizeof(T) == 2;
+  SKV_DEV void put(T* base, T* lo, int64_t i, float v) const {
+    base[i] = from_f32<T>(v);
+    if constexpr (kSplit)
+      if (lo) lo[i] = from_f32<T>(bf16_lo_part(v));
+  }
   SKV_DEV void operator()(int row, int col, float v0, float v1) const {
     if (rs) {
       v0 *= rs[row];
@@ -240,9 +277,9 @@ struct EpiQKV {
       float c = rope_cos[(int64_t)p * P + i], s = rope_sin[(int64_t)p * P + i];
       float y0, y1;
       rope_pair(v0, v1, c, s, y0, y1);
-      T* qp = q + (int64_t)row * dq + col;
-      qp[0] = from_f32<T>(y0);
-      qp[P] = from_f32<T>(y1);
+      const int64_t qi = (int64_t)row * dq + col;
+      put(q, q_lo, qi, y0);
+      put(q, q_lo, qi + P, y1);
       return;
     }
     int sl = slot[row];
@@ -253,12 +290,12 @@ struct EpiQKV {
       float c = rope_cos[(int64_t)p * P + i], s = rope_sin[(int64_t)p * P + i];
       float y0, y1;
       rope_pair(v0, v1, c, s, y0, y1);
-      cache.k[kv_index(sl, h, i, cache.hkv, dh)] = from_f32<T>(y0);
-      cache.k[kv_index(sl, h, i + P, cache.hkv, dh)] = from_f32<T>(y1);
+      put(cache.k, k_lo, kv_index(sl, h, i, cache.hkv, dh), y0);
+      put(cache.k, k_lo, kv_index(sl, h, i + P, cache.hkv, dh), y1);
     } else {
       int vc = col - dq - dkv, h = vc / dh, i = vc % dh;
-      cache.v[kv_index(sl, h, i, cache.hkv, dh)] = from_f32<T>(v0);
-      cache.v[kv_index(sl, h, i + P, cache.hkv, dh)] = from_f32<T>(v1);
+      put(cache.v, v_lo, kv_index(sl, h, i, cache.hkv, dh), v0);
+      put(cache.v, v_lo, kv_index(sl, h, i + P, cache.hkv, dh), v1);
     }
   }
   SKV_DEV float scale(int row) const { return rs ? rs[row] : 1.0f; }
@@ -275,9 +312,14 @@ struct EpiQKV {
     float y0[8], y1[8];
     if (col < dq) {
       rope8(a, b, rope_cos, rope_sin, pos[row], P, col % dh, y0, y1);
-      T* qp = q + (int64_t)row * dq + col;
-      store8(qp, y0);
-      store8(qp + P, y1);
+      const int64_t qi = (int64_t)row * dq + col;
+      store8(q + qi, y0);
+      store8(q + qi + P, y1);
+      if constexpr (kSplit)
+        if (q_lo) {
+          store8_lo(q_lo + qi, y0);
+          store8_lo(q_lo + qi + P, y1);
+        }
       return;
     }
     int sl = slot[row];
@@ -285,12 +327,24 @@ struct EpiQKV {
     if (col < dq + dkv) {
       int kc = col - dq, h = kc / dh, i = kc % dh;
       rope8(a, b, rope_cos, rope_sin, pos[row], P, i, y0, y1);
-      store8(cache.k + kv_index(sl, h, i, cache.hkv, dh), y0);
-      store8(cache.k + kv_index(sl, h, i + P, cache.hkv, dh), y1);
+      const int64_t i0 = kv_index(sl, h, i, cache.hkv, dh), i1 = kv_index(sl, h, i + P, cache.hkv, dh);
+      store8(cache.k + i0, y0);
+      store8(cache.k + i1, y1);
+      if constexpr (kSplit)
+        if (k_lo) {
+          store8_lo(k_lo + i0, y0);
+          store8_lo(k_lo + i1, y1);
+        }
     } else {
       int vc = col - dq - dkv, h = vc / dh, i = vc % dh;
-      store8(cache.v + kv_index(sl, h, i, cache.hkv, dh), a);
-      store8(cache.v + kv_index(sl, h, i + P, cache.hkv, dh), b);
+      const int64_t i0 = kv_index(sl, h, i, cache.hkv, dh), i1 = kv_index(sl, h, i + P, cache.hkv, dh);
+      store8(cache.v + i0, a);
+      store8(cache.v + i1, b);
+      if constexpr (kSplit)
+        if (v_lo) {
+          store8_lo(v_lo + i0, a);
+          store8_lo(v_lo + i1, b);
+        }
     }
   }
 };

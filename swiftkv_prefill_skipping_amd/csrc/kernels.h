@@ -33,8 +33,8 @@ constexpr int kSkinnyMaxRows = 32;
 // panels of panel_rows (kSkinnyPanelRows or kPanelRows) rows.  Requires
 // K % 256 == 0, N % 128 == 0.
 //
-// Row RMSNorm folded into the product (rn.ss_in != NULL): A holds bf16(x)
-// of rows whose gains sit in B, and rn.ss_in [M, nparts] holds partial sums
+// Row RMSNorm applied by the product (rn.ss_in != NULL): A holds
+// bf16(x * gain) of the rows, and rn.ss_in [M, nparts] holds partial sums
 // of squares of x; the finalize scales each row's products by
 // 1 / sqrt(sum * inv_d + eps) before the epilogue.  EpiResidualRow writes
 // the new rows' partials (one per 128 columns) to rn.ss_out [M, N / 128].
@@ -69,10 +69,12 @@ template <typename T>
 hipError_t launch_rmsnorm(const float* x, const int32_t* rows_idx, const float* gamma, int rows, int d, float eps,
                           T* y, hipStream_t stream);
 
-// Un-normalised input of the next projection: y = bf16(x) in the panel
-// layout (d columns, d % 32 == 0) and r[row] = 1 / sqrt(mean x^2 + eps).
-hipError_t launch_rows_rms_panel(const float* x, int rows, int d, float eps, bf16_t* y, float* r,
-                                 hipStream_t stream);
+// Input of the next projection before its RMSNorm factor: y = bf16(x *
+// gamma) in the panel layout (d columns, d % 32 == 0; gamma NULL = 1) and
+// r[row] = 1 / sqrt(mean x^2 + eps).  split: y is the split-bf16 form of
+// x * gamma with 2d columns, hi at column c and lo at column d + c.
+hipError_t launch_rows_rms_panel(const float* x, const float* gamma, int rows, int d, float eps, bool split, bf16_t* y,
+                                 float* r, hipStream_t stream);
 // r[row] from the d/16 partial sums of squares per row that EpiResidual
 // writes (summed in a fixed order); d % 16 == 0.
 hipError_t launch_rms_from_partials(const float* ss, int rows, int d, float eps, float* r, hipStream_t stream);
@@ -80,12 +82,12 @@ hipError_t launch_rms_from_partials(const float* ss, int rows, int d, float eps,
 // y[r, :] = x[rows_idx[r], :]  (fp32 rows)
 hipError_t launch_gather_rows(const float* x, const int32_t* rows_idx, int rows, int d, float* y,
                               hipStream_t stream);
-// The skinny products' un-normalised input: act[r, :] = bf16(x[src, :]) and
-// ss[r, c] = sum of x[src, 128 c .. 128 c + 128]^2, with src = rows_idx[r]
-// (rows_idx NULL: src = r); y (optional) receives a copy of the fp32 row.
-// d % 128 == 0.
-hipError_t launch_rows_act_ss(const float* x, const int32_t* rows_idx, int rows, int d, float* y, bf16_t* act,
-                              float* ss, hipStream_t stream);
+// The skinny products' input before its RMSNorm factor: act[r, :] =
+// bf16(x[src, :] * gamma) (gamma NULL = 1) and ss[r, c] = sum of x[src,
+// 128 c .. 128 c + 128]^2, with src = rows_idx[r] (rows_idx NULL: src = r);
+// y (optional) receives a copy of the fp32 row.  d % 128 == 0.
+hipError_t launch_rows_act_ss(const float* x, const int32_t* rows_idx, const float* gamma, int rows, int d, float* y,
+                              bf16_t* act, float* ss, hipStream_t stream);
 
 // Causal GQA flash attention for prompt tokens (bf16, MFMA): q [T, hq, dh],
 // K/V from one cache slot, o [T, hq * dh] in the panel layout (panel_off with
@@ -95,6 +97,15 @@ hipError_t launch_rows_act_ss(const float* x, const int32_t* rows_idx, int rows,
 hipError_t launch_attn_prefill_bf16(const bf16_t* q, CacheSlot<bf16_t> cache, const int32_t* cu_seqlens,
                                     const int32_t* ctx_lens, const int32_t* block_tables, int max_blocks, int batch,
                                     int max_new, int hq, bf16_t* o, hipStream_t stream);
+
+// The same attention in split-bf16 form: q / q_lo, the cache slot's K/V and
+// their low parts in `lo` (same geometry) are the two parts of each
+// operand; o gets 2 hq * dh columns, the output's high parts at column c and
+// low parts at hq * dh + c.
+hipError_t launch_attn_prefill_split(const bf16_t* q, const bf16_t* q_lo, CacheSlot<bf16_t> cache,
+                                     CacheSlot<bf16_t> lo, const int32_t* cu_seqlens, const int32_t* ctx_lens,
+                                     const int32_t* block_tables, int max_blocks, int batch, int max_new, int hq,
+                                     bf16_t* o, hipStream_t stream);
 
 // The same attention with K/V from a per-token FP8 cache slot.
 hipError_t launch_attn_prefill_fp8(const bf16_t* q, Fp8Slot cache, const int32_t* cu_seqlens, const int32_t* ctx_lens,
