@@ -226,6 +226,25 @@ typedef struct {
  * of the two ctx arrays given. */
 skv_status skv_step(skv_model* m, skv_kv_cache* c, const skv_step_batch* batch, float* logits, void* stream);
 
+/* For callers that cannot allocate device memory during a call (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): skv_step over a batch of at most 32 new tokens (decode steps,
+ * short chunks) on a bf16 model with a bf16 cache, with every scratch
+ * buffer of the call (residual rows, bf16 rows, split-K and attention
+ * partials, per-token metadata) taken from a static device array of
+ * 64 MiB that the library holds on each device for the life of the
+ * process, instead of the model's workspace.  Same arguments, results,
+ * asynchrony and ownership as skv_step; it calls no allocator.  The array
+ * is shared by every call on a device and keeps the last call's contents:
+ * calls that overlap on one device (different streams, or different
+ * threads) race on it and must be serialised by the caller.  Errors:
+ * skv_step's, plus INVALID_ARG for more than 32 new tokens or a call whose
+ * scratch (which grows with rows x q heads x the longest context) exceeds
+ * 64 MiB, or no model created on the current device; UNSUPPORTED for an
+ * fp32 model or an FP8 cache. */
+skv_status skv_step_noalloc(skv_model* m, skv_kv_cache* c, const skv_step_batch* batch, float* logits,
+                            void* stream);
+
 /* Closed-form FLOPs of a prefill over prompts of the given lengths (host
  * array).  full = the unmodified model (all layers for every token, LM head
  * for the last token); swiftkv = layers 1..l for every token, one K/V

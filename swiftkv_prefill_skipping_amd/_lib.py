@@ -50,7 +50,7 @@ class skv_step_batch(Structure):
 
 EXPORTED = ["skv_model_create", "skv_model_load_globals", "skv_model_load_layer", "skv_model_destroy",
             "skv_kv_cache_create", "skv_kv_cache_destroy", "skv_num_kv_slots", "skv_kv_cache_view", "skv_kv_cache_scales", "skv_prefill",
-            "skv_step",
+            "skv_step", "skv_step_noalloc",
             "skv_flops", "skv_profile_enable", "skv_profile_read", "skv_mfma_probe", "skv_last_error"]
 
 _lib = None
@@ -84,6 +84,7 @@ def lib():
         L.skv_kv_cache_scales.argtypes = [vp, c_int32, POINTER(skv_tensor_view), POINTER(skv_tensor_view)]
         L.skv_prefill.argtypes = [vp, vp, POINTER(skv_batch), vp, vp]
         L.skv_step.argtypes = [vp, vp, POINTER(skv_step_batch), vp, vp]
+        L.skv_step_noalloc.argtypes = [vp, vp, POINTER(skv_step_batch), vp, vp]
         L.skv_flops.argtypes = [POINTER(skv_model_config), vp, c_int32, POINTER(c_double), POINTER(c_double)]
         L.skv_profile_enable.argtypes = [vp, c_int32, c_int32]
         L.skv_profile_read.argtypes = [vp, POINTER(c_double), POINTER(c_int64), POINTER(c_double), POINTER(c_double)]
@@ -170,6 +171,10 @@ def skv_prefill(model: int, cache: int, batch: skv_batch, logits_ptr: int, strea
 
 def skv_step(model: int, cache: int, batch: skv_step_batch, logits_ptr: int, stream: int = 0) -> None:
     check(lib().skv_step(model, cache, ctypes.byref(batch), logits_ptr, stream))
+
+
+def skv_step_noalloc(model: int, cache: int, batch: skv_step_batch, logits_ptr: int, stream: int = 0) -> None:
+    check(lib().skv_step_noalloc(model, cache, ctypes.byref(batch), logits_ptr, stream))
 
 
 def skv_flops(cfg: skv_model_config, seqlens) -> tuple:

@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -36,6 +37,46 @@ size_t round_up(size_t a, size_t b) { return (a + b - 1) / b * b; }
 
 }  // namespace
 
+// Scratch of skv_step_noalloc: every buffer a row-path call writes besides
+// its inputs and outputs (residual rows, bf16 rows, split-K and attention
+// partials, per-token metadata) is carved out of this array.  Each device
+// holds its own copy for the life of the process.  Host code never passes
+// `scratch` itself to a kernel: it uses the device address that
+// hipGetSymbolAddress returned on that device (noalloc_scratch below).
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Look up (once per device, with that device current) the device address of
+// this device's `scratch`.  Called by skv_model_create.
+skv_status noalloc_scratch_init() {
+  int dev = 0;
+  SKV_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return fail(SKV_ERR_UNSUPPORTED, "device index beyond the scratch table");
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    SKV_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p) return fail(SKV_ERR_HIP, "hipGetSymbolAddress returned NULL for the scratch array");
+    g_scratch_ptr[dev] = p;
+  }
+  return SKV_OK;
+}
+
+// The current device's scratch address (NULL if no model was created on it).
+void* noalloc_scratch() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
 
 // Weights of layers 1..l feed the prompt-token GEMMs and are kept in the
 // panel layout with 256-row panels; those of skipped layers (and the LM
@@ -257,6 +298,7 @@ skv_status skv_model_create(const skv_model_config* cfg, skv_model** out) {
   if (!out) return fail(SKV_ERR_INVALID_ARG, "out is NULL");
   *out = nullptr;
   SKV_TRY(validate_config(cfg));
+  SKV_TRY(noalloc_scratch_init());
   skv_model* m = new skv_model();
   m->cfg = *cfg;
   const auto& c = m->cfg;
@@ -692,7 +734,7 @@ skv_status skv_mfma_probe(int32_t random_operands, int32_t iters, void* stream, 
 namespace {
 
 // Scratch of one call: the buffers the row path and the last-token path
-// write (the model's own workspace).
+// write (the model's own workspace, or a caller-independent static array).
 struct Work {
   float* x = nullptr;  // fp32 residual stream of the new tokens [T, d]
   float* y = nullptr;  // last tokens' residual stream [B, d]
@@ -1022,7 +1064,7 @@ skv_status run_step(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, const S
 
 namespace {
 
-// Shared argument checks of skv_prefill / skv_step;
+// Shared argument checks of skv_prefill / skv_step / skv_step_noalloc;
 // ctx_host NULL = no cached positions.  Fills si on success.
 skv_status check_batch(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, const int32_t* ctx_host,
                        const int32_t* ctx_dev, float* logits, StepInfo& si) {
@@ -1091,4 +1133,58 @@ extern "C" skv_status skv_step(skv_model* m, skv_kv_cache* kc, const skv_step_ba
   if (!sb->ctx_lens_host != !sb->ctx_lens)
     return fail(SKV_ERR_INVALID_ARG, "ctx_lens_host and ctx_lens must both be set or both be NULL");
   return check_and_run(m, kc, &sb->tokens, sb->ctx_lens_host, sb->ctx_lens, logits, stream);
+}
+
+extern "C" skv_status skv_step_noalloc(skv_model* m, skv_kv_cache* kc, const skv_step_batch* sb, float* logits,
+                                      void* stream) {
+  if (!sb) return fail(SKV_ERR_INVALID_ARG, "NULL argument");
+  if (!sb->ctx_lens_host != !sb->ctx_lens)
+    return fail(SKV_ERR_INVALID_ARG, "ctx_lens_host and ctx_lens must both be set or both be NULL");
+  StepInfo si;
+  SKV_TRY(check_batch(m, kc, &sb->tokens, sb->ctx_lens_host, sb->ctx_lens, logits, si));
+  if (!m->bf16) return fail(SKV_ERR_UNSUPPORTED, "skv_step_noalloc needs a bf16 model");
+  if (kc->fp8) return fail(SKV_ERR_UNSUPPORTED, "skv_step_noalloc does not take an FP8 cache");
+  const skv_batch* bt = &sb->tokens;
+  if (bt->total_tokens > kRowPathMax)
+    return fail(SKV_ERR_INVALID_ARG, "skv_step_noalloc takes at most " + std::to_string(kRowPathMax) +
+                                         " new tokens per call");
+  char* base = (char*)noalloc_scratch();
+  if (!base) return fail(SKV_ERR_INVALID_ARG, "no model was created on the current device");
+  const auto& c = m->cfg;
+  const size_t T = bt->total_tokens, B = bt->batch, RY = std::max(T, B), d = c.d_model, dq = m->dq, dkv = m->dkv,
+               f = c.ffn_dim, V = c.vocab;
+  int64_t pe = 0;
+  for (const auto& nk : {std::make_pair(dq + 2 * dkv, d), std::make_pair(dq, d), std::make_pair(d, dq),
+                         std::make_pair(2 * f, d), std::make_pair(d, f), std::make_pair(V, d),
+                         std::make_pair((size_t)std::max(m->G, 1) * 2 * dkv, d)})
+    pe = std::max(pe, skinny_partial_elems((int)nk.first, (int)nk.second));
+  const int64_t ae = attn_rows_ws_elems((int)RY, si.max_total, c.n_q_heads, c.head_dim, true);
+  // carve 256-byte aligned regions
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = round_up(off + std::max(bytes, (size_t)1), 256);
+    return base + o;
+  };
+  Work w;
+  w.x = (float*)take(T * d * 4);
+  w.y = (float*)take(B * d * 4);
+  w.ya = take(RY * d * 2);
+  w.yq = take(RY * dq * 2);
+  w.yo = take(RY * dq * 2);
+  w.yh = take(RY * f * 2);
+  w.rss = (float*)take(RY * (d / 128) * 4);
+  w.partial = (float*)take((size_t)pe * 4);
+  w.partial_elems = pe;
+  w.attn_ws = (float*)take((size_t)ae * 4);
+  w.pos = (int32_t*)take(T * 4);
+  w.slot = (int32_t*)take(T * 4);
+  w.seq = (int32_t*)take(T * 4);
+  w.last_pos = (int32_t*)take(B * 4);
+  w.last_row = (int32_t*)take(B * 4);
+  w.profile = false;
+  if (off > kNoAllocScratchBytes)
+    return fail(SKV_ERR_INVALID_ARG, "skv_step_noalloc needs " + std::to_string(off) + " bytes of scratch, more than its " +
+                                         std::to_string(kNoAllocScratchBytes) + " (fewer rows or shorter contexts)");
+  return run_step<bf16_t>(m, kc, bt, si, logits, (hipStream_t)stream, w);
 }
