@@ -65,13 +65,16 @@ def log(*a):
 def cpu_baseline(workload, batch, cached, n_prompts=3):
     """Time the oracle on the host cores over the batch's three shortest prompts (10-15 s of work at the 8B shape)."""
     from threadpoolctl import threadpool_info
+    import skv_inputs as si
     from oracle import swiftkv_oracle as O
-    from tests.helpers import dims_of, oracle_weights
     sel = [int(b) for b in np.argsort(batch.lengths, kind="stable")[:n_prompts]]
-    W = oracle_weights(workload, cached)
+    s = workload.shape
+    dims = O.Dims(s.n_layers, s.d_model, s.n_q_heads, s.n_kv_heads, s.head_dim, s.ffn_dim, s.vocab, s.rope_theta,
+                  s.rms_eps)
+    gw = si.global_weights(s, workload.dtype)
+    W = O.LazyWeights(si.as_f32(gw["embed"]), si.as_f32(gw["final_norm"]), si.as_f32(gw["lm_head"]), cached.make)
     t0 = time.perf_counter()
-    O.swiftkv_prefill(dims_of(workload.shape), W, [batch.tokens[b] for b in sel], workload.swiftkv_l,
-                      workload.acrosskv_g)
+    O.swiftkv_prefill(dims, W, [batch.tokens[b] for b in sel], workload.swiftkv_l, workload.acrosskv_g)
     dt = time.perf_counter() - t0
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     n = int(sum(int(batch.lengths[b]) for b in sel))
@@ -237,13 +240,12 @@ def main():
         return
     import skv_inputs as si
     from swiftkv_prefill_skipping_amd import _lib as L, runner
-    from tests.helpers import CachedLayers
 
     w = si.WORKLOADS[args.workload]
     batch = si.make_batch(w)
     T, B = batch.total_tokens, len(batch.lengths)
     log(f"[bench] workload {w.name}: {B} prompts, {T} tokens, lengths {list(batch.lengths)}")
-    cached = CachedLayers() if not args.no_cpu_baseline else None
+    cached = si.CachedLayers() if not args.no_cpu_baseline else None
     t0 = time.time()
     extra = 4  # blocks per prompt beyond its prefill, for the decode measurement
     model = runner.load_seeded_model(w, T, B, batch.max_seqlen + extra * batch.block_size,

@@ -246,6 +246,20 @@ def as_f32(a: np.ndarray) -> np.ndarray:
     return bf16_to_f32(a) if a.dtype == np.uint16 else np.asarray(a, dtype=np.float32)
 
 
+class CachedLayers:
+    """Keeps each layer's generated arrays (bf16 bits or fp32) as a loader hands them over, and widens them to fp32
+    on request, so a second consumer of the same seeded weights need not generate them again."""
+
+    def __init__(self):
+        self.layers = {}
+
+    def hook(self, i, w):
+        self.layers[i] = w
+
+    def make(self, i):
+        return {k: as_f32(v) for k, v in self.layers[i].items()}
+
+
 @dataclass
 class Batch:
     lengths: np.ndarray            # int64 [B]

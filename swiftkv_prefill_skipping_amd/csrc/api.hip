@@ -87,6 +87,10 @@ struct LayerDev {
   float* ffn_norm = nullptr;
   void* wqkv = nullptr;  // unskipped: [dq + 2 dkv, d]; skipped: [dq, d]
   void* wo = nullptr;    // [d, dq]
+  // layer 1 of a bf16 model with a split first layer: [W | W] with twice the
+  // columns (panel layout), the B operand of the split-bf16 QKV and O GEMMs
+  void* wqkv2 = nullptr;  // [dq + 2 dkv, 2 d]
+  void* wo2 = nullptr;    // [d, 2 dq]
   void* wgu = nullptr;   // [2f, d], gate/up interleaved in blocks of P_mlp rows
   void* wdown = nullptr; // [d, f]
   int panel_rows = 0;    // 0: row-major; else the panel height of the layout
@@ -102,6 +106,13 @@ struct skv_model {
   bool bf16;
   size_t esz;
   int G;       // AcrossKV groups of skipped layers
+  // Prompt tokens run layer 1 in split-bf16 form (bf16 model, l >= 1): the
+  // QKV GEMM takes the hi and lo parts of its input (K doubled against
+  // [W | W]); with a bf16 cache the attention also computes with both parts
+  // of q, K and V, and the O GEMM with both parts of its input.  Layer 1
+  // writes the whole residual stream (the embeddings are small), so its
+  // rounding dominates what deeper layers inherit.
+  bool split1 = false;
   int p_mlp;   // gate/up interleave distance
   int dq, dkv;
   std::vector<void*> allocs;
@@ -122,6 +133,7 @@ struct skv_model {
   float* x = nullptr;
   void* act = nullptr;
   void* qbuf = nullptr;
+  void* qlo = nullptr;  // split layer 1: low parts of q [T, dq]
   void* obuf = nullptr;
   void* hbuf = nullptr;
   int32_t* pos = nullptr;
@@ -171,6 +183,10 @@ struct skv_kv_cache {
   bool fp8 = false;
   float* ks = nullptr;  // FP8: per-token scales [n_slots][num_blocks * block_size]
   float* vs = nullptr;
+  // split first layer: low parts of layer 1's K and V in the slot layout
+  // (written with the slot, read by the split prompt attention)
+  void* klo = nullptr;
+  void* vlo = nullptr;
 };
 
 namespace {
@@ -343,15 +359,25 @@ skv_status skv_model_create(const skv_model_config* cfg, skv_model** out) {
     ALLOC(L.wdown, round_up(d, r) * f * E);
   }
   if (m->G > 0) ALLOC(m->wkv_skip, round_up((size_t)m->G * 2 * dkv, R) * d * E);
+  m->split1 = m->bf16 && c.swiftkv_l >= 1;
   m->staging_bytes = std::max({2 * f * d, (dq + 2 * dkv) * d, d * dq, d * f}) * E;
+  // split layer 1: W row-major plus [W | W] row-major side by side
+  if (m->split1) m->staging_bytes = std::max(m->staging_bytes, std::max(3 * (dq + 2 * dkv) * d, 3 * d * dq) * E);
   ALLOC(m->staging, m->staging_bytes);
   ALLOC(m->gamma_stage, d * E);
 
   const size_t Tp = round_up(T, R);  // token rows of the panel-layout activations
   ALLOC(m->x, T * d * 4);
-  ALLOC(m->act, Tp * d * E);
+  const size_t acols = m->split1 ? 2 * d : d, ocols = m->split1 ? 2 * dq : dq;
+  ALLOC(m->act, Tp * acols * E);
   ALLOC(m->qbuf, T * dq * E);
-  ALLOC(m->obuf, Tp * dq * E);
+  if (m->split1) {
+    ALLOC(m->qlo, T * dq * E);
+    LayerDev& L1 = m->layers[0];
+    ALLOC(L1.wqkv2, round_up(dq + 2 * dkv, kPanelRows) * 2 * d * E);
+    ALLOC(L1.wo2, round_up(d, kPanelRows) * 2 * dq * E);
+  }
+  ALLOC(m->obuf, Tp * ocols * E);
   ALLOC(m->hbuf, Tp * f * E);
   ALLOC(m->pos, T * 4);
   ALLOC(m->slot, T * 4);
@@ -402,7 +428,7 @@ skv_status skv_model_create(const skv_model_config* cfg, skv_model** out) {
 
   // the panel padding rows of the activations are read (never stored) by
   // the GEMMs: start them at zero so they hold finite values
-  if (hipMemset(m->act, 0, Tp * d * E) != hipSuccess || hipMemset(m->obuf, 0, Tp * dq * E) != hipSuccess ||
+  if (hipMemset(m->act, 0, Tp * acols * E) != hipSuccess || hipMemset(m->obuf, 0, Tp * ocols * E) != hipSuccess ||
       hipMemset(m->hbuf, 0, Tp * f * E) != hipSuccess || hipDeviceSynchronize() != hipSuccess)
     return bail(fail(SKV_ERR_HIP, "clearing the activation buffers failed"));
 
@@ -483,6 +509,21 @@ static skv_status load_matrix(skv_model* m, void* dst, const void* src, size_t r
   return SKV_OK;
 }
 
+// The panel layout of [W | W] (rows x 2K, the B operand of a split-bf16
+// GEMM) from the row-major W (rows x K) at the start of the staging buffer;
+// the doubled rows are built in the staging buffer after W.
+static skv_status load_doubled(skv_model* m, void* dst, size_t rows, size_t K) {
+  const size_t E = m->esz;
+  if (3 * rows * K * E > m->staging_bytes) return fail(SKV_ERR_UNSUPPORTED, "staging buffer too small to double W");
+  char* src = (char*)m->staging;
+  char* dbl = src + rows * K * E;
+  SKV_HIP(hipMemcpy2D(dbl, 2 * K * E, src, K * E, K * E, rows, hipMemcpyDeviceToDevice));
+  SKV_HIP(hipMemcpy2D(dbl + K * E, 2 * K * E, src, K * E, K * E, rows, hipMemcpyDeviceToDevice));
+  SKV_HIP(launch_to_panels((const bf16_t*)dbl, (int)rows, (int)(2 * K), kPanelRows, (bf16_t*)dst, 0));
+  SKV_HIP(hipDeviceSynchronize());
+  return SKV_OK;
+}
+
 skv_status skv_model_load_globals(skv_model* m, const void* embed, const void* final_norm, const void* lm_head) {
   if (!m) return fail(SKV_ERR_INVALID_ARG, "model is NULL");
   const size_t d = m->cfg.d_model, V = m->cfg.vocab;
@@ -513,6 +554,7 @@ skv_status skv_model_load_layer(skv_model* m, int32_t layer, const skv_layer_wei
       SKV_HIP(launch_to_panels((const bf16_t*)m->staging, (int)(dq + 2 * dkv), (int)d, L.panel_rows,
                                (bf16_t*)L.wqkv, 0));
       SKV_HIP(hipDeviceSynchronize());
+      if (layer == 1 && m->split1) SKV_TRY(load_doubled(m, L.wqkv2, dq + 2 * dkv, d));
     }
   } else {
     SKV_TRY(load_matrix(m, L.wqkv, w->wq, dq, d, L.panel_rows, "wq"));
@@ -538,6 +580,10 @@ skv_status skv_model_load_layer(skv_model* m, int32_t layer, const skv_layer_wei
     }
   }
   SKV_TRY(load_matrix(m, L.wo, w->wo, d, dq, L.panel_rows, "wo"));
+  if (layer == 1 && m->split1) {
+    SKV_TRY(copy_in(m->staging, w->wo, d * dq * E, "wo"));
+    SKV_TRY(load_doubled(m, L.wo2, d, dq));
+  }
   SKV_TRY(load_matrix(m, L.wdown, w->w_down, d, f, L.panel_rows, "w_down"));
   // gate/up: interleave rows in blocks of P_mlp into L.wgu (row-major), then
   // (bf16) into the layer's panel layout through the staging buffer
@@ -597,10 +643,24 @@ skv_status skv_kv_cache_create(const skv_model* m, int32_t num_blocks, int32_t b
     if (vs) (void)hipFree(vs);
     return fail(SKV_ERR_HIP, "KV cache clear failed");
   }
+  void *klo = nullptr, *vlo = nullptr;
+  if (m->split1 && !fp8) {
+    const size_t lb = (size_t)slot_elems * m->esz;
+    if (hipMalloc(&klo, lb) != hipSuccess || hipMalloc(&vlo, lb) != hipSuccess ||
+        hipMemset(klo, 0, lb) != hipSuccess || hipMemset(vlo, 0, lb) != hipSuccess ||
+        hipDeviceSynchronize() != hipSuccess) {
+      (void)hipGetLastError();
+      for (void* p : {k, v, klo, vlo})
+        if (p) (void)hipFree(p);
+      return fail(SKV_ERR_OOM, "KV cache low-part allocation failed");
+    }
+  }
   skv_kv_cache* kc = new skv_kv_cache{m, num_blocks, block_size, n_slots, k, v, slot_elems};
   kc->fp8 = fp8;
   kc->ks = ks;
   kc->vs = vs;
+  kc->klo = klo;
+  kc->vlo = vlo;
   *out = kc;
   return SKV_OK;
 }
@@ -611,6 +671,8 @@ void skv_kv_cache_destroy(skv_kv_cache* c) {
   (void)hipFree(c->v);
   if (c->ks) (void)hipFree(c->ks);
   if (c->vs) (void)hipFree(c->vs);
+  if (c->klo) (void)hipFree(c->klo);
+  if (c->vlo) (void)hipFree(c->vlo);
   delete c;
 }
 
@@ -855,6 +917,10 @@ skv_status run_step(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, const S
     const CacheSlot<T> cs = slot_of(cache_slot);
     const int nq = with_kv ? dq + 2 * dkv : dq;
     EpiQKV<T> eq{yq, kv8 ? stage : cs, row_pos, with_kv ? kv_slot : nullptr, m->rope_cos, m->rope_sin, dq, dkv, dh, P};
+    if (with_kv && cache_slot == 0 && kc->klo) {  // keep layer 1's low parts for the split prompt attention
+      eq.k_lo = (T*)kc->klo;
+      eq.v_lo = (T*)kc->vlo;
+    }
     EpiSwiGLU<T> esw{yh, f, m->p_mlp};
     // bf16: ya holds bf16(x * gain) and rss the partial sums of squares of
     // x on entry and on exit; each normalised product scales by 1 / rms(x)
@@ -917,8 +983,8 @@ skv_status run_step(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, const S
   };
   if (panel_path && (l > 0 || m->G > 0)) {
     Prof p(pm, SKV_K_RMSNORM, s, 0, (double)T_ * d * (4 + E));
-    SKV_HIP(launch_rows_rms_panel(w.x, l > 0 ? gain_before(1) : nullptr, T_, d, c.rms_eps, false, (bf16_t*)act, m->rrow,
-                                  s));
+    SKV_HIP(launch_rows_rms_panel(w.x, l > 0 ? gain_before(1) : nullptr, T_, d, c.rms_eps, m->split1, (bf16_t*)act,
+                                  m->rrow, s));
   }
   const float* rrow = panel_path ? m->rrow : nullptr;
 
@@ -934,12 +1000,23 @@ skv_status run_step(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, const S
       Prof p(pm, SKV_K_RMSNORM, s, 0, (double)T_ * d * (4 + E));
       SKV_HIP(launch_rmsnorm<T>(w.x, nullptr, Ly.attn_norm, T_, d, c.rms_eps, act, s));
     }
+    // split-bf16 layer 1: the QKV GEMM contracts over both parts of its
+    // input (K doubled); with a bf16 cache the attention computes with both
+    // parts and the O GEMM contracts over both parts of the attention output
+    const bool split = kBf16 && i == 1 && m->split1;
+    const bool split_attn = split && kc->klo != nullptr;
     {
       const int N = dq + 2 * dkv;
       EpiQKV<T> epi{qbuf, kv8 ? stage : cs, w.pos, kv_slot, m->rope_cos, m->rope_sin, dq, dkv, dh, P, rrow};
+      if (split_attn) {
+        epi.q_lo = (T*)m->qlo;
+        epi.k_lo = (T*)kc->klo;
+        epi.v_lo = (T*)kc->vlo;
+      }
       Prof p(pm, SKV_K_GEMM_QKV, s, 2.0 * T_ * N * d, gemm_bytes(T_, N, d, E, E));
       if constexpr (kBf16)
-        SKV_HIP(launch_gemm_bf16((const bf16_t*)act, (const bf16_t*)Ly.wqkv, T_, N, d, epi, m->gemm_ws, m->gemm_ws_elems, s));
+        SKV_HIP(launch_gemm_bf16((const bf16_t*)act, (const bf16_t*)(split ? Ly.wqkv2 : Ly.wqkv), T_, N,
+                                 split ? 2 * d : d, epi, m->gemm_ws, m->gemm_ws_elems, s));
       else if (P == 16)
         SKV_HIP((launch_gemm_f32<16>((const float*)act, d, (const float*)Ly.wqkv, d, T_, N, d, epi, s)));
       else if (P == 32)
@@ -955,9 +1032,16 @@ skv_status run_step(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, const S
           SKV_HIP(launch_attn_prefill_fp8((const bf16_t*)qbuf, slot8_of(i - 1), bt->cu_seqlens, si.ctx_dev,
                                           bt->block_tables, bt->max_blocks_per_seq, B, si.max_new, hq, (bf16_t*)obuf,
                                           s));
-      } else if constexpr (kBf16)
-        SKV_HIP(launch_attn_prefill_bf16((const bf16_t*)qbuf, cs, bt->cu_seqlens, si.ctx_dev, bt->block_tables,
-                                         bt->max_blocks_per_seq, B, si.max_new, hq, (bf16_t*)obuf, s));
+      } else if constexpr (kBf16) {
+        if (split_attn)
+          SKV_HIP(launch_attn_prefill_split((const bf16_t*)qbuf, (const bf16_t*)m->qlo, cs,
+                                            CacheSlot<bf16_t>{(bf16_t*)kc->klo, (bf16_t*)kc->vlo, c.n_kv_heads, dh},
+                                            bt->cu_seqlens, si.ctx_dev, bt->block_tables, bt->max_blocks_per_seq, B,
+                                            si.max_new, hq, (bf16_t*)obuf, s));
+        else
+          SKV_HIP(launch_attn_prefill_bf16((const bf16_t*)qbuf, cs, bt->cu_seqlens, si.ctx_dev, bt->block_tables,
+                                           bt->max_blocks_per_seq, B, si.max_new, hq, (bf16_t*)obuf, s));
+      }
       else
         SKV_HIP(launch_attn_rows<T>(qbuf, cs, w.seq, w.pos, bt->block_tables, bt->max_blocks_per_seq, T_,
                                     si.max_total, hq, w.attn_ws, obuf, s));
@@ -967,7 +1051,8 @@ skv_status run_step(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, const S
                       kBf16 ? Ly.ffn_norm : nullptr};
       Prof p(pm, SKV_K_GEMM_O, s, 2.0 * T_ * d * dq, gemm_bytes(T_, d, dq, E, kBf16 ? 8 + 2 + 0.25 : 8));
       if constexpr (kBf16)
-        SKV_HIP(launch_gemm_bf16((const bf16_t*)obuf, (const bf16_t*)Ly.wo, T_, d, dq, epi, m->gemm_ws, m->gemm_ws_elems, s));
+        SKV_HIP(launch_gemm_bf16((const bf16_t*)obuf, (const bf16_t*)(split_attn ? Ly.wo2 : Ly.wo), T_, d,
+                                 split_attn ? 2 * dq : dq, epi, m->gemm_ws, m->gemm_ws_elems, s));
       else
         SKV_HIP((launch_gemm_f32<16>((const float*)obuf, dq, (const float*)Ly.wo, dq, T_, d, dq, epi, s)));
     }

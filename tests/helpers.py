@@ -1,6 +1,8 @@
 """Shared helpers of the tests: seeded inputs -> oracle inputs, error metrics."""
 from __future__ import annotations
 
+import json
+import os
 import sys
 
 import numpy as np
@@ -14,17 +16,7 @@ def dims_of(shape: si.ModelShape) -> O.Dims:
                   shape.vocab, shape.rope_theta, shape.rms_eps)
 
 
-class CachedLayers:
-    """Layer weights kept as generated (bf16 bits or fp32) and widened to fp32 on request."""
-
-    def __init__(self):
-        self.layers = {}
-
-    def hook(self, i, w):
-        self.layers[i] = w
-
-    def make(self, i):
-        return {k: si.as_f32(v) for k, v in self.layers[i].items()}
+CachedLayers = si.CachedLayers
 
 
 def oracle_weights(w: si.Workload, cached: CachedLayers = None) -> O.WeightSource:
@@ -59,3 +51,25 @@ def say(*a):
             print(*a, file=sys.stderr, flush=True)
     else:
         print(*a, file=sys.stderr, flush=True)
+
+
+FULLSIZE_DIR = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "fullsize")
+
+
+def fullsize_fixture(name: str):
+    """The stored oracle results of one full-size workload (tests/golden/make_fullsize_fixtures.py), or None.
+
+    Returns a dict with: meta; prompts / logits (float64 from the stored float16)
+    / logits_floor; kv_prompts / kv_pos / kv [Q, slots, 2, S, hkv, dh] /
+    kv_floor [Q, slots, 2, 2]; full_prompts / full_npos / full_floor
+    [R, slots, 2, 2].  Floors are (max-relative, Frobenius) of the oracle's
+    bf16-storage evaluation against its plain one over the same elements."""
+    path = os.path.join(FULLSIZE_DIR, f"{name}.npz")
+    if not os.path.exists(path):
+        return None
+    z = np.load(path, allow_pickle=False)
+    out = {k: z[k] for k in z.files if k != "meta"}
+    out["meta"] = json.loads(str(z["meta"]))
+    out["logits"] = out["logits"].astype(np.float64)
+    out["kv"] = out["kv"].astype(np.float64)
+    return out

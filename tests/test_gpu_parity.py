@@ -64,62 +64,92 @@ def frob_rel(got, ref) -> float:
     return float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300))
 
 
-# bf16-limited regime: a tensor whose bf16-storage evaluation itself differs
-# from the fp32 evaluation by more than the bar passes if the GPU is no worse
-# than that (1.5x on the max-normalised error, 1.1x + 1e-3 on the norm ratio)
-BF16_MAX_FACTOR, BF16_FROB_FACTOR, BF16_FROB_SLACK = 1.5, 1.1, 1e-3
+# bf16-limited regime.  On the deep layers of the random-init 8B / 70B shapes,
+# storing activations in bf16 alone moves the outputs further than the bar:
+# the oracle evaluated with bf16 storage (its store= points) differs from
+# the plain evaluation by more than 2e-2 there.  A tensor whose own floor
+# (that difference, over the same elements, from a CPU evaluation) is at
+# least the bar passes if the GPU is no further than 1.2x the floor on the
+# max-normalised error and 1.1x + 1e-3 on the Frobenius ratio.  A tensor
+# whose floor is below the bar must meet the bar.
+BF16_MAX_FACTOR, BF16_FROB_FACTOR, BF16_FROB_SLACK = 1.2, 1.1, 1e-3
 
 
-def compare(w, batch, logits, cache, ores, prompts, tol=None, label="", bf16_ref=None, npos=None):
-    """Compare every KV slot and the logits of the given prompts; print the whole error profile, then assert.
+def judge(e, fg, floor, tol):
+    """'strict' (e < tol), 'limited' (floor >= tol and within the factors of it) or 'fail'.
 
-    Per tensor: e = max|gpu - oracle| / max|oracle| must stay below tol.
-    With ``bf16_ref`` (the oracle evaluated with bf16 storage), a tensor
-    with e >= tol still passes if e <= 1.5 e_bf16 and
-    frob(gpu) <= 1.1 frob(bf16) + 1e-3, e_bf16 / frob(bf16) being the same
-    measures of the bf16-storage evaluation against the plain one.
-    With ``npos`` the oracle ran on the first npos tokens of each prompt:
-    only KV positions < npos are compared (causality makes them the same
-    function) and the logits are not.
-    """
-    tol = tol if tol is not None else TOL[w.dtype]
-    worst, fails, lines, limited = 0.0, [], [], 0
-    lg = logits.float().cpu().numpy()
+    e / fg: the GPU's max-relative error and Frobenius ratio against the
+    plain oracle; floor: (max-relative, Frobenius) of the bf16-storage
+    evaluation against the plain one over the same elements, or None."""
+    if e < tol:
+        return "strict"
+    if floor is not None:
+        er, fr = float(floor[0]), float(floor[1])
+        if er >= tol and e <= BF16_MAX_FACTOR * er and fg <= BF16_FROB_FACTOR * fr + BF16_FROB_SLACK:
+            return "limited"
+    return "fail"
 
-    def judge(g, o, r, name):
-        nonlocal worst, limited
-        e = max_rel(g, o)
-        worst = max(worst, e)
-        if e < tol:
+
+class Tally:
+    """Per-tensor verdicts of one comparison, printed as a profile before the assertion."""
+
+    def __init__(self, label, tol):
+        self.label, self.tol = label, tol
+        self.worst, self.fails, self.limited, self.ratio = 0.0, [], 0, 0.0
+
+    def check(self, got, ref, floor, name):
+        e, fg = max_rel(got, ref), frob_rel(got, ref)
+        self.worst = max(self.worst, e)
+        v = judge(e, fg, floor, self.tol)
+        if floor is not None and e >= self.tol:
+            self.ratio = max(self.ratio, e / max(float(floor[0]), 1e-30))
+        if v == "strict":
             return f"{e:.1e}"
-        if r is not None:
-            er, fg, fr = max_rel(r, o), frob_rel(g, o), frob_rel(r, o)
-            if e <= BF16_MAX_FACTOR * er and fg <= BF16_FROB_FACTOR * fr + BF16_FROB_SLACK:
-                limited += 1
-                return f"{e:.1e}(bf16 {er:.1e}, frob {fg:.1e}/{fr:.1e})"
-            fails.append(f"{name}: {e:.3e} (bf16-storage {er:.3e}; frob {fg:.3e} vs {fr:.3e})")
+        if v == "limited":
+            self.limited += 1
+            return f"{e:.1e}(floor {float(floor[0]):.1e})"
+        if floor is not None:
+            self.fails.append(f"{name}: {e:.3e} (floor {float(floor[0]):.3e}, frob {fg:.3e} vs {float(floor[1]):.3e})")
         else:
-            fails.append(f"{name}: {e:.3e}")
+            self.fails.append(f"{name}: {e:.3e}")
         return f"{e:.1e}!"
 
+    def finish(self, lines):
+        _say(f"[parity] {self.label}: worst max-rel error {self.worst:.3e} (bar {self.tol}; {self.limited} tensors in "
+             f"the bf16-limited regime, worst error / floor among them {self.ratio:.2f})")
+        for ln in lines:
+            _say(ln)
+        assert not self.fails, f"{self.label}: " + "; ".join(self.fails[:8]) + (" ..." if len(self.fails) > 8 else "")
+        return self.worst
+
+
+def compare(w, batch, logits, cache, ores, prompts, tol=None, label="", floors=None, npos=None):
+    """Compare every KV slot and the logits of the given prompts; print the whole error profile, then assert.
+
+    Per tensor: e = max|gpu - oracle| / max|oracle| must stay below tol,
+    except in the bf16-limited regime (see judge): ``floors`` maps
+    (prompt, slot, 0 or 1) for K / V and (prompt, "logits") to the
+    (max-relative, Frobenius) floor of that tensor.  With ``npos`` the oracle
+    ran on the first npos tokens of each prompt: only KV positions < npos are
+    compared (causality makes them the same function) and the logits are not.
+    """
+    tol = tol if tol is not None else TOL[w.dtype]
+    floors = floors or {}
+    tally = Tally(label, tol)
+    lines = []
+    lg = logits.float().cpu().numpy()
     for ob, b in enumerate(prompts):
         gkv = gpu_kv(cache, w, batch, b, npos)
         assert set(gkv) == set(ores.kv[ob]), "slot sets differ"
         row = []
         for s in sorted(gkv):
-            rk = bf16_ref.kv[ob][s] if bf16_ref is not None else (None, None)
-            ek = judge(gkv[s][0], ores.kv[ob][s][0], rk[0], f"prompt {b} slot {s} K")
-            ev = judge(gkv[s][1], ores.kv[ob][s][1], rk[1], f"prompt {b} slot {s} V")
+            ek = tally.check(gkv[s][0], ores.kv[ob][s][0], floors.get((b, s, 0)), f"prompt {b} slot {s} K")
+            ev = tally.check(gkv[s][1], ores.kv[ob][s][1], floors.get((b, s, 1)), f"prompt {b} slot {s} V")
             row.append(f"{s}:{ek}/{ev}")
-        el = "-" if npos is not None else judge(lg[b], ores.logits[ob], bf16_ref.logits[ob] if bf16_ref is not None
-                                                 else None, f"prompt {b} logits")
+        el = "-" if npos is not None else tally.check(lg[b], ores.logits[ob], floors.get((b, "logits")),
+                                                      f"prompt {b} logits")
         lines.append(f"  prompt {b}: logits {el}; slot K/V " + " ".join(row))
-    _say(f"[parity] {label}: worst max-rel error {worst:.3e} (bar {tol}; {limited} tensors in the bf16-limited "
-         f"regime)")
-    for ln in lines:
-        _say(ln)
-    assert not fails, f"{label}: " + "; ".join(fails[:8]) + (" ..." if len(fails) > 8 else "")
-    return worst
+    return tally.finish(lines)
 
 
 def oracle_for(w, batch, prompts, cached=None):
