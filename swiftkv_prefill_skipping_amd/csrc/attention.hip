@@ -694,9 +694,14 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const T* __restrict__ q,
 //    reduce-scatter over the four blocks with the permlane swaps leaves
 //    head b's sums in the lanes of block b.
 // Writes (max, sum, unnormalised o) per head and chunk like attn_rows_kernel.
+// F8: K/V come from the per-token FP8 cache c8; a lane's codes (32 of a key
+// row for the scores, 8 per key for P.V, half the bytes of the bf16 loads)
+// are decoded and multiplied by their token's scale into the same bf16
+// operands, so everything after the loads is shared.
 constexpr int DC_KEYS = 64;
+template <bool F8>
 __global__ __launch_bounds__(256) void attn_dec_kernel(const bf16_t* __restrict__ q, CacheSlot<bf16_t> cache,
-                                                       const int32_t* __restrict__ row_seq,
+                                                       Fp8Slot c8, const int32_t* __restrict__ row_seq,
                                                        const int32_t* __restrict__ row_pos,
                                                        const int32_t* __restrict__ bt, int max_blocks, int hq,
                                                        int nchunks, float scale, float* __restrict__ ws) {
@@ -733,12 +738,27 @@ __global__ __launch_bounds__(256) void attn_dec_kernel(const bf16_t* __restrict_
     // The bf16 pairs for v_dot2c_f32_bf16 are taken from bf16x8 vectors by
     // shufflevector: hipcc 7.2 lowers a bit_cast of a u32x4 element to bf16x2
     // feeding the dot2 builtin to element 0 of the vector every time.
-    bf16x8_t kv[4][4];
+    // bf16: K of the lane's four keys, issued first; F8: their codes and
+    // scales, decoded pass by pass in the score loop
+    bf16x8_t kv[F8 ? 1 : 4][4];
+    u32x4_t kc[F8 ? 4 : 1][2];
+    float ksc[F8 ? 4 : 1];
+    if constexpr (F8) {
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const bf16_t* kr = cache.k + kv_index(blk[p] * kBlockSize + kq, g, j * 32, hkv, DH);
+      for (int p = 0; p < 4; ++p) {
+        const int sl = blk[p] * kBlockSize + kq;
+        const uint8_t* kr = c8.k + kv_index(sl, g, j * 32, hkv, DH);
+        kc[p][0] = *reinterpret_cast<const u32x4_t*>(kr);
+        kc[p][1] = *reinterpret_cast<const u32x4_t*>(kr + 16);
+        ksc[p] = c8.ks[sl];
+      }
+    } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) kv[p][i] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(kr + i * 8));
+      for (int p = 0; p < 4; ++p) {
+        const bf16_t* kr = cache.k + kv_index(blk[p] * kBlockSize + kq, g, j * 32, hkv, DH);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) kv[p][i] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(kr + i * 8));
+      }
     }
     bf16x8_t qv[RW_HG][4];
 #pragma unroll
@@ -750,12 +770,31 @@ __global__ __launch_bounds__(256) void attn_dec_kernel(const bf16_t* __restrict_
     float sc[4][RW_HG];
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
+      bf16x8_t kp[4];
+      if constexpr (F8) {
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          float x[16];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) decode4_e4m3_hw(kc[p][h2][e], x + 4 * e);
+#pragma unroll
+          for (int i2 = 0; i2 < 2; ++i2) {
+            const float* y = x + 8 * i2;
+            const float s8 = ksc[p];
+            kp[2 * h2 + i2] = as_bf16x8(u32x4_t{pack_bf16x2(y[0] * s8, y[1] * s8), pack_bf16x2(y[2] * s8, y[3] * s8),
+                                                pack_bf16x2(y[4] * s8, y[5] * s8), pack_bf16x2(y[6] * s8, y[7] * s8)});
+          }
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) kp[i] = kv[p][i];
+      }
       float acc[RW_HG] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int hh = 0; hh < RW_HG; ++hh) {
-          const bf16x8_t kx = kv[p][i], qx = qv[hh][i];
+          const bf16x8_t kx = kp[i], qx = qv[hh][i];
           float a = acc[hh];
           a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(kx, kx, 0, 1), __builtin_shufflevector(qx, qx, 0, 1), a, false);
           a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(kx, kx, 2, 3), __builtin_shufflevector(qx, qx, 2, 3), a, false);
@@ -770,11 +809,24 @@ __global__ __launch_bounds__(256) void attn_dec_kernel(const bf16_t* __restrict_
         sc[p][hh] = p * 16 + kq < nk ? a * scale : -INFINITY;  // a select: garbage past the context never propagates
       }
     }
-    // V of the lane's 16 keys, in flight while the softmax runs
+    // V of the lane's 16 keys, in flight while the softmax runs (F8: codes
+    // and scales, decoded after the softmax)
     bf16x8_t vv[16];
+    u32x2_t vcode[F8 ? 16 : 1];
+    float vsc[F8 ? 16 : 1];
+    if constexpr (F8) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-      vv[i] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(cache.v + kv_index(vblk * kBlockSize + i, g, vc * 8, hkv, DH)));
+      for (int i = 0; i < 16; ++i) {
+        const int sl = vblk * kBlockSize + i;
+        vcode[i] = *reinterpret_cast<const u32x2_t*>(c8.v + kv_index(sl, g, vc * 8, hkv, DH));
+        vsc[i] = c8.vs[sl];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        vv[i] = as_bf16x8(
+            *reinterpret_cast<const u32x4_t*>(cache.v + kv_index(vblk * kBlockSize + i, g, vc * 8, hkv, DH)));
+    }
     // softmax statistics over the chunk, per head (lanes of a quad agree)
     float mh[RW_HG], lh[RW_HG];
     f32x4_t pe[4];
@@ -805,6 +857,17 @@ __global__ __launch_bounds__(256) void attn_dec_kernel(const bf16_t* __restrict_
     if (j == 0) {
 #pragma unroll
       for (int p = 0; p < 4; ++p) ps_s[wave][p * 16 + kq] = pe[p];
+    }
+    if constexpr (F8) {  // each key's 8 codes times its scale, as bf16 pairs
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float s8 = vsc[i];
+        float x[8];
+        decode4_e4m3_hw(vcode[i].x, x);
+        decode4_e4m3_hw(vcode[i].y, x + 4);
+        vv[i] = as_bf16x8(u32x4_t{pack_bf16x2(x[0] * s8, x[1] * s8), pack_bf16x2(x[2] * s8, x[3] * s8),
+                                  pack_bf16x2(x[4] * s8, x[5] * s8), pack_bf16x2(x[6] * s8, x[7] * s8)});
+      }
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's probabilities are in LDS
     // o[hh][8 vc .. + 8] over the 16 keys of block vb
@@ -957,11 +1020,11 @@ hipError_t attn_rows_impl(const T* q, CacheSlot<T> cache, Fp8Slot c8, const int3
                           hipStream_t stream) {
   if (rows <= 0) return hipSuccess;
   const float scale = 1.0f / sqrtf((float)cache.dh);
-  if constexpr (sizeof(T) == 2 && !F8) {
+  if constexpr (sizeof(T) == 2) {
     if (cache.dh == 128) {
       const int nch = (max_ctx + DC_KEYS - 1) / DC_KEYS;
-      hipLaunchKernelGGL(attn_dec_kernel, dim3(rows, cache.hkv, (nch + 3) / 4), dim3(256), 0, stream, q, cache,
-                         row_seq, row_pos, block_tables, max_blocks, hq, nch, scale, ws);
+      hipLaunchKernelGGL((attn_dec_kernel<F8>), dim3(rows, cache.hkv, (nch + 3) / 4), dim3(256), 0, stream, q,
+                         cache, c8, row_seq, row_pos, block_tables, max_blocks, hq, nch, scale, ws);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
       hipLaunchKernelGGL(attn_combine_kernel<T>, dim3(rows, hq), dim3(4 * RW_MAXDH), 0, stream, ws, hq, cache.dh, nch, o);

@@ -25,8 +25,8 @@ struct Fp8Slot {
   int dh;
 };
 
-// E4M3 code -> fp32 value (exact).  The NaN code is never produced by the
-// quantiser and decodes as 480.
+// E4M3 code -> fp32 value (exact), in vector ALU operations.  The NaN code
+// is never produced by the quantiser and decodes as 480.
 SKV_DEV float e4m3_to_f32(uint32_t c) {
   const uint32_t e = (c >> 3) & 15, m = c & 7;
   const float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
@@ -51,10 +51,27 @@ SKV_DEV uint32_t f32_to_e4m3(float y) {
   return s | ((uint32_t)(e + 7) << 3) | m;
 }
 
-// 16 codes (one 16-byte load, element order preserved) -> 16 floats.
+// Four codes packed in a dword (byte b = code b) -> four floats through
+// gfx950's hardware conversion (v_cvt_pk_f32_fp8: OCP E4M3, exact).
+SKV_DEV void decode4_e4m3_hw(uint32_t w, float* out) {
+  const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  out[0] = lo[0];
+  out[1] = lo[1];
+  out[2] = hi[0];
+  out[3] = hi[1];
+}
+
+// 16 codes (one 16-byte load, element order preserved) -> 16 floats, with
+// e4m3_to_f32 (the prompt attention's register-staged tiles keep fewer
+// values live this way) or with the hardware conversion.
 SKV_DEV void decode16_e4m3(u32x4_t w, float* out) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int b = 0; b < 4; ++b) out[4 * i + b] = e4m3_to_f32((w[i] >> (8 * b)) & 255u);
+}
+SKV_DEV void decode16_e4m3_hw(u32x4_t w, float* out) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) decode4_e4m3_hw(w[i], out + 4 * i);
 }
