@@ -74,13 +74,14 @@ def cpu_baseline(workload, batch, cached, n_prompts=3):
     gw = si.global_weights(s, workload.dtype)
     W = O.LazyWeights(si.as_f32(gw["embed"]), si.as_f32(gw["final_norm"]), si.as_f32(gw["lm_head"]), cached.make)
     t0 = time.perf_counter()
-    O.swiftkv_prefill(dims, W, [batch.tokens[b] for b in sel], workload.swiftkv_l, workload.acrosskv_g)
+    r = O.swiftkv_prefill(dims, W, [batch.tokens[b] for b in sel], workload.swiftkv_l, workload.acrosskv_g)
     dt = time.perf_counter() - t0
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     n = int(sum(int(batch.lengths[b]) for b in sel))
     return {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "flops": r.flops, "gflops_per_s": round(r.flops / dt / 1e9, 1),
             "sample": f"prompts {sel} of the batch ({n} tokens) through the whole path, fp32 NumPy oracle, "
-                      f"{dt:.1f} s wall"}
+                      f"{dt:.1f} s wall, {r.flops / 1e12:.2f} TFLOP counted by the oracle"}
 
 
 def copy_calibration(mib: int):
@@ -209,12 +210,73 @@ def measure_fp8(w, batch, db, logits, stream, args, extra, ms_bf16, dec_bf16):
     return out
 
 
+# dominant kernel class of each workload's step (the one its roofline object covers)
+DOMINANT = {"llama8b_l16_b16": "gemm_gateup", "llama8b_l24_g4_b32": "gemm_gateup", "llama70b_l40_b32": "gemm_gateup",
+            "llama8b_l16_long32k": "attn_prefill", "tiny_fp32_l2": "gemm_gateup"}
+KERNEL_TEXT = {"gemm_gateup": "gemm_gateup (bf16 MFMA GEMM + SwiGLU epilogue)",
+               "attn_prefill": "attn_prefill8 (causal GQA flash attention, bf16 MFMA)"}
+
+
+def measure_workload(name, steps, warmup, stream):
+    """Load one workload's model, time `steps` prefill steps of its batch (after `warmup`), with HIP events on the
+    launch stream around every launch of its dominant kernel class.  Returns its sub-object of the JSON line."""
+    import torch
+    import skv_inputs as si
+    from swiftkv_prefill_skipping_amd import _lib as L, runner
+    w = si.WORKLOADS[name]
+    batch = si.make_batch(w)
+    T, B = batch.total_tokens, len(batch.lengths)
+    t0 = time.time()
+    model = runner.load_seeded_model(w, T, B, batch.max_seqlen)
+    cache = runner.Cache(model, batch.num_blocks)
+    db = runner.device_batch(batch)
+    logits = torch.empty((B, w.shape.vocab), dtype=torch.float32, device="cuda")
+    log(f"[bench] {name}: {B} prompts, {T} tokens; model loaded in {time.time() - t0:.1f} s")
+    for _ in range(warmup):
+        runner.prefill(model, cache, db, logits, stream)
+    torch.cuda.synchronize()
+    dom = DOMINANT[name]
+    L.skv_profile_enable(model.handle, L.KERNEL_CLASS_NAMES.index(dom), True)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        runner.prefill(model, cache, db, logits, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    prof = L.skv_profile_read(model.handle)
+    L.skv_profile_enable(model.handle, L.KERNEL_CLASS_NAMES.index(dom), False)
+    ms = e0.elapsed_time(e1) / steps
+    assert torch.isfinite(logits).all()
+    full, swift = L.skv_flops(model.cfg, batch.lengths)
+    t = ms / 1e3
+    avg = prof["total_ms"] / max(prof["launches"], 1)
+    fpl = prof["flops"] / max(prof["launches"], 1)
+    ach = fpl / (avg / 1e3) / 1e12
+    log(f"[bench] {name}: {ms:.2f} ms/step, {T / t:.0f} tokens/s; {dom} {ach:.0f} TFLOP/s")
+    cache.close()
+    model.close()
+    return {"workload": name, "prompts": B, "prompt_tokens": T, "swiftkv_l": w.swiftkv_l, "acrosskv_g": w.acrosskv_g,
+            "steps": steps, "warmup": warmup, "ms_per_step": round(ms, 3), "tokens_per_s": round(T / t, 1),
+            "normalized_tflops": round(full / t / 1e12, 2), "actual_tflops": round(swift / t / 1e12, 2),
+            "normalized_frac_of_bf16_peak": round(full / t / 1e12 / MI355X_BF16_DENSE_TFLOPS, 4),
+            "actual_frac_of_bf16_peak": round(swift / t / 1e12 / MI355X_BF16_DENSE_TFLOPS, 4),
+            "flops_full_depth": full, "flops_swiftkv": swift,
+            "roofline": {"kernel": KERNEL_TEXT[dom], "bound": "mfma", "achieved": round(ach, 2),
+                         "peak": MI355X_BF16_DENSE_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(ach / MI355X_BF16_DENSE_TFLOPS, 4), "traffic": None,
+                         "avg_launch_ms": round(avg, 4), "launches": prof["launches"], "flops_per_launch": fpl,
+                         "algorithmic_bytes_per_launch": prof["bytes"] / max(prof["launches"], 1)}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama8b_l16_b16")
+    ap.add_argument("--other-workloads", default="llama8b_l24_g4_b32,llama70b_l40_b32,llama8b_l16_long32k",
+                    help="comma-separated workloads also timed (a sub-object each in 'workloads'); empty = none")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-mfma-probe", action="store_true",
                     help="skip the pure-MFMA throughput probe (random and constant operands)")
@@ -384,6 +446,12 @@ def main():
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on the host")
         res["cpu_baseline"] = cpu_baseline(w, batch, cached)
+    del cached
+    others = [n for n in args.other_workloads.split(",") if n and n != w.name]
+    if others:
+        model.close()
+        cache.close()
+        res["workloads"] = {n: measure_workload(n, min(args.steps, 5), min(args.warmup, 2), stream) for n in others}
     print(json.dumps(res), flush=True)
 
 

@@ -246,10 +246,15 @@ skv_status skv_step_noalloc(skv_model* m, skv_kv_cache* c, const skv_step_batch*
                             void* stream);
 
 /* Closed-form FLOPs of a prefill over prompts of the given lengths (host
- * array).  full = the unmodified model (all layers for every token, LM head
- * for the last token); swiftkv = layers 1..l for every token, one K/V
- * projection per group for every token, layers l+1..L for the last token.
- * Matmuls count 2mnk, attention 4*ctx*head_dim per query per head. */
+ * array), counted the way the summary page's section 3.4 Table 1 ("FLOPs per
+ * prefill token", Llama-3.1-70B) breaks a forward pass down: the K/V, Q/O
+ * and MLP projections, attention and the vocabulary projection.
+ * full = the unmodified model (all layers for every token, LM head for the
+ * last token); swiftkv = layers 1..l for every token, one K/V projection
+ * per AcrossKV group for every token (Eq. 2 / Eq. KV_group), layers l+1..L
+ * for the last token.  Matmuls count 2mnk, attention 4*ctx*head_dim per
+ * query per head.  Host only.  INVALID_ARG for a bad config, a negative
+ * batch, NULL seqlens with batch > 0 or a NULL output. */
 skv_status skv_flops(const skv_model_config* cfg, const int32_t* seqlens, int32_t batch, double* full,
                      double* swiftkv);
 

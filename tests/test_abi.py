@@ -82,12 +82,6 @@ def test_fp32_validation():
     assert swift < full
 
 
-def test_kv_memory_slots_closed_form():
-    # the library's slot count is l + ceil((L - l) / g), the AcrossKV memory formula
-    for L_, l, g in [(32, 16, 1), (32, 16, 4), (32, 24, 4), (80, 40, 1), (4, 1, 2)]:
-        assert O.kv_slots(L_, l, g) == l + -(-(L_ - l) // g)
-
-
 def test_step_rejects_null_arguments_without_a_device():
     L = _lib()
     import ctypes
