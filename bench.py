@@ -329,7 +329,8 @@ def main():
     torch.cuda.synchronize()
     log("[bench] warmup done")
 
-    dominant = L.SKV_K_GEMM_GATEUP
+    dom_name = DOMINANT.get(w.name, "gemm_gateup")
+    dominant = L.KERNEL_CLASS_NAMES.index(dom_name)
     L.skv_profile_enable(model.handle, dominant, True)
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
@@ -385,7 +386,7 @@ def main():
         "actual_frac_of_bf16_peak": round(act_tf / MI355X_BF16_DENSE_TFLOPS, 4),
         "flops_full_depth": full,
         "flops_swiftkv": swift,
-        "roofline": {"kernel": "gemm_gateup (bf16 MFMA GEMM + SwiGLU epilogue)", "bound": "mfma",
+        "roofline": {"kernel": KERNEL_TEXT[dom_name], "bound": "mfma",
                      "achieved": round(achieved, 2), "peak": MI355X_BF16_DENSE_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / MI355X_BF16_DENSE_TFLOPS, 4),
                      "traffic": (measured_traffic("EpiSwiGLUPanel") or {}).get("bytes") if w.name == "llama8b_l16_b16"
@@ -441,7 +442,7 @@ def main():
             "cus": pr["random_operands"]["cus"], "max_clock_mhz": pr["random_operands"]["max_clock_mhz"],
             **{k: {"tflops": round(v["tflops"], 1), "clock_mhz": round(v["clock_mhz"], 0),
                    "frac_of_bf16_peak": round(v["tflops"] / MI355X_BF16_DENSE_TFLOPS, 4)} for k, v in pr.items()},
-            "gemm_gateup_frac_of_random_operand_probe": round(achieved / pr["random_operands"]["tflops"], 4)}
+            f"{dom_name}_frac_of_random_operand_probe": round(achieved / pr["random_operands"]["tflops"], 4)}
         log(f"[bench] MFMA probe: {res['mfma_probe']}")
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on the host")
