@@ -50,6 +50,14 @@ typedef s16x4_t short4_lds_t;
 constexpr int FA_DH = 128;
 constexpr int FA_KT = 64;  // keys per tile
 
+// Physical 16-byte chunk of logical chunk c in key row r of a K/V tile:
+// c ^ kv_swz(r), kv_swz swapping the two 2-bit halves of r & 15.  A phase
+// of the score reads (sixteen consecutive keys at one chunk) covers all
+// sixteen chunk positions, and so does a phase of the transposing P.V reads
+// (four consecutive keys times four consecutive chunks), so neither read
+// conflicts on the banks.
+SKV_DEV int kv_swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
 
 // x combined with lane (l ^ 32)'s value through gfx950's v_permlane32_swap:
 // the swap leaves lane l holding (value of lane l & 31, value of lane l | 32),
@@ -134,10 +142,10 @@ SKV_DEV void f8_qk(const bf16_t* sk, const bf16_t* sk_lo, const bf16x8_t* qf, co
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
       const int key = st * 32 + (lane & 31);
-      bf16x8_t kf = as_bf16x8(*reinterpret_cast<const u32x4_t*>(sk + key * FA_DH + ((ch ^ (key & 15)) << 3)));
+      bf16x8_t kf = as_bf16x8(*reinterpret_cast<const u32x4_t*>(sk + key * FA_DH + ((ch ^ kv_swz(key)) << 3)));
       sacc[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sacc[st], 0, 0, 0);
       if constexpr (SPLIT) {
-        const int off = key * FA_DH + ((ch ^ (key & 15)) << 3);
+        const int off = key * FA_DH + ((ch ^ kv_swz(key)) << 3);
         bf16x8_t kl = as_bf16x8(*reinterpret_cast<const u32x4_t*>(sk_lo + off));
         sacc[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kl, qf[ks], sacc[st], 0, 0, 0);
         sacc[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf_lo[ks], sacc[st], 0, 0, 0);
@@ -212,7 +220,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int lrow = (wave & 1) * 8 + i * 4 + (lane >> 4);  // key row within the 16-key block
-    src_off[i] = lrow * FA_DH + (((lane & 15) ^ lrow) << 3);
+    src_off[i] = lrow * FA_DH + (((lane & 15) ^ kv_swz(lrow)) << 3);
   }
   auto block_of = [&](int t) {
     const int bi = t * (FA_KT / kBlockSize) + r_blk;
@@ -237,8 +245,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       hi[e] = pack_bf16x2(x[8 + 2 * e] * sc, x[8 + 2 * e + 1] * sc);
     }
     bf16_t* row = &smem[buf][fk * FA_DH];
-    *reinterpret_cast<u32x4_t*>(row + (((2 * fq) ^ (fk & 15)) << 3)) = lo;
-    *reinterpret_cast<u32x4_t*>(row + (((2 * fq + 1) ^ (fk & 15)) << 3)) = hi;
+    *reinterpret_cast<u32x4_t*>(row + (((2 * fq) ^ kv_swz(fk)) << 3)) = lo;
+    *reinterpret_cast<u32x4_t*>(row + (((2 * fq + 1) ^ kv_swz(fk)) << 3)) = hi;
   };
   auto issue = [&](const bf16_t* base_ptr, int blk, int buf) {
     const bf16_t* src = base_ptr + ((int64_t)blk * hkv + g) * (kBlockSize * FA_DH);
@@ -336,15 +344,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const int k1 = kk * 16 + 4 * hh + ta, k2 = k1 + 8;
         typedef __attribute__((address_space(3))) short4_lds_t* lds_s4p;
         s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s4p)(sv + k1 * FA_DH + (((d >> 3) ^ (k1 & 15)) << 3) + (d & 7)));
+            (lds_s4p)(sv + k1 * FA_DH + (((d >> 3) ^ kv_swz(k1)) << 3) + (d & 7)));
         s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s4p)(sv + k2 * FA_DH + (((d >> 3) ^ (k2 & 15)) << 3) + (d & 7)));
+            (lds_s4p)(sv + k2 * FA_DH + (((d >> 3) ^ kv_swz(k2)) << 3) + (d & 7)));
         u32x2_t lo2 = __builtin_bit_cast(u32x2_t, lo), hi2 = __builtin_bit_cast(u32x2_t, hi);
         bf16x8_t vf = as_bf16x8(u32x4_t{lo2.x, lo2.y, hi2.x, hi2.y});
         oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kk], oacc[dt], 0, 0, 0);
         if constexpr (SPLIT) {
-          const int o1 = k1 * FA_DH + (((d >> 3) ^ (k1 & 15)) << 3) + (d & 7);
-          const int o2 = k2 * FA_DH + (((d >> 3) ^ (k2 & 15)) << 3) + (d & 7);
+          const int o1 = k1 * FA_DH + (((d >> 3) ^ kv_swz(k1)) << 3) + (d & 7);
+          const int o2 = k2 * FA_DH + (((d >> 3) ^ kv_swz(k2)) << 3) + (d & 7);
           s16x4_t llo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4p)(sv_lo + o1));
           s16x4_t lhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4p)(sv_lo + o2));
           u32x2_t a2 = __builtin_bit_cast(u32x2_t, llo), b2 = __builtin_bit_cast(u32x2_t, lhi);
