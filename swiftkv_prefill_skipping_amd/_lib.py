@@ -68,6 +68,15 @@ def lib():
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m swiftkv_prefill_skipping_amd.build`")
+        # One HIP runtime per process: the torch wheel bundles its own
+        # libamdhip64.so.7 under the same soname as the system one this
+        # library links, and whichever is mapped first serves both.  Torch
+        # finds no device on a runtime other than its own, so it is loaded
+        # first whenever it is installed.
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         L = ctypes.CDLL(LIB_PATH)
         vp = c_void_p
         L.skv_model_create.argtypes = [POINTER(skv_model_config), POINTER(c_void_p)]

@@ -8,9 +8,14 @@
 //
 // Tile 256 x 256, k-stages of 32.  256 threads = 4 wave64s, one per SIMD;
 // wave w owns output rows 128*(w&1) .. +128 and columns 128*(w>>1) .. +128
-// as 4 x 4 tiles of v_mfma_f32_32x32x16_bf16 (256 accumulator registers).
-// The MFMA takes the B fragment as its first operand, so each lane ends up
-// holding one output row (lane & 31) and runs of four consecutive columns.
+// as 8 x 8 tiles of v_mfma_f32_16x16x32_bf16 (256 accumulator registers).
+// The 16x16x32 form rather than 32x32x16: with operands whose bits toggle
+// like these weights', a CU full of back-to-back 32x32x16 MFMAs draws the
+// chip to its power limit at ~1.83 GHz (1.84 PFLOP/s), while the same work
+// as 16x16x32 MFMAs holds ~2.13 GHz (2.10 PFLOP/s); with constant operands
+// both run at ~2.39 GHz.  The MFMA takes the B fragment as its first
+// operand, so each lane ends up holding one output row (lane & 15) and runs
+// of four consecutive columns.
 //
 // Operand staging: global -> LDS directly (global_load_lds_dwordx4, no
 // register round trip) into a ring of kNBuf 32 KB stages, kNBuf - 1 of them
@@ -19,11 +24,15 @@
 // read by one ds_read_b128 pass (16 lanes, 256 B, all 64 banks) cover all
 // 16 bank groups: the fragment reads are conflict free.
 //
-// Schedule: each k-stage is two k-substeps of 16 MFMAs; the fragment reads
-// of the next substep are interleaved with the first 8 MFMAs of the current
-// one.  One workgroup barrier per stage publishes the next stage and frees
-// the current buffer, whose next load goes out in two halves, one in each
-// of the following two substeps, between their last 8 MFMAs.
+// Schedule: each k-stage is 64 MFMAs in two halves (row tiles 0..3, then
+// 4..7, every column tile).  The first half reads the second half's A
+// fragments; the second half reads the next stage's fragments (A row tiles
+// 0..3 into the registers the first half freed, the B fragments into a
+// second set, the two sets alternating by stage parity), all early enough
+// to land before the next stage needs them.  One workgroup barrier per
+// stage, between the halves, publishes the next stage and frees the
+// current buffer, whose next load goes out in two halves, one in each of
+// the following two half-stages, between their MFMAs.
 //
 // Epilogue: the accumulators go through LDS (each wave stages 32 rows x 128
 // columns of fp32 at a time in a padded, conflict-free layout), so the
@@ -38,6 +47,8 @@
 // remapped so each XCD processes a contiguous run of tiles, and runs are
 // ordered in groups of kGroupM row tiles so concurrently resident tiles share
 // A and B panels in that XCD's L2.
+#include <type_traits>
+
 #include "common.h"
 #include "epilogues.h"
 #include "kernels.h"
@@ -204,8 +215,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(const bf16_t* __
     unit = bid;
     tile = plan.dp_tiles + unit / plan.splits;
     const int sp = unit % plan.splits;
-    kb = sp * nk_all / plan.splits;
-    ke = (sp + 1) * nk_all / plan.splits;
+    // ranges in whole pairs of stages: every range has an even stage count
+    kb = 2 * (sp * (nk_all / 2) / plan.splits);
+    ke = 2 * ((sp + 1) * (nk_all / 2) / plan.splits);
   }
   int tm, tn;
   tile_coords(tile, tiles_m, tiles_n, tm, tn);
@@ -225,8 +237,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(const bf16_t* __
   // l % CH.  Wave w moves row groups w*LPW/2 .. +LPW/2 of both A and B.
   constexpr int LH = LPW / 2;
   const int nkb = K / BK;
-  const bf16_t* a_panel = A + (int64_t)tm * nkb * (BM * BK);
-  const bf16_t* b_panel = B + (int64_t)tn * nkb * (BN * BK);
+  // (from stage kb on: the loads below count stages from the range start)
+  const bf16_t* a_panel = A + ((int64_t)tm * nkb + kb) * (BM * BK);
+  const bf16_t* b_panel = B + ((int64_t)tn * nkb + kb) * (BN * BK);
   int g_off[LH];
 #pragma unroll
   for (int i = 0; i < LH; ++i) {
@@ -248,37 +261,33 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(const bf16_t* __
   };
   auto gload = [&](int buf, int stage_idx) { gload_part(buf, stage_idx, 0, LH); };
 
-  f32x16_t acc[4][4];
+  f32x4_t acc[8][8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16_t{0};
+    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int frag_row = lane & 31;
-  const int khalf = lane >> 5;
-  const int swz = swizzle<CH>(frag_row);  // rows 32 apart share it
-  const int a_off = (wm * 128 + frag_row) * BK;
-  const int b_off = BM * BK + (wn * 128 + frag_row) * BK;
+  // A fragment (16 rows x 32 k): lane l holds row l & 15, k-chunk l >> 4;
+  // rows 16 apart share the swizzle
+  const int frag_row = lane & 15;
+  const int swz = swizzle<CH>(frag_row);
+  const int fch = ((lane >> 4) ^ swz) << 3;
+  const int a_off = (wm * 128 + frag_row) * BK + fch;
+  const int b_off = BM * BK + (wn * 128 + frag_row) * BK + fch;
 
-  // fragments of one k-substep (16 deep): 4 A row tiles, 4 B column tiles
-  bf16x8_t af[2][4], bfr[2][4];
-  auto fload = [&](int buf, int kk, int slot) {
-    const bf16_t* sa = smem[buf] + a_off;
-    const bf16_t* sb = smem[buf] + b_off;
-    const int ch = ((kk * 2 + khalf) ^ swz) << 3;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) af[slot][i] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(sa + i * 32 * BK + ch));
-#pragma unroll
-    for (int j = 0; j < 4; ++j) bfr[slot][j] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(sb + j * 32 * BK + ch));
+  // fragments: 8 A row tiles of the current stage, 8 B column tiles in
+  // each of two sets (set = stage parity)
+  bf16x8_t af[8], bfr[2][8];
+  auto read_a = [&](int buf, int i) {
+    af[i] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(smem[buf] + a_off + i * 16 * BK));
   };
-  // acc[i][j] (transposed tile): lane holds output row i*32 + (lane & 31),
-  // columns j*32 + 8*(v/4) + 4*(lane/32) + (v%4)
-  auto compute = [&](int slot) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[slot][j], af[slot][i], acc[i][j], 0, 0, 0);
+  auto read_b = [&](int set, int buf, int j) {
+    bfr[set][j] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(smem[buf] + b_off + j * 16 * BK));
+  };
+  // acc[i][j] (transposed tile): lane holds output row i*16 + (lane & 15),
+  // columns j*16 + 4*(lane/16) + v
+  auto mfma = [&](int set, int i, int j) {
+    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[set][j], af[i], acc[i][j], 0, 0, 0);
   };
 
   // Epilogue geometry.  unit (pass i, it): row wm*128 + i*32 + it*8 + er,
@@ -288,10 +297,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(const bf16_t* __
   // them would make its wait cover them as well.  (Loading pass 0 during the
   // last k-stages instead was measured slower: every CU reaches its epilogue
   // at the same time, so those loads only move the HBM burst earlier.)
-  const int er = lane >> 3;        // row within a group of 8
-  const int ec = (lane & 7) * 8;   // first of eight columns, 0..56
-  const int wr = lane & 31;        // row written by this lane
-  const int wc = 4 * (lane >> 5);  // column offset within a group of 8
+  const int er = lane >> 3;       // row within a group of 8
+  const int ec = (lane & 7) * 8;  // first of eight columns, 0..56
   const int lcol = wn * 128 + ec;
   const bool cols_ok = n0 + wn * 128 < N;
   using Ahead = EpiAhead<Epi>;
@@ -304,110 +311,145 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(const bf16_t* __
   };
 
   const int nk = ke - kb;
-  static_assert(NSUB == 2 && LH % 2 == 0, "two k-substeps per stage, loads in two halves");
+  static_assert(NSUB == 2 && LH % 2 == 0 && LH / 2 == 2, "32-deep stages, loads in two halves of 4");
 
   // Pipeline: all NBUF buffers are filled up front.  The barrier in the
   // middle of stage s publishes stage s+1 (every wave has landed its share)
-  // and frees the buffer of stage s (its last fragments are in registers).
-  // Stage s+NBUF then goes into that buffer in two halves: the first during
-  // the second k-substep of stage s, the second during the first k-substep
-  // of stage s+1, so each substep's 16 MFMAs carry LPW/2 direct loads and
-  // the load issue never bunches up behind the barrier.  At the barrier of
-  // stage s the loads issued after stage s+1's are those of stages s+2 and
-  // s+3 (LPW each), whenever both exist; near the end the wait drains all.
-  // The flags are constants at each call site, so every stage body is one
-  // straight-line block and the group barriers interleave its loads and LDS
-  // reads with the MFMAs.
+  // and frees the buffer of stage s (its fragments are in registers by
+  // then).  Stage s+NBUF then goes into that buffer in two halves: the
+  // first during the second half of stage s, the second during the first
+  // half of stage s+1, so each half-stage's 32 MFMAs carry LPW/2 direct
+  // loads and the load issue never bunches up behind the barrier.  At the
+  // barrier of stage s the loads issued after stage s+1's are those of
+  // stages s+2 and s+3 (LPW each), whenever both exist; near the end the
+  // wait drains all.  The flags are constants at each call site, so every
+  // stage body is one straight-line block and the group barriers interleave
+  // its loads and LDS reads with the MFMAs.
   //   load_a: first half of stage s+NBUF, after the barrier
   //   load_b: second half of stage s+NBUF-1, before the barrier
-  auto stage = [&](int s, bool load_a, bool load_b, bool next) {
-    const int cur = s % NBUF;
-    // substep 0: the fragments of substep 1 are read between its first 8
-    // MFMAs, the second half of the previous stage's load between the rest
-    fload(cur, 1, 1);
-    if (load_b) gload_part((s + NBUF - 1) % NBUF, kb + s + NBUF - 1, LH / 2, LH);
-    compute(0);
+  auto stage = [&](auto parity, int s, bool load_a, bool load_b, bool next) {
+    constexpr int P = decltype(parity)::value;
+    const int cur = s % NBUF, nxt = (s + 1) % NBUF;
+    // first half: row tiles 0..3; reads the A fragments of row tiles 4..7
+    // and issues the second half of the previous stage's load
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    for (int i = 4; i < 8; ++i) read_a(cur, i);
+    if (load_b) gload_part((s + NBUF - 1) % NBUF, s + NBUF - 1, LH / 2, LH);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mfma(P, i, j);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     }
     if (load_b) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x020, LPW / 8, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      for (int g = 0; g < 4; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
       }
     } else {
-      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
     if (next) {
       if (load_a || load_b) wait_vm_then_barrier<2 * LPW>();
       else wait_vm_then_barrier<0>();
     }
-    // substep 1: the next stage's first fragments, then the first half of
-    // stage s+NBUF into the freed buffer
-    if (next) fload((s + 1) % NBUF, 0, 0);
-    if (load_a) gload_part(cur, kb + s + NBUF, 0, LH / 2);
-    compute(1);
+    // second half: row tiles 4..7; reads the next stage's fragments (A
+    // row tiles 0..3, the other B set) and issues the first half of stage
+    // s+NBUF into the freed buffer
     if (next) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      for (int i = 0; i < 4; ++i) read_a(nxt, i);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) read_b(1 - P, nxt, j);
+    }
+    if (load_a) gload_part(cur, s + NBUF, 0, LH / 2);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int i = 4; i < 8; ++i) mfma(P, i, j);
+    if (next) {
+#pragma unroll
+      for (int g = 0; g < 12; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
     }
     if (load_a) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int g = 0; g < 4; ++g) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x020, LPW / 8, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
   };
   const int pre = min(NBUF, nk);
-  for (int p = 0; p < pre; ++p) gload(p, kb + p);
+  for (int p = 0; p < pre; ++p) gload(p, p);
   if (pre == 1) wait_vm_then_barrier<0>();
   else if (pre == 2) wait_vm_then_barrier<LPW>();
   else if (pre == 3) wait_vm_then_barrier<2 * LPW>();
   else wait_vm_then_barrier<3 * LPW>();
-  fload(0, 0, 0);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) read_b(0, 0, j);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) read_a(0, i);
   __builtin_amdgcn_sched_barrier(0);
-  int s = 0;
-  if (nk > NBUF) stage(s++, true, false, true);
-  for (; s < nk - NBUF; ++s) stage(s, true, true, true);
-  if (s >= 1 && s == nk - NBUF) stage(s++, false, true, true);
-  for (; s < nk - 1; ++s) stage(s, false, false, true);
-  stage(s, false, false, false);
+  // Stage s of nk (nk even, so every call site knows its parity):
+  //   load_a = s < nk - NBUF, load_b = 1 <= s <= nk - NBUF, next = s < nk - 1
+  using Even = std::integral_constant<int, 0>;
+  using Odd = std::integral_constant<int, 1>;
+  static_assert(NBUF == 4, "stage sequence written for four buffers");
+  if (nk >= 6) {
+    stage(Even{}, 0, true, false, true);
+    int s = 1;
+    for (; s < nk - 5; s += 2) {
+      stage(Odd{}, s, true, true, true);
+      stage(Even{}, s + 1, true, true, true);
+    }
+    stage(Odd{}, nk - 5, true, true, true);
+    stage(Even{}, nk - 4, false, true, true);
+    stage(Odd{}, nk - 3, false, false, true);
+    stage(Even{}, nk - 2, false, false, true);
+    stage(Odd{}, nk - 1, false, false, false);
+  } else if (nk == 4) {
+    stage(Even{}, 0, false, false, true);
+    stage(Odd{}, 1, false, false, true);
+    stage(Even{}, 2, false, false, true);
+    stage(Odd{}, 3, false, false, false);
+  } else {
+    stage(Even{}, 0, false, false, true);
+    stage(Odd{}, 1, false, false, false);
+  }
 
   // Epilogues that take their pairs from registers (SwiGLU: a lane's gate
-  // columns j*32 + 8g + 4*(lane/32) + e and their up partners sit in
-  // acc[i][j] and acc[i][j+2] for j < 2) skip the LDS staging; each call
-  // writes four consecutive bf16 of a row.
+  // columns j*16 + 4*(lane/16) + v and their up partners sit in acc[i][j]
+  // and acc[i][j+4] for j < 4) skip the LDS staging; each call writes four
+  // consecutive bf16 of a row.
   if constexpr (FromRegisters<Epi>::value && !SPLIT) {
     {
       if (!cols_ok) return;
-      const int row0 = m0 + wm * 128 + (lane & 31);
-      const int col0 = n0 + wn * 128 + 4 * (lane >> 5);
-      float sr[4];
+      const int row0 = m0 + wm * 128 + (lane & 15);
+      const int col0 = n0 + wn * 128 + 4 * (lane >> 4);
+      float sr[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sr[i] = row0 + i * 32 < M ? epi.scale(row0 + i * 32) : 0.f;
+      for (int i = 0; i < 8; ++i) sr[i] = row0 + i * 16 < M ? epi.scale(row0 + i * 16) : 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (row0 + i * 32 < M) {
+      for (int i = 0; i < 8; ++i) {
+        if (row0 + i * 16 < M) {
 #pragma unroll
-          for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              const float gv[4] = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
-              const float uv[4] = {acc[i][j + 2][4 * g], acc[i][j + 2][4 * g + 1], acc[i][j + 2][4 * g + 2],
-                                   acc[i][j + 2][4 * g + 3]};
-              epi.vec4s(row0 + i * 32, col0 + j * 32 + 8 * g, gv, uv, sr[i]);
-            }
+          for (int j = 0; j < 4; ++j) {
+            const float gv[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+            const float uv[4] = {acc[i][j + 4][0], acc[i][j + 4][1], acc[i][j + 4][2], acc[i][j + 4][3]};
+            epi.vec4s(row0 + i * 16, col0 + j * 16, gv, uv, sr[i]);
+          }
         }
         // one row block at a time: bounds the values copied out of the
         // accumulators that are live at once
@@ -425,14 +467,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(const bf16_t* __
   if (!split && cols_ok) load_pass(0);
 #pragma clang loop unroll(full)
   for (int i = 0; i < 4; ++i) {
-    // stage rows i*32 .. +32 of this wave's block: tile (i, j) value v is
-    // column j*32 + 8*(v/4) + wc + (v%4) of row wr
+    // stage rows i*32 .. +32 of this wave's block: tile (2i+h, j) value v
+    // is column j*16 + 4*(lane/16) + v of staged row h*16 + (lane & 15)
 #pragma clang loop unroll(full)
-    for (int j = 0; j < 4; ++j)
+    for (int h = 0; h < 2; ++h)
 #pragma clang loop unroll(full)
-      for (int g = 0; g < 4; ++g)
-        *reinterpret_cast<f32x4_t*>(stg + wr * kStageLd + j * 32 + 8 * g + wc) =
-            f32x4_t{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+      for (int j = 0; j < 8; ++j)
+        *reinterpret_cast<f32x4_t*>(stg + (h * 16 + (lane & 15)) * kStageLd + j * 16 + 4 * (lane >> 4)) =
+            acc[2 * i + h][j];
     wait_lds();
     if (!split && cols_ok && i < 3) load_pass(i + 1);
 #pragma clang loop unroll(full)
@@ -504,7 +546,7 @@ hipError_t launch_gemm_cfg(const bf16_t* A, const bf16_t* B, int M, int N, int K
                            int64_t ws_elems, hipStream_t stream) {
   constexpr int BK = kPanelCols;
   if (M <= 0) return hipSuccess;
-  if (K % BK != 0 || N % 128 != 0) return hipErrorInvalidValue;
+  if (K % (2 * BK) != 0 || N % 128 != 0) return hipErrorInvalidValue;
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   const int P = num_cus();
   const int nk = K / BK;

@@ -19,7 +19,10 @@ _hip = None
 def _hiprt():
     global _hip
     if _hip is None:
-        _hip = ctypes.CDLL("libamdhip64.so")
+        # by soname, so the runtime already mapped (torch's, see _lib.lib)
+        # is the one returned rather than a second copy
+        L.lib()
+        _hip = ctypes.CDLL("libamdhip64.so.7")
         _hip.hipMemcpy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
         _hip.hipMemcpy.restype = ctypes.c_int
     return _hip

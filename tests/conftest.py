@@ -7,6 +7,13 @@ if ROOT not in sys.path:
 
 
 def pytest_configure(config):
+    # torch first: its bundled HIP runtime must be the process's one (the
+    # library's loader does the same; this covers tests that load the
+    # library by other routes)
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     from tests import helpers
     helpers.CAPMAN = config.pluginmanager.getplugin("capturemanager")
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
