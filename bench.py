@@ -438,7 +438,8 @@ def main():
         pr = {k: L.skv_mfma_probe(k == "random_operands", 20000, stream.cuda_stream)
               for k in ("random_operands", "constant_operands")}
         res["mfma_probe"] = {
-            "kernel": "v_mfma_f32_32x32x16_bf16, 16 independent accumulators per wave, 4 waves per CU, no memory",
+            "kernel": "v_mfma_f32_16x16x32_bf16 (the GEMMs' instruction), 64 independent accumulators per wave, "
+                      "4 waves per CU, no memory",
             "cus": pr["random_operands"]["cus"], "max_clock_mhz": pr["random_operands"]["max_clock_mhz"],
             **{k: {"tflops": round(v["tflops"], 1), "clock_mhz": round(v["clock_mhz"], 0),
                    "frac_of_bf16_peak": round(v["tflops"] / MI355X_BF16_DENSE_TFLOPS, 4)} for k, v in pr.items()},

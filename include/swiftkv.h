@@ -282,9 +282,9 @@ skv_status skv_profile_read(skv_model* m, double* total_ms, int64_t* launches, d
 
 /* Measurement aid, not part of the method: the dense bf16 MFMA throughput
  * of this GPU.  Runs one workgroup of 4 waves per compute unit, each wave
- * issuing iters x 32 v_mfma_f32_32x32x16_bf16 on 16 independent
- * accumulators from operands held in registers (no memory traffic in the
- * loop), once untimed and once timed with HIP events on `stream`;
+ * issuing iters x 64 v_mfma_f32_16x16x32_bf16 (the GEMMs' instruction) on
+ * 64 independent accumulators from operands held in registers (no memory
+ * traffic in the loop), once untimed and once timed with HIP events on `stream`;
  * synchronous (returns when the timed run is done; allocates and frees
  * its own small device buffers).  random_operands != 0 fills the operands
  * with random sign and mantissa bits at the magnitudes of N(0, 0.02)

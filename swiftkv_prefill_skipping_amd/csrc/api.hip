@@ -783,7 +783,7 @@ skv_status skv_mfma_probe(int32_t random_operands, int32_t iters, void* stream, 
       mhz += (double)c[2 * g] / (double)c[2 * g + 1] * 100.0;
       ++used;
     }
-  const double flops = 2.0 * 32 * 32 * 16 * mfma_probe_per_iter() * (double)iters * 4 * n;
+  const double flops = (double)mfma_probe_flops_per_mfma() * mfma_probe_per_iter() * (double)iters * 4 * n;
   *tflops = ms > 0.f ? flops / ((double)ms * 1e9) : 0.0;
   *clock_mhz = used ? mhz / used : 0.0;
   *cus = n;

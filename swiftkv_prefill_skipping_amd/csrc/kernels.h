@@ -154,9 +154,11 @@ template <typename T>
 hipError_t launch_to_f32(const T* in, int64_t n, float* out, hipStream_t stream);
 
 // Pure-MFMA throughput probe (calib.hip): `grid` workgroups of 4 waves, each
-// wave issuing mfma_probe_per_iter() 32x32x16 bf16 MFMAs per iteration from
-// the 16 x 64 bf16x8 operands in `in`; clk[2g] / clk[2g+1] = shader-clock
-// cycles / 100 MHz ticks of workgroup g's loop.  out: grid * 256 floats.
+// wave issuing mfma_probe_per_iter() 16x16x32 bf16 MFMAs (of
+// mfma_probe_flops_per_mfma() FLOPs) per iteration from the 16 x 64 bf16x8
+// operands in `in`; clk[2g] / clk[2g+1] = shader-clock cycles / 100 MHz
+// ticks of workgroup g's loop.  out: grid * 256 floats.
 int mfma_probe_per_iter();
+int mfma_probe_flops_per_mfma();
 hipError_t launch_mfma_probe(const bf16x8_t* in, int iters, int grid, float* out, unsigned long long* clk,
                              hipStream_t stream);

@@ -292,6 +292,6 @@ def test_mfma_probe_reports_plausible_figures():
         r = L.skv_mfma_probe(rnd, 2000, s.cuda_stream)
         assert r["cus"] == torch.cuda.get_device_properties(0).multi_processor_count
         assert 100.0 < r["clock_mhz"] <= r["max_clock_mhz"] * 1.05, r
-        # 4 waves x 32x32x16 MFMA (32 cycles each) per CU: 4096 FLOP per CU per clock
+        # 4 waves x 16x16x32 MFMA (16 cycles each) per CU: 4096 FLOP per CU per clock
         dense_at_clock = r["cus"] * 4096 * r["clock_mhz"] * 1e6 / 1e12
         assert 0.3 * dense_at_clock < r["tflops"] < 1.05 * dense_at_clock, r
