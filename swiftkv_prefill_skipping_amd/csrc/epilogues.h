@@ -10,6 +10,14 @@
 // lane stores whole 16-byte runs.  An epilogue that reads the output it
 // updates (the residual add) also offers pre8(row, col), which loads those
 // values early, and vec8(row, col, a, b, pre), which consumes them.
+//
+// On gfx9 one vector-memory counter covers loads and stores, so a load
+// issued after a store can only be waited for together with that store.
+// The MFMA GEMM therefore reads everything its epilogue needs (per-row
+// positions, cache slots and RMSNorm factors; RoPE tables; RMSNorm gains)
+// before the stores it would otherwise queue behind: the epilogues offer
+// those reads separately (row_info, rope_tab, gains8) and vec8 forms that
+// take their results.
 #pragma once
 #include "common.h"
 
@@ -100,7 +108,23 @@ struct EpiResidual {
     load8(p + P, r.r1);
     return r;
   }
+  // the next RMSNorm's gains of the pair's columns (1 without a gain)
+  SKV_DEV void gains8(int col, float* g0, float* g1) const {
+    if (gain) {
+      load8(gain + col, g0);
+      load8(gain + col + P, g1);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) g0[e] = g1[e] = 1.0f;
+    }
+  }
   SKV_DEV void vec8(int row, int col, const float* a, const float* b, const Pre& r) const {
+    float g0[8], g1[8];
+    gains8(col, g0, g1);
+    vec8g(row, col, a, b, r, g0, g1);
+  }
+  SKV_DEV void vec8g(int row, int col, const float* a, const float* b, const Pre& r, const float* g0,
+                     const float* g1) const {
     float* p = x + (int64_t)row * ld + col;
     float y0[8], y1[8];
 #pragma unroll
@@ -114,15 +138,10 @@ struct EpiResidual {
       float q = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) q += y0[e] * y0[e] + y1[e] * y1[e];
-      if (gain) {
-        float g0[8], g1[8];
-        load8(gain + col, g0);
-        load8(gain + col + P, g1);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          y0[e] *= g0[e];
-          y1[e] *= g1[e];
-        }
+      for (int e = 0; e < 8; ++e) {
+        y0[e] *= g0[e];
+        y1[e] *= g1[e];
       }
       store8(act + panel_off(row, col, ld), y0);
       store8(act + panel_off(row, col + P, ld), y1);
@@ -227,15 +246,13 @@ SKV_DEV void rope_pair(float x0, float x1, float c, float s, float& y0, float& y
   y1 = x1 * c + x0 * s;
 }
 
-// Eight rotate-half pairs (x0[e], x1[e]) at angle index i0 + e of position p.
-SKV_DEV void rope8(const float* x0, const float* x1, const float* rope_cos, const float* rope_sin, int p, int P,
-                   int i0, float* y0, float* y1) {
-  float c[8], s[8];
-  load8(rope_cos + (int64_t)p * P + i0, c);
-  load8(rope_sin + (int64_t)p * P + i0, s);
-#pragma unroll
-  for (int e = 0; e < 8; ++e) rope_pair(x0[e], x1[e], c[e], s[e], y0[e], y1[e]);
-}
+// Per-row values of the RoPE / KV-cache epilogues: the row's RMSNorm
+// factor, position and cache slot.
+struct RowInfo {
+  float sr;
+  int pos;
+  int slot;
+};
 
 // Q/K/V projection of an unskipped layer (or Q alone for the last-token
 // path, where n_cols == dq).  Columns [0, dq) are query heads, [dq, dq+dkv)
@@ -299,19 +316,32 @@ struct EpiQKV {
     }
   }
   SKV_DEV float scale(int row) const { return rs ? rs[row] : 1.0f; }
-  SKV_DEV void vec8(int row, int col, const float* a_in, const float* b_in) const {
-    vec8s(row, col, a_in, b_in, scale(row));
+  SKV_DEV RowInfo row_info(int row) const { return RowInfo{scale(row), pos[row], slot[row]}; }
+  // q and k columns are rotated; a pair's angle index is col % dh for both
+  SKV_DEV bool roped(int col) const { return col < dq + dkv; }
+  SKV_DEV void rope_tab(int p, int col, float* c, float* s) const {
+    load8(rope_cos + (int64_t)p * P + col % dh, c);
+    load8(rope_sin + (int64_t)p * P + col % dh, s);
   }
-  SKV_DEV void vec8s(int row, int col, const float* a_in, const float* b_in, float sr) const {
+  SKV_DEV void vec8(int row, int col, const float* a_in, const float* b_in) const {
+    const RowInfo ri = row_info(row);
+    float c[8], s[8];
+    if (roped(col)) rope_tab(ri.pos, col, c, s);
+    vec8t(row, col, a_in, b_in, ri, c, s);
+  }
+  // c, s: the rotation of the pair's eight angles (q and k columns only)
+  SKV_DEV void vec8t(int row, int col, const float* a_in, const float* b_in, const RowInfo& ri, const float* c,
+                     const float* s) const {
     float a[8], b[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      a[e] = a_in[e] * sr;
-      b[e] = b_in[e] * sr;
+      a[e] = a_in[e] * ri.sr;
+      b[e] = b_in[e] * ri.sr;
     }
     float y0[8], y1[8];
     if (col < dq) {
-      rope8(a, b, rope_cos, rope_sin, pos[row], P, col % dh, y0, y1);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) rope_pair(a[e], b[e], c[e], s[e], y0[e], y1[e]);
       const int64_t qi = (int64_t)row * dq + col;
       store8(q + qi, y0);
       store8(q + qi + P, y1);
@@ -322,11 +352,12 @@ struct EpiQKV {
         }
       return;
     }
-    int sl = slot[row];
+    const int sl = ri.slot;
     if (sl < 0) return;
     if (col < dq + dkv) {
       int kc = col - dq, h = kc / dh, i = kc % dh;
-      rope8(a, b, rope_cos, rope_sin, pos[row], P, i, y0, y1);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) rope_pair(a[e], b[e], c[e], s[e], y0[e], y1[e]);
       const int64_t i0 = kv_index(sl, h, i, cache.hkv, dh), i1 = kv_index(sl, h, i + P, cache.hkv, dh);
       store8(cache.k + i0, y0);
       store8(cache.k + i1, y1);
@@ -389,24 +420,36 @@ struct EpiKVSkip {
     }
   }
   SKV_DEV float scale(int row) const { return rs ? rs[row] : 1.0f; }
-  SKV_DEV void vec8(int row, int col, const float* a_in, const float* b_in) const {
-    vec8s(row, col, a_in, b_in, scale(row));
+  SKV_DEV RowInfo row_info(int row) const { return RowInfo{scale(row), pos[row], slot[row]}; }
+  // K columns are rotated; a pair's angle index is col % dh
+  SKV_DEV bool roped(int col) const { return col % (2 * dkv) < dkv; }
+  SKV_DEV void rope_tab(int p, int col, float* c, float* s) const {
+    load8(rope_cos + (int64_t)p * P + col % dh, c);
+    load8(rope_sin + (int64_t)p * P + col % dh, s);
   }
-  SKV_DEV void vec8s(int row, int col, const float* a_in, const float* b_in, float sr) const {
-    int sl = slot[row];
+  SKV_DEV void vec8(int row, int col, const float* a_in, const float* b_in) const {
+    const RowInfo ri = row_info(row);
+    float c[8], s[8];
+    if (roped(col)) rope_tab(ri.pos, col, c, s);
+    vec8t(row, col, a_in, b_in, ri, c, s);
+  }
+  SKV_DEV void vec8t(int row, int col, const float* a_in, const float* b_in, const RowInfo& ri, const float* cs,
+                     const float* sn) const {
+    const int sl = ri.slot;
     if (sl < 0) return;
     float a[8], b[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      a[e] = a_in[e] * sr;
-      b[e] = b_in[e] * sr;
+      a[e] = a_in[e] * ri.sr;
+      b[e] = b_in[e] * ri.sr;
     }
     int g = col / (2 * dkv);
     int c = col - g * 2 * dkv;
     if (c < dkv) {
       int h = c / dh, i = c % dh;
       float y0[8], y1[8];
-      rope8(a, b, rope_cos, rope_sin, pos[row], P, i, y0, y1);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) rope_pair(a[e], b[e], cs[e], sn[e], y0[e], y1[e]);
       T* kp = k0 + g * slot_stride;
       store8(kp + kv_index(sl, h, i, hkv, dh), y0);
       store8(kp + kv_index(sl, h, i + P, hkv, dh), y1);

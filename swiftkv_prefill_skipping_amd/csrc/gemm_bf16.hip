@@ -125,41 +125,73 @@ struct StageShape {
   static constexpr int NSUB = BK / 16;
 };
 
-// Epilogue read-ahead: the residual add loads the values it updates one
-// epilogue pass ahead (so those loads overlap the previous pass); every
-// other epilogue only stores and has nothing to load.
+// What an epilogue reads, and when.  Every read is issued before the
+// stores it would otherwise wait behind (one vector-memory counter covers
+// loads and stores on gfx9):
+//   Lane: per-lane constants (a lane's columns are the same in every
+//         pass), read at the start of the epilogue;
+//   Row:  per-row values of each of the lane's 16 rows, read at the start
+//         of the epilogue;
+//   Pre:  per-unit values, read one pass ahead (before the previous pass's
+//         stores).
+// The defaults read nothing.
 template <class Epi>
 struct EpiAhead {
+  struct Lane {};
+  struct Row {};
   struct Pre {};
-  static SKV_DEV Pre load(const Epi&, int, int) { return {}; }
-  static SKV_DEV void apply(const Epi& e, int row, int col, const float* a, const float* b, const Pre&) {
+  static SKV_DEV Lane lane(const Epi&, int) { return {}; }
+  static SKV_DEV Row row(const Epi&, int) { return {}; }
+  static SKV_DEV Pre load(const Epi&, int, int, const Row&) { return {}; }
+  static SKV_DEV void apply(const Epi& e, int row, int col, const float* a, const float* b, const Lane&, const Row&,
+                            const Pre&) {
     e.vec8(row, col, a, b);
   }
 };
-// Epilogues that scale each row by a factor they read (the RMSNorm factor
-// of an un-normalised input) load it one pass ahead as well.
+// RoPE / KV-cache epilogues: each row's RMSNorm factor, position and cache
+// slot up front; a unit's RoPE rotation (q and k columns) one pass ahead.
 template <class Epi>
-struct EpiAheadScaled {
+struct EpiAheadRope {
+  struct Lane {};
+  using Row = RowInfo;
   struct Pre {
-    float sr;
+    float c[8], s[8];
   };
-  static SKV_DEV Pre load(const Epi& e, int row, int) { return {e.scale(row)}; }
-  static SKV_DEV void apply(const Epi& e, int row, int col, const float* a, const float* b, const Pre& p) {
-    e.vec8s(row, col, a, b, p.sr);
+  static SKV_DEV Lane lane(const Epi&, int) { return {}; }
+  static SKV_DEV Row row(const Epi& e, int r) { return e.row_info(r); }
+  static SKV_DEV Pre load(const Epi& e, int, int col, const Row& ri) {
+    Pre p;
+    if (e.roped(col)) e.rope_tab(ri.pos, col, p.c, p.s);
+    return p;
+  }
+  static SKV_DEV void apply(const Epi& e, int row, int col, const float* a, const float* b, const Lane&,
+                            const Row& ri, const Pre& p) {
+    e.vec8t(row, col, a, b, ri, p.c, p.s);
   }
 };
 template <>
-struct EpiAhead<EpiSwiGLUPanel> : EpiAheadScaled<EpiSwiGLUPanel> {};
+struct EpiAhead<EpiQKV<bf16_t>> : EpiAheadRope<EpiQKV<bf16_t>> {};
 template <>
-struct EpiAhead<EpiQKV<bf16_t>> : EpiAheadScaled<EpiQKV<bf16_t>> {};
-template <>
-struct EpiAhead<EpiKVSkip<bf16_t>> : EpiAheadScaled<EpiKVSkip<bf16_t>> {};
+struct EpiAhead<EpiKVSkip<bf16_t>> : EpiAheadRope<EpiKVSkip<bf16_t>> {};
+// Residual add: the next RMSNorm's gains of the lane's columns up front,
+// the residual values it updates one pass ahead.
 template <>
 struct EpiAhead<EpiResidual> {
+  struct Lane {
+    float g0[8], g1[8];
+  };
+  struct Row {};
   using Pre = EpiResidual::Pre;
-  static SKV_DEV Pre load(const EpiResidual& e, int row, int col) { return e.pre8(row, col); }
-  static SKV_DEV void apply(const EpiResidual& e, int row, int col, const float* a, const float* b, const Pre& p) {
-    e.vec8(row, col, a, b, p);
+  static SKV_DEV Lane lane(const EpiResidual& e, int col) {
+    Lane l;
+    e.gains8(col, l.g0, l.g1);
+    return l;
+  }
+  static SKV_DEV Row row(const EpiResidual&, int) { return {}; }
+  static SKV_DEV Pre load(const EpiResidual& e, int row, int col, const Row&) { return e.pre8(row, col); }
+  static SKV_DEV void apply(const EpiResidual& e, int row, int col, const float* a, const float* b, const Lane& l,
+                            const Row&, const Pre& p) {
+    e.vec8g(row, col, a, b, p, l.g0, l.g1);
   }
 };
 
@@ -302,12 +334,22 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(const bf16_t* __
   const int lcol = wn * 128 + ec;
   const bool cols_ok = n0 + wn * 128 < N;
   using Ahead = EpiAhead<Epi>;
+  typename Ahead::Lane lane_c;
+  typename Ahead::Row rows[4][4];
   typename Ahead::Pre ahead[2][4];
   auto unit_row = [&](int i, int it) { return wm * 128 + i * 32 + it * 8 + er; };
+  auto load_rows = [&]() {
+    lane_c = Ahead::lane(epi, n0 + lcol);
+#pragma clang loop unroll(full)
+    for (int i = 0; i < 4; ++i)
+#pragma clang loop unroll(full)
+      for (int it = 0; it < 4; ++it)
+        if (m0 + unit_row(i, it) < M) rows[i][it] = Ahead::row(epi, m0 + unit_row(i, it));
+  };
   auto load_pass = [&](int i) {
 #pragma clang loop unroll(full)
     for (int it = 0; it < 4; ++it)
-      if (m0 + unit_row(i, it) < M) ahead[i & 1][it] = Ahead::load(epi, m0 + unit_row(i, it), n0 + lcol);
+      if (m0 + unit_row(i, it) < M) ahead[i & 1][it] = Ahead::load(epi, m0 + unit_row(i, it), n0 + lcol, rows[i][it]);
   };
 
   const int nk = ke - kb;
@@ -464,7 +506,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(const bf16_t* __
   // reading the last stage, so the stage buffers can be reused.
   wait_lds_then_barrier();
   float* stg = reinterpret_cast<float*>(&smem[0][0]) + wave * kStageWave;
-  if (!split && cols_ok) load_pass(0);
+  if (!split && cols_ok) {
+    load_rows();
+    load_pass(0);
+  }
 #pragma clang loop unroll(full)
   for (int i = 0; i < 4; ++i) {
     // stage rows i*32 .. +32 of this wave's block: tile (2i+h, j) value v
@@ -489,7 +534,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(const bf16_t* __
         store8(part, a);
         store8(part + 64, b);
       } else if (cols_ok) {
-        if (m0 + lrow < M) Ahead::apply(epi, m0 + lrow, n0 + lcol, a, b, ahead[i & 1][it]);
+        if (m0 + lrow < M) Ahead::apply(epi, m0 + lrow, n0 + lcol, a, b, lane_c, rows[i][it], ahead[i & 1][it]);
       }
     }
     wait_lds();
