@@ -433,43 +433,29 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(const bf16_t* __
     }
     __builtin_amdgcn_sched_barrier(0);
   };
-  const int pre = min(NBUF, nk);
-  for (int p = 0; p < pre; ++p) gload(p, p);
-  if (pre == 1) wait_vm_then_barrier<0>();
-  else if (pre == 2) wait_vm_then_barrier<LPW>();
-  else if (pre == 3) wait_vm_then_barrier<2 * LPW>();
-  else wait_vm_then_barrier<3 * LPW>();
+  // every range has at least NBUF stages: fill the ring, wait for stage 0
+  for (int p = 0; p < NBUF; ++p) gload(p, p);
+  wait_vm_then_barrier<(NBUF - 1) * LPW>();
 #pragma unroll
   for (int j = 0; j < 8; ++j) read_b(0, 0, j);
 #pragma unroll
   for (int i = 0; i < 4; ++i) read_a(0, i);
   __builtin_amdgcn_sched_barrier(0);
-  // Stage s of nk (nk even, so every call site knows its parity):
+  // Stage s of nk (nk even and >= 6, so every call site knows its parity):
   //   load_a = s < nk - NBUF, load_b = 1 <= s <= nk - NBUF, next = s < nk - 1
   using Even = std::integral_constant<int, 0>;
   using Odd = std::integral_constant<int, 1>;
   static_assert(NBUF == 4, "stage sequence written for four buffers");
-  if (nk >= 6) {
-    stage(Even{}, 0, true, false, true);
-    int s = 1;
-    for (; s < nk - 5; s += 2) {
-      stage(Odd{}, s, true, true, true);
-      stage(Even{}, s + 1, true, true, true);
-    }
-    stage(Odd{}, nk - 5, true, true, true);
-    stage(Even{}, nk - 4, false, true, true);
-    stage(Odd{}, nk - 3, false, false, true);
-    stage(Even{}, nk - 2, false, false, true);
-    stage(Odd{}, nk - 1, false, false, false);
-  } else if (nk == 4) {
-    stage(Even{}, 0, false, false, true);
-    stage(Odd{}, 1, false, false, true);
-    stage(Even{}, 2, false, false, true);
-    stage(Odd{}, 3, false, false, false);
-  } else {
-    stage(Even{}, 0, false, false, true);
-    stage(Odd{}, 1, false, false, false);
+  stage(Even{}, 0, true, false, true);
+  for (int s = 1; s < nk - 5; s += 2) {
+    stage(Odd{}, s, true, true, true);
+    stage(Even{}, s + 1, true, true, true);
   }
+  stage(Odd{}, nk - 5, true, true, true);
+  stage(Even{}, nk - 4, false, true, true);
+  stage(Odd{}, nk - 3, false, false, true);
+  stage(Even{}, nk - 2, false, false, true);
+  stage(Odd{}, nk - 1, false, false, false);
 
   // Epilogues that take their pairs from registers (SwiGLU: a lane's gate
   // columns j*16 + 4*(lane/16) + v and their up partners sit in acc[i][j]
@@ -591,7 +577,9 @@ hipError_t launch_gemm_cfg(const bf16_t* A, const bf16_t* B, int M, int N, int K
                            int64_t ws_elems, hipStream_t stream) {
   constexpr int BK = kPanelCols;
   if (M <= 0) return hipSuccess;
-  if (K % (2 * BK) != 0 || N % 128 != 0) return hipErrorInvalidValue;
+  // whole pairs of 32-column stages, at least six per tile (and per K-split
+  // unit, below)
+  if (K % (2 * BK) != 0 || K < 6 * BK || N % 128 != 0) return hipErrorInvalidValue;
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   const int P = num_cus();
   const int nk = K / BK;
@@ -602,7 +590,7 @@ hipError_t launch_gemm_cfg(const bf16_t* A, const bf16_t* B, int M, int N, int K
   // the fp32 partial-tile store, ~10 % of a tile at K = 4096), plus the
   // summing pass over all rem*s partial tiles (~13 % of a tile per P of
   // them at K = 4096); measured on the MI355X at K = 4096 and 14336.  At
-  // least 2 k-stages per unit; partial tiles must fit the workspace.
+  // least 6 k-stages per unit; partial tiles must fit the workspace.
   SplitPlan plan{tiles, 1, ws};
   const int rem = tiles % P;
   if (ws != nullptr && rem != 0) {
@@ -610,7 +598,7 @@ hipError_t launch_gemm_cfg(const bf16_t* A, const bf16_t* B, int M, int N, int K
     double best = 1.0;
     int best_s = 1;
     const int64_t cap = ws_elems / ((int64_t)BM * BN);
-    for (int s = 2; s <= nk / 2 && (int64_t)rem * s <= cap; ++s) {
+    for (int s = 2; s <= nk / 6 && (int64_t)rem * s <= cap; ++s) {
       const double cost = (double)((rem * s + P - 1) / P) * (1.0 / s + fixed) + sum * rem * s / P;
       if (cost < best) {
         best = cost;

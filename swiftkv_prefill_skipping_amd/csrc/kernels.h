@@ -10,7 +10,7 @@
 // C[M,N] = A[M,K] B[N,K]^T on MFMA (bf16 in, fp32 accumulate), pair distance 64.
 // A and B are in the panel layout (panel_off; row counts rounded up to 256,
 // padding rows are read but their results are never stored).  Requires
-// K % 32 == 0, N % 128 == 0.  ws (gemm_bf16_ws_elems() floats, or NULL)
+// K % 64 == 0, K >= 192, N % 128 == 0.  ws (gemm_bf16_ws_elems() floats, or NULL)
 // holds the split partial tiles of a partly filled last wave.
 template <class Epi>
 hipError_t launch_gemm_bf16(const bf16_t* A, const bf16_t* B, int M, int N, int K, const Epi& epi, float* ws,
