@@ -1,7 +1,12 @@
-// fp32 GEMM on the vector ALUs for fp32 models: C[M,N] = A[M,K] B[N,K]^T.
-// 32 x 2P output tile per 256-thread workgroup; thread (c, g) owns columns
-// (c, c + P) of RPT consecutive rows, so epilogue pairs stay in one thread.
-// Operands are staged through LDS in 32-wide k slices.
+// fp32 GEMM on the matrix cores for fp32 models: C[M,N] = A[M,K] B[N,K]^T
+// with v_mfma_f32_16x16x4f32 (fp32 operands, fp32 accumulation).  A
+// 256-thread workgroup computes a 64 x 2P tile: wave w owns rows
+// 16w .. 16w + 15 and all 2P columns as 2P/16 accumulator tiles.  The MFMA
+// takes the B fragment as its first operand, so lane l holds output row
+// l & 15 and columns 16j + 4(l >> 4) + v of tile j; the pair partner of
+// column c < P sits in tile j + P/16 of the same lane, so the epilogue's
+// pairs (c, c + P) stay in one thread.  Operands are staged through LDS in
+// 32-wide k slices.
 #include "common.h"
 #include "epilogues.h"
 #include "kernels.h"
@@ -11,17 +16,17 @@ namespace {
 template <int P, class Epi>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__ A, const float* __restrict__ B,
                                                        int M, int N, int K, int lda, int ldb, Epi epi) {
-  constexpr int BMf = 32, BNf = 2 * P, BKf = 32;
-  constexpr int GROUPS = 256 / P;
-  constexpr int RPT = BMf / GROUPS;
+  constexpr int BMf = 64, BNf = 2 * P, BKf = 32;
+  constexpr int NT = BNf / 16;  // accumulator tiles per wave
+  static_assert(P % 16 == 0, "pair distance");
   __shared__ float As[BMf][BKf + 1];
   __shared__ float Bs[BNf][BKf + 1];
   const int m0 = blockIdx.y * BMf, n0 = blockIdx.x * BNf;
-  const int tid = threadIdx.x;
-  const int c = tid % P, rg = tid / P;
-  float acc0[RPT], acc1[RPT];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int r16 = lane & 15, kq = lane >> 4;
+  f32x4_t acc[NT];
 #pragma unroll
-  for (int r = 0; r < RPT; ++r) acc0[r] = acc1[r] = 0.f;
+  for (int j = 0; j < NT; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   for (int k0 = 0; k0 < K; k0 += BKf) {
     for (int idx = tid; idx < BMf * BKf; idx += 256) {
@@ -35,23 +40,21 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
       Bs[r][kk] = (gr < N && gk < K) ? B[(int64_t)gr * ldb + gk] : 0.f;
     }
     __syncthreads();
-#pragma unroll 4
-    for (int kk = 0; kk < BKf; ++kk) {
-      float b0 = Bs[c][kk], b1 = Bs[c + P][kk];
 #pragma unroll
-      for (int r = 0; r < RPT; ++r) {
-        float a = As[rg * RPT + r][kk];
-        acc0[r] = fmaf(a, b0, acc0[r]);
-        acc1[r] = fmaf(a, b1, acc1[r]);
-      }
+    for (int kk = 0; kk < BKf; kk += 4) {
+      const float a = As[w * 16 + r16][kk + kq];
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(Bs[j * 16 + r16][kk + kq], a, acc[j], 0, 0, 0);
     }
     __syncthreads();
   }
+  const int row = m0 + w * 16 + r16;
+  if (row >= M) return;
 #pragma unroll
-  for (int r = 0; r < RPT; ++r) {
-    int row = m0 + rg * RPT + r;
-    if (row < M) epi(row, n0 + c, acc0[r], acc1[r]);
-  }
+  for (int j = 0; j < NT / 2; ++j)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) epi(row, n0 + j * 16 + 4 * kq + v, acc[j][v], acc[j + NT / 2][v]);
 }
 
 }  // namespace
@@ -60,7 +63,7 @@ template <int P, class Epi>
 hipError_t launch_gemm_f32(const float* A, int lda, const float* B, int ldb, int M, int N, int K, const Epi& epi,
                            hipStream_t stream) {
   if (M <= 0) return hipSuccess;
-  dim3 grid(N / (2 * P), (M + 31) / 32);
+  dim3 grid(N / (2 * P), (M + 63) / 64);
   hipLaunchKernelGGL((gemm_f32_kernel<P, Epi>), grid, dim3(256), 0, stream, A, B, M, N, K, lda, ldb, epi);
   return hipGetLastError();
 }

@@ -17,7 +17,8 @@ hipError_t launch_gemm_bf16(const bf16_t* A, const bf16_t* B, int M, int N, int 
                             int64_t ws_elems, hipStream_t stream);
 int64_t gemm_bf16_ws_elems();
 
-// Same product in fp32 on the vector ALUs (fp32 models), pair distance P
+// Same product in fp32 on the matrix cores (v_mfma_f32_16x16x4f32, fp32
+// models), pair distance P
 // (P in {16, 32, 64}); requires N % (2P) == 0.
 template <int P, class Epi>
 hipError_t launch_gemm_f32(const float* A, int lda, const float* B, int ldb, int M, int N, int K, const Epi& epi,
