@@ -113,6 +113,17 @@ SKV_DEV float wave_sum_x(float v) {
   return v;
 }
 
+// Transposing LDS read (ds_read_b64_tr_b16) through a restrict-qualified
+// pointer.  The alias scope the qualifier gives the access lets the
+// compiler's wait insertion see that the read does not touch the ring
+// buffers the direct-to-LDS loads in flight are filling; through a plain
+// pointer it waits for every such load (vmcnt(0)) before the first read.
+// The kernel's own barrier waits publish each tile before it is read.
+SKV_DEV s16x4_t lds_read_tr(const bf16_t* __restrict__ p) {
+  typedef __attribute__((address_space(3))) short4_lds_t* lds_s4p;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4p)(p));
+}
+
 SKV_DEV void wait_loads_then_barrier() {
   __builtin_amdgcn_sched_barrier(0);
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -158,8 +169,8 @@ SKV_DEV void f8_qk(const bf16_t* sk, const bf16_t* sk_lo, const bf16x8_t* qf, co
 // registers: each thread fetches 16 codes of one key and its scale, and
 // writes code * scale as bf16 into the same LDS layout the direct loads
 // produce; everything after the tile loads is shared.
-template <bool F8, bool SPLIT>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_prefill8_kernel(
+template <bool F8, bool SPLIT, int NW = 8>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_prefill8_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ q_lo, CacheSlot<bf16_t> cache, CacheSlot<bf16_t> lo,
     Fp8Slot c8, const int32_t* __restrict__ cu, const int32_t* __restrict__ ctx, const int32_t* __restrict__ bt,
     int max_blocks, int hq, int rep, float scale_log2, bf16_t* __restrict__ o) {
@@ -178,10 +189,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int N = cu[b + 1] - tok0;  // new queries, at positions C .. C + N - 1
   const int C = ctx ? ctx[b] : 0;  // positions cached before them
   const int NK = C + N;            // keys
-  const int nqb = (N + 63) / 64;
+  static_assert(NW == 8 || (NW == 4 && !F8 && !SPLIT), "the 4-wave form serves the plain bf16 cache");
+  constexpr int QT = NW * 8;  // queries per workgroup
+  const int nqb = (N + QT - 1) / QT;
   const int qb = gridDim.y - 1 - blockIdx.y;
   if (qb >= nqb) return;
-  const int q0w = qb * 64;
+  const int q0w = qb * QT;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -193,7 +206,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int hkv = cache.hkv;
   const int dq = hq * FA_DH;
 
-  const int kend = min(NK, C + q0w + 64);
+  const int kend = min(NK, C + q0w + QT);
   const int ntiles = (kend + FA_KT - 1) / FA_KT;
   const int nblk_need = (kend + kBlockSize - 1) / kBlockSize;
   const int32_t* btb = bt + (int64_t)b * max_blocks;
@@ -215,13 +228,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // land at tile row (instruction base + l/16), physical chunk l%16, so it
   // fetches logical chunk (l%16) ^ (row & 15).  Entries past the keys this
   // workgroup needs read block 0, a valid block of the prompt.
-  const int r_blk = wave >> 1;
-  int src_off[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int lrow = (wave & 1) * 8 + i * 4 + (lane >> 4);  // key row within the 16-key block
-    src_off[i] = lrow * FA_DH + (((lane & 15) ^ kv_swz(lrow)) << 3);
-  }
+  // (4 waves: wave w moves all 16 rows of block w, four instructions each.)
+  constexpr int NLI = NW == 8 ? 2 : 4;  // load instructions per wave per K or V tile
+  const int r_blk = NW == 8 ? wave >> 1 : wave;
+  const int row0 = NW == 8 ? (wave & 1) * 8 : 0;
+  // key row row0 + i*4 + lane/16 has kv_swz = ((lane/16) & 3) << 2 | (row0/4 + i) & 3
+  const int src_base = (row0 + (lane >> 4)) * FA_DH;
+  const int src_chunk = (lane & 15) ^ (((lane >> 4) & 3) << 2);
+  auto src_off = [&](int i) { return src_base + i * 4 * FA_DH + ((src_chunk ^ ((row0 / 4 + i) & 3)) << 3); };
   auto block_of = [&](int t) {
     const int bi = t * (FA_KT / kBlockSize) + r_blk;
     return btb[bi < nblk_need ? bi : 0];
@@ -252,9 +266,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const bf16_t* src = base_ptr + ((int64_t)blk * hkv + g) * (kBlockSize * FA_DH);
     typedef __attribute__((address_space(3))) void* lds_ptr;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const bf16_t* sp = src + src_off[i];
-      __builtin_amdgcn_global_load_lds(sp, (lds_ptr)(&smem[buf][(r_blk * 16 + (wave & 1) * 8 + i * 4) * FA_DH]), 16, 0,
+    for (int i = 0; i < NLI; ++i) {
+      const bf16_t* sp = src + src_off(i);
+      __builtin_amdgcn_global_load_lds(sp, (lds_ptr)(&smem[buf][(r_blk * 16 + row0 + i * 4) * FA_DH]), 16, 0,
                                        0);
     }
   };
@@ -342,19 +356,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       for (int dt = 0; dt < 4; ++dt) {
         const int d = dt * 32 + 16 * ((lane >> 4) & 1) + 4 * tb;
         const int k1 = kk * 16 + 4 * hh + ta, k2 = k1 + 8;
-        typedef __attribute__((address_space(3))) short4_lds_t* lds_s4p;
-        s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s4p)(sv + k1 * FA_DH + (((d >> 3) ^ kv_swz(k1)) << 3) + (d & 7)));
-        s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s4p)(sv + k2 * FA_DH + (((d >> 3) ^ kv_swz(k2)) << 3) + (d & 7)));
+        s16x4_t lo = lds_read_tr(sv + k1 * FA_DH + (((d >> 3) ^ kv_swz(k1)) << 3) + (d & 7));
+        s16x4_t hi = lds_read_tr(sv + k2 * FA_DH + (((d >> 3) ^ kv_swz(k2)) << 3) + (d & 7));
         u32x2_t lo2 = __builtin_bit_cast(u32x2_t, lo), hi2 = __builtin_bit_cast(u32x2_t, hi);
         bf16x8_t vf = as_bf16x8(u32x4_t{lo2.x, lo2.y, hi2.x, hi2.y});
         oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kk], oacc[dt], 0, 0, 0);
         if constexpr (SPLIT) {
           const int o1 = k1 * FA_DH + (((d >> 3) ^ kv_swz(k1)) << 3) + (d & 7);
           const int o2 = k2 * FA_DH + (((d >> 3) ^ kv_swz(k2)) << 3) + (d & 7);
-          s16x4_t llo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4p)(sv_lo + o1));
-          s16x4_t lhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4p)(sv_lo + o2));
+          s16x4_t llo = lds_read_tr(sv_lo + o1);
+          s16x4_t lhi = lds_read_tr(sv_lo + o2);
           u32x2_t a2 = __builtin_bit_cast(u32x2_t, llo), b2 = __builtin_bit_cast(u32x2_t, lhi);
           bf16x8_t vl = as_bf16x8(u32x4_t{a2.x, a2.y, b2.x, b2.y});
           oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vl, pf[kk], oacc[dt], 0, 0, 0);
@@ -971,16 +982,34 @@ __global__ __launch_bounds__(4 * RW_MAXDH) void attn_combine_kernel(const float*
 
 }  // namespace
 
+// Batches whose sequences bring at most this many new tokens take the
+// 4-wave form (32 queries per workgroup, two workgroups per CU): a
+// workgroup's fixed cost (block-table reads, then Q and the first K/V tiles
+// from HBM, and the output pass) is a large share of a short prompt's few
+// tiles, and a second workgroup on the CU runs while one waits in it.  On
+// long prompts the 8-wave form's shared K/V tiles win.
+#ifndef SKV_ATTN_SHORT_MAX_NEW
+#define SKV_ATTN_SHORT_MAX_NEW 2048
+#endif
+constexpr int kAttnShortMaxNew = SKV_ATTN_SHORT_MAX_NEW;
+
 hipError_t launch_attn_prefill_bf16(const bf16_t* q, CacheSlot<bf16_t> cache, const int32_t* cu_seqlens,
                                     const int32_t* ctx_lens, const int32_t* block_tables, int max_blocks, int batch,
                                     int max_new, int hq, bf16_t* o, hipStream_t stream) {
   if (batch <= 0 || max_new <= 0) return hipSuccess;
   const int rep = hq / cache.hkv;
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)FA_DH);
-  dim3 grid(batch * (hq / 4), (max_new + 63) / 64);
-  hipLaunchKernelGGL((attn_prefill8_kernel<false, false>), grid, dim3(512), 0, stream, q, nullptr, cache,
-                     CacheSlot<bf16_t>{nullptr, nullptr, cache.hkv, cache.dh}, Fp8Slot{}, cu_seqlens, ctx_lens,
-                     block_tables, max_blocks, hq, rep, scale_log2, o);
+  if (max_new <= kAttnShortMaxNew) {
+    dim3 grid(batch * (hq / 4), (max_new + 31) / 32);
+    hipLaunchKernelGGL((attn_prefill8_kernel<false, false, 4>), grid, dim3(256), 0, stream, q, nullptr, cache,
+                       CacheSlot<bf16_t>{nullptr, nullptr, cache.hkv, cache.dh}, Fp8Slot{}, cu_seqlens, ctx_lens,
+                       block_tables, max_blocks, hq, rep, scale_log2, o);
+  } else {
+    dim3 grid(batch * (hq / 4), (max_new + 63) / 64);
+    hipLaunchKernelGGL((attn_prefill8_kernel<false, false>), grid, dim3(512), 0, stream, q, nullptr, cache,
+                       CacheSlot<bf16_t>{nullptr, nullptr, cache.hkv, cache.dh}, Fp8Slot{}, cu_seqlens, ctx_lens,
+                       block_tables, max_blocks, hq, rep, scale_log2, o);
+  }
   return hipGetLastError();
 }
 
