@@ -1,7 +1,7 @@
 """Throughput of the SwiftKV prefill on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--no-full-depth]
-                    [--no-decode] [--no-fp8] [--no-mfma-probe]
+                    [--no-decode] [--no-fp8] [--no-mfma-probe] [--no-vendor-gemm]
     python bench.py --copy-calibration MIB   # plain device copy of known size, for HBM counter scaling
 
 One step = one skv_prefill call over the whole batch (every row of the hot
@@ -138,6 +138,33 @@ def time_calls(fn, steps, warmup, stream):
     e1.record(stream)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / steps
+
+
+def vendor_gemm(M, N, K, ours_ms, reps=10):
+    """The vendor library's bf16 GEMM (torch.matmul -> hipBLASLt, plain bf16 output) on the dominant GEMM's
+    shape, next to the library's own call of that GEMM (with its fused epilogue), on the same GPU: context for
+    the roofline fraction, not part of the timed step."""
+    import torch
+    g = torch.Generator(device="cuda").manual_seed(11)
+    a = ((torch.rand(M, K, device="cuda", generator=g) - 0.5) * 0.07).to(torch.bfloat16)
+    b = ((torch.rand(N, K, device="cuda", generator=g) - 0.5) * 0.07).to(torch.bfloat16)
+    bt = b.t()
+    for _ in range(3):
+        c = a @ bt
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        c = a @ bt
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del a, b, bt, c
+    torch.cuda.empty_cache()
+    tf = 2.0 * M * N * K / (ms / 1e3) / 1e12
+    return {"library": "hipBLASLt (torch.matmul, bf16 in and out, no epilogue)", "M": M, "N": N, "K": K,
+            "ms": round(ms, 4), "tflops": round(tf, 1), "frac_of_bf16_peak": round(tf / MI355X_BF16_DENSE_TFLOPS, 4),
+            "ours_ms_with_epilogue": round(ours_ms, 4), "ours_vs_vendor_time": round(ours_ms / ms, 4)}
 
 
 def measure_decode(model, cache, w, batch, extra, logits, stream, args):
@@ -280,6 +307,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-mfma-probe", action="store_true",
                     help="skip the pure-MFMA throughput probe (random and constant operands)")
+    ap.add_argument("--no-vendor-gemm", action="store_true",
+                    help="skip timing the vendor library's GEMM on the dominant GEMM's shape")
     ap.add_argument("--no-full-depth", action="store_true",
                     help="skip timing the same batch through all layers (l = L) with the same kernels")
     ap.add_argument("--no-decode", action="store_true",
@@ -396,6 +425,9 @@ def main():
                      "avg_launch_ms": round(avg_launch_ms, 4), "launches": prof["launches"],
                      "flops_per_launch": flops_per_launch},
     }
+    if not args.no_vendor_gemm and w.dtype == "bf16" and dom_name == "gemm_gateup":
+        res["vendor_gemm"] = vendor_gemm(T, 2 * w.shape.ffn_dim, w.shape.d_model, avg_launch_ms)
+        log(f"[bench] vendor GEMM: {res['vendor_gemm']}")
     if not args.no_decode and w.dtype == "bf16":
         runner.prefill(model, cache, db, logits, stream)
         res["decode_step"] = measure_decode(model, cache, w, batch, extra, logits, stream, args)
