@@ -283,6 +283,20 @@ def test_small_model_long_context():
     compare(w, batch, logits, cache, ores, [0, 1], tol=TOL, label=w.name)
 
 
+def test_attention_forms_either_side_of_the_short_prompt_threshold():
+    """Prompt attention has a 4-wave form for batches whose sequences bring at most 2048 new tokens and the
+    8-wave form above that: a batch at the threshold (2048 and 700 tokens) and one just past it (2049 and
+    700), each against the oracle, every KV slot and the logits, on the 3-layer model with 128-dim heads."""
+    for lengths in ((2048, 700), (2049, 700)):
+        w = si.small_workload(f"attn_forms_{lengths[0]}", n_layers=3, d_model=512, n_q_heads=8, n_kv_heads=2,
+                              head_dim=128, ffn_dim=512, vocab=1024, l=2, g=1, lengths=lengths, seed=41,
+                              weight_seed=141)
+        batch = si.make_batch(w)
+        model, cache, db, logits = run_gpu(w, batch)
+        ores = O.swiftkv_prefill(dims_of(w.shape), oracle_weights(w), batch.tokens, w.swiftkv_l, w.acrosskv_g)
+        compare(w, batch, logits, cache, ores, [0, 1], tol=TOL, label=w.name)
+
+
 def test_midsize_split_tail_gemms():
     """d_model 4096 over 5000 tokens: the O, gate/up and down GEMMs have 320 tiles on 256 CUs, so their
     last wave runs as K-split partial tiles plus the fixed-order reduction."""
