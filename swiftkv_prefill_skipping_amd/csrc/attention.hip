@@ -725,7 +725,12 @@ __global__ __launch_bounds__(256) void attn_dec_kernel(const bf16_t* __restrict_
                                                        const int32_t* __restrict__ bt, int max_blocks, int hq,
                                                        int nchunks, float scale, float* __restrict__ ws) {
   constexpr int DH = 128;
-  __shared__ f32x4_t ps_s[4][DC_KEYS];  // [wave][key] -> probabilities of the wave's four heads
+  // [wave][key] -> probabilities of the wave's four heads.  Key k of 16-key
+  // block b sits at b * 17 + k: the P.V reads have the four 16-lane groups
+  // of a wave read one entry of each block at once, and with blocks 256 B
+  // apart those four 16-byte reads fell on the same banks (3.2 conflict
+  // cycles per LDS instruction on the counter)
+  __shared__ f32x4_t ps_s[4][4 * 17];
   const int r = blockIdx.x, g = blockIdx.y;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int c = blockIdx.z * 4 + wave;
@@ -875,7 +880,7 @@ __global__ __launch_bounds__(256) void attn_dec_kernel(const bf16_t* __restrict_
     }
     if (j == 0) {
 #pragma unroll
-      for (int p = 0; p < 4; ++p) ps_s[wave][p * 16 + kq] = pe[p];
+      for (int p = 0; p < 4; ++p) ps_s[wave][p * 17 + kq] = pe[p];
     }
     if constexpr (F8) {  // each key's 8 codes times its scale, as bf16 pairs
 #pragma unroll
@@ -897,7 +902,7 @@ __global__ __launch_bounds__(256) void attn_dec_kernel(const bf16_t* __restrict_
       for (int e = 0; e < 8; ++e) o[hh][e] = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const f32x4_t pk = ps_s[wave][vb * 16 + i];  // zero past the context
+      const f32x4_t pk = ps_s[wave][vb * 17 + i];  // zero past the context
       const bool live = vb * 16 + i < nk;
       const u32x4_t raw = __builtin_bit_cast(u32x4_t, vv[i]);
 #pragma unroll
