@@ -194,7 +194,9 @@ def measure_chunked(model, cache, w, batch, stream, args, ms_one_shot, swift_flo
         live = [b for b in range(B) if ctx[b] < batch.lengths[b]]
         ns = [int(min(chunk, batch.lengths[b] - ctx[b])) for b in live]
         toks = np.concatenate([batch.tokens[b][ctx[b]:ctx[b] + n] for b, n in zip(live, ns)])
-        calls.append(runner.device_step(toks, ns, ctx[live], batch.block_tables[live]))
+        # logits only where the chunk ends its prompt: a call of unfinished chunks alone stops after layer l
+        need = [int(ctx[b] + n == batch.lengths[b]) for b, n in zip(live, ns)]
+        calls.append(runner.device_step(toks, ns, ctx[live], batch.block_tables[live], need))
         ctx[live] += ns
     lgc = [torch.empty((c.struct.tokens.batch, w.shape.vocab), dtype=torch.float32, device="cuda") for c in calls]
 

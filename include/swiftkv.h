@@ -204,6 +204,10 @@ typedef struct {
   skv_batch tokens;
   const int32_t* ctx_lens_host; /* host   [batch] */
   const int32_t* ctx_lens;      /* device [batch], same values */
+  /* host [batch] or NULL (= every entry nonzero): nonzero where the call is
+   * to produce sequence b's next-token logits (a decode token, a prompt's
+   * final chunk); 0 for a prompt chunk that more chunks follow. */
+  const int32_t* need_logits_host;
 } skv_step_batch;
 
 /* One forward pass over a mixed batch of prompt chunks and decode tokens
@@ -219,6 +223,10 @@ typedef struct {
  *  4. logits[b, :] = RMSNorm(y_b; final gain) W_lm^T, the next-token logits
  *     after that token (a decode token's, a final prompt chunk's first
  *     generated token; a caller ignores the row of an unfinished chunk).
+ * When need_logits_host marks no sequence, steps 3 and 4 are skipped: only
+ * a prompt's last token runs the layers past l, and a chunk that more
+ * chunks follow does not hold it; the call then writes no logits and
+ * `logits` may be NULL.  Otherwise every row is computed as above.
  * A decode token is a sequence with one new token.  Splitting a prompt into
  * chunks fed one call after another yields the cache and final logits of
  * skv_prefill over the whole prompt.  Same asynchrony, ownership and errors

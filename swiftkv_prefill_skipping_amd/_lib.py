@@ -45,7 +45,8 @@ class skv_batch(Structure):
 
 
 class skv_step_batch(Structure):
-    _fields_ = [("tokens", skv_batch), ("ctx_lens_host", c_void_p), ("ctx_lens", c_void_p)]
+    _fields_ = [("tokens", skv_batch), ("ctx_lens_host", c_void_p), ("ctx_lens", c_void_p),
+                ("need_logits_host", c_void_p)]
 
 
 EXPORTED = ["skv_model_create", "skv_model_load_globals", "skv_model_load_layer", "skv_model_destroy",

@@ -840,6 +840,7 @@ struct StepInfo {
   int max_total = 0;                 // longest cached + new
   double attn_flops = 0;             // 4 * keys * dh * hq summed over the new tokens
   double ctx_tokens = 0;             // keys attended by the last tokens, summed
+  bool need_last = true;             // some sequence needs its next-token logits
 };
 
 template <typename T>
@@ -1119,7 +1120,10 @@ skv_status run_step(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, const S
     if (kv8) SKV_TRY(quantize(T_, m->G, l));
   }
 
-  // ---- last new token of each sequence through layers l+1..L, then the LM head
+  // ---- last new token of each sequence through layers l+1..L, then the LM
+  // head (only a prompt's last token goes past layer l: a call of unfinished
+  // chunks alone stops here)
+  if (!si.need_last) return SKV_OK;
   Prof plast(pm, SKV_K_LAST_TOKEN, s, last_flops, last_bytes);
   if constexpr (kBf16)
     SKV_HIP(launch_rows_act_ss(w.x, w.last_row, gain_before(l + 1), B, d, w.y, (bf16_t*)ya, w.rss, s));
@@ -1152,8 +1156,16 @@ namespace {
 // Shared argument checks of skv_prefill / skv_step / skv_step_noalloc;
 // ctx_host NULL = no cached positions.  Fills si on success.
 skv_status check_batch(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, const int32_t* ctx_host,
-                       const int32_t* ctx_dev, float* logits, StepInfo& si) {
-  if (!m || !kc || !bt || !logits) return fail(SKV_ERR_INVALID_ARG, "NULL argument");
+                       const int32_t* ctx_dev, float* logits, StepInfo& si, const int32_t* need_host = nullptr) {
+  if (!m || !kc || !bt) return fail(SKV_ERR_INVALID_ARG, "NULL argument");
+  bool need_last = true;
+  if (need_host) {
+    if (bt->batch < 1 || bt->batch > m->cfg.max_batch)
+      return fail(SKV_ERR_INVALID_ARG, "batch must lie in 1..max_batch");
+    need_last = false;
+    for (int b = 0; b < bt->batch; ++b) need_last = need_last || need_host[b] != 0;
+  }
+  if (need_last && !logits) return fail(SKV_ERR_INVALID_ARG, "NULL argument");
   if (kc->m != m) return fail(SKV_ERR_INVALID_ARG, "cache was created for another model");
   const auto& c = m->cfg;
   if (!m->globals_loaded) return fail(SKV_ERR_INVALID_ARG, "embedding / LM head not loaded");
@@ -1172,6 +1184,7 @@ skv_status check_batch(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, cons
   const double dh = c.head_dim, hq = c.n_q_heads;
   si = StepInfo{};
   si.ctx_dev = ctx_dev;
+  si.need_last = need_last;
   for (int b = 0; b < B; ++b) {
     const int n = cu[b + 1] - cu[b];
     const int cx = ctx_host ? ctx_host[b] : 0;
@@ -1196,9 +1209,9 @@ skv_status check_batch(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, cons
 }
 
 skv_status check_and_run(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, const int32_t* ctx_host,
-                         const int32_t* ctx_dev, float* logits, void* stream) {
+                         const int32_t* ctx_dev, float* logits, void* stream, const int32_t* need_host = nullptr) {
   StepInfo si;
-  SKV_TRY(check_batch(m, kc, bt, ctx_host, ctx_dev, logits, si));
+  SKV_TRY(check_batch(m, kc, bt, ctx_host, ctx_dev, logits, si, need_host));
   hipStream_t s = (hipStream_t)stream;
   const Work w = model_work(m);
   if (m->bf16) return run_step<bf16_t>(m, kc, bt, si, logits, s, w);
@@ -1217,7 +1230,7 @@ extern "C" skv_status skv_step(skv_model* m, skv_kv_cache* kc, const skv_step_ba
   if (!sb) return fail(SKV_ERR_INVALID_ARG, "NULL argument");
   if (!sb->ctx_lens_host != !sb->ctx_lens)
     return fail(SKV_ERR_INVALID_ARG, "ctx_lens_host and ctx_lens must both be set or both be NULL");
-  return check_and_run(m, kc, &sb->tokens, sb->ctx_lens_host, sb->ctx_lens, logits, stream);
+  return check_and_run(m, kc, &sb->tokens, sb->ctx_lens_host, sb->ctx_lens, logits, stream, sb->need_logits_host);
 }
 
 extern "C" skv_status skv_step_noalloc(skv_model* m, skv_kv_cache* kc, const skv_step_batch* sb, float* logits,
@@ -1226,7 +1239,7 @@ extern "C" skv_status skv_step_noalloc(skv_model* m, skv_kv_cache* kc, const skv
   if (!sb->ctx_lens_host != !sb->ctx_lens)
     return fail(SKV_ERR_INVALID_ARG, "ctx_lens_host and ctx_lens must both be set or both be NULL");
   StepInfo si;
-  SKV_TRY(check_batch(m, kc, &sb->tokens, sb->ctx_lens_host, sb->ctx_lens, logits, si));
+  SKV_TRY(check_batch(m, kc, &sb->tokens, sb->ctx_lens_host, sb->ctx_lens, logits, si, sb->need_logits_host));
   if (!m->bf16) return fail(SKV_ERR_UNSUPPORTED, "skv_step_noalloc needs a bf16 model");
   if (kc->fp8) return fail(SKV_ERR_UNSUPPORTED, "skv_step_noalloc does not take an FP8 cache");
   const skv_batch* bt = &sb->tokens;

@@ -205,11 +205,14 @@ class DeviceStep:
     ctx_dev: object
     ctx_host: np.ndarray
     struct: L.skv_step_batch
+    need_host: object = None
 
 
-def device_step(token_ids, new_lens, ctx_lens, block_tables) -> DeviceStep:
+def device_step(token_ids, new_lens, ctx_lens, block_tables, need_logits=None) -> DeviceStep:
     """Device copies of a step batch: sequence b brings new_lens[b] of the
-    packed token_ids after ctx_lens[b] cached positions; block_tables [B, m]."""
+    packed token_ids after ctx_lens[b] cached positions; block_tables [B, m].
+    need_logits (optional, [B]): 0 for a prompt chunk that more chunks follow;
+    a call with no nonzero entry writes no logits."""
     torch = _torch()
     new_lens = np.asarray(new_lens, dtype=np.int32)
     cu = np.zeros(len(new_lens) + 1, dtype=np.int32)
@@ -223,8 +226,9 @@ def device_step(token_ids, new_lens, ctx_lens, block_tables) -> DeviceStep:
     inner = L.skv_batch(len(new_lens), int(cu[-1]), int(new_lens.max()), bt.shape[1], cu.ctypes.data, bt.ctypes.data,
                         tok.data_ptr(), cu_d.data_ptr(), bt_d.data_ptr())
     db = DeviceBatch(None, tok, cu_d, bt_d, cu, bt, inner)
-    st = L.skv_step_batch(inner, ctx.ctypes.data, ctx_d.data_ptr())
-    return DeviceStep(db, ctx_d, ctx, st)
+    need = None if need_logits is None else np.ascontiguousarray(need_logits, dtype=np.int32)
+    st = L.skv_step_batch(inner, ctx.ctypes.data, ctx_d.data_ptr(), need.ctypes.data if need is not None else None)
+    return DeviceStep(db, ctx_d, ctx, st, need)
 
 
 def step(model: Model, cache: Cache, ds: DeviceStep, logits=None, stream=None):

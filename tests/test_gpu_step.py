@@ -181,3 +181,69 @@ def test_step_host_side_errors():
         L.skv_step(model.handle, cache.handle, half, logits.data_ptr(), 0)
     call([3, 3])                               # a good call still works
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("l,g,kv_fp8", [(2, 2, False), (1, 1, True)])
+def test_unfinished_chunks_skip_the_deep_layers(l, g, kv_fp8):
+    """A call whose sequences are all prompt chunks that more chunks follow (need_logits_host all 0) stops
+    after layer l and writes no logits: only a prompt's last token runs the layers past l.  The same chunk
+    schedule with and without the marks leaves a bitwise-identical cache and bitwise-identical logits in
+    the calls that end prompts, and the all-unfinished call leaves its logits buffer untouched."""
+    import torch
+    from swiftkv_prefill_skipping_amd import runner
+    from tests.test_gpu_parity import gpu_kv
+    lengths = (300, 170, 150)  # chunks of 100: the first call ends no prompt
+    w = si.small_workload(f"unfinished_l{l}_g{g}", l=l, g=g, lengths=lengths, seed=61)
+    batch = si.make_batch(w, shuffle=True)
+    chunk = 100
+    model = runner.load_seeded_model(w, chunk * len(lengths), len(lengths), max(lengths), kv_fp8=kv_fp8)
+    caches, ended = [], []
+    skipped = 0
+    for marked in (False, True):
+        cache = runner.Cache(model, batch.num_blocks)
+        ctx = np.zeros(len(lengths), dtype=np.int64)
+        rows = {}
+        while (ctx < batch.lengths).any():
+            live = [b for b in range(len(lengths)) if ctx[b] < batch.lengths[b]]
+            ns = [int(min(chunk, batch.lengths[b] - ctx[b])) for b in live]
+            toks = np.concatenate([batch.tokens[b][ctx[b]:ctx[b] + n] for b, n in zip(live, ns)])
+            ends = [int(ctx[b] + n == batch.lengths[b]) for b, n in zip(live, ns)]
+            ds = runner.device_step(toks, ns, ctx[live], batch.block_tables[live], ends if marked else None)
+            lg = torch.full((len(live), w.shape.vocab), 7.0, dtype=torch.float32, device="cuda")
+            runner.step(model, cache, ds, lg)
+            torch.cuda.synchronize()
+            if marked and not any(ends):
+                skipped += 1
+                assert bool((lg == 7.0).all()), "a call of unfinished chunks wrote logits"
+            for i, (b, e) in enumerate(zip(live, ends)):
+                if e:
+                    rows[b] = lg[i].clone()
+            ctx[live] += ns
+        caches.append(cache)
+        ended.append(rows)
+    assert skipped == 1
+    _say(f"[case] unfinished chunks l={l} g={g} fp8={kv_fp8}")
+    for b in range(len(lengths)):
+        assert torch.equal(ended[0][b], ended[1][b]), b
+        k0 = gpu_kv(caches[0], w, batch, b)
+        k1 = gpu_kv(caches[1], w, batch, b)
+        for s_ in k0:
+            assert np.array_equal(k0[s_][0], k1[s_][0]) and np.array_equal(k0[s_][1], k1[s_][1]), (b, s_)
+
+
+def test_need_logits_host_rules():
+    """Some sequence needing logits with a NULL logits pointer is an argument error, checked before any work."""
+    import torch
+    from swiftkv_prefill_skipping_amd import _lib as L, runner
+    w = si.small_workload("need_rules", l=1, g=1, lengths=(40, 20), seed=67)
+    batch = si.make_batch(w)
+    model = runner.load_seeded_model(w, 64, 2, 48)
+    cache = runner.Cache(model, batch.num_blocks)
+    toks = np.zeros(2, dtype=np.int32)
+    ds = runner.device_step(toks, [1, 1], [3, 3], batch.block_tables, [0, 1])
+    with pytest.raises(L.SkvError) as e:
+        L.skv_step(model.handle, cache.handle, ds.struct, 0, 0)
+    assert e.value.status == L.SKV_ERR_INVALID_ARG
+    ds0 = runner.device_step(toks, [1, 1], [3, 3], batch.block_tables, [0, 0])
+    L.skv_step(model.handle, cache.handle, ds0.struct, 0, 0)
+    torch.cuda.synchronize()
