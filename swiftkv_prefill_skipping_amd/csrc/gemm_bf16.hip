@@ -379,10 +379,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(const bf16_t* __
 #pragma unroll
     for (int i = 4; i < 8; ++i) read_a(cur, i);
     if (load_b) gload_part((s + NBUF - 1) % NBUF, s + NBUF - 1, LH / 2, LH);
+    // A fragment outer: eight MFMAs in a row share their second operand
+    // (measured 0.3-1.2 % faster per call than B outer, 4 alternating runs
+    // on one box, on every shape of the step)
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) mfma(P, i, j);
+      for (int j = 0; j < 8; ++j) mfma(P, i, j);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
@@ -415,9 +418,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(const bf16_t* __
     }
     if (load_a) gload_part(cur, s + NBUF, 0, LH / 2);
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
+    for (int i = 4; i < 8; ++i)
 #pragma unroll
-      for (int i = 4; i < 8; ++i) mfma(P, i, j);
+      for (int j = 0; j < 8; ++j) mfma(P, i, j);
     if (next) {
 #pragma unroll
       for (int g = 0; g < 12; ++g) {
