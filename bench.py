@@ -243,7 +243,7 @@ def measure_fp8(w, batch, db, logits, stream, args, extra, ms_bf16, dec_bf16):
 DOMINANT = {"llama8b_l16_b16": "gemm_gateup", "llama8b_l24_g4_b32": "gemm_gateup", "llama70b_l40_b32": "gemm_gateup",
             "llama8b_l16_long32k": "attn_prefill", "tiny_fp32_l2": "gemm_gateup"}
 KERNEL_TEXT = {"gemm_gateup": "gemm_gateup (bf16 MFMA GEMM + SwiGLU epilogue)",
-               "attn_prefill": "attn_prefill8 (causal GQA flash attention, bf16 MFMA)"}
+               "attn_prefill": "attn_prefill8 (causal GQA flash attention, bf16 MFMA; plain form: every layer but layer 1)"}
 
 
 def measure_workload(name, steps, warmup, stream):
@@ -283,9 +283,26 @@ def measure_workload(name, steps, warmup, stream):
     fpl = prof["flops"] / max(prof["launches"], 1)
     ach = fpl / (avg / 1e3) / 1e12
     log(f"[bench] {name}: {ms:.2f} ms/step, {T / t:.0f} tokens/s; {dom} {ach:.0f} TFLOP/s")
+    split_form = None
+    if dom == "attn_prefill" and model.cfg.dtype == L.SKV_BF16:
+        # layer 1's split-bf16 attention is its own kernel instance (three products per block, same
+        # algorithmic FLOPs): timed apart, over one more step, so the roofline above covers the plain form only
+        cls = L.KERNEL_CLASS_NAMES.index("attn_prefill_split")
+        L.skv_profile_enable(model.handle, cls, True)
+        runner.prefill(model, cache, db, logits, stream)
+        torch.cuda.synchronize()
+        sp = L.skv_profile_read(model.handle)
+        L.skv_profile_enable(model.handle, cls, False)
+        if sp["launches"]:
+            sms = sp["total_ms"] / sp["launches"]
+            split_form = {"kernel": "attn_prefill8, split-bf16 form (layer 1)", "launches": sp["launches"],
+                          "avg_launch_ms": round(sms, 4),
+                          "algorithmic_tflops": round(sp["flops"] / sp["launches"] / (sms / 1e3) / 1e12, 2),
+                          "time_vs_plain_form": round(sms / avg, 3)}
+            log(f"[bench] {name}: split-form attention {sms:.3f} ms per launch ({sms / avg:.2f}x the plain form)")
     cache.close()
     model.close()
-    return {"workload": name, "prompts": B, "prompt_tokens": T, "swiftkv_l": w.swiftkv_l, "acrosskv_g": w.acrosskv_g,
+    out = {"workload": name, "prompts": B, "prompt_tokens": T, "swiftkv_l": w.swiftkv_l, "acrosskv_g": w.acrosskv_g,
             "steps": steps, "warmup": warmup, "ms_per_step": round(ms, 3), "tokens_per_s": round(T / t, 1),
             "normalized_tflops": round(full / t / 1e12, 2), "actual_tflops": round(swift / t / 1e12, 2),
             "normalized_frac_of_bf16_peak": round(full / t / 1e12 / MI355X_BF16_DENSE_TFLOPS, 4),
@@ -296,6 +313,9 @@ def measure_workload(name, steps, warmup, stream):
                          "frac": round(ach / MI355X_BF16_DENSE_TFLOPS, 4), "traffic": None,
                          "avg_launch_ms": round(avg, 4), "launches": prof["launches"], "flops_per_launch": fpl,
                          "algorithmic_bytes_per_launch": prof["bytes"] / max(prof["launches"], 1)}}
+    if split_form is not None:
+        out["roofline"]["split_form"] = split_form
+    return out
 
 
 def main():

@@ -266,7 +266,11 @@ skv_status skv_step_noalloc(skv_model* m, skv_kv_cache* c, const skv_step_batch*
 skv_status skv_flops(const skv_model_config* cfg, const int32_t* seqlens, int32_t batch, double* full,
                      double* swiftkv);
 
-/* Kernel classes that skv_profile_* can time. */
+/* Kernel classes that skv_profile_* can time.  SKV_K_ATTN_PREFILL is the
+ * prompt-token attention of every layer that runs it in plain form;
+ * SKV_K_ATTN_PREFILL_SPLIT is layer 1's attention in split-bf16 form (bf16
+ * models, bf16 cache), which issues three products per score and per
+ * output block, so its rate is kept apart. */
 typedef enum {
   SKV_K_GEMM_QKV = 0,
   SKV_K_ATTN_PREFILL = 1,
@@ -276,7 +280,8 @@ typedef enum {
   SKV_K_GEMM_KVSKIP = 5,
   SKV_K_RMSNORM = 6,
   SKV_K_LAST_TOKEN = 7,
-  SKV_K_NUM = 8
+  SKV_K_ATTN_PREFILL_SPLIT = 8,
+  SKV_K_NUM = 9
 } skv_kernel_class;
 
 /* Bracket every launch of one kernel class with HIP events on the prefill

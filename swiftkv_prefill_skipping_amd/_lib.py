@@ -16,9 +16,9 @@ SKV_OK, SKV_ERR_INVALID_ARG, SKV_ERR_OOM, SKV_ERR_HIP, SKV_ERR_UNSUPPORTED = 0, 
 SKV_BF16, SKV_FP32, SKV_FP8_E4M3 = 0, 1, 2
 SKV_KV_MODEL, SKV_KV_FP8 = 0, 1
 (SKV_K_GEMM_QKV, SKV_K_ATTN_PREFILL, SKV_K_GEMM_O, SKV_K_GEMM_GATEUP, SKV_K_GEMM_DOWN, SKV_K_GEMM_KVSKIP,
- SKV_K_RMSNORM, SKV_K_LAST_TOKEN) = range(8)
+ SKV_K_RMSNORM, SKV_K_LAST_TOKEN, SKV_K_ATTN_PREFILL_SPLIT) = range(9)
 KERNEL_CLASS_NAMES = ["gemm_qkv", "attn_prefill", "gemm_o", "gemm_gateup", "gemm_down", "gemm_kvskip", "rmsnorm",
-                      "last_token"]
+                      "last_token", "attn_prefill_split"]
 
 
 class skv_model_config(Structure):

@@ -1027,7 +1027,7 @@ skv_status run_step(skv_model* m, skv_kv_cache* kc, const skv_batch* bt, const S
     }
     if (kv8) SKV_TRY(quantize(T_, 1, i - 1));
     {
-      Prof p(pm, SKV_K_ATTN_PREFILL, s, si.attn_flops, attn_bytes);
+      Prof p(pm, split_attn ? SKV_K_ATTN_PREFILL_SPLIT : SKV_K_ATTN_PREFILL, s, si.attn_flops, attn_bytes);
       if (kv8) {
         if constexpr (kBf16)
           SKV_HIP(launch_attn_prefill_fp8((const bf16_t*)qbuf, slot8_of(i - 1), bt->cu_seqlens, si.ctx_dev,

@@ -18,7 +18,7 @@
 //    The score accumulator holds, in lane half h and element e of 16-key
 //    step kk, key kk*16 + 8*(e/4) + 4*h + e%4; the V^T reads gather the same
 //    keys, so both operands agree.  K and V tiles share one LDS layout
-//    ([64 keys][128 dims], 16-byte chunk c of key row r at c ^ (r & 15)).
+//    ([64 keys][128 dims], 16-byte chunk c of key row r at c ^ kv_swz(r)).
 //    O^T is transposed through LDS at the end and written 8 bytes per lane
 //    into the panel layout of the O projection's A operand.
 //    K/V tiles move global -> LDS directly (global_load_lds_dwordx4) into
@@ -331,7 +331,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         p[e] = __builtin_amdgcn_exp2f(fmaf(sacc[st][vb8 + e], scale_log2, mneg));
-        ls += p[e];
+        if constexpr (SPLIT) ls += p[e];
       }
       pf[kk] = as_bf16x8(u32x4_t{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
                                  pack_bf16x2(p[6], p[7])});
@@ -342,6 +342,23 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         pf_lo[kk] = as_bf16x8(u32x4_t{pack_bf16x2(pl[0], pl[1]), pack_bf16x2(pl[2], pl[3]), pack_bf16x2(pl[4], pl[5]),
                                       pack_bf16x2(pl[6], pl[7])});
       }
+    }
+    if constexpr (!SPLIT) {
+      // The row sum of the bf16 probabilities the P.V products use, two per
+      // v_dot2_f32_bf16 against (1, 1): half the vector instructions of a
+      // sum over the fp32 values, and the normaliser then matches the
+      // weights exactly.  Two chains keep the dependent adds apart.
+      const bf16x2_t one2 = {(__bf16)1.0f, (__bf16)1.0f};
+      float l2[2] = {0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const bf16x8_t v = pf[kk];
+        l2[0] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1), one2, l2[0], false);
+        l2[1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3), one2, l2[1], false);
+        l2[0] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), one2, l2[0], false);
+        l2[1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), one2, l2[1], false);
+      }
+      ls = l2[0] + l2[1];
     }
     ls = xor32_sum(ls);
     l_run += ls;
