@@ -226,18 +226,30 @@ struct EpiSwiGLUPanel {
     store8(h + panel_off(row, oc, F), y);
   }
   // The GEMM hands this epilogue its gate/up pairs straight from the
-  // accumulator registers (a lane holds four consecutive gate columns of a
-  // row and their up partners 64 columns on), without staging them in LDS.
+  // accumulator registers, without staging them in LDS: lane group rg =
+  // lane / 16 holds gate columns col + 4 rg .. +4 of two adjacent 16-column
+  // blocks (g0 / g1, col and col + 16) of one row, and their up partners 64
+  // columns on.  One permlane16 swap per packed dword trades values between
+  // the groups of a pair (0 <-> 1, 2 <-> 3; both lanes hold the same row), so
+  // group rg ends with eight consecutive outputs of block rg & 1, from
+  // column 8 (rg >> 1) of it: one 16-byte store per lane instead of two of
+  // 8 bytes, and each store instruction covers whole 64-byte panel rows.
   static constexpr bool kFromRegisters = true;
-  SKV_DEV void vec4s(int row, int col, const float* g, const float* u, float sr) const {
-    const int oc = (col >> 7) * P + (col & (2 * P - 1));
+  SKV_DEV void vec4x2s(int row, int col, const float* g0, const float* u0, const float* g1, const float* u1, float sr,
+                       int rg) const {
     const float ce = sr * -1.4426950408889634f;
     const float s2 = sr * sr;
-    float y[4];
+    float y0[4], y1[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      y[e] = (g[e] * u[e]) * (s2 * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g[e] * ce)));
-    *reinterpret_cast<u32x2_t*>(h + panel_off(row, oc, F)) = u32x2_t{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+    for (int e = 0; e < 4; ++e) {
+      y0[e] = (g0[e] * u0[e]) * (s2 * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g0[e] * ce)));
+      y1[e] = (g1[e] * u1[e]) * (s2 * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g1[e] * ce)));
+    }
+    const auto a = __builtin_amdgcn_permlane16_swap(pack_bf16x2(y0[0], y0[1]), pack_bf16x2(y1[0], y1[1]), false, false);
+    const auto b = __builtin_amdgcn_permlane16_swap(pack_bf16x2(y0[2], y0[3]), pack_bf16x2(y1[2], y1[3]), false, false);
+    const int c = col + (rg & 1) * 16 + (rg >> 1) * 8;
+    const int oc = (c >> 7) * P + (c & (2 * P - 1));
+    *reinterpret_cast<u32x4_t*>(h + panel_off(row, oc, F)) = u32x4_t{a[0], b[0], a[1], b[1]};
   }
 };
 

@@ -198,7 +198,7 @@ struct EpiAhead<EpiResidual> {
 };
 
 // Epilogues with kFromRegisters take their column pairs straight from the
-// accumulators (vec4s) instead of through the LDS staging.
+// accumulators (vec4x2s) instead of through the LDS staging.
 template <class Epi, class = void>
 struct FromRegisters {
   static constexpr bool value = false;
@@ -464,13 +464,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(const bf16_t* __
 
   // Epilogues that take their pairs from registers (SwiGLU: a lane's gate
   // columns j*16 + 4*(lane/16) + v and their up partners sit in acc[i][j]
-  // and acc[i][j+4] for j < 4) skip the LDS staging; each call writes four
-  // consecutive bf16 of a row.
+  // and acc[i][j+4] for j < 4) skip the LDS staging; each call takes two
+  // adjacent column blocks of a row block.  The row bound is the same for
+  // lanes l and l + 16, which the call's lane exchange pairs.
   if constexpr (FromRegisters<Epi>::value && !SPLIT) {
     {
       if (!cols_ok) return;
       const int row0 = m0 + wm * 128 + (lane & 15);
-      const int col0 = n0 + wn * 128 + 4 * (lane >> 4);
+      const int col0 = n0 + wn * 128;
+      const int rg = lane >> 4;
       float sr[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) sr[i] = row0 + i * 16 < M ? epi.scale(row0 + i * 16) : 0.f;
@@ -478,10 +480,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(const bf16_t* __
       for (int i = 0; i < 8; ++i) {
         if (row0 + i * 16 < M) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float gv[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
-            const float uv[4] = {acc[i][j + 4][0], acc[i][j + 4][1], acc[i][j + 4][2], acc[i][j + 4][3]};
-            epi.vec4s(row0 + i * 16, col0 + j * 16, gv, uv, sr[i]);
+          for (int j = 0; j < 4; j += 2) {
+            const float g0[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+            const float u0[4] = {acc[i][j + 4][0], acc[i][j + 4][1], acc[i][j + 4][2], acc[i][j + 4][3]};
+            const float g1[4] = {acc[i][j + 1][0], acc[i][j + 1][1], acc[i][j + 1][2], acc[i][j + 1][3]};
+            const float u1[4] = {acc[i][j + 5][0], acc[i][j + 5][1], acc[i][j + 5][2], acc[i][j + 5][3]};
+            epi.vec4x2s(row0 + i * 16, col0 + j * 16, g0, u0, g1, u1, sr[i], rg);
           }
         }
         // one row block at a time: bounds the values copied out of the
