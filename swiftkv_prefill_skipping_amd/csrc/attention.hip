@@ -964,6 +964,212 @@ __global__ __launch_bounds__(256) void attn_dec_kernel(const bf16_t* __restrict_
   }
 }
 
+// Single-pass form of attn_dec_kernel (bf16 cache) for contexts of at most
+// DC1_MAX_KEYS keys: one workgroup per (row, kv head), one wave per 64-key
+// chunk, so the chunks' (max, sum, o) meet in LDS and the workgroup writes
+// the normalised output itself: no workspace, no combine launch.  A wave's
+// chunk work is attn_dec_kernel's (the same loads and arithmetic), except
+// that the head group's q sits in LDS, read by every wave, rather than in
+// each wave's registers: a 16-wave workgroup leaves a wave 128 registers.
+// The chunks are combined in chunk order.
+constexpr int DC1_WAVES = 16;
+constexpr int DC1_MAX_KEYS = DC1_WAVES * DC_KEYS;
+constexpr int DC1_MAX_REP = 16;  // a multiple of RW_HG
+__global__ __launch_bounds__(DC1_WAVES * 64) void attn_dec1_kernel(const bf16_t* __restrict__ q,
+                                                                   CacheSlot<bf16_t> cache,
+                                                                   const int32_t* __restrict__ row_seq,
+                                                                   const int32_t* __restrict__ row_pos,
+                                                                   const int32_t* __restrict__ bt, int max_blocks,
+                                                                   int hq, float scale, bf16_t* __restrict__ out) {
+  constexpr int DH = 128;
+  __shared__ __attribute__((aligned(16))) bf16_t q_s[DC1_MAX_REP * DH];
+  __shared__ f32x4_t ps_s[DC1_WAVES][4 * 17];  // as in attn_dec_kernel
+  __shared__ float po_s[DC1_WAVES][RW_HG][DH];
+  __shared__ float pm_s[DC1_WAVES][RW_HG], pl_s[DC1_WAVES][RW_HG];
+  const int r = blockIdx.x, g = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int hkv = cache.hkv;
+  const int rep = hq / hkv;
+  const int ctx = row_pos[r] + 1;
+  const int seq = row_seq[r];
+  // at most DC1_WAVES chunks: the launcher checks the rows' longest context
+  const int nch = min((ctx + DC_KEYS - 1) / DC_KEYS, DC1_WAVES);
+  const bool active = wave < nch;
+  const int kbeg = wave * DC_KEYS;
+  const int nk = active ? min(DC_KEYS, ctx - kbeg) : 0;
+  const bf16_t* qg = q + ((int64_t)r * hq + g * rep) * DH;
+  // q of the group's heads into LDS; heads up to the next multiple of four
+  // are zero, so every wave reads four heads without a branch
+  const int rep4 = (rep + RW_HG - 1) / RW_HG * RW_HG;
+  for (int i = tid; i < rep4 * (DH / 8); i += DC1_WAVES * 64)
+    *reinterpret_cast<u32x4_t*>(q_s + i * 8) =
+        i < rep * (DH / 8) ? *reinterpret_cast<const u32x4_t*>(qg + i * 8) : u32x4_t{0u, 0u, 0u, 0u};
+  int blk[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+    blk[b] = active && kbeg + 16 * b < ctx ? bt[(int64_t)seq * max_blocks + kbeg / kBlockSize + b] : 0;
+  const int kq = lane >> 2, j = lane & 3;   // score layout
+  const int vb = lane >> 4, vc = lane & 15;  // P.V layout
+  const int vblk = vb == 0 ? blk[0] : vb == 1 ? blk[1] : vb == 2 ? blk[2] : blk[3];
+  __syncthreads();  // q in LDS
+  for (int h0 = 0; h0 < rep; h0 += RW_HG) {
+    const int nh = min(RW_HG, rep - h0);
+    if (active) {
+      // scores in two halves of two 16-key passes: K of a half (32
+      // registers) and q slice i of four heads (16 registers, from LDS) at a
+      // time, which keeps the wave within its 128 registers
+      float acc[4][RW_HG];
+#pragma unroll
+      for (int p = 0; p < 4; ++p)
+#pragma unroll
+        for (int hh = 0; hh < RW_HG; ++hh) acc[p][hh] = 0.f;
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        bf16x8_t kv[2][4];
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) {
+          const bf16_t* kr = cache.k + kv_index(blk[2 * half + pp] * kBlockSize + kq, g, j * 32, hkv, DH);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) kv[pp][i] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(kr + i * 8));
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          bf16x8_t qv[RW_HG];
+#pragma unroll
+          for (int hh = 0; hh < RW_HG; ++hh)
+            qv[hh] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(q_s + (h0 + hh) * DH + j * 32 + i * 8));
+#pragma unroll
+          for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+            for (int hh = 0; hh < RW_HG; ++hh) {
+              const bf16x8_t kx = kv[pp][i], qx = qv[hh];
+              float a = acc[2 * half + pp][hh];
+              a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(kx, kx, 0, 1), __builtin_shufflevector(qx, qx, 0, 1), a, false);
+              a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(kx, kx, 2, 3), __builtin_shufflevector(qx, qx, 2, 3), a, false);
+              a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(kx, kx, 4, 5), __builtin_shufflevector(qx, qx, 4, 5), a, false);
+              a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(kx, kx, 6, 7), __builtin_shufflevector(qx, qx, 6, 7), a, false);
+              acc[2 * half + pp][hh] = a;
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      float sc[4][RW_HG];
+#pragma unroll
+      for (int p = 0; p < 4; ++p)
+#pragma unroll
+        for (int hh = 0; hh < RW_HG; ++hh) {
+          float a = xor_add(acc[p][hh], 1, true);
+          a = xor_add(a, 2, true);
+          sc[p][hh] = p * 16 + kq < nk ? a * scale : -INFINITY;
+        }
+      // the first half of the lane's V rows goes out now (the second after
+      // the first's products: 32 registers of V at a time)
+      bf16x8_t vv[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        vv[i] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(cache.v + kv_index(vblk * kBlockSize + i, g, vc * 8, hkv, DH)));
+      float mh[RW_HG], lh[RW_HG];
+      f32x4_t pe[4];
+#pragma unroll
+      for (int hh = 0; hh < RW_HG; ++hh) {
+        float m = fmaxf(fmaxf(sc[0][hh], sc[1][hh]), fmaxf(sc[2][hh], sc[3][hh]));
+        m = fmaxf(m, dpp_f<0x141>(m));
+        m = fmaxf(m, dpp_f<0x128>(m));
+        {
+          auto t = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+          m = fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
+        }
+        m = xor32_max(m);
+        float l = 0.f;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const float e = sc[p][hh] == -INFINITY ? 0.f : __expf(sc[p][hh] - m);
+          l += e;
+          pe[p][hh] = e;
+        }
+        l = xor_add(l, 4, true);
+        l = xor_add(l, 8, true);
+        l = xor_add(l, 16, true);
+        l = xor_add(l, 32, true);
+        mh[hh] = m;
+        lh[hh] = l;
+      }
+      if (j == 0) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) ps_s[wave][p * 17 + kq] = pe[p];
+      }
+      if (lane < RW_HG) {  // the chunk's statistics, from lanes 0..3
+        pm_s[wave][lane] = lane == 0 ? mh[0] : lane == 1 ? mh[1] : lane == 2 ? mh[2] : mh[3];
+        pl_s[wave][lane] = lane == 0 ? lh[0] : lane == 1 ? lh[1] : lane == 2 ? lh[2] : lh[3];
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's probabilities are in LDS
+      float o[RW_HG][8];
+#pragma unroll
+      for (int hh = 0; hh < RW_HG; ++hh)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[hh][e] = 0.f;
+#pragma unroll
+      for (int vh = 0; vh < 2; ++vh) {
+        if (vh == 1) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            vv[i] = as_bf16x8(
+                *reinterpret_cast<const u32x4_t*>(cache.v + kv_index(vblk * kBlockSize + 8 + i, g, vc * 8, hkv, DH)));
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int key = vh * 8 + i;
+          const f32x4_t pk = ps_s[wave][vb * 17 + key];
+          const bool live = vb * 16 + key < nk;
+          const u32x4_t raw = __builtin_bit_cast(u32x4_t, vv[i]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t w2 = live ? raw[e] : 0u;
+            const float v0 = __uint_as_float(w2 << 16), v1 = __uint_as_float(w2 & 0xffff0000u);
+#pragma unroll
+            for (int hh = 0; hh < RW_HG; ++hh) {
+              o[hh][2 * e] = fmaf(pk[hh], v0, o[hh][2 * e]);
+              o[hh][2 * e + 1] = fmaf(pk[hh], v1, o[hh][2 * e + 1]);
+            }
+          }
+        }
+      }
+      float t2[2][8], u[8];
+#pragma unroll
+      for (int hp = 0; hp < 2; ++hp)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(o[hp][e]), __float_as_uint(o[hp + 2][e]), false, false);
+          t2[hp][e] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+        }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(t2[0][e]), __float_as_uint(t2[1][e]), false, false);
+        u[e] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+      }
+      // head vb's partial sums, dims 8 vc .. + 8
+#pragma unroll
+      for (int e = 0; e < 8; e += 4)
+        *reinterpret_cast<f32x4_t*>(&po_s[wave][vb][vc * 8 + e]) = f32x4_t{u[e], u[e + 1], u[e + 2], u[e + 3]};
+    }
+    __syncthreads();  // every chunk's partials in LDS
+    if (tid < nh * DH) {
+      const int hh = tid / DH, d = tid % DH;
+      float M = -INFINITY;
+      for (int c = 0; c < nch; ++c) M = fmaxf(M, pm_s[c][hh]);
+      float L = 0.f, A = 0.f;
+      for (int c = 0; c < nch; ++c) {
+        const float e = __expf(pm_s[c][hh] - M);
+        L += pl_s[c][hh] * e;
+        A += po_s[c][hh][d] * e;
+      }
+      out[((int64_t)r * hq + g * rep + h0 + hh) * DH + d] = f32_to_bf16(A / L);
+    }
+    __syncthreads();  // partials read before the next head group overwrites them
+  }
+}
+
 // One (row, head): 4 chunk groups x head_dim threads.  Group q takes chunks
 // q, q+4, ... in order; the maximum, then the weighted sums, are combined
 // across the groups in group order (fixed, deterministic).  Four groups cut
@@ -1080,6 +1286,13 @@ hipError_t attn_rows_impl(const T* q, CacheSlot<T> cache, Fp8Slot c8, const int3
   if (rows <= 0) return hipSuccess;
   const float scale = 1.0f / sqrtf((float)cache.dh);
   if constexpr (sizeof(T) == 2) {
+    if constexpr (!F8) {
+      if (cache.dh == 128 && max_ctx <= DC1_MAX_KEYS && hq / cache.hkv <= DC1_MAX_REP) {
+        hipLaunchKernelGGL(attn_dec1_kernel, dim3(rows, cache.hkv), dim3(DC1_WAVES * 64), 0, stream, q, cache,
+                           row_seq, row_pos, block_tables, max_blocks, hq, scale, o);
+        return hipGetLastError();
+      }
+    }
     if (cache.dh == 128) {
       const int nch = (max_ctx + DC_KEYS - 1) / DC_KEYS;
       hipLaunchKernelGGL((attn_dec_kernel<F8>), dim3(rows, cache.hkv, (nch + 3) / 4), dim3(256), 0, stream, q,
