@@ -36,7 +36,9 @@
 //    ALU): attention of an explicit list of query rows (the last prompt
 //    token of each prompt at layers l+1..L, decode rows; every token for
 //    fp32 models), split over key chunks (64 keys for bf16 rows of head_dim
-//    128, 256 otherwise) with a fixed-order combine.
+//    128, 256 otherwise) with a fixed-order combine.  attn_dec1_kernel does
+//    the same for bf16 rows of contexts up to 1024 keys in one launch, the
+//    chunks of a row and kv head combined inside one workgroup.
 #include <math.h>
 
 #include "common.h"
@@ -1016,23 +1018,27 @@ __global__ __launch_bounds__(DC1_WAVES * 64) void attn_dec1_kernel(const bf16_t*
   for (int h0 = 0; h0 < rep; h0 += RW_HG) {
     const int nh = min(RW_HG, rep - h0);
     if (active) {
-      // scores in two halves of two 16-key passes: K of a half (32
-      // registers) and q slice i of four heads (16 registers, from LDS) at a
-      // time, which keeps the wave within its 128 registers
+      // every K load of the chunk goes out first (64 registers); the scores
+      // then take two 16-key passes and one q slice of four heads (16
+      // registers, from LDS) at a time, which keeps the wave within its 128
+      // registers
       float acc[4][RW_HG];
 #pragma unroll
       for (int p = 0; p < 4; ++p)
 #pragma unroll
         for (int hh = 0; hh < RW_HG; ++hh) acc[p][hh] = 0.f;
+      bf16x8_t kvall[2][2][4];
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        bf16x8_t kv[2][4];
+      for (int half = 0; half < 2; ++half)
 #pragma unroll
         for (int pp = 0; pp < 2; ++pp) {
           const bf16_t* kr = cache.k + kv_index(blk[2 * half + pp] * kBlockSize + kq, g, j * 32, hkv, DH);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) kv[pp][i] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(kr + i * 8));
+          for (int i = 0; i < 4; ++i) kvall[half][pp][i] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(kr + i * 8));
         }
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        bf16x8_t (&kv)[2][4] = kvall[half];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           bf16x8_t qv[RW_HG];
