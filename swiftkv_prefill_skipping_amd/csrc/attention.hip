@@ -966,19 +966,22 @@ __global__ __launch_bounds__(256) void attn_dec_kernel(const bf16_t* __restrict_
   }
 }
 
-// Single-pass form of attn_dec_kernel (bf16 cache) for contexts of at most
+// Single-pass form of attn_dec_kernel for contexts of at most
 // DC1_MAX_KEYS keys: one workgroup per (row, kv head), one wave per 64-key
 // chunk, so the chunks' (max, sum, o) meet in LDS and the workgroup writes
 // the normalised output itself: no workspace, no combine launch.  A wave's
 // chunk work is attn_dec_kernel's (the same loads and arithmetic), except
 // that the head group's q sits in LDS, read by every wave, rather than in
 // each wave's registers: a 16-wave workgroup leaves a wave 128 registers.
-// The chunks are combined in chunk order.
+// The chunks are combined in chunk order.  F8: the codes and scales of the
+// per-token FP8 cache, decoded into the same bf16 operands as in
+// attn_dec_kernel<true>.
 constexpr int DC1_WAVES = 16;
 constexpr int DC1_MAX_KEYS = DC1_WAVES * DC_KEYS;
 constexpr int DC1_MAX_REP = 16;  // a multiple of RW_HG
+template <bool F8>
 __global__ __launch_bounds__(DC1_WAVES * 64) void attn_dec1_kernel(const bf16_t* __restrict__ q,
-                                                                   CacheSlot<bf16_t> cache,
+                                                                   CacheSlot<bf16_t> cache, Fp8Slot c8,
                                                                    const int32_t* __restrict__ row_seq,
                                                                    const int32_t* __restrict__ row_pos,
                                                                    const int32_t* __restrict__ bt, int max_blocks,
@@ -1027,18 +1030,50 @@ __global__ __launch_bounds__(DC1_WAVES * 64) void attn_dec1_kernel(const bf16_t*
       for (int p = 0; p < 4; ++p)
 #pragma unroll
         for (int hh = 0; hh < RW_HG; ++hh) acc[p][hh] = 0.f;
-      bf16x8_t kvall[2][2][4];
+      bf16x8_t kvall[F8 ? 1 : 2][2][4];
+      u32x4_t kc[F8 ? 4 : 1][2];  // F8: 32 codes of the lane's key per pass
+      float ksc[F8 ? 4 : 1];
 #pragma unroll
       for (int half = 0; half < 2; ++half)
 #pragma unroll
         for (int pp = 0; pp < 2; ++pp) {
-          const bf16_t* kr = cache.k + kv_index(blk[2 * half + pp] * kBlockSize + kq, g, j * 32, hkv, DH);
+          const int sl = blk[2 * half + pp] * kBlockSize + kq;
+          if constexpr (F8) {
+            const uint8_t* kr = c8.k + kv_index(sl, g, j * 32, hkv, DH);
+            kc[2 * half + pp][0] = *reinterpret_cast<const u32x4_t*>(kr);
+            kc[2 * half + pp][1] = *reinterpret_cast<const u32x4_t*>(kr + 16);
+            ksc[2 * half + pp] = c8.ks[sl];
+          } else {
+            const bf16_t* kr = cache.k + kv_index(sl, g, j * 32, hkv, DH);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) kvall[half][pp][i] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(kr + i * 8));
+            for (int i = 0; i < 4; ++i) kvall[half][pp][i] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(kr + i * 8));
+          }
         }
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
-        bf16x8_t (&kv)[2][4] = kvall[half];
+        bf16x8_t kv[2][4];
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) {
+          if constexpr (F8) {  // code * the key's scale, as bf16
+            const float s8 = ksc[2 * half + pp];
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+              float x[16];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) decode4_e4m3_hw(kc[2 * half + pp][h2][e], x + 4 * e);
+#pragma unroll
+              for (int i2 = 0; i2 < 2; ++i2) {
+                const float* y = x + 8 * i2;
+                kv[pp][2 * h2 + i2] =
+                    as_bf16x8(u32x4_t{pack_bf16x2(y[0] * s8, y[1] * s8), pack_bf16x2(y[2] * s8, y[3] * s8),
+                                      pack_bf16x2(y[4] * s8, y[5] * s8), pack_bf16x2(y[6] * s8, y[7] * s8)});
+              }
+            }
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) kv[pp][i] = kvall[half][pp][i];
+          }
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           bf16x8_t qv[RW_HG];
@@ -1071,10 +1106,23 @@ __global__ __launch_bounds__(DC1_WAVES * 64) void attn_dec1_kernel(const bf16_t*
         }
       // the first half of the lane's V rows goes out now (the second after
       // the first's products: 32 registers of V at a time)
-      bf16x8_t vv[8];
+      // F8: a key's 8 codes (one dword pair) and its scale, decoded when used
+      bf16x8_t vv[F8 ? 1 : 8];
+      u32x2_t vcode[F8 ? 8 : 1];
+      float vsc[F8 ? 8 : 1];
+      auto load_v = [&](int k0) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        vv[i] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(cache.v + kv_index(vblk * kBlockSize + i, g, vc * 8, hkv, DH)));
+        for (int i = 0; i < 8; ++i) {
+          const int sl = vblk * kBlockSize + k0 + i;
+          if constexpr (F8) {
+            vcode[i] = *reinterpret_cast<const u32x2_t*>(c8.v + kv_index(sl, g, vc * 8, hkv, DH));
+            vsc[i] = c8.vs[sl];
+          } else {
+            vv[i] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(cache.v + kv_index(sl, g, vc * 8, hkv, DH)));
+          }
+        }
+      };
+      load_v(0);
       float mh[RW_HG], lh[RW_HG];
       f32x4_t pe[4];
 #pragma unroll
@@ -1117,18 +1165,23 @@ __global__ __launch_bounds__(DC1_WAVES * 64) void attn_dec1_kernel(const bf16_t*
         for (int e = 0; e < 8; ++e) o[hh][e] = 0.f;
 #pragma unroll
       for (int vh = 0; vh < 2; ++vh) {
-        if (vh == 1) {
-#pragma unroll
-          for (int i = 0; i < 8; ++i)
-            vv[i] = as_bf16x8(
-                *reinterpret_cast<const u32x4_t*>(cache.v + kv_index(vblk * kBlockSize + 8 + i, g, vc * 8, hkv, DH)));
-        }
+        if (vh == 1) load_v(8);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const int key = vh * 8 + i;
           const f32x4_t pk = ps_s[wave][vb * 17 + key];
           const bool live = vb * 16 + key < nk;
-          const u32x4_t raw = __builtin_bit_cast(u32x4_t, vv[i]);
+          u32x4_t raw;
+          if constexpr (F8) {
+            float x[8];
+            decode4_e4m3_hw(vcode[i].x, x);
+            decode4_e4m3_hw(vcode[i].y, x + 4);
+            const float s8 = vsc[i];
+            raw = u32x4_t{pack_bf16x2(x[0] * s8, x[1] * s8), pack_bf16x2(x[2] * s8, x[3] * s8),
+                          pack_bf16x2(x[4] * s8, x[5] * s8), pack_bf16x2(x[6] * s8, x[7] * s8)};
+          } else {
+            raw = __builtin_bit_cast(u32x4_t, vv[i]);
+          }
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const uint32_t w2 = live ? raw[e] : 0u;
@@ -1292,12 +1345,10 @@ hipError_t attn_rows_impl(const T* q, CacheSlot<T> cache, Fp8Slot c8, const int3
   if (rows <= 0) return hipSuccess;
   const float scale = 1.0f / sqrtf((float)cache.dh);
   if constexpr (sizeof(T) == 2) {
-    if constexpr (!F8) {
-      if (cache.dh == 128 && max_ctx <= DC1_MAX_KEYS && hq / cache.hkv <= DC1_MAX_REP) {
-        hipLaunchKernelGGL(attn_dec1_kernel, dim3(rows, cache.hkv), dim3(DC1_WAVES * 64), 0, stream, q, cache,
-                           row_seq, row_pos, block_tables, max_blocks, hq, scale, o);
-        return hipGetLastError();
-      }
+    if (cache.dh == 128 && max_ctx <= DC1_MAX_KEYS && hq / cache.hkv <= DC1_MAX_REP) {
+      hipLaunchKernelGGL((attn_dec1_kernel<F8>), dim3(rows, cache.hkv), dim3(DC1_WAVES * 64), 0, stream, q, cache,
+                         c8, row_seq, row_pos, block_tables, max_blocks, hq, scale, o);
+      return hipGetLastError();
     }
     if (cache.dh == 128) {
       const int nch = (max_ctx + DC_KEYS - 1) / DC_KEYS;
