@@ -39,7 +39,7 @@ cached positions already (a prompt chunk after earlier chunks, a decode
 token); its new tokens run steps 2-3 attending to the cache as well, and its
 last new token runs step 4 and 5.
 
-Readings where the pages are silent (each one is listed in the design doc):
+Readings where the pages are silent:
   * Llama block: pre-norm RMSNorm, GQA attention with RoPE (rotate-half,
     inv_freq_i = theta^(-2i/dh), no frequency scaling), SwiGLU MLP
     W_d(silu(W_g a) * W_u a), no biases, untied LM head.
