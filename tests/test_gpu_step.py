@@ -133,6 +133,17 @@ def test_decode_steps_bf16(l, g):
     run_schedule(w, (205, 134, 69), sched, label=f"decode l={l} g={g}")
 
 
+@pytest.mark.parametrize("hq,hkv", [(8, 2), (8, 1)], ids=["rep4", "rep8"])
+def test_decode_rows_either_side_of_the_single_pass_threshold(hq, hkv):
+    """Decode rows whose contexts reach 1023 and 1024 keys (the longest the single-pass row attention takes) and
+    then 1025 (the chunked kernel and its combine pass), with 4 or 8 query heads per kv head (one or two head
+    groups per workgroup), against the oracle at every call."""
+    w = si.small_workload(f"step_dec1_{hq}_{hkv}", n_layers=3, n_q_heads=hq, n_kv_heads=hkv, l=1, g=1,
+                          lengths=(1025, 300), seed=53)
+    sched = [[(0, 1022), (1, 297)]] + [[(0, 1), (1, 1)]] * 3
+    run_schedule(w, (1025, 300), sched, label=f"single-pass threshold hq={hq} hkv={hkv}")
+
+
 def test_row_path_chunks_and_decode_bf16():
     """Small mixed batches: a 20-token chunk with two decode tokens, a 32-token chunk (the largest row-path batch),
     then 33 tokens (the smallest tiled batch) after a cached prefix."""
