@@ -188,7 +188,7 @@ typedef struct {
  * default stream); the caller synchronises.  Every layer must have been
  * loaded.  Errors (host-side, nothing enqueued): INVALID_ARG for
  * inconsistent cu_seqlens, an empty prompt, total_tokens > max_tokens,
- * batch > max_batch, a prompt longer than max_seqlen, a block table entry
+ * batch < 1 or > max_batch, a prompt longer than max_seqlen, a block table entry
  * outside [0, num_blocks) or too few blocks; HIP on launch failure. */
 skv_status skv_prefill(skv_model* m, skv_kv_cache* c, const skv_batch* batch, float* logits, void* stream);
 

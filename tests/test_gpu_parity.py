@@ -278,6 +278,11 @@ def test_host_side_errors():
                       s.cu_seqlens, s.block_tables)
     with pytest.raises(L.SkvError):                           # batch above max_batch
         L.skv_prefill(model.handle, cache.handle, big, logits.data_ptr(), 0)
+    zero_cu = np.zeros(1, dtype=np.int32)
+    empty = L.skv_batch(0, 0, 0, s.max_blocks_per_seq, zero_cu.ctypes.data, db.bt_host.ctypes.data, s.token_ids,
+                        s.cu_seqlens, s.block_tables)
+    with pytest.raises(L.SkvError):                           # a batch of no prompt
+        L.skv_prefill(model.handle, cache.handle, empty, logits.data_ptr(), 0)
     L.skv_prefill(model.handle, cache.handle, st, logits.data_ptr(), 0)   # the good one still works
 
 
