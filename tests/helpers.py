@@ -1,6 +1,7 @@
 """Shared helpers of the tests: seeded inputs -> oracle inputs, error metrics."""
 from __future__ import annotations
 
+import hashlib
 import json
 import os
 import sys
@@ -51,6 +52,20 @@ def say(*a):
             print(*a, file=sys.stderr, flush=True)
     else:
         print(*a, file=sys.stderr, flush=True)
+
+
+def oracle_code_sha256(source: bytes) -> str:
+    """SHA-256 of a Python module's code: its syntax tree with every docstring removed (comments never reach
+    the tree), so edits to comments and docstrings leave it unchanged."""
+    import ast
+    tree = ast.parse(source)
+    for node in ast.walk(tree):
+        body = getattr(node, "body", None)
+        if (isinstance(node, (ast.Module, ast.FunctionDef, ast.AsyncFunctionDef, ast.ClassDef)) and body
+                and isinstance(body[0], ast.Expr) and isinstance(body[0].value, ast.Constant)
+                and isinstance(body[0].value.value, str)):
+            node.body = body[1:] or [ast.Pass()]
+    return hashlib.sha256(ast.dump(tree, include_attributes=False).encode()).hexdigest()
 
 
 FULLSIZE_DIR = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "fullsize")
