@@ -140,7 +140,16 @@ __global__ __launch_bounds__(256) void rms_from_partials_kernel(const float* __r
   if (r >= rows) return;  // whole waves
   const float* p = ss + (int64_t)r * units;
   float t = 0.f;
-  for (int u = lane; u < units; u += 64) t += p[u];
+  if (units % 256 == 0) {
+    // a lane sums four consecutive partials per 256 (one 16-byte load each,
+    // all issued before the adds), then the wave reduces
+    for (int u0 = 0; u0 < units; u0 += 256) {
+      const f32x4_t v = *reinterpret_cast<const f32x4_t*>(p + u0 + lane * 4);
+      t += (v[0] + v[1]) + (v[2] + v[3]);
+    }
+  } else {
+    for (int u = lane; u < units; u += 64) t += p[u];
+  }
   t = warp_sum(t);
   if (lane == 0) r_out[r] = 1.0f / sqrtf(t / (float)d + eps);
 }
